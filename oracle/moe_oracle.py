@@ -1,0 +1,278 @@
+"""CPU oracle for the single-GPU sparse MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module:
+only the tests, the smoke check and the CPU-baseline leg of the benchmark call
+it.  It shares no code with the HIP library.
+
+Plain NumPy, written from the method's definitions, one function per step:
+
+  * Sparse MoE routing-math page (arman1o1.github.io), section 0, layer-output
+    equation: y_t = h_t + sum_j SwiGLU^S_j(h_t) + sum_{i in TopK} g_{t,i} SwiGLU^R_i(h_t),
+    with SwiGLU(h) = (SiLU(h W_gate) * (h W_up)) W_down.
+  * Same page, section 2, biased selection and unbiased gate:
+    I_t = TopK({s_{t,i} + b_i}, K), g_{t,i} = s_{t,i} / sum_{j in I_t} s_{t,j};
+    bias update b_i <- b_i + gamma * sign(cbar - c_i), c_i = #{t : i in I_t},
+    cbar = K T / E_r.
+  * Same page, section 1 and its classical-router listing: softmax router,
+    top-K of p, renormalised over the picked experts, clamp 1e-12.
+  * Same page, section 4, item 2: router matmul and score function in fp32.
+  * Same page, section 4, item 1: MaxVio = (max_i c_i - cbar) / cbar.
+  * Same page, section 3: sort token copies by expert, run each expert on its
+    rows, weight by the gate, add back.
+
+Precision.  The pages fix the router at fp32: z is the fp64 dot product of
+the exact inputs rounded once to fp32, s = sigma(z) is evaluated in fp64 and
+rounded to fp32, and the selection compares fp32 values v = fl32(s + b).  The
+expert math, the gates and the combine are fp64.  The bias update is one fp32
+add of +-gamma or 0, with the sign decided in integers (K*T vs E_r*c_i).
+
+Readings where the pages are silent (each listed in the design notes):
+  * ties in v: the lower expert index wins;
+  * topk_idx is reported in ascending expert id (a canonical order);
+  * the gate denominator is summed in ascending expert id;
+  * sign(0) = 0, so an expert exactly at the fair share keeps its bias;
+  * inside an expert's segment, rows are in ascending token order;
+  * for softmax + bias (no workload uses it) the bias is added to p.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+GATE_CLAMP = 1e-12
+
+
+# ---------------------------------------------------------------- inputs
+
+def to_f64(x: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of a bf16 (uint16 bit patterns) or fp32 array."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if x.dtype == np.float32 or x.dtype == np.float64:
+        return x.astype(np.float64)
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+# ---------------------------------------------------------------- router
+
+def router_logits(h: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """z_{t,i} = h_t . e_i, fp64 accumulation rounded once to fp32.  [T, E_r]"""
+    return (to_f64(h) @ to_f64(e).T).astype(np.float32)
+
+
+def sigmoid_scores(z: np.ndarray) -> np.ndarray:
+    """s = 1 / (1 + exp(-z)), evaluated in fp64, rounded to fp32."""
+    z64 = z.astype(np.float64)
+    return (1.0 / (1.0 + np.exp(-z64))).astype(np.float32)
+
+
+def softmax_scores(z: np.ndarray) -> np.ndarray:
+    """p = exp(z - max z) / sum exp(z - max z) over all E_r, fp64, rounded to fp32."""
+    z64 = z.astype(np.float64)
+    ez = np.exp(z64 - z64.max(axis=-1, keepdims=True))
+    return (ez / ez.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def scores(z: np.ndarray, fn: str) -> np.ndarray:
+    if fn == "sigmoid":
+        return sigmoid_scores(z)
+    if fn == "softmax":
+        return softmax_scores(z)
+    raise ValueError(fn)
+
+
+def biased_values(s: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """v = fl32(s + b): the values the selection ranks (b absent -> v = s)."""
+    if b is None:
+        return s.astype(np.float32)
+    return (s.astype(np.float32) + b.astype(np.float32)[None, :]).astype(np.float32)
+
+
+def biased_topk(s: np.ndarray, b: Optional[np.ndarray], K: int) -> np.ndarray:
+    """I_t = the K largest v_{t,i}; equal v -> lower i first.
+
+    Returned as int32 [T, K] in ascending expert id.
+    """
+    v = biased_values(s, b)
+    order = np.argsort(-v, axis=-1, kind="stable")  # descending v, ties by lower index
+    return np.sort(order[:, :K], axis=-1).astype(np.int32)
+
+
+def topk_margin(s: np.ndarray, b: Optional[np.ndarray], K: int) -> np.ndarray:
+    """v_(K) - v_(K+1) per token (inf when K == E_r): small margins are near-ties."""
+    v = biased_values(s, b).astype(np.float64)
+    if K >= v.shape[1]:
+        return np.full(v.shape[0], np.inf)
+    srt = -np.sort(-v, axis=-1)
+    return srt[:, K - 1] - srt[:, K]
+
+
+def gates(s: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """g_{t,k} = s_{t,idx[t,k]} / max(sum over the picked experts, 1e-12), fp32 out.
+
+    The denominator is accumulated over the picked experts in ascending id.
+    """
+    picked = np.take_along_axis(s.astype(np.float64), idx.astype(np.int64), axis=-1)
+    den = np.zeros(picked.shape[0], dtype=np.float64)
+    for k in range(picked.shape[1]):
+        den = den + picked[:, k]
+    den = np.maximum(den, GATE_CLAMP)
+    return (picked / den[:, None]).astype(np.float32)
+
+
+def load_count(idx: np.ndarray, E_r: int) -> np.ndarray:
+    """c_i = #{t : i in I_t} as int32 [E_r]."""
+    return np.bincount(idx.reshape(-1).astype(np.int64), minlength=E_r).astype(np.int32)
+
+
+def route(h, e, b, K: int, fn: str):
+    """Router + biased top-K + unbiased gates + load count (one layer call)."""
+    z = router_logits(h, e)
+    s = scores(z, fn)
+    idx = biased_topk(s, b, K)
+    g = gates(s, idx)
+    c = load_count(idx, e.shape[0])
+    return dict(z=z, s=s, idx=idx, gates=g, loads=c)
+
+
+# ---------------------------------------------------------------- dispatch
+
+def permute(idx: np.ndarray, E_r: int):
+    """Expert-sorted order of the T*K token copies.
+
+    offsets[E_r + 1]: exclusive scan of the loads; inside expert i's segment the
+    rows are in ascending token order.  row_token[r] is the source token of
+    permuted row r; slot_row[t*K + k] is the permuted row of copy (t, k).
+    """
+    T, K = idx.shape
+    c = load_count(idx, E_r)
+    offsets = np.zeros(E_r + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(c)
+    flat_e = idx.reshape(-1).astype(np.int64)
+    flat_t = np.repeat(np.arange(T, dtype=np.int64), K)
+    order = np.lexsort((flat_t, flat_e))          # by expert, then by token
+    row_token = flat_t[order]
+    slot_row = np.empty(T * K, dtype=np.int64)
+    slot_row[order] = np.arange(T * K, dtype=np.int64)
+    return offsets.astype(np.int32), row_token.astype(np.int32), slot_row.astype(np.int32)
+
+
+# ---------------------------------------------------------------- experts
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU(x) = x * sigma(x)."""
+    return x / (1.0 + np.exp(-x))
+
+
+def swiglu(x, w_gate, w_up, w_down) -> np.ndarray:
+    """(SiLU(x W_gate^T) * (x W_up^T)) W_down^T in fp64; weights in [out, in] layout."""
+    x64 = to_f64(x) if x.dtype != np.float64 else x
+    a = x64 @ to_f64(w_gate).T
+    u = x64 @ to_f64(w_up).T
+    return (silu(a) * u) @ to_f64(w_down).T
+
+
+ExpertSource = Union[Sequence, Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]]
+
+
+def _expert(weights: ExpertSource, i: int):
+    if callable(weights):
+        return weights(i)
+    wg, wu, wd = weights
+    return wg[i], wu[i], wd[i]
+
+
+def grouped_swiglu(x: np.ndarray, offsets: np.ndarray, row_index: Optional[np.ndarray],
+                   weights: ExpertSource, groups: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Run expert g on rows offsets[g]:offsets[g+1] of the grouped input.
+
+    Grouped row r reads x[row_index[r]] (or x[r] when row_index is None).
+    Returns fp64 [rows, d_model]; rows of groups not listed in `groups` stay 0.
+    """
+    rows = int(offsets[-1])
+    x64 = to_f64(x)
+    src = np.arange(rows) if row_index is None else row_index.astype(np.int64)
+    out = np.zeros((rows, x64.shape[1]), dtype=np.float64)
+    n_groups = len(offsets) - 1
+    for gi in (range(n_groups) if groups is None else groups):
+        lo, hi = int(offsets[gi]), int(offsets[gi + 1])
+        if hi == lo:
+            continue
+        wg, wu, wd = _expert(weights, gi)
+        out[lo:hi] = swiglu(x64[src[lo:hi]], wg, wu, wd)
+    return out
+
+
+def shared_experts(h: np.ndarray, weights: Optional[ExpertSource], E_s: int) -> np.ndarray:
+    """Sum over the always-active experts (gate 1) on every token, fp64 [T, d]."""
+    h64 = to_f64(h)
+    out = np.zeros_like(h64)
+    for j in range(E_s):
+        wg, wu, wd = _expert(weights, j)
+        out += swiglu(h64, wg, wu, wd)
+    return out
+
+
+# ---------------------------------------------------------------- combine
+
+def combine(h: np.ndarray, y_shared: Optional[np.ndarray], y_perm: np.ndarray,
+            slot_row: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """y_t = h_t + y_shared_t + sum_k g_{t,k} * y_perm[slot_row[t,k]], fp64."""
+    h64 = to_f64(h)
+    T = h64.shape[0]
+    K = g.shape[1]
+    y = h64.copy()
+    if y_shared is not None:
+        y += y_shared
+    sr = slot_row.reshape(T, K).astype(np.int64)
+    for k in range(K):
+        y += g[:, k:k + 1].astype(np.float64) * y_perm[sr[:, k]]
+    return y
+
+
+# ---------------------------------------------------------------- bias update
+
+def bias_update(b: np.ndarray, loads: np.ndarray, T: int, K: int, gamma: float) -> np.ndarray:
+    """b_i <- fl32(b_i + gamma * sign(cbar - c_i)), cbar = K T / E_r.
+
+    sign(cbar - c_i) = sign(K*T - E_r*c_i) is decided in integers.
+    """
+    E_r = loads.shape[0]
+    diff = np.int64(K) * np.int64(T) - np.int64(E_r) * loads.astype(np.int64)
+    sgn = np.sign(diff).astype(np.float32)
+    return (b.astype(np.float32) + np.float32(gamma) * sgn).astype(np.float32)
+
+
+def max_vio(loads: np.ndarray, T: int, K: int) -> float:
+    """MaxVio = (max_i c_i - cbar) / cbar."""
+    cbar = K * T / loads.shape[0]
+    return (float(loads.max()) - cbar) / cbar
+
+
+def load_stats(loads: np.ndarray, T: int, K: int):
+    return dict(max_load=int(loads.max()), min_load=int(loads.min()),
+                max_vio=max_vio(loads, T, K))
+
+
+# ---------------------------------------------------------------- layer
+
+def layer_forward(h, e, b, K: int, fn: str, routed: ExpertSource,
+                  shared: Optional[ExpertSource] = None, E_s: int = 0,
+                  gamma: Optional[float] = None):
+    """One full layer call: route, dispatch, routed + shared experts, combine,
+    and (when gamma is given) the per-step bias update after counting."""
+    E_r = e.shape[0]
+    T = h.shape[0]
+    r = route(h, e, b, K, fn)
+    offsets, row_token, slot_row = permute(r["idx"], E_r)
+    y_perm = grouped_swiglu(h, offsets, row_token, routed)
+    y_sh = shared_experts(h, shared, E_s) if E_s else None
+    y = combine(h, y_sh, y_perm, slot_row, r["gates"])
+    out = dict(r, offsets=offsets, row_token=row_token, slot_row=slot_row,
+               y_perm=y_perm, y_shared=y_sh, y=y)
+    if gamma is not None:
+        b0 = b if b is not None else np.zeros(E_r, dtype=np.float32)
+        out["b_new"] = bias_update(b0, r["loads"], T, K, gamma)
+        out["stats"] = load_stats(r["loads"], T, K)
+    return out

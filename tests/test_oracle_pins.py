@@ -1,0 +1,425 @@
+"""Pins of the CPU oracle to facts fixed outside it (CPU only).
+
+Each test ties one oracle function to a worked example printed on the pages, a
+closed form, a library routine, brute force on tiny inputs, or an invariant
+of the method, so that a dropped term, a flipped sign, a wrong index or a
+transposed operand fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ sigmoid
+
+def test_sigmoid_worked_example():
+    ex = _load("sigmoid_worked_example.json")
+    z = np.array([ex["logits"]], dtype=np.float32)
+    s = O.sigmoid_scores(z)[0]
+    assert np.allclose(np.round(s.astype(np.float64), 2), ex["scores_2dp"], atol=0, rtol=0)
+
+
+def test_router_logits_not_transposed():
+    # h . e_i with e a 4-cycle permutation matrix: z_i = h_{pi(i)}; the
+    # transposed product would apply the inverse cycle.
+    ex = _load("sigmoid_worked_example.json")
+    h = np.array([ex["logits"]], dtype=np.float32)
+    perm = [1, 2, 3, 0]
+    e = np.zeros((4, 4), dtype=np.float32)
+    for i, j in enumerate(perm):
+        e[i, j] = 1.0
+    z = O.router_logits(h, e)[0]
+    assert np.array_equal(z, h[0, perm])
+    s = O.sigmoid_scores(z[None, :])[0]
+    assert np.allclose(np.round(s.astype(np.float64), 2), np.array(ex["scores_2dp"])[perm])
+
+
+def test_router_logits_correctly_rounded():
+    rng = np.random.default_rng(1)
+    h = rng.standard_normal((5, 37)).astype(np.float32)
+    e = rng.standard_normal((6, 37)).astype(np.float32)
+    z = O.router_logits(h, e)
+    for t in range(5):
+        for i in range(6):
+            exact = math.fsum(float(a) * float(b) for a, b in zip(h[t], e[i]))
+            assert z[t, i] == np.float32(exact)
+
+
+def test_router_logits_bf16_inputs_exact():
+    # bf16 bit patterns widen exactly: 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25
+    h = np.array([[0x3F80, 0xC000, 0x3E80]], dtype=np.uint16)
+    e = np.array([[1.0, 1.0, 4.0], [0.5, 0.0, 0.0]], dtype=np.float32)
+    z = O.router_logits(h, e)
+    assert z.tolist() == [[0.0, 0.5]]
+
+
+def test_sigmoid_matches_library():
+    z = np.linspace(-30, 30, 2001).astype(np.float32)[None, :]
+    s = O.sigmoid_scores(z)
+    ref = scipy.special.expit(z.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(s, ref)
+
+
+def test_softmax_matches_library():
+    rng = np.random.default_rng(2)
+    z = (rng.standard_normal((16, 8)) * 3).astype(np.float32)
+    p = O.softmax_scores(z)
+    ref = scipy.special.softmax(z.astype(np.float64), axis=-1)
+    assert np.max(np.abs(p - ref)) < 1e-7
+
+
+# ------------------------------------------------------------------ top-K
+
+def _brute_topk(v_row, K):
+    """Lexicographically first K-subset of maximum exact sum."""
+    best, best_sum = None, None
+    for sub in itertools.combinations(range(len(v_row)), K):
+        tot = sum(float(v_row[i]) for i in sub)  # dyadic inputs: exact
+        if best_sum is None or tot > best_sum:
+            best, best_sum = sub, tot
+    return list(best)
+
+
+@pytest.mark.parametrize("E,K", [(4, 1), (5, 2), (8, 2), (8, 3), (10, 3)])
+def test_topk_brute_force(E, K):
+    rng = np.random.default_rng(E * 10 + K)
+    for trial in range(40):
+        T = 6
+        # dyadic values on a coarse grid so ties are frequent and every sum is exact
+        s = (rng.integers(0, 16, size=(T, E)) / 16.0).astype(np.float32)
+        b = (rng.integers(-4, 5, size=E) / 64.0).astype(np.float32)
+        idx = O.biased_topk(s, b, K)
+        v = O.biased_values(s, b)
+        for t in range(T):
+            assert idx[t].tolist() == _brute_topk(v[t], K)
+
+
+def test_topk_ignores_constant_bias_shift():
+    rng = np.random.default_rng(3)
+    s = (rng.integers(0, 256, size=(64, 16)) / 256.0).astype(np.float32)
+    b = (rng.integers(-8, 9, size=16) / 256.0).astype(np.float32)
+    idx0 = O.biased_topk(s, b, 4)
+    idx1 = O.biased_topk(s, b + np.float32(0.0625), 4)
+    assert np.array_equal(idx0, idx1)
+
+
+def test_topk_all_experts_when_K_equals_E():
+    rng = np.random.default_rng(4)
+    s = rng.random((10, 6)).astype(np.float32)
+    idx = O.biased_topk(s, None, 6)
+    assert np.array_equal(idx, np.tile(np.arange(6), (10, 1)))
+
+
+def test_topk_bias_changes_pick():
+    # The bias moves the pick; without it the top-1 is the largest score.
+    s = np.array([[0.77, 0.73, 0.45, 0.50]], dtype=np.float32)
+    assert O.biased_topk(s, None, 1).tolist() == [[0]]
+    b = np.array([-0.1, 0.1, 0.1, 0.0], dtype=np.float32)
+    assert O.biased_topk(s, b, 1).tolist() == [[1]]
+
+
+def test_router_permutation_equivariant():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((32, 24)).astype(np.float32)
+    e = rng.standard_normal((12, 24)).astype(np.float32)
+    b = (rng.random(12) * 0.02 - 0.01).astype(np.float32)
+    perm = rng.permutation(32)
+    r0 = O.route(h, e, b, 3, "sigmoid")
+    r1 = O.route(h[perm], e, b, 3, "sigmoid")
+    assert np.array_equal(r1["idx"], r0["idx"][perm])
+    assert np.array_equal(r1["gates"], r0["gates"][perm])
+    assert np.array_equal(np.sort(r1["loads"]), np.sort(r0["loads"]))
+    assert np.array_equal(r1["loads"], r0["loads"])
+
+
+# ------------------------------------------------------------------ gates
+
+def test_gates_sum_to_one_and_use_unbiased_scores():
+    rng = np.random.default_rng(6)
+    for K in (1, 2, 8):
+        s = rng.random((200, 32)).astype(np.float32)
+        b = (rng.random(32) * 0.2 - 0.1).astype(np.float32)
+        idx = O.biased_topk(s, b, K)
+        g = O.gates(s, idx)
+        assert np.all(np.abs(g.astype(np.float64).sum(-1) - 1.0) <= 4 * K * 2.0 ** -24)
+        # proportional to the unbiased s of the picked experts
+        picked = np.take_along_axis(s, idx, axis=-1).astype(np.float64)
+        ratio = g.astype(np.float64) / picked
+        assert np.allclose(ratio, ratio[:, :1], rtol=1e-6)
+
+
+def test_gates_bit_identical_when_selection_unchanged():
+    rng = np.random.default_rng(7)
+    s = rng.random((500, 16)).astype(np.float32)
+    b0 = (rng.random(16) * 0.02 - 0.01).astype(np.float32)
+    b1 = b0 + (rng.random(16) * 0.002 - 0.001).astype(np.float32)
+    i0 = O.biased_topk(s, b0, 4)
+    i1 = O.biased_topk(s, b1, 4)
+    same = np.all(i0 == i1, axis=-1)
+    assert same.sum() > 400 and (~same).sum() > 0
+    g0 = O.gates(s, i0)
+    g1 = O.gates(s, i1)
+    assert np.array_equal(g0[same].view(np.uint32), g1[same].view(np.uint32))
+
+
+def test_gate_clamp_for_zero_scores():
+    s = np.zeros((2, 4), dtype=np.float32)
+    idx = O.biased_topk(s, None, 2)
+    assert idx.tolist() == [[0, 1], [0, 1]]
+    assert np.all(O.gates(s, idx) == 0.0)
+
+
+def test_softmax_gates_K_equals_E_is_plain_softmax():
+    rng = np.random.default_rng(8)
+    z = (rng.standard_normal((20, 8)) * 2).astype(np.float32)
+    p = O.softmax_scores(z)
+    idx = O.biased_topk(p, None, 8)
+    g = O.gates(p, idx)
+    assert np.max(np.abs(g - scipy.special.softmax(z.astype(np.float64), axis=-1))) < 2e-7
+
+
+# ------------------------------------------------------------------ loads / permute
+
+def test_loads_and_permutation_invariants():
+    rng = np.random.default_rng(9)
+    T, E, K = 300, 16, 4
+    s = rng.random((T, E)).astype(np.float32)
+    idx = O.biased_topk(s, None, K)
+    c = O.load_count(idx, E)
+    assert c.sum() == T * K
+    for i in range(E):
+        assert c[i] == sum(1 for t in range(T) if i in idx[t])
+    off, row_token, slot_row = O.permute(idx, E)
+    assert off[0] == 0 and off[-1] == T * K and np.array_equal(np.diff(off), c)
+    # inverse maps
+    flat_t = np.repeat(np.arange(T), K)
+    assert np.array_equal(row_token[slot_row], flat_t)
+    # each copy lands in its expert's segment, ascending token order inside it
+    flat_e = idx.reshape(-1)
+    for r_slot, e_id in zip(slot_row, flat_e):
+        assert off[e_id] <= r_slot < off[e_id + 1]
+    for i in range(E):
+        seg = row_token[off[i]:off[i + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_total_collapse():
+    T, E, K = 50, 8, 2
+    s = np.tile(np.linspace(0.1, 0.9, E, dtype=np.float32), (T, 1))
+    idx = O.biased_topk(s, None, K)
+    c = O.load_count(idx, E)
+    assert c.tolist() == [0] * 6 + [T, T]
+    off, row_token, slot_row = O.permute(idx, E)
+    assert off.tolist() == [0] * 7 + [T, 2 * T]
+    assert row_token.tolist() == list(range(T)) * 2
+
+
+# ------------------------------------------------------------------ bias update
+
+def test_bias_update_worked_example():
+    ex = _load("bias_update_example.json")
+    loads = np.array(ex["loads"], dtype=np.int32)
+    assert loads.sum() == ex["T"] * ex["K"]
+    assert O.max_vio(loads, ex["T"], ex["K"]) == pytest.approx(ex["max_vio"], abs=1e-12)
+    b1 = O.bias_update(np.array(ex["b0"], dtype=np.float32), loads, ex["T"], ex["K"], ex["gamma"])
+    assert np.array_equal(b1, np.array(ex["b1"], dtype=np.float32))
+
+
+def test_bias_update_worked_example_from_routing():
+    # Four tokens whose top-1 lands on E1, E1, E1, E4 give the example's loads.
+    ex = _load("bias_update_example.json")
+    s = np.array([[0.77, 0.73, 0.45, 0.50],
+                  [0.90, 0.10, 0.20, 0.30],
+                  [0.80, 0.70, 0.60, 0.50],
+                  [0.10, 0.20, 0.30, 0.40]], dtype=np.float32)
+    idx = O.biased_topk(s, np.zeros(4, np.float32), 1)
+    c = O.load_count(idx, 4)
+    assert c.tolist() == ex["loads"]
+    b1 = O.bias_update(np.zeros(4, np.float32), c, 4, 1, ex["gamma"])
+    assert np.array_equal(b1, np.array(ex["b1"], dtype=np.float32))
+
+
+def test_bias_update_fixed_points():
+    loads = np.array([16, 16, 16, 16], dtype=np.int32)   # every c_i equals cbar = 16
+    b = np.array([0.5, -0.25, 0.0, 1e-3], dtype=np.float32)
+    assert np.array_equal(O.bias_update(b, loads, 32, 2, 0.1), b)
+    loads2 = np.array([40, 0, 20, 4], dtype=np.int32)
+    assert np.array_equal(O.bias_update(b, loads2, 32, 2, 0.0), b)
+
+
+def test_bias_update_integer_sign_non_integer_fair_share():
+    # cbar = K*T/E = 3*5/4 = 3.75 is not an integer: c=3 -> +gamma, c=4 -> -gamma
+    loads = np.array([3, 4, 4, 4], dtype=np.int32)
+    b1 = O.bias_update(np.zeros(4, np.float32), loads, 5, 3, 0.5)
+    assert b1.tolist() == [0.5, -0.5, -0.5, -0.5]
+
+
+def test_bias_trajectory_resumable():
+    rng = np.random.default_rng(10)
+    E, d, K, T = 8, 16, 2, 64
+    e = rng.standard_normal((E, d)).astype(np.float32)
+    e[0] += 0.75
+    batches = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(12)]
+
+    def run(b, steps):
+        for h in steps:
+            r = O.route(h, e, b, K, "sigmoid")
+            b = O.bias_update(b, r["loads"], T, K, 0.01)
+        return b
+
+    b_full = run(np.zeros(E, np.float32), batches)
+    b_half = run(np.zeros(E, np.float32), batches[:5])
+    b_resumed = run(b_half.copy(), batches[5:])
+    assert np.array_equal(b_full.view(np.uint32), b_resumed.view(np.uint32))
+
+
+def test_bias_balances_skewed_router():
+    """The routing-math page's verification structure (section 5), our own RNG:
+    T=512, d=64, E=8, K=2, gamma=0.02, centroid rows 0/1 shifted by 0.75/0.5,
+    60 fresh batches.  The page checks one step of one seed; with another RNG a
+    single step's max load ratio c/cbar is noisy (the skewed expert's scores are
+    nearly 0 or 1, so its load reacts steeply to the bias), so here, for each of
+    8 seeds, the max load ratio averaged over the last 10 steps must be below
+    1.30 and below the starting ratio."""
+    for seed in range(8):
+        rng = np.random.default_rng(seed)
+        T, d, E, K, gamma = 512, 64, 8, 2, 0.02
+        e = (rng.uniform(-1, 1, size=(E, d)) / math.sqrt(d)).astype(np.float32)
+        e[0] += np.float32(0.75)
+        e[1] += np.float32(0.50)
+        b = np.zeros(E, np.float32)
+        h0 = rng.standard_normal((T, d)).astype(np.float32)
+        initial = O.route(h0, e, b, K, "sigmoid")["loads"].max() / (K * T / E)
+        ratios = []
+        for _ in range(60):
+            r = O.route(rng.standard_normal((T, d)).astype(np.float32), e, b, K, "sigmoid")
+            b = O.bias_update(b, r["loads"], T, K, gamma)
+            ratios.append(r["loads"].max() / (K * T / E))
+        late = float(np.mean(ratios[-10:]))
+        assert initial > 1.5
+        assert late < 1.30 and late < initial
+
+
+# ------------------------------------------------------------------ experts / layer
+
+def test_swiglu_worked_example():
+    ex = _load("swiglu_worked_example.json")
+    ln3 = math.log(3.0)
+
+    def val(v):
+        return {"ln3": ln3, "-ln3": -ln3}.get(v, v) if isinstance(v, str) else v
+
+    wg = np.array([[val(v) for v in row] for row in ex["w_gate"]], dtype=np.float64)
+    wu = np.array(ex["w_up"], dtype=np.float64)
+    wd = np.array(ex["w_down"], dtype=np.float64)
+    x = np.array([ex["x"]], dtype=np.float64)
+    y = O.swiglu(x, wg, wu, wd)[0]
+    assert np.allclose(y, np.array(ex["y_in_units_of_ln3"]) * ln3, rtol=1e-14, atol=0)
+
+
+def test_silu_closed_forms():
+    x = np.array([0.0, math.log(3.0), -math.log(3.0), 50.0, -50.0])
+    ref = np.array([0.0, 0.75 * math.log(3.0), -0.25 * math.log(3.0), 50.0, 0.0])
+    assert np.allclose(O.silu(x), ref, rtol=1e-15, atol=1e-18)
+
+
+def _small_layer(rng, T, d, f, E, E_s, dtype=np.float32):
+    h = rng.standard_normal((T, d)).astype(dtype)
+    e = (rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    w = (
+        (rng.standard_normal((E, f, d)) / math.sqrt(d)).astype(dtype),
+        (rng.standard_normal((E, f, d)) / math.sqrt(d)).astype(dtype),
+        (rng.standard_normal((E, d, f)) / math.sqrt(f)).astype(dtype),
+    )
+    ws = (
+        (rng.standard_normal((E_s, f, d)) / math.sqrt(d)).astype(dtype),
+        (rng.standard_normal((E_s, f, d)) / math.sqrt(d)).astype(dtype),
+        (rng.standard_normal((E_s, d, f)) / math.sqrt(f)).astype(dtype),
+    ) if E_s else None
+    return h, e, w, ws
+
+
+def test_layer_reduces_to_dense_ffn():
+    # E_r = 1, K = 1, no shared expert: the gate is s/s = 1, so y = h + SwiGLU(h).
+    rng = np.random.default_rng(11)
+    h, e, w, _ = _small_layer(rng, 20, 12, 10, 1, 0)
+    out = O.layer_forward(h, e, None, 1, "sigmoid", w)
+    assert np.all(out["gates"] == 1.0)
+    dense = h.astype(np.float64) + O.swiglu(h, w[0][0], w[1][0], w[2][0])
+    assert np.allclose(out["y"], dense, rtol=0, atol=1e-12)
+
+
+def test_layer_identical_experts_any_routing():
+    # All routed experts equal: sum_k g_k = 1 makes y = h + shared + SwiGLU(h).
+    rng = np.random.default_rng(12)
+    T, d, f, E, K = 40, 16, 24, 6, 3
+    h, e, w, ws = _small_layer(rng, T, d, f, E, 1)
+    w = tuple(np.repeat(m[:1], E, axis=0) for m in w)
+    b = (rng.random(E) * 0.1).astype(np.float32)
+    out = O.layer_forward(h, e, b, K, "sigmoid", w, ws, 1)
+    routed = O.swiglu(h, w[0][0], w[1][0], w[2][0])
+    ref = h.astype(np.float64) + O.swiglu(h, ws[0][0], ws[1][0], ws[2][0]) + routed
+    # the fp32 gates sum to 1 within 4*K*2^-24
+    tol = 4 * K * 2.0 ** -24 * np.abs(routed).max() + 1e-12
+    assert np.allclose(out["y"], ref, rtol=0, atol=tol)
+
+
+def test_layer_gate_expert_pairing():
+    # Expert i = expert 0 with W_down scaled by (i + 1): y - h = SwiGLU_0(h) * sum_k g_k (idx_k + 1).
+    rng = np.random.default_rng(13)
+    T, d, f, E, K = 30, 8, 12, 5, 2
+    h, e, w, _ = _small_layer(rng, T, d, f, E, 0)
+    wg = np.repeat(w[0][:1], E, axis=0)
+    wu = np.repeat(w[1][:1], E, axis=0)
+    wd = np.stack([w[2][0].astype(np.float64) * (i + 1) for i in range(E)])
+    out = O.layer_forward(h, e, None, K, "sigmoid", (wg, wu, wd))
+    base = O.swiglu(h, wg[0], wu[0], wd[0])
+    scale = (out["gates"].astype(np.float64) * (out["idx"] + 1)).sum(-1)
+    assert np.allclose(out["y"] - h.astype(np.float64), base * scale[:, None], rtol=0, atol=1e-12)
+
+
+def test_layer_zero_down_projection_is_identity():
+    rng = np.random.default_rng(14)
+    h, e, w, ws = _small_layer(rng, 16, 8, 8, 4, 1)
+    w = (w[0], w[1], np.zeros_like(w[2]))
+    ws = (ws[0], ws[1], np.zeros_like(ws[2]))
+    out = O.layer_forward(h, e, None, 2, "sigmoid", w, ws, 1)
+    assert np.array_equal(out["y"], h.astype(np.float64))
+
+
+def test_layer_down_projection_linearity():
+    rng = np.random.default_rng(15)
+    h, e, w, ws = _small_layer(rng, 16, 8, 8, 4, 1)
+    y1 = O.layer_forward(h, e, None, 2, "softmax", w, ws, 1)["y"]
+    w2 = (w[0], w[1], w[2] * np.float32(2))
+    ws2 = (ws[0], ws[1], ws[2] * np.float32(2))
+    y2 = O.layer_forward(h, e, None, 2, "softmax", w2, ws2, 1)["y"]
+    h64 = h.astype(np.float64)
+    assert np.allclose(y2 - h64, 2 * (y1 - h64), rtol=0, atol=1e-12)
+
+
+def test_grouped_swiglu_is_per_expert_dense():
+    rng = np.random.default_rng(16)
+    T, d, f, E, K = 24, 8, 16, 4, 2
+    h, e, w, _ = _small_layer(rng, T, d, f, E, 0)
+    r = O.route(h, e, None, K, "sigmoid")
+    off, row_token, _ = O.permute(r["idx"], E)
+    y = O.grouped_swiglu(h, off, row_token, w)
+    for i in range(E):
+        rows = [t for t in range(T) if i in r["idx"][t]]
+        ref = O.swiglu(h[rows], w[0][i], w[1][i], w[2][i])
+        assert np.allclose(y[off[i]:off[i + 1]], ref, rtol=0, atol=1e-13)
