@@ -1,0 +1,221 @@
+"""Throughput of one sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dsv3_prefill]
+
+One step = the whole layer on one batch: route (fp32 router, biased top-K,
+gates, loads) -> permute -> grouped SwiGLU over the routed experts -> shared
+expert -> combine -> bias update (gamma = 0.001).  Inputs are seeded synthetic
+tensors already resident in HBM; the token batch rotates over several copies so
+the 256 MB Infinity Cache cannot serve them from one step to the next (the
+22.6 GB of weights never fit anyway).  Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s at DeepSeek-V3 shape (1 GPU); % bf16 MFMA peak / % HBM BW"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def algorithmic(cfg, n_touched, n_touched_shared):
+    """Algorithmic bytes / flops of the gate/up launch and of the whole layer.
+
+    Per touched routed or shared expert: W_gate + W_up = 2 * d * f bf16 words
+    (gate/up launch) and W_down = d * f words (down launch).  Per token: h read
+    once (d words) and y written once (d words).  Per assignment row: the
+    activation (f words) written by gate/up.  Expert flops: 6 d f per row
+    (2 d f each for gate, up and down), rows = T*K routed + T*E_s shared.
+    """
+    d, f, T, K = cfg.d_model, cfg.d_ffn, cfg.T, cfg.K
+    eb = 2 if cfg.dtype == "bf16" else 4
+    gateup_bytes = n_touched * 2 * d * f * eb + T * d * eb + T * K * f * eb
+    gateup_flops = 4.0 * d * f * T * K
+    layer_bytes = (n_touched + n_touched_shared) * 3 * d * f * eb + 2 * T * d * eb
+    layer_flops = 6.0 * d * f * T * (K + cfg.E_s) + 2.0 * T * d * cfg.E_r
+    return gateup_bytes, gateup_flops, layer_bytes, layer_flops
+
+
+def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256):
+    """Time the oracle on a bounded sample of the same workload on host cores.
+
+    Sample: routing of all T tokens; the routed experts 0..sample_experts-1 on
+    all their rows; the shared expert on sample_shared tokens; the full combine
+    and bias update.  Expert time is scaled by E_r / sample_experts and the
+    shared-expert time by T / sample_shared to a whole-layer estimate.
+    """
+    import numpy as np
+
+    from oracle import moe_oracle as O
+    from synthetic import host_array
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+        threads = max([n for _, n in blas if n] or [1])
+    except Exception:  # threadpoolctl missing
+        blas, threads = [], len(os.sched_getaffinity(0))
+    h = host_array(lay.h)
+    e = host_array(lay.e)
+    w = {i: (host_array(lay.w_gate[i]), host_array(lay.w_up[i]), host_array(lay.w_down[i]))
+         for i in range(sample_experts)}
+    ws = (host_array(lay.ws_gate[0]), host_array(lay.ws_up[0]), host_array(lay.ws_down[0])) \
+        if cfg.E_s else None
+
+    t0 = time.perf_counter()
+    r = O.route(h, e, b_host, cfg.K, cfg.score)
+    off, rt, sr = O.permute(r["idx"], cfg.E_r)
+    t_route = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    y_perm = O.grouped_swiglu(h, off, rt, lambda i: w[i], groups=range(sample_experts))
+    t_exp = time.perf_counter() - t0
+    rows = int(off[sample_experts])
+
+    t_sh = 0.0
+    if ws is not None:
+        t0 = time.perf_counter()
+        O.swiglu(h[:sample_shared], *ws)
+        t_sh = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
+    O.combine(h, None, y_perm, sr, r["gates"])
+    O.bias_update(b_host if b_host is not None else np.zeros(cfg.E_r, np.float32), r["loads"],
+                  cfg.T, cfg.K, 0.001)
+    t_comb = time.perf_counter() - t0
+
+    est = t_route + t_exp * cfg.E_r / sample_experts + t_comb
+    if ws is not None:
+        est += t_sh * cfg.T / sample_shared
+    measured = t_route + t_exp + t_sh + t_comb
+    log(f"cpu oracle: route {t_route:.2f}s, {sample_experts} experts ({rows} rows) {t_exp:.2f}s,"
+        f" shared on {sample_shared} tokens {t_sh:.2f}s, combine {t_comb:.2f}s -> layer est "
+        f"{est:.1f}s")
+    return dict(
+        value=cfg.T / est, unit="tokens/s", cores=int(threads), kind="oracle",
+        sample=(f"oracle (NumPy fp64, BLAS {blas}) on: routing of all {cfg.T} tokens, routed "
+                f"experts 0-{sample_experts - 1} of {cfg.E_r} on their {rows} rows, shared "
+                f"expert on {sample_shared} of {cfg.T} tokens, full combine + bias update; "
+                f"expert time x{cfg.E_r / sample_experts:g}, shared time "
+                f"x{cfg.T / sample_shared:g} -> whole-layer estimate {est:.2f} s "
+                f"({measured:.2f} s measured)"),
+    )
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--rotate", type=int, default=10, help="token batches cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("bench.py measures the single-GPU layer forward only: this build has no "
+            "multi-GPU path (expert parallelism is out of scope). Run with --gpus 1.")
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_biased_amd import (LayerShape, MoELayer, load,
+                                                   moe_profile_enable, moe_profile_report)
+    from synthetic import CONFIGS, host_array, make_layer, make_tokens
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    load()
+    cfg = CONFIGS[args.workload]
+    log(f"workload {cfg.name}: T={cfg.T} d_model={cfg.d_model} E_r={cfg.E_r} K={cfg.K} "
+        f"E_s={cfg.E_s} d_ffn={cfg.d_ffn} {cfg.dtype} {cfg.score}")
+    t0 = time.perf_counter()
+    lay = make_layer(cfg, device="cuda")
+    hs = [lay.h] + [make_tokens(cfg, step=i, device="cuda") for i in range(1, args.rotate)]
+    torch.cuda.synchronize()
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f}s "
+        f"({cfg.weight_bytes() / 1e9:.2f} GB of expert weights)")
+    shape = LayerShape(cfg.T, cfg.d_model, cfg.E_r, cfg.K, cfg.E_s, cfg.d_ffn, cfg.dtype,
+                       cfg.score)
+    run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
+                   lay.ws_down)
+    b = lay.b.clone() if lay.b is not None else None
+    b_host0 = host_array(lay.b) if lay.b is not None else None
+    gamma = cfg.gamma if b is not None else None
+    stream = torch.cuda.current_stream()
+    run.profile_tags = True
+
+    for i in range(args.warmup):
+        run.forward(hs[i % len(hs)], b, gamma, stream)
+    torch.cuda.synchronize()
+    moe_profile_report()  # drop warm-up records
+    moe_profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run.forward(hs[i % len(hs)], b, gamma, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    moe_profile_enable(False)
+    prof = moe_profile_report()
+    ev_ms = ev0.elapsed_time(ev1)
+
+    ms_per_step = wall * 1000.0 / args.steps
+    tokens_per_s = cfg.T / (ms_per_step / 1000.0)
+    loads = run.loads.cpu().numpy()
+    n_touched = int((loads > 0).sum())
+    gu_bytes, gu_flops, layer_bytes, layer_flops = algorithmic(cfg, n_touched, cfg.E_s)
+    stages = {k: round(v[1] / v[0], 5) for k, v in prof.items()}
+    log("per-kernel average ms: " + json.dumps(stages))
+    log(f"wall {wall * 1000:.2f} ms, events {ev_ms:.2f} ms over {args.steps} steps")
+    routed_ms = stages["routed.gateup_bf16"]
+    achieved = gu_bytes / (routed_ms / 1000.0) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="gateup_bf16 (routed experts)", avg_ms=round(routed_ms, 4),
+                    algorithmic_bytes=gu_bytes,
+                    mfma_tflops=round(gu_flops / (routed_ms / 1000.0) / 1e12, 1),
+                    mfma_frac=round(gu_flops / (routed_ms / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4))
+    layer = dict(algorithmic_bytes=layer_bytes, flops=layer_flops,
+                 hbm_gbs=round(layer_bytes / (ms_per_step / 1000.0) / 1e9, 1),
+                 hbm_frac=round(layer_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                 mfma_tflops=round(layer_flops / (ms_per_step / 1000.0) / 1e12, 1),
+                 mfma_frac=round(layer_flops / (ms_per_step / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 experts_touched=n_touched, stats=run.stats_host())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, lay, b_host0)
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian tokens and weights, random-init experts)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d_model} E_r={cfg.E_r} "
+                               f"K={cfg.K} E_s={cfg.E_s} d_ffn={cfg.d_ffn} {cfg.score} router, "
+                               f"bias update gamma={cfg.gamma}",
+                   "tokens_per_step": cfg.T, "parallelism": "single GPU"},
+        "roofline": roofline, "layer": layer, "stages_ms": stages, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,224 @@
+/*
+ * moe.h -- C ABI of the single-GPU sparse Mixture-of-Experts layer forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (Sparse MoE routing-math page, arman1o1.github.io, section 0,
+ * layer-output equation) is
+ *
+ *     y_t = h_t + sum_{j<E_s} SwiGLU^S_j(h_t) + sum_{i in I_t} g_{t,i} SwiGLU^R_i(h_t),
+ *     SwiGLU(h) = (SiLU(h W_gate) * (h W_up)) W_down,
+ *
+ * with biased selection I_t = TopK({s_{t,i} + b_i}, K), unbiased gates
+ * g_{t,i} = s_{t,i} / sum_{j in I_t} s_{t,j}, and the per-step bias update
+ * b_i <- b_i + gamma * sign(cbar - c_i) (same page, section 2).
+ *
+ * Five entry points, called in this order for one layer forward:
+ *   moe_route -> moe_permute -> moe_grouped_swiglu (routed, then shared)
+ *   -> moe_combine -> moe_bias_update (training steps only).
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.  The
+ *     caller owns all memory; no entry point allocates or frees.
+ *   - Matrices are row-major and densely packed.  Expert weights use the
+ *     [out, in] layout of a linear layer: W_gate, W_up [n, d_ffn, d_model] and
+ *     W_down [n, d_model, d_ffn], stacked over experts.
+ *   - bf16 data is passed as raw 16-bit bfloat16 words; fp32 is IEEE binary32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream: it neither synchronises
+ *     with the host nor copies data back to it.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     non-OK status means nothing was enqueued; moe_last_error() then returns
+ *     a message for the calling thread.  Device-side contents (expert ids,
+ *     offsets, row indices) are bounds-checked in the kernels: out-of-range
+ *     entries are skipped, never dereferenced.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, K > E_r, ...            */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not built: shape alignment, dtype mix  */
+  MOE_ERR_HIP = 3           /* the HIP runtime reported an error on launch      */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_SIGMOID = 0,  /* s = sigmoid(z): DeepSeek-V3 affinity                      */
+  MOE_SOFTMAX = 1   /* p = softmax(z) over all E_r experts: Mixtral / GShard     */
+} moe_score_fn;
+
+/* Load statistics written by moe_bias_update (device memory). */
+typedef struct {
+  int32_t max_load;  /* max_i c_i                                                */
+  int32_t min_load;  /* min_i c_i                                                */
+  float max_vio;     /* (max_i c_i - cbar) / cbar, cbar = K T / E_r              */
+  int32_t reserved;
+} moe_bias_stats;
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/*
+ * moe_route -- router scores, biased top-K selection, unbiased gates, loads.
+ *
+ * Defined by: Sparse MoE routing-math page, section 2 (biased selection and
+ * unbiased gate equations; sigmoid affinity s = sigma(h^T e)); section 1 and
+ * its classical-router listing (softmax, top-K, renormalise, clamp 1e-12);
+ * section 4 item 2 (router matmul and score function in fp32).
+ *
+ *   h        [T, d_model]   tokens, fp32 or bf16 (h_dtype)
+ *   e        [E_r, d_model] fp32 expert centroids
+ *   b        [E_r] fp32 selection bias, or NULL for b = 0 (softmax configs)
+ *   topk_idx [T, K] int32 out: the K picked experts, ascending expert id
+ *   gates    [T, K] fp32 out: g = s_i / max(sum_{j in I_t} s_j, 1e-12), the
+ *            denominator summed in ascending expert id; aligned with topk_idx
+ *   loads    [E_r] int32 out: c_i = #{t : i in I_t} (zeroed by this call)
+ *
+ * z = h . e_i is accumulated in fp32; the selection ranks v = fl32(s + b);
+ * equal v -> the lower expert id is picked.  With MOE_SOFTMAX and a non-NULL
+ * b, the bias is added to p.
+ * Limits: 1 <= K <= min(E_r, MOE_MAX_TOPK), E_r <= 512, d_model % 8 == 0.
+ */
+moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn,
+                     const void* h, moe_dtype h_dtype, const float* e, const float* b,
+                     int32_t* topk_idx, float* gates, int32_t* loads, void* stream);
+
+/*
+ * moe_permute -- dispatch: expert histogram, exclusive scan, stable
+ * permutation of the T*K token copies, and (optionally) the row gather.
+ *
+ * Defined by: Sparse MoE routing-math page, section 3 (sort local tokens by
+ * target expert id; per-expert token lists of the layer listing, in token
+ * order) and the Routing-and-Load-Balancing page, section 5 (admission in
+ * token order).  No capacity limit: every copy is kept.
+ *
+ *   topk_idx  [T, K] int32 expert ids (entries outside [0, E_r) are skipped)
+ *   h         [T, d_model] tokens (only read when x_perm != NULL)
+ *   offsets   [E_r + 1] int32 out: exclusive scan of the loads;
+ *             offsets[E_r] = number of kept copies (T*K for valid ids)
+ *   row_token [T*K] int32 out: source token of permuted row r; rows inside an
+ *             expert's segment are in ascending token order; entries past
+ *             offsets[E_r] are set to -1
+ *   slot_row  [T*K] int32 out: permuted row of copy (t, k) (-1 if skipped)
+ *   x_perm    [T*K, d_model] out, or NULL: x_perm[r] = h[row_token[r]]
+ *   workspace device scratch of at least moe_permute_workspace_size(T, E_r)
+ *             bytes
+ * Fully deterministic: no result depends on thread timing.
+ */
+size_t moe_permute_workspace_size(int T, int E_r);
+moe_status moe_permute(int T, int d_model, int E_r, int K, const int32_t* topk_idx,
+                       const void* h, moe_dtype dtype, int32_t* offsets, int32_t* row_token,
+                       int32_t* slot_row, void* x_perm, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_swiglu -- one grouped SwiGLU over variable-size row groups:
+ * group g runs expert g on rows offsets[g] .. offsets[g+1]-1.
+ *
+ * Defined by: Sparse MoE routing-math page, section 0 (SwiGLU expert) and
+ * section 3 (all local experts in one grouped GEMM over variable-sized token
+ * buckets); Expert-Parallelism page (mohakchugh.is-a.dev), inference section
+ * (variable token counts per expert without padding).
+ *
+ *   n_groups   number of experts in this call (E_r for routed, E_s for shared)
+ *   rows       size of the grouped row space (T*K routed, E_s*T shared)
+ *   offsets    [n_groups + 1] int32 device: non-decreasing, offsets[0] = 0,
+ *              offsets[n_groups] <= rows (clamped into [0, rows] on device)
+ *   row_index  [rows] int32 device: grouped row r reads x[row_index[r]]
+ *              (gather on load; entries outside [0, x_rows) give a zero row),
+ *              or NULL: grouped row r reads x[r]
+ *   x          [x_rows, d_model] input rows, fp32 or bf16 (dtype)
+ *   w_gate, w_up [n_groups, d_ffn, d_model]; w_down [n_groups, d_model, d_ffn]
+ *   row_scale  [rows] fp32 per-row output factor (a gate), or NULL (= 1)
+ *   y          [rows, d_model] out: SwiGLU_g(x_row) * row_scale; rows past
+ *              offsets[n_groups] are not written
+ *   workspace  device scratch of at least moe_grouped_swiglu_workspace_size()
+ *              bytes (the SiLU(gate)*up activations and the tile list)
+ * bf16: fp32 accumulation on the matrix cores; the activation is rounded to
+ * bf16 before W_down and y to bf16 (round to nearest even).
+ * Limits: bf16 needs d_model % 64 == 0 and d_ffn % 64 == 0; fp32 needs
+ * d_model % 16 == 0 and d_ffn % 16 == 0.
+ */
+size_t moe_grouped_swiglu_workspace_size(int n_groups, int d_model, int d_ffn, int rows,
+                                         moe_dtype dtype);
+moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                              const int32_t* offsets, const int32_t* row_index,
+                              const void* x, moe_dtype dtype, const void* w_gate,
+                              const void* w_up, const void* w_down, const float* row_scale,
+                              void* y, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * moe_combine -- gate-weighted sum of the expert outputs plus the residual and
+ * the shared experts:
+ *     y_t = h_t + sum_{j<E_s} y_shared[j, t] + sum_k gates[t,k] * y_perm[slot_row[t*K+k]]
+ *
+ * Defined by: Sparse MoE routing-math page, section 0 (layer-output equation)
+ * and section 3 (un-permute and accumulate the gate-weighted sum).
+ *
+ *   h        [T, d_model], y_shared [E_s, T, d_model] (NULL when E_s == 0),
+ *   y_perm   [T*K, d_model], all in `dtype`
+ *   slot_row [T*K] int32 (entries outside [0, T*K) contribute nothing)
+ *   gates    [T, K] fp32
+ *   y        [T, d_model] out (dtype), fp32 accumulation in a fixed order,
+ *            bf16 output rounded to nearest even.  Deterministic.
+ * Limits: d_model % 8 == 0.
+ */
+moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h,
+                       const void* y_shared, const void* y_perm, const int32_t* slot_row,
+                       const float* gates, moe_dtype dtype, void* y, void* stream);
+
+/*
+ * moe_bias_update -- auxiliary-loss-free bias step after the loads of the
+ * batch are counted:  b_i <- b_i + gamma * sign(cbar - c_i), cbar = K T / E_r.
+ *
+ * Defined by: Sparse MoE routing-math page, section 2 (bias update equation);
+ * Mixture of Experts designs page (raminaeye.github.io), section 1 worked
+ * example (sign 0 leaves a bias unchanged); section 4 item 1 of the
+ * routing-math page (MaxVio).
+ *
+ *   loads [E_r] int32 (from moe_route);  b [E_r] fp32, updated in place
+ *   stats device moe_bias_stats out, or NULL
+ * The sign is decided in integers (K*T vs E_r*c_i); the update is one fp32
+ * add of +gamma, -gamma or 0, so it is bit-reproducible.  gamma = 0 freezes b.
+ */
+moe_status moe_bias_update(int T, int E_r, int K, float gamma, const int32_t* loads, float* b,
+                           moe_bias_stats* stats, void* stream);
+
+/*
+ * Optional kernel timing (benchmarking aid, not needed for the layer).
+ * moe_profile_enable(1): from then on every kernel the library launches is
+ * bracketed by a pair of hipEvents recorded on the stream it runs on.
+ * moe_profile_report waits for the recorded events, writes one text line per
+ * kernel name -- "name launches total_ms min_ms max_ms" -- into the host
+ * buffer `buf` (NUL-terminated) and clears the records.  Returns
+ * MOE_ERR_INVALID_ARG if the buffer is too small.  Events are created once and
+ * reused; no device memory is allocated.
+ */
+moe_status moe_profile_enable(int on);
+/* Prefix for the names of the records that follow (host string, copied;
+ * NULL or "" clears it), e.g. to tell the routed and the shared grouped
+ * SwiGLU calls apart. */
+moe_status moe_profile_tag(const char* tag);
+moe_status moe_profile_report(char* buf, size_t buf_bytes);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* moe_last_error(void);
+
+/* Library version string (host memory, static). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

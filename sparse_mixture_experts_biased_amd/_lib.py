@@ -1,0 +1,164 @@
+"""ctypes binding of libmoe_mi355x.so: one Python function per C entry point,
+same names and argument order.  Argument marshalling only -- every step of
+the layer runs in the HIP library.  Tensors are passed by device pointer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SIGMOID, MOE_SOFTMAX = 0, 1
+
+EXPORTED = ["moe_route", "moe_permute_workspace_size", "moe_permute",
+            "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
+            "moe_bias_update", "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
+            "moe_version"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+class MoeBiasStats(ctypes.Structure):
+    _fields_ = [("max_load", ctypes.c_int32), ("min_load", ctypes.c_int32),
+                ("max_vio", ctypes.c_float), ("reserved", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_i, _p, _f, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_mixture_experts_biased_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "moe_route": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p], _i),
+        "moe_permute_workspace_size": ([_i, _i], _sz),
+        "moe_permute": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
+        "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
+        "moe_grouped_swiglu": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
+                                _sz, _p], _i),
+        "moe_combine": ([_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p], _i),
+        "moe_bias_update": ([_i, _i, _i, _f, _p, _p, _p, _p], _i),
+        "moe_profile_enable": ([_i], _i),
+        "moe_profile_tag": ([ctypes.c_char_p], _i),
+        "moe_profile_report": ([ctypes.c_char_p, _sz], _i),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_version": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None -> NULL); plain ints pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError("tensor arguments must live on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        msg = load().moe_last_error().decode(errors="replace")
+        raise MoeError(status, msg)
+
+
+def moe_version() -> str:
+    return load().moe_version().decode()
+
+
+def moe_last_error() -> str:
+    return load().moe_last_error().decode(errors="replace")
+
+
+def moe_route(T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx, gates, loads, stream=None):
+    _check(load().moe_route(T, d_model, E_r, K, fn, _ptr(h), h_dtype, _ptr(e), _ptr(b),
+                            _ptr(topk_idx), _ptr(gates), _ptr(loads), _stream(stream)))
+
+
+def moe_permute_workspace_size(T, E_r) -> int:
+    return int(load().moe_permute_workspace_size(T, E_r))
+
+
+def moe_permute(T, d_model, E_r, K, topk_idx, h, dtype, offsets, row_token, slot_row, x_perm,
+                workspace, workspace_bytes, stream=None):
+    _check(load().moe_permute(T, d_model, E_r, K, _ptr(topk_idx), _ptr(h), dtype, _ptr(offsets),
+                              _ptr(row_token), _ptr(slot_row), _ptr(x_perm), _ptr(workspace),
+                              workspace_bytes, _stream(stream)))
+
+
+def moe_grouped_swiglu_workspace_size(n_groups, d_model, d_ffn, rows, dtype) -> int:
+    return int(load().moe_grouped_swiglu_workspace_size(n_groups, d_model, d_ffn, rows, dtype))
+
+
+def moe_grouped_swiglu(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, dtype,
+                       w_gate, w_up, w_down, row_scale, y, workspace, workspace_bytes,
+                       stream=None):
+    _check(load().moe_grouped_swiglu(n_groups, d_model, d_ffn, rows, x_rows, _ptr(offsets),
+                                     _ptr(row_index), _ptr(x), dtype, _ptr(w_gate), _ptr(w_up),
+                                     _ptr(w_down), _ptr(row_scale), _ptr(y), _ptr(workspace),
+                                     workspace_bytes, _stream(stream)))
+
+
+def moe_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates, dtype, y,
+                stream=None):
+    _check(load().moe_combine(T, d_model, K, E_s, _ptr(h), _ptr(y_shared), _ptr(y_perm),
+                              _ptr(slot_row), _ptr(gates), dtype, _ptr(y), _stream(stream)))
+
+
+def moe_bias_update(T, E_r, K, gamma, loads, b, stats, stream=None):
+    _check(load().moe_bias_update(T, E_r, K, float(gamma), _ptr(loads), _ptr(b), _ptr(stats),
+                                  _stream(stream)))
+
+
+def moe_profile_enable(on: bool = True):
+    _check(load().moe_profile_enable(1 if on else 0))
+
+
+def moe_profile_tag(tag: str = ""):
+    _check(load().moe_profile_tag(tag.encode()))
+
+
+def moe_profile_report() -> dict:
+    """{kernel name: (launches, total_ms, min_ms, max_ms)} since the last report."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check(load().moe_profile_report(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, n, tot, mn, mx = line.split()
+        out[name] = (int(n), float(tot), float(mn), float(mx))
+    return out

@@ -1,0 +1,306 @@
+// C ABI of the MoE layer library: host-side argument validation, then the
+// asynchronous kernel launches.  Nothing here allocates device memory,
+// synchronises with the device or copies data back to the host.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "swiglu_tiles.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool valid_dtype(moe_dtype d) { return d == MOE_F32 || d == MOE_BF16; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+static_assert(sizeof(moe_bias_stats) == sizeof(moe::BiasStats), "stats layout");
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
+                     moe_dtype h_dtype, const float* e, const float* b, int32_t* topk_idx,
+                     float* gates, int32_t* loads, void* stream) {
+  if (T < 1 || d_model < 1 || E_r < 1 || K < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%d d_model=%d E_r=%d K=%d must be >= 1", T,
+                d_model, E_r, K);
+  if (K > E_r) return fail(MOE_ERR_INVALID_ARG, "moe_route: K=%d > E_r=%d", K, E_r);
+  if (K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: K=%d > %d", K, MOE_MAX_TOPK);
+  if (E_r > 512) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E_r=%d > 512", E_r);
+  if (fn != MOE_SIGMOID && fn != MOE_SOFTMAX)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown score function %d", (int)fn);
+  if (!valid_dtype(h_dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_route: bad dtype");
+  if (d_model % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route: d_model=%d not a multiple of 8", d_model);
+  if (!h || !e || !topk_idx || !gates || !loads)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  if (static_cast<long long>(T) * K > INT32_MAX || static_cast<long long>(T) * d_model > (1LL << 40))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: sizes overflow");
+  return hip_status(moe::launch_route(T, d_model, E_r, K, (int)fn, h, h_dtype == MOE_BF16, e, b,
+                                      topk_idx, gates, loads, as_stream(stream)),
+                    "moe_route");
+}
+
+size_t moe_permute_workspace_size(int T, int E_r) {
+  if (T < 1 || E_r < 1) return 0;
+  return moe::permute_workspace_bytes(T, E_r);
+}
+
+moe_status moe_permute(int T, int d_model, int E_r, int K, const int32_t* topk_idx,
+                       const void* h, moe_dtype dtype, int32_t* offsets, int32_t* row_token,
+                       int32_t* slot_row, void* x_perm, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (T < 1 || E_r < 1 || K < 1 || d_model < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: T=%d d_model=%d E_r=%d K=%d must be >= 1", T,
+                d_model, E_r, K);
+  if (K > E_r || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: K=%d out of range", K);
+  if (E_r > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_permute: E_r=%d > %d", E_r, MOE_MAX_EXPERTS);
+  if (static_cast<long long>(T) * K > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: T*K overflows int32");
+  if (!topk_idx || !offsets || !row_token || !slot_row || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  if (workspace_bytes < moe::permute_workspace_bytes(T, E_r))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: workspace %zu < %zu bytes", workspace_bytes,
+                moe::permute_workspace_bytes(T, E_r));
+  if (x_perm) {
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_permute: x_perm needs h");
+    if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_permute: bad dtype");
+    if (d_model % 8 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_permute: d_model=%d not a multiple of 8", d_model);
+  }
+  const int eb = dtype == MOE_BF16 ? 2 : 4;
+  return hip_status(moe::launch_permute(T, d_model, E_r, K, topk_idx, h, eb, offsets, row_token,
+                                        slot_row, x_perm, workspace, as_stream(stream)),
+                    "moe_permute");
+}
+
+size_t moe_grouped_swiglu_workspace_size(int n_groups, int d_model, int d_ffn, int rows,
+                                         moe_dtype dtype) {
+  (void)d_model;
+  if (n_groups < 1 || d_ffn < 1 || rows < 0 || !valid_dtype(dtype)) return 0;
+  return moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
+}
+
+moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                              const int32_t* offsets, const int32_t* row_index, const void* x,
+                              moe_dtype dtype, const void* w_gate, const void* w_up,
+                              const void* w_down, const float* row_scale, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_groups < 1 || d_model < 1 || d_ffn < 1 || rows < 0 || x_rows < 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_grouped_swiglu: n_groups=%d d_model=%d d_ffn=%d rows=%d x_rows=%d", n_groups,
+                d_model, d_ffn, rows, x_rows);
+  if (n_groups > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu: n_groups=%d > %d", n_groups,
+                MOE_MAX_EXPERTS);
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: bad dtype");
+  if (!offsets || !x || !w_gate || !w_up || !w_down || !y || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: null pointer");
+  if (row_index == nullptr && x_rows < rows)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: x_rows=%d < rows=%d without row_index",
+                x_rows, rows);
+  const int align = dtype == MOE_BF16 ? 64 : 16;
+  if (d_model % align || d_ffn % align)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_grouped_swiglu: d_model=%d and d_ffn=%d must be multiples of %d", d_model,
+                d_ffn, align);
+  if (static_cast<long long>(rows) * d_ffn > (1LL << 40) ||
+      static_cast<long long>(d_model) * d_ffn > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: sizes overflow");
+  const size_t need = moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  if (rows == 0) return MOE_OK;
+  hipError_t err;
+  if (dtype == MOE_BF16)
+    err = moe::launch_swiglu_bf16(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index,
+                                  static_cast<const uint16_t*>(x),
+                                  static_cast<const uint16_t*>(w_gate),
+                                  static_cast<const uint16_t*>(w_up),
+                                  static_cast<const uint16_t*>(w_down), row_scale,
+                                  static_cast<uint16_t*>(y), workspace, as_stream(stream));
+  else
+    err = moe::launch_swiglu_f32(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index,
+                                 static_cast<const float*>(x), static_cast<const float*>(w_gate),
+                                 static_cast<const float*>(w_up),
+                                 static_cast<const float*>(w_down), row_scale,
+                                 static_cast<float*>(y), workspace, as_stream(stream));
+  return hip_status(err, "moe_grouped_swiglu");
+}
+
+moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h, const void* y_shared,
+                       const void* y_perm, const int32_t* slot_row, const float* gates,
+                       moe_dtype dtype, void* y, void* stream) {
+  if (T < 1 || d_model < 1 || K < 1 || E_s < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: T=%d d_model=%d K=%d E_s=%d", T, d_model, K,
+                E_s);
+  if (K > MOE_MAX_TOPK) return fail(MOE_ERR_INVALID_ARG, "moe_combine: K=%d > %d", K, MOE_MAX_TOPK);
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_combine: bad dtype");
+  if (d_model % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_combine: d_model=%d not a multiple of 8", d_model);
+  if (!h || !y_perm || !slot_row || !gates || !y || (E_s > 0 && !y_shared))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
+  if (static_cast<long long>(T) * K > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: T*K overflows int32");
+  return hip_status(moe::launch_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates,
+                                        dtype == MOE_BF16, y, as_stream(stream)),
+                    "moe_combine");
+}
+
+moe_status moe_bias_update(int T, int E_r, int K, float gamma, const int32_t* loads, float* b,
+                           moe_bias_stats* stats, void* stream) {
+  if (T < 1 || E_r < 1 || K < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_bias_update: T=%d E_r=%d K=%d must be >= 1", T, E_r, K);
+  if (E_r > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_bias_update: E_r=%d > %d", E_r, MOE_MAX_EXPERTS);
+  if (!(gamma >= 0.0f) || gamma > 1e30f)
+    return fail(MOE_ERR_INVALID_ARG, "moe_bias_update: gamma must be finite and >= 0");
+  if (!loads || !b) return fail(MOE_ERR_INVALID_ARG, "moe_bias_update: null pointer");
+  return hip_status(moe::launch_bias_update(T, E_r, K, gamma, loads, b,
+                                            reinterpret_cast<moe::BiasStats*>(stats),
+                                            as_stream(stream)),
+                    "moe_bias_update");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- profiling
+
+namespace {
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+  bool closed;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::string g_prof_tag;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace moe {
+
+int prof_begin(hipStream_t s, const char* name) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return -1;
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return -1;
+  if (hipEventRecord(a, s) != hipSuccess) return -1;
+  g_prof_recs.push_back(ProfRec{g_prof_tag + name, a, b, false});
+  return static_cast<int>(g_prof_recs.size()) - 1;
+}
+
+void prof_end(int token, hipStream_t s) {
+  if (token < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (token >= static_cast<int>(g_prof_recs.size())) return;
+  ProfRec& r = g_prof_recs[token];
+  if (hipEventRecord(r.b, s) == hipSuccess) r.closed = true;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_tag(const char* tag) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_tag = tag ? tag : "";
+  return MOE_OK;
+}
+
+moe_status moe_profile_report(char* buf, size_t buf_bytes) {
+  if (!buf || buf_bytes == 0) return fail(MOE_ERR_INVALID_ARG, "moe_profile_report: no buffer");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  struct Agg { int n = 0; double tot = 0, mn = 1e30, mx = 0; };
+  std::map<std::string, Agg> agg;
+  moe_status st = MOE_OK;
+  for (ProfRec& r : g_prof_recs) {
+    if (r.closed) {
+      float ms = 0.0f;
+      if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+        st = fail(MOE_ERR_HIP, "moe_profile_report: event query failed");
+      } else {
+        Agg& a = agg[r.name];
+        a.n += 1;
+        a.tot += ms;
+        a.mn = std::min(a.mn, static_cast<double>(ms));
+        a.mx = std::max(a.mx, static_cast<double>(ms));
+      }
+    }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  std::string out;
+  char line[256];
+  for (auto& kv : agg) {
+    snprintf(line, sizeof(line), "%s %d %.6f %.6f %.6f\n", kv.first.c_str(), kv.second.n,
+             kv.second.tot, kv.second.mn, kv.second.mx);
+    out += line;
+  }
+  if (out.size() + 1 > buf_bytes) return fail(MOE_ERR_INVALID_ARG, "moe_profile_report: buffer too small");
+  memcpy(buf, out.c_str(), out.size() + 1);
+  return st;
+}
+
+}  // extern "C"
+
+namespace moe {
+size_t swiglu_workspace_bytes(int n_groups, int d_model, int d_ffn, int rows, int bf16) {
+  (void)d_model;
+  return swiglu_layout(nullptr, n_groups, d_ffn, rows, bf16 ? 2 : 4, 32).bytes;
+}
+}  // namespace moe

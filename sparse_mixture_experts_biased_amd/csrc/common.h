@@ -1,0 +1,93 @@
+// Shared device helpers and the launch-side declarations of every kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (quiet NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------- sizes
+
+constexpr int kWave = 64;
+#define MOE_MAX_TOPK_DEV 16
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- launches
+// Each returns the hipError_t of its last launch.
+
+// router
+hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h_bf16,
+                        const float* e, const float* b, int32_t* idx, float* gates,
+                        int32_t* loads, hipStream_t s);
+
+// dispatch
+constexpr int kPermChunk = 256;  // tokens per histogram / rank chunk
+size_t permute_workspace_bytes(int T, int E);
+hipError_t launch_permute(int T, int d, int E, int K, const int32_t* idx, const void* h,
+                          int elem_bytes, int32_t* offsets, int32_t* row_token,
+                          int32_t* slot_row, void* x_perm, void* ws, hipStream_t s);
+
+// grouped SwiGLU
+size_t swiglu_workspace_bytes(int n_groups, int d_model, int d_ffn, int rows, int bf16);
+hipError_t launch_swiglu_f32(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                             const int32_t* offsets, const int32_t* row_index, const float* x,
+                             const float* wg, const float* wu, const float* wd,
+                             const float* row_scale, float* y, void* ws, hipStream_t s);
+hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                              const int32_t* offsets, const int32_t* row_index,
+                              const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                              const uint16_t* wd, const float* row_scale, uint16_t* y,
+                              void* ws, hipStream_t s);
+
+// combine
+hipError_t launch_combine(int T, int d, int K, int E_s, const void* h, const void* y_shared,
+                          const void* y_perm, const int32_t* slot_row, const float* gates,
+                          int bf16, void* y, hipStream_t s);
+
+// bias update
+struct BiasStats {
+  int32_t max_load, min_load;
+  float max_vio;
+  int32_t reserved;
+};
+hipError_t launch_bias_update(int T, int E, int K, float gamma, const int32_t* loads, float* b,
+                              BiasStats* stats, hipStream_t s);
+
+// small utilities
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+
+// Optional event timing of the library's kernels (off unless enabled through
+// moe_profile_enable).  prof_begin returns a token for prof_end, or -1.
+int prof_begin(hipStream_t s, const char* name);
+void prof_end(int token, hipStream_t s);
+
+struct ProfScope {
+  int tok;
+  hipStream_t s;
+  ProfScope(hipStream_t st, const char* name) : tok(prof_begin(st, name)), s(st) {}
+  ~ProfScope() { prof_end(tok, s); }
+};
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Workspace layout and the device-side tile list of the grouped SwiGLU.
+//
+// The groups' row counts live on the device (they come from the router), so
+// the host never reads them: a one-workgroup kernel turns the offsets into a
+// list of row tiles, and the GEMM grids are sized for the worst case
+// (ceil(rows / BM) + n_groups tiles); blocks past the real tile count exit.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct TileInfo {
+  int32_t group;
+  int32_t m0;    // first grouped row of the tile
+  int32_t m1;    // one past the group's last row (rows >= m1 are masked)
+  int32_t pad;
+};
+
+struct SwigluWorkspace {
+  void* act;                  // [rows, d_ffn] SiLU(gate) * up
+  int32_t* group_tile_start;  // [n_groups + 1] prefix count of tiles per group
+  TileInfo* tiles;            // [max_tiles]
+  int32_t* meta;              // [0] = number of tiles
+  size_t bytes;
+};
+
+inline int max_tiles_for(int rows, int n_groups, int bm) { return (rows + bm - 1) / bm + n_groups; }
+
+// Carve the caller's workspace; `base` may be nullptr to only size it.
+inline SwigluWorkspace swiglu_layout(void* base, int n_groups, int d_ffn, int rows,
+                                     int elem_bytes, int min_bm) {
+  SwigluWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t at = off;
+    off = align_up(off + n, 256);
+    return base ? static_cast<char*>(base) + at : nullptr;
+  };
+  w.act = take(static_cast<size_t>(rows) * d_ffn * elem_bytes);
+  w.group_tile_start = reinterpret_cast<int32_t*>(take((n_groups + 1) * sizeof(int32_t)));
+  w.tiles = reinterpret_cast<TileInfo*>(
+      take(static_cast<size_t>(max_tiles_for(rows, n_groups, min_bm)) * sizeof(TileInfo)));
+  w.meta = reinterpret_cast<int32_t*>(take(4 * sizeof(int32_t)));
+  w.bytes = off;
+  return w;
+}
+
+hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* offsets,
+                              const SwigluWorkspace& w, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,130 @@
+"""One MoE layer forward driven through the C ABI.
+
+MoELayer owns the intermediate device buffers (allocated once, with torch, at
+construction) and calls the five entry points in order on one stream:
+
+    moe_route -> moe_permute -> moe_grouped_swiglu (routed experts)
+    -> moe_grouped_swiglu (shared experts) -> moe_combine -> moe_bias_update
+
+Layer output (Sparse MoE routing-math page, section 0):
+    y_t = h_t + sum_j SwiGLU^S_j(h_t) + sum_{i in I_t} g_{t,i} SwiGLU^R_i(h_t)
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class LayerShape:
+    T: int
+    d_model: int
+    E_r: int
+    K: int
+    E_s: int
+    d_ffn: int
+    dtype: str    # "bf16" or "f32"
+    score: str    # "sigmoid" or "softmax"
+
+
+class MoELayer:
+    def __init__(self, shape: LayerShape, e, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
+                 ws_down=None, device="cuda"):
+        s = self.shape = shape
+        self.profile_tags = False   # label routed / shared launches in the kernel timing
+        self.dt = L.MOE_BF16 if s.dtype == "bf16" else L.MOE_F32
+        self.tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+        self.fn = L.MOE_SIGMOID if s.score == "sigmoid" else L.MOE_SOFTMAX
+        self.e, self.w_gate, self.w_up, self.w_down = e, w_gate, w_up, w_down
+        self.ws_gate, self.ws_up, self.ws_down = ws_gate, ws_up, ws_down
+        T, K, E, d = s.T, s.K, s.E_r, s.d_model
+        TK = T * K
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty((T, K), **i32)
+        self.gates = torch.empty((T, K), dtype=torch.float32, device=device)
+        self.loads = torch.empty((E,), **i32)
+        self.offsets = torch.empty((E + 1,), **i32)
+        self.row_token = torch.empty((TK,), **i32)
+        self.slot_row = torch.empty((TK,), **i32)
+        self.perm_ws_bytes = L.moe_permute_workspace_size(T, E)
+        self.perm_ws = torch.empty((self.perm_ws_bytes,), dtype=torch.uint8, device=device)
+        self.y_perm = torch.empty((TK, d), dtype=self.tdt, device=device)
+        ws_bytes = L.moe_grouped_swiglu_workspace_size(E, d, s.d_ffn, TK, self.dt)
+        if s.E_s:
+            ws_bytes = max(ws_bytes, L.moe_grouped_swiglu_workspace_size(
+                s.E_s, d, s.d_ffn, s.E_s * T, self.dt))
+            self.sh_offsets = (torch.arange(s.E_s + 1, **i32) * T).contiguous()
+            self.sh_rows = torch.arange(T, **i32).repeat(s.E_s).contiguous()
+            self.y_shared = torch.empty((s.E_s * T, d), dtype=self.tdt, device=device)
+        else:
+            self.sh_offsets = self.sh_rows = self.y_shared = None
+        self.sw_ws_bytes = ws_bytes
+        self.sw_ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=device)
+        self.y = torch.empty((T, d), dtype=self.tdt, device=device)
+        self.stats = torch.zeros((4,), dtype=torch.int32, device=device)
+
+    # individual stages -------------------------------------------------
+    def route(self, h, b, stream=None):
+        s = self.shape
+        L.moe_route(s.T, s.d_model, s.E_r, s.K, self.fn, h, self.dt, self.e, b, self.topk_idx,
+                    self.gates, self.loads, stream)
+
+    def permute(self, h=None, x_perm=None, stream=None):
+        s = self.shape
+        L.moe_permute(s.T, s.d_model, s.E_r, s.K, self.topk_idx, h, self.dt, self.offsets,
+                      self.row_token, self.slot_row, x_perm, self.perm_ws, self.perm_ws_bytes,
+                      stream)
+
+    def routed_experts(self, h, stream=None):
+        s = self.shape
+        if self.profile_tags:
+            L.moe_profile_tag("routed.")
+        L.moe_grouped_swiglu(s.E_r, s.d_model, s.d_ffn, s.T * s.K, s.T, self.offsets,
+                             self.row_token, h, self.dt, self.w_gate, self.w_up, self.w_down,
+                             None, self.y_perm, self.sw_ws, self.sw_ws_bytes, stream)
+        if self.profile_tags:
+            L.moe_profile_tag("")
+
+    def shared_experts(self, h, stream=None):
+        s = self.shape
+        if not s.E_s:
+            return
+        if self.profile_tags:
+            L.moe_profile_tag("shared.")
+        L.moe_grouped_swiglu(s.E_s, s.d_model, s.d_ffn, s.E_s * s.T, s.T, self.sh_offsets,
+                             self.sh_rows, h, self.dt, self.ws_gate, self.ws_up, self.ws_down,
+                             None, self.y_shared, self.sw_ws, self.sw_ws_bytes, stream)
+        if self.profile_tags:
+            L.moe_profile_tag("")
+
+    def combine(self, h, stream=None):
+        s = self.shape
+        L.moe_combine(s.T, s.d_model, s.K, s.E_s, h, self.y_shared, self.y_perm, self.slot_row,
+                      self.gates, self.dt, self.y, stream)
+
+    def bias_update(self, b, gamma, stream=None):
+        s = self.shape
+        L.moe_bias_update(s.T, s.E_r, s.K, gamma, self.loads, b, self.stats, stream)
+
+    # whole layer --------------------------------------------------------
+    def forward(self, h, b: Optional[torch.Tensor] = None, gamma: Optional[float] = None,
+                stream=None):
+        """One layer forward; when gamma is given, b is updated in place after
+        the loads are counted (the update affects the next call)."""
+        self.route(h, b, stream)
+        self.permute(stream=stream)
+        self.routed_experts(h, stream)
+        self.shared_experts(h, stream)
+        self.combine(h, stream)
+        if gamma is not None and b is not None:
+            self.bias_update(b, gamma, stream)
+        return self.y
+
+    def stats_host(self):
+        st = self.stats.cpu()
+        return dict(max_load=int(st[0]), min_load=int(st[1]),
+                    max_vio=float(st[2:3].view(torch.float32)[0]))

@@ -14,7 +14,7 @@ from dataclasses import dataclass, replace
 @dataclass(frozen=True)
 class LayerConfig:
     name: str
-    index: int            # stable small integer used in seed keys
+    index: int            # stable small integer used in the token seed keys
     T: int
     d_model: int
     E_r: int
@@ -30,6 +30,11 @@ class LayerConfig:
     mixture: int = 0      # >0: tokens from a Gaussian mixture with this many components
     mixture_scale: float = 4.0
     hot_experts: int = 0  # experts whose centroids are aligned with mixture components
+    layer_index: int = -1  # seed index of the layer's parameters (-1: same as index)
+
+    @property
+    def param_index(self) -> int:
+        return self.index if self.layer_index < 0 else self.layer_index
 
     @property
     def rows(self) -> int:
@@ -56,16 +61,17 @@ CONFIGS = {
     "dsv3_prefill": LayerConfig("dsv3_prefill", 2, T=4096, d_model=7168, E_r=256, K=8,
                                 E_s=1, d_ffn=2048, dtype="bf16", score="sigmoid",
                                 bias="uniform", bias_range=0.01, gamma=0.001),
-    # Decode-sized batch at DeepSeek-V3 shape.
+    # Decode-sized batch through the same DeepSeek-V3 layer (same parameters).
     "dsv3_decode": LayerConfig("dsv3_decode", 3, T=64, d_model=7168, E_r=256, K=8,
                                E_s=1, d_ffn=2048, dtype="bf16", score="sigmoid",
-                               bias="uniform", bias_range=0.01, gamma=0.001),
-    # Skewed-load training steps at DeepSeek-V3 shape: 4-component mixture tokens,
-    # 8 hot experts, b0 = 0, gamma = 0.001, 20 steps.
+                               bias="uniform", bias_range=0.01, gamma=0.001,
+                               layer_index=2),
+    # Skewed-load training steps through the same DeepSeek-V3 expert weights:
+    # 4-component mixture tokens, 8 hot experts, b0 = 0, gamma = 0.001, 20 steps.
     "dsv3_skewed": LayerConfig("dsv3_skewed", 4, T=16384, d_model=7168, E_r=256, K=8,
                                E_s=1, d_ffn=2048, dtype="bf16", score="sigmoid",
                                bias="zero", gamma=0.001, steps=20, mixture=4,
-                               mixture_scale=4.0, hot_experts=8),
+                               mixture_scale=4.0, hot_experts=8, layer_index=2),
 }
 
 

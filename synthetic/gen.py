@@ -106,7 +106,7 @@ def make_tokens(cfg: LayerConfig, step: int = 0, device="cpu", base: int = 0) ->
 def make_centroids(cfg: LayerConfig, device="cpu", base: int = 0,
                    beta: Optional[float] = None) -> torch.Tensor:
     e = _normal((cfg.E_r, cfg.d_model), 1.0 / math.sqrt(cfg.d_model),
-                seed_of(base, cfg.index, "e"), device, torch.float32)
+                seed_of(base, cfg.param_index, "e"), device, torch.float32)
     if cfg.hot_experts:
         if beta is None:
             raise ValueError("the skewed workload needs its alignment strength beta")
@@ -126,7 +126,7 @@ def make_bias(cfg: LayerConfig, device="cpu", base: int = 0) -> Optional[torch.T
     if cfg.bias == "zero":
         return torch.zeros(cfg.E_r, dtype=torch.float32, device=device)
     r = np.float32(cfg.bias_range).item()
-    u = torch.rand(cfg.E_r, generator=_gen(seed_of(base, cfg.index, "b"), device),
+    u = torch.rand(cfg.E_r, generator=_gen(seed_of(base, cfg.param_index, "b"), device),
                    device=device, dtype=torch.float32)
     return u.mul_(2.0 * r).sub_(r)
 
@@ -135,7 +135,7 @@ def _expert_stack(cfg, tag, n, rows, cols, std, device, base):
     dt = _tdtype(cfg)
     out = torch.empty((n, rows, cols), dtype=dt, device=device)
     for i in range(n):
-        out[i] = _normal((rows, cols), std, seed_of(base, cfg.index, tag, i), device, dt)
+        out[i] = _normal((rows, cols), std, seed_of(base, cfg.param_index, tag, i), device, dt)
     return out
 
 
@@ -144,9 +144,10 @@ def make_expert(cfg: LayerConfig, i: int, shared: bool = False, device="cpu", ba
     dt = _tdtype(cfg)
     d, f = cfg.d_model, cfg.d_ffn
     pre = "ws_" if shared else "w_"
-    wg = _normal((f, d), 1.0 / math.sqrt(d), seed_of(base, cfg.index, pre + "gate", i), device, dt)
-    wu = _normal((f, d), 1.0 / math.sqrt(d), seed_of(base, cfg.index, pre + "up", i), device, dt)
-    wd = _normal((d, f), 1.0 / math.sqrt(f), seed_of(base, cfg.index, pre + "down", i), device, dt)
+    pi = cfg.param_index
+    wg = _normal((f, d), 1.0 / math.sqrt(d), seed_of(base, pi, pre + "gate", i), device, dt)
+    wu = _normal((f, d), 1.0 / math.sqrt(d), seed_of(base, pi, pre + "up", i), device, dt)
+    wd = _normal((d, f), 1.0 / math.sqrt(f), seed_of(base, pi, pre + "down", i), device, dt)
     return wg, wu, wd
 
 

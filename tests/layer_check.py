@@ -1,0 +1,138 @@
+"""End-to-end layer check shared by the full-size GPU tests.
+
+The GPU runs the whole layer through the C ABI; the oracle routes every token
+from the same inputs, and recomputes the layer output of a sample of tokens
+(all tokens when T is small) plus the expert outputs of a sample of experts.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from gpu_common import NEAR_TIE, check_route, out_tol, rel_err, say, to_host_f64
+from oracle import moe_oracle as O
+from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
+from synthetic import host_array
+
+
+def runner_for(lay, T=None):
+    c = lay.cfg
+    shape = LayerShape(T or c.T, c.d_model, c.E_r, c.K, c.E_s, c.d_ffn, c.dtype, c.score)
+    return MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
+                    lay.ws_down)
+
+
+def _expert_source(w_gate, w_up, w_down):
+    def get(i):
+        return host_array(w_gate[i]), host_array(w_up[i]), host_array(w_down[i])
+    return get
+
+
+def check_permutation_valid(idx, offsets, row_token, slot_row, E):
+    """Properties any correct dispatch of `idx` has (used when a near-tie flip
+    makes the GPU's picks differ from the oracle's)."""
+    T, K = idx.shape
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    assert np.array_equal(np.diff(offsets), counts) and offsets[0] == 0
+    flat_t = np.repeat(np.arange(T), K)
+    assert np.array_equal(row_token[slot_row], flat_t)
+    for i in range(E):
+        seg = row_token[offsets[i]:offsets[i + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all((idx[seg] == i).any(axis=1))
+
+
+def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=0,
+                check_all_tokens=False):
+    """Run one layer forward on the GPU and compare with the oracle.
+
+    Returns a dict with near-tie / flip counts and the observed errors."""
+    c = lay.cfg
+    T, E, K = h.shape[0], c.E_r, c.K
+    b_dev = b_in.clone() if b_in is not None else None
+    run.forward(h, b_dev, gamma)
+    torch.cuda.synchronize()
+    idx = run.topk_idx.cpu().numpy()
+    off = run.offsets.cpu().numpy()
+    rt = run.row_token.cpu().numpy()
+    sr = run.slot_row.cpu().numpy()
+
+    n_near, n_flip, r = check_route(h, lay.e, b_in, K, c.score, run.topk_idx, run.gates,
+                                    run.loads, E)
+    flipped = np.nonzero(~np.all(idx == r["idx"], axis=1))[0]
+    if n_flip == 0:
+        o_off, o_rt, o_sr = O.permute(r["idx"], E)
+        assert np.array_equal(off, o_off)
+        assert np.array_equal(rt, o_rt) and np.array_equal(sr, o_sr)
+    else:
+        check_permutation_valid(idx, off, rt, sr, E)
+    res = dict(near_ties=n_near, flipped=n_flip, b_new=b_dev)
+
+    # bias update after counting (bit-exact when the loads agree)
+    if gamma is not None and b_in is not None:
+        b_ref = O.bias_update(host_array(b_in), r["loads"] if n_flip == 0 else
+                              run.loads.cpu().numpy(), T, K, gamma)
+        b_gpu = host_array(b_dev)
+        if n_flip == 0:
+            assert np.array_equal(b_gpu.view(np.uint32), b_ref.view(np.uint32))
+        st = run.stats_host()
+        ls = O.load_stats(run.loads.cpu().numpy(), T, K)
+        assert st["max_load"] == ls["max_load"] and st["min_load"] == ls["min_load"]
+        assert abs(st["max_vio"] - ls["max_vio"]) <= 1e-6 * max(1.0, abs(ls["max_vio"]))
+        res["stats"] = st
+
+    rng = np.random.default_rng(seed)
+    experts = _expert_source(lay.w_gate, lay.w_up, lay.w_down)
+    shared = _expert_source(lay.ws_gate, lay.ws_up, lay.ws_down) if c.E_s else None
+    h_host = host_array(h)
+    tol = out_tol(c.dtype)
+
+    # layer output on a token sample (tokens whose picks flipped are excluded)
+    cand = np.setdiff1d(np.arange(T), flipped)
+    toks = cand if (check_all_tokens or len(cand) <= n_tok_sample) else np.sort(
+        rng.choice(cand, n_tok_sample, replace=False))
+    idx_s, g_s = r["idx"][toks], r["gates"][toks]
+    off_s, rt_s, sr_s = O.permute(idx_s, E)
+    y_perm_s = O.grouped_swiglu(h_host[toks], off_s, rt_s, experts)
+    y_sh_s = O.shared_experts(h_host[toks], shared, c.E_s) if c.E_s else None
+    y_ref = O.combine(h_host[toks], y_sh_s, y_perm_s, sr_s, g_s)
+    y_gpu = to_host_f64(run.y)[toks]
+    err = rel_err(y_gpu, y_ref)
+    h64 = O.to_f64(h_host[toks])
+    err_delta = rel_err(y_gpu - h64, y_ref - h64)
+    say(f"layer y: max|d|/max|y| = {err:.2e}; on y - h: {err_delta:.2e} ({len(toks)} tokens)")
+    assert err <= tol
+    # the expert part (y - h), with one output rounding of y allowed per element
+    assert np.all(np.abs((y_gpu - h64) - (y_ref - h64))
+                  <= tol * np.max(np.abs(y_ref - h64)) + 2.0 ** -8 * np.abs(y_ref))
+    res["y_rel_err"] = err
+    res["y_minus_h_rel_err"] = err_delta
+
+    # routed expert outputs (y_perm) of a sample of non-empty experts, all their rows
+    if n_flip == 0:
+        nonempty = np.nonzero(np.diff(off) > 0)[0]
+        ex = nonempty if len(nonempty) <= n_exp_sample else np.sort(
+            rng.choice(nonempty, n_exp_sample, replace=False))
+        y_perm = run.y_perm
+        worst = 0.0
+        for i in ex:
+            lo, hi = int(off[i]), int(off[i + 1])
+            rows = rt[lo:hi]
+            if hi - lo > 256:
+                pick = np.sort(rng.choice(hi - lo, 256, replace=False))
+            else:
+                pick = np.arange(hi - lo)
+            wg, wu, wd = experts(int(i))
+            ref = O.swiglu(h_host[rows[pick]], wg, wu, wd)
+            got = to_host_f64(y_perm[lo:hi])[pick]
+            e_i = rel_err(got, ref)
+            worst = max(worst, e_i)
+            assert e_i <= tol, f"expert {i}: {e_i}"
+        res["expert_rel_err"] = worst
+        say(f"expert outputs: worst max|d|/max|ref| = {worst:.2e} over experts {ex.tolist()}")
+        if c.E_s:
+            ysh = to_host_f64(run.y_shared).reshape(c.E_s, T, c.d_model)
+            for j in range(c.E_s):
+                ref = O.swiglu(h_host[toks], *shared(j))
+                assert rel_err(ysh[j][toks], ref) <= tol
+    return res

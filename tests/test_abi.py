@@ -1,0 +1,107 @@
+"""The C-ABI library: it loads, exports every function include/moe.h declares,
+and rejects invalid arguments on the host without launching anything (CPU
+only: none of these calls reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_biased_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine",
+              "moe_bias_update"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sorted(_declared()) == sorted(L.EXPORTED)
+
+
+def test_version():
+    assert "gfx950" in L.moe_version()
+
+
+def _st(rc):
+    return rc, L.moe_last_error()
+
+
+def test_route_rejects_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert _st(lib.moe_route(0, 128, 8, 2, 0, P, 1, P, None, P, P, P, None))[0] == L.MOE_ERR_INVALID_ARG
+    rc, msg = _st(lib.moe_route(64, 128, 8, 9, 0, P, 1, P, None, P, P, P, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "K=9 > E_r=8" in msg
+    assert lib.moe_route(64, 128, 32, 17, 0, P, 1, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 128, 8, 2, 0, None, 1, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 100, 8, 2, 0, P, 1, P, None, P, P, P, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(64, 128, 1024, 2, 0, P, 1, P, None, P, P, P, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(64, 128, 8, 2, 7, P, 1, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 128, 8, 2, 0, P, 5, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_permute_rejects_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    need = L.moe_permute_workspace_size(100, 8)
+    assert need > 0
+    rc, msg = _st(lib.moe_permute(100, 64, 8, 2, P, None, 1, P, P, P, None, P, need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    assert lib.moe_permute(100, 64, 8, 2, P, None, 1, P, P, P, P, P, need, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(100, 64, 2000, 2, P, None, 1, P, P, P, None, P, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute(100, 64, 8, 0, P, None, 1, P, P, P, None, P, need, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_grouped_swiglu_rejects_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    need = L.moe_grouped_swiglu_workspace_size(8, 256, 512, 1000, L.MOE_BF16)
+    assert need >= 1000 * 512 * 2
+    assert L.moe_grouped_swiglu_workspace_size(8, 256, 512, 1000, L.MOE_F32) >= 1000 * 512 * 4
+    rc, msg = _st(lib.moe_grouped_swiglu(8, 256, 512, 1000, 500, P, P, P, 1, P, P, P, None, P, P,
+                                         need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    rc, msg = _st(lib.moe_grouped_swiglu(8, 200, 512, 1000, 500, P, P, P, 1, P, P, P, None, P, P,
+                                         need, None))
+    assert rc == L.MOE_ERR_UNSUPPORTED and "multiples of 64" in msg
+    assert lib.moe_grouped_swiglu(8, 256, 512, 1000, 500, P, None, P, 1, P, P, P, None, P, P,
+                                  need, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_swiglu(8, 256, 512, 1000, 500, None, P, P, 1, P, P, P, None, P, P,
+                                  need, None) == L.MOE_ERR_INVALID_ARG
+    # zero rows is a valid no-op
+    assert lib.moe_grouped_swiglu(8, 256, 512, 0, 500, P, P, P, 1, P, P, P, None, P, P,
+                                  need, None) == L.MOE_OK
+
+
+def test_combine_and_bias_update_reject_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    assert lib.moe_combine(10, 64, 2, 1, P, None, P, P, P, 1, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(10, 60, 2, 0, P, None, P, P, P, 1, P, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(10, 64, 17, 0, P, None, P, P, P, 1, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(10, 8, 2, -0.1, P, P, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(10, 8, 2, float("nan"), P, P, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(10, 8, 2, 0.1, None, P, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(10, 4096, 2, 0.1, P, P, None, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        L._ptr(t)

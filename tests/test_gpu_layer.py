@@ -1,0 +1,60 @@
+"""End-to-end layer parity on the GPU for the tiny fp32 layer and the
+Mixtral-8x7B-shaped layer (full sizes; the oracle recomputes a token sample
+and an expert sample at Mixtral size)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import say
+from layer_check import check_layer, runner_for
+from oracle import moe_oracle as O
+from synthetic import CONFIGS, host_array, make_layer
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def test_tiny_fp32_layer_and_one_bias_update():
+    cfg = CONFIGS["tiny_fp32"]
+    say(f"{cfg.name}: T={cfg.T} d={cfg.d_model} E={cfg.E_r} K={cfg.K}")
+    lay = make_layer(cfg, device="cuda")
+    run = runner_for(lay)
+    b0 = lay.b.clone()
+    res = check_layer(lay, lay.h, b0, cfg.gamma, run, check_all_tokens=True)
+    say(str(res))
+    # one update with gamma = 0.1 against cbar = 16, then re-route with the new b:
+    b1 = b0.clone()
+    run.forward(lay.h, b1, cfg.gamma)
+    torch.cuda.synchronize()
+    ref_b1 = O.bias_update(host_array(b0), O.route(host_array(lay.h), host_array(lay.e),
+                                                   host_array(b0), cfg.K, cfg.score)["loads"],
+                           cfg.T, cfg.K, cfg.gamma)
+    assert np.array_equal(host_array(b1).view(np.uint32), ref_b1.view(np.uint32))
+    idx0, g0 = run.topk_idx.clone(), run.gates.clone()
+    run.route(lay.h, b1)
+    torch.cuda.synchronize()
+    same = (idx0 == run.topk_idx).all(dim=1)
+    assert torch.equal(g0[same].view(torch.int32), run.gates[same].view(torch.int32))
+    check_layer(lay, lay.h, b1, None, run, check_all_tokens=True)
+
+
+def test_mixtral_layer_full_size():
+    cfg = CONFIGS["mixtral_8x7b"]
+    say(f"{cfg.name}: T={cfg.T} d={cfg.d_model} E={cfg.E_r} K={cfg.K} d_ffn={cfg.d_ffn}")
+    lay = make_layer(cfg, device="cuda")
+    run = runner_for(lay)
+    res = check_layer(lay, lay.h, None, None, run, n_tok_sample=12, n_exp_sample=3, seed=1)
+    say(str(res))
+
+
+def test_mixtral_layer_ragged_tokens():
+    cfg = CONFIGS["mixtral_8x7b"].with_tokens(333)
+    lay = make_layer(cfg, device="cuda")
+    run = runner_for(lay)
+    check_layer(lay, lay.h, None, None, run, n_tok_sample=8, n_exp_sample=2, seed=2)

@@ -1,0 +1,335 @@
+"""Per-entry-point parity on the GPU at sizes the oracle finishes in seconds:
+each HIP entry point gets oracle-made (or generator-made) inputs and its output
+is compared with the oracle's on the same inputs.  Shapes span several tiles
+and ragged tails; edge cases: empty experts, total collapse, K = 1, K = E_r,
+invalid expert ids, softmax with a bias."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import GATE_TOL, check_route, out_tol, rel_err, say, to_host_f64
+from oracle import moe_oracle as O
+from sparse_mixture_experts_biased_amd import _lib as L
+from synthetic import host_array
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    L.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def _tokens(T, d, dtype, seed, scale=1.0):
+    x = torch.randn((T, d), generator=_gen(seed), device=DEV) * scale
+    return x.to(dtype)
+
+
+def _centroids(E, d, seed):
+    return (torch.randn((E, d), generator=_gen(seed), device=DEV) / math.sqrt(d)).contiguous()
+
+
+def _route_gpu(h, e, b, K, fn):
+    T, d = h.shape
+    E = e.shape[0]
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    loads = torch.empty((E,), dtype=torch.int32, device=DEV)
+    dt = L.MOE_BF16 if h.dtype == torch.bfloat16 else L.MOE_F32
+    L.moe_route(T, d, E, K, fn, h, dt, e, b, idx, gates, loads)
+    torch.cuda.synchronize()
+    return idx, gates, loads
+
+
+ROUTE_CASES = [
+    # T, d, E, K, fn, dtype, bias
+    (64, 128, 8, 2, "sigmoid", torch.float32, "zero"),
+    (333, 256, 8, 2, "softmax", torch.bfloat16, None),
+    (200, 512, 256, 8, "sigmoid", torch.bfloat16, "uniform"),
+    (77, 192, 64, 6, "sigmoid", torch.float32, "uniform"),
+    (50, 128, 16, 1, "sigmoid", torch.bfloat16, "uniform"),
+    (40, 128, 12, 12, "sigmoid", torch.float32, "uniform"),   # K = E_r
+    (129, 256, 512, 16, "sigmoid", torch.bfloat16, "uniform"),
+    (90, 128, 32, 4, "softmax", torch.float32, "uniform"),    # softmax + bias on p
+]
+
+
+@pytest.mark.parametrize("T,d,E,K,fn,dtype,bias", ROUTE_CASES)
+def test_route_parity(T, d, E, K, fn, dtype, bias):
+    say(f"moe_route T={T} d={d} E={E} K={K} {fn} {dtype}")
+    h = _tokens(T, d, dtype, 1000 + T)
+    e = _centroids(E, d, 2000 + E)
+    b = None
+    if bias == "zero":
+        b = torch.zeros(E, device=DEV)
+    elif bias == "uniform":
+        b = (torch.rand(E, generator=_gen(3000 + E), device=DEV) * 0.02 - 0.01)
+    idx, gates, loads = _route_gpu(h, e, b, K, L.MOE_SIGMOID if fn == "sigmoid" else L.MOE_SOFTMAX)
+    n_near, n_flip, _ = check_route(h, e, b, K, fn, idx, gates, loads, E)
+    say(f"near-ties {n_near}, flipped {n_flip}")
+
+
+def test_route_deterministic_and_gates_bias_invariant():
+    T, d, E, K = 500, 256, 64, 4
+    h = _tokens(T, d, torch.bfloat16, 11)
+    e = _centroids(E, d, 12)
+    b0 = torch.rand(E, generator=_gen(13), device=DEV) * 0.02 - 0.01
+    b1 = b0 + torch.rand(E, generator=_gen(14), device=DEV) * 0.002 - 0.001
+    i0, g0, c0 = _route_gpu(h, e, b0, K, L.MOE_SIGMOID)
+    i0b, g0b, c0b = _route_gpu(h, e, b0, K, L.MOE_SIGMOID)
+    assert torch.equal(i0, i0b) and torch.equal(g0.view(torch.int32), g0b.view(torch.int32))
+    assert torch.equal(c0, c0b)
+    i1, g1, _ = _route_gpu(h, e, b1, K, L.MOE_SIGMOID)
+    same = (i0 == i1).all(dim=1)
+    assert same.sum() > 0 and (~same).sum() > 0
+    # the bias only picks: identical selections give bit-identical gates
+    assert torch.equal(g0[same].view(torch.int32), g1[same].view(torch.int32))
+
+
+def test_route_worked_example_bias_moves_pick():
+    # The "cat" token of the Mixture of Experts designs page, section 1:
+    # logits 1.2, 1.0, -0.2, 0.0 (scores 0.77, 0.73, 0.45, 0.50); a bias of
+    # (-0.1, +0.1, +0.1, 0) moves its top-1 from E1 to E2 while the gate stays s/s = 1.
+    h = torch.tensor([[1.2, 1.0, -0.2, 0.0, 0, 0, 0, 0]], device=DEV, dtype=torch.float32)
+    e = torch.zeros((4, 8), device=DEV)
+    for i in range(4):
+        e[i, i] = 1.0
+    i0, g0, c0 = _route_gpu(h, e, torch.zeros(4, device=DEV), 1, L.MOE_SIGMOID)
+    i1, g1, c1 = _route_gpu(h, e, torch.tensor([-0.1, 0.1, 0.1, 0.0], device=DEV), 1,
+                            L.MOE_SIGMOID)
+    assert i0.item() == 0 and i1.item() == 1
+    assert g0.item() == 1.0 and g1.item() == 1.0
+    assert c0.tolist() == [1, 0, 0, 0] and c1.tolist() == [0, 1, 0, 0]
+    i2, g2, _ = _route_gpu(h, e, None, 2, L.MOE_SIGMOID)
+    s = 1.0 / (1.0 + np.exp(-np.array([1.2, 1.0])))
+    assert i2.tolist() == [[0, 1]]
+    assert np.allclose(g2.cpu().numpy()[0], s / s.sum(), atol=GATE_TOL)
+
+
+def _permute_gpu(idx, E, h=None):
+    T, K = idx.shape
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    row_token = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    slot_row = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    wsb = L.moe_permute_workspace_size(T, E)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    x_perm = None
+    dt = L.MOE_BF16
+    if h is not None:
+        x_perm = torch.empty((T * K, h.shape[1]), dtype=h.dtype, device=DEV)
+        dt = L.MOE_BF16 if h.dtype == torch.bfloat16 else L.MOE_F32
+    L.moe_permute(T, h.shape[1] if h is not None else 8, E, K, idx, h, dt, offsets, row_token,
+                  slot_row, x_perm, ws, wsb)
+    torch.cuda.synchronize()
+    return offsets, row_token, slot_row, x_perm
+
+
+@pytest.mark.parametrize("T,E,K", [(1, 4, 2), (255, 8, 2), (256, 8, 2), (1000, 256, 8),
+                                   (3, 64, 2), (4097, 1024, 3), (16384, 256, 8)])
+def test_permute_parity(T, E, K):
+    say(f"moe_permute T={T} E={E} K={K}")
+    rng = np.random.default_rng(T * 7 + E)
+    v = rng.random((T, E)).astype(np.float32)
+    idx = O.biased_topk(v, None, K)
+    off, rt, sr, _ = _permute_gpu(torch.from_numpy(idx).to(DEV), E)
+    o_off, o_rt, o_sr = O.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    assert np.array_equal(rt.cpu().numpy(), o_rt)
+    assert np.array_equal(sr.cpu().numpy(), o_sr)
+
+
+def test_permute_total_collapse_and_gather():
+    T, E, K, d = 700, 16, 2, 64
+    idx = np.tile(np.array([[3, 9]], dtype=np.int32), (T, 1))
+    h = _tokens(T, d, torch.bfloat16, 21)
+    off, rt, sr, xp = _permute_gpu(torch.from_numpy(idx).to(DEV), E, h)
+    o_off, o_rt, o_sr = O.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), o_off) and np.array_equal(rt.cpu().numpy(), o_rt)
+    assert np.array_equal(sr.cpu().numpy(), o_sr)
+    assert torch.equal(xp, h[rt.long()])
+
+
+def test_permute_skips_invalid_ids():
+    T, E, K = 300, 8, 2
+    rng = np.random.default_rng(5)
+    idx = O.biased_topk(rng.random((T, E)).astype(np.float32), None, K)
+    bad = idx.copy()
+    bad[7, 1] = -1
+    bad[100, 0] = E
+    off, rt, sr, _ = _permute_gpu(torch.from_numpy(bad).to(DEV), E)
+    keep = (bad >= 0) & (bad < E)
+    assert int(off[-1]) == keep.sum() == T * K - 2
+    srh = sr.cpu().numpy().reshape(T, K)
+    assert srh[7, 1] == -1 and srh[100, 0] == -1
+    rth = rt.cpu().numpy()
+    assert np.all(rth[T * K - 2:] == -1)
+    # the kept copies are a valid stable permutation
+    counts = np.bincount(bad[keep], minlength=E)
+    assert np.array_equal(np.diff(off.cpu().numpy()), counts)
+    for i in range(E):
+        seg = rth[off[i]:off[i + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def _swiglu_gpu(x, offsets, row_index, wg, wu, wd, rows, row_scale=None):
+    n_groups = wg.shape[0]
+    d, f = x.shape[1], wg.shape[1]
+    dt = L.MOE_BF16 if x.dtype == torch.bfloat16 else L.MOE_F32
+    wsb = L.moe_grouped_swiglu_workspace_size(n_groups, d, f, rows, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    y = torch.zeros((rows, d), dtype=x.dtype, device=DEV)
+    L.moe_grouped_swiglu(n_groups, d, f, rows, x.shape[0], offsets, row_index, x, dt, wg, wu, wd,
+                         row_scale, y, ws, wsb)
+    torch.cuda.synchronize()
+    return y
+
+
+def _weights(E, d, f, dtype, seed):
+    g = _gen(seed)
+    wg = (torch.randn((E, f, d), generator=g, device=DEV) / math.sqrt(d)).to(dtype)
+    wu = (torch.randn((E, f, d), generator=g, device=DEV) / math.sqrt(d)).to(dtype)
+    wd = (torch.randn((E, d, f), generator=g, device=DEV) / math.sqrt(f)).to(dtype)
+    return wg, wu, wd
+
+
+SWIGLU_CASES = [
+    # T, d, f, E, K, dtype
+    (64, 128, 256, 8, 2, torch.float32),
+    (333, 256, 192, 5, 2, torch.bfloat16),     # partial column tile (192 = 128 + 64)
+    (300, 512, 256, 16, 4, torch.bfloat16),
+    (3, 128, 128, 64, 2, torch.bfloat16),      # mostly empty experts
+    (1000, 256, 128, 4, 1, torch.bfloat16),    # big groups: many row tiles
+    (97, 64, 64, 3, 3, torch.bfloat16),        # K = E_r, smallest aligned sizes
+    (150, 96, 80, 6, 2, torch.float32),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,K,dtype", SWIGLU_CASES)
+def test_grouped_swiglu_parity(T, d, f, E, K, dtype):
+    say(f"moe_grouped_swiglu T={T} d={d} f={f} E={E} K={K} {dtype}")
+    rng = np.random.default_rng(T + d + f)
+    idx = O.biased_topk(rng.random((T, E)).astype(np.float32), None, K)
+    off, rt, _ = O.permute(idx, E)
+    x = _tokens(T, d, dtype, 40 + T)
+    wg, wu, wd = _weights(E, d, f, dtype, 50 + E)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(rt).to(DEV), wg, wu, wd,
+                    T * K)
+    w_host = (host_array(wg), host_array(wu), host_array(wd))
+    ref = O.grouped_swiglu(host_array(x), off, rt, w_host)
+    err = rel_err(to_host_f64(y), ref)
+    say(f"max|d|/max|ref| = {err:.3e}")
+    assert err <= out_tol("bf16" if dtype == torch.bfloat16 else "f32")
+    # per expert too, so a wrong or missing expert cannot hide behind the others
+    for i in range(E):
+        lo, hi = off[i], off[i + 1]
+        if hi > lo:
+            assert rel_err(to_host_f64(y)[lo:hi], ref[lo:hi]) <= 4 * out_tol(
+                "bf16" if dtype == torch.bfloat16 else "f32")
+
+
+def test_grouped_swiglu_row_scale_and_direct_rows():
+    T, d, f, E = 257, 128, 128, 3
+    x = _tokens(T, d, torch.bfloat16, 61)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, 62)
+    off = np.array([0, 100, 100, 257], dtype=np.int32)    # one empty group
+    scale = torch.rand(T, generator=_gen(63), device=DEV)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), None, wg, wu, wd, T, scale)
+    ref = O.grouped_swiglu(host_array(x), off, None,
+                           (host_array(wg), host_array(wu), host_array(wd)))
+    ref = ref * scale.cpu().numpy().astype(np.float64)[:, None]
+    assert rel_err(to_host_f64(y), ref) <= out_tol("bf16")
+
+
+def test_grouped_swiglu_bad_row_index_reads_zero_row():
+    T, d, f, E = 40, 64, 64, 2
+    x = _tokens(T, d, torch.bfloat16, 71)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, 72)
+    off = np.array([0, 20, 40], dtype=np.int32)
+    ri = np.arange(40, dtype=np.int32) % T
+    ri[5] = -3
+    ri[30] = 10_000
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(ri).to(DEV), wg, wu, wd, 40)
+    yh = to_host_f64(y)
+    assert np.all(yh[5] == 0) and np.all(yh[30] == 0)   # SwiGLU(0) = 0
+
+
+def _combine_gpu(h, y_shared, y_perm, slot_row, gates, E_s):
+    T, d = h.shape
+    K = gates.shape[1]
+    dt = L.MOE_BF16 if h.dtype == torch.bfloat16 else L.MOE_F32
+    y = torch.empty_like(h)
+    L.moe_combine(T, d, K, E_s, h, y_shared, y_perm, slot_row, gates, dt, y)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("T,d,K,E_s,dtype", [(64, 128, 2, 0, torch.float32),
+                                             (333, 256, 8, 1, torch.bfloat16),
+                                             (100, 7168, 8, 2, torch.bfloat16),
+                                             (31, 64, 1, 0, torch.bfloat16)])
+def test_combine_parity(T, d, K, E_s, dtype):
+    say(f"moe_combine T={T} d={d} K={K} E_s={E_s} {dtype}")
+    rng = np.random.default_rng(T + K)
+    h = _tokens(T, d, dtype, 81)
+    yp = _tokens(T * K, d, dtype, 82, 0.3)
+    ys = _tokens(E_s * T, d, dtype, 83, 0.5) if E_s else None
+    perm = rng.permutation(T * K).astype(np.int32)
+    g = rng.random((T, K)).astype(np.float32)
+    g /= g.sum(1, keepdims=True)
+    y = _combine_gpu(h, ys, yp, torch.from_numpy(perm).to(DEV), torch.from_numpy(g).to(DEV), E_s)
+    ysh = to_host_f64(ys).reshape(E_s, T, d).sum(0) if E_s else None
+    ref = O.combine(host_array(h), ysh, to_host_f64(yp), perm, g)
+    yh = to_host_f64(y)
+    # fp32 accumulation then one rounding of the output
+    tol = (2.0 ** -7) * np.abs(ref) + 1e-6 if dtype == torch.bfloat16 else 1e-5 * np.abs(ref) + 1e-6
+    assert np.all(np.abs(yh - ref) <= tol)
+
+
+def _bias_gpu(T, K, gamma, loads, b):
+    E = loads.shape[0]
+    lt = torch.from_numpy(loads.astype(np.int32)).to(DEV)
+    bt = torch.from_numpy(b.astype(np.float32)).to(DEV)
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    L.moe_bias_update(T, E, K, gamma, lt, bt, st)
+    torch.cuda.synchronize()
+    sth = st.cpu()
+    return bt.cpu().numpy(), (int(sth[0]), int(sth[1]), float(sth[2:3].view(torch.float32)[0]))
+
+
+def test_bias_update_worked_example(golden_dir):
+    import json
+    import os
+    with open(os.path.join(golden_dir, "bias_update_example.json")) as f:
+        ex = json.load(f)
+    b1, st = _bias_gpu(ex["T"], ex["K"], ex["gamma"], np.array(ex["loads"]), np.array(ex["b0"]))
+    assert np.array_equal(b1, np.array(ex["b1"], dtype=np.float32))
+    assert st[0] == 3 and st[1] == 0 and st[2] == pytest.approx(ex["max_vio"], rel=1e-7)
+
+
+@pytest.mark.parametrize("T,E,K,gamma", [(64, 8, 2, 0.1), (4096, 256, 8, 0.001),
+                                         (5, 4, 3, 0.5), (16384, 256, 8, 0.0),
+                                         (1000, 1024, 7, 0.01)])
+def test_bias_update_parity(T, E, K, gamma):
+    rng = np.random.default_rng(E + K)
+    loads = rng.multinomial(T * K, np.ones(E) / E).astype(np.int32)
+    if K * T % E == 0:
+        loads[0] = K * T // E  # one expert exactly at the fair share: bias unchanged
+    b = (rng.random(E) * 0.02 - 0.01).astype(np.float32)
+    b1, st = _bias_gpu(T, K, gamma, loads, b)
+    ref = O.bias_update(b, loads, T, K, gamma)
+    assert np.array_equal(b1.view(np.uint32), ref.view(np.uint32))
+    ls = O.load_stats(loads, T, K)
+    assert st[0] == ls["max_load"] and st[1] == ls["min_load"]
+    assert st[2] == pytest.approx(ls["max_vio"], rel=1e-6, abs=1e-7)
