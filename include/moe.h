@@ -83,14 +83,21 @@ typedef struct {
  *            denominator summed in ascending expert id; aligned with topk_idx
  *   loads    [E_r] int32 out: c_i = #{t : i in I_t} (zeroed by this call)
  *
- * z = h . e_i is accumulated in fp32; the selection ranks v = fl32(s + b);
- * equal v -> the lower expert id is picked.  With MOE_SOFTMAX and a non-NULL
- * b, the bias is added to p.
- * Limits: 1 <= K <= min(E_r, MOE_MAX_TOPK), E_r <= 512, d_model % 8 == 0.
+ *   workspace device scratch of at least moe_route_workspace_size() bytes
+ *            (partial logits; 0 bytes and NULL allowed for fp32 tokens)
+ *
+ * z = h . e_i has fp32 accuracy (bf16 tokens: e split exactly into three bf16
+ * parts on the matrix cores, fp32 accumulation; fp32 tokens: fp32 FMA); the
+ * selection ranks v = fl32(s + b); equal v -> the lower expert id is picked.
+ * With MOE_SOFTMAX and a non-NULL b, the bias is added to p.  Deterministic.
+ * Limits: 1 <= K <= min(E_r, MOE_MAX_TOPK), E_r <= 512, d_model % 8 == 0
+ * (bf16 tokens: d_model % 32 == 0).
  */
+size_t moe_route_workspace_size(int T, int d_model, int E_r, moe_dtype h_dtype);
 moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn,
                      const void* h, moe_dtype h_dtype, const float* e, const float* b,
-                     int32_t* topk_idx, float* gates, int32_t* loads, void* stream);
+                     int32_t* topk_idx, float* gates, int32_t* loads, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /*
  * moe_permute -- dispatch: expert histogram, exclusive scan, stable

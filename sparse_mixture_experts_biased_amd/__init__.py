@@ -9,12 +9,12 @@ from ._lib import (MOE_BF16, MOE_F32, MOE_SIGMOID, MOE_SOFTMAX, MoeBiasStats, Mo
                    load, moe_bias_update, moe_combine, moe_grouped_swiglu,
                    moe_grouped_swiglu_workspace_size, moe_last_error, moe_permute,
                    moe_permute_workspace_size, moe_profile_enable, moe_profile_report, moe_profile_tag,
-                   moe_route,
+                   moe_route, moe_route_workspace_size,
                    moe_version)
 from .layer import LayerShape, MoELayer
 
 __all__ = ["MOE_BF16", "MOE_F32", "MOE_SIGMOID", "MOE_SOFTMAX", "MoeBiasStats", "MoeError",
            "load", "moe_bias_update", "moe_combine", "moe_grouped_swiglu",
            "moe_grouped_swiglu_workspace_size", "moe_last_error", "moe_permute",
-           "moe_permute_workspace_size", "moe_profile_enable", "moe_profile_report", "moe_profile_tag", "moe_route",
+           "moe_permute_workspace_size", "moe_profile_enable", "moe_profile_report", "moe_profile_tag", "moe_route", "moe_route_workspace_size",
            "moe_version", "LayerShape", "MoELayer"]

@@ -15,7 +15,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SIGMOID, MOE_SOFTMAX = 0, 1
 
-EXPORTED = ["moe_route", "moe_permute_workspace_size", "moe_permute",
+EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "moe_bias_update", "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -47,7 +47,8 @@ def load() -> ctypes.CDLL:
                           "`python -m sparse_mixture_experts_biased_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
-        "moe_route": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p], _i),
+        "moe_route_workspace_size": ([_i, _i, _i, _i], _sz),
+        "moe_route": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _sz, _p], _i),
         "moe_permute_workspace_size": ([_i, _i], _sz),
         "moe_permute": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
         "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
@@ -105,9 +106,15 @@ def moe_last_error() -> str:
     return load().moe_last_error().decode(errors="replace")
 
 
-def moe_route(T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx, gates, loads, stream=None):
+def moe_route_workspace_size(T, d_model, E_r, h_dtype) -> int:
+    return int(load().moe_route_workspace_size(T, d_model, E_r, h_dtype))
+
+
+def moe_route(T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx, gates, loads, workspace,
+              workspace_bytes, stream=None):
     _check(load().moe_route(T, d_model, E_r, K, fn, _ptr(h), h_dtype, _ptr(e), _ptr(b),
-                            _ptr(topk_idx), _ptr(gates), _ptr(loads), _stream(stream)))
+                            _ptr(topk_idx), _ptr(gates), _ptr(loads), _ptr(workspace),
+                            workspace_bytes, _stream(stream)))
 
 
 def moe_permute_workspace_size(T, E_r) -> int:

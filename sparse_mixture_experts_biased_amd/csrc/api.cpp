@@ -46,9 +46,15 @@ const char* moe_last_error(void) { return g_err; }
 
 const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
 
+size_t moe_route_workspace_size(int T, int d_model, int E_r, moe_dtype h_dtype) {
+  if (T < 1 || d_model < 1 || E_r < 1 || !valid_dtype(h_dtype)) return 0;
+  return moe::route_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16);
+}
+
 moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
                      moe_dtype h_dtype, const float* e, const float* b, int32_t* topk_idx,
-                     float* gates, int32_t* loads, void* stream) {
+                     float* gates, int32_t* loads, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (T < 1 || d_model < 1 || E_r < 1 || K < 1)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%d d_model=%d E_r=%d K=%d must be >= 1", T,
                 d_model, E_r, K);
@@ -61,12 +67,18 @@ moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn, const 
   if (!valid_dtype(h_dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_route: bad dtype");
   if (d_model % 8 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "moe_route: d_model=%d not a multiple of 8", d_model);
+  if (h_dtype == MOE_BF16 && d_model % 32 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route: bf16 tokens need d_model %% 32 == 0 (got %d)",
+                d_model);
   if (!h || !e || !topk_idx || !gates || !loads)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  const size_t need = moe::route_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace %zu < %zu bytes", workspace_bytes, need);
   if (static_cast<long long>(T) * K > INT32_MAX || static_cast<long long>(T) * d_model > (1LL << 40))
     return fail(MOE_ERR_INVALID_ARG, "moe_route: sizes overflow");
   return hip_status(moe::launch_route(T, d_model, E_r, K, (int)fn, h, h_dtype == MOE_BF16, e, b,
-                                      topk_idx, gates, loads, as_stream(stream)),
+                                      topk_idx, gates, loads, workspace, as_stream(stream)),
                     "moe_route");
 }
 

@@ -38,9 +38,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Each returns the hipError_t of its last launch.
 
 // router
+int route_splits(int T, int d, int E, int h_bf16);
+size_t route_workspace_bytes(int T, int d, int E, int h_bf16);
 hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h_bf16,
                         const float* e, const float* b, int32_t* idx, float* gates,
-                        int32_t* loads, hipStream_t s);
+                        int32_t* loads, void* ws, hipStream_t s);
 
 // dispatch
 constexpr int kPermChunk = 256;  // tokens per histogram / rank chunk

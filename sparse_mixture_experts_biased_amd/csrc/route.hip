@@ -1,17 +1,26 @@
-// Router: z = h . e (fp32), score function, biased top-K, unbiased gates and
-// the load histogram, fused in one kernel.
+// Router: z = h . e (fp32 accuracy), score function, biased top-K, unbiased
+// gates and the load histogram.
 //
 // Method: Sparse MoE routing-math page (arman1o1.github.io), section 2
 // (I_t = TopK(s + b, K), g = s / sum_{I_t} s, sigmoid affinity) and the
 // classical-router listing of section 1 (softmax, top-K, renormalise, clamp
 // 1e-12); section 4 item 2 keeps the router in fp32.
 //
-// Layout: one workgroup of 256 threads owns BT = 16 tokens and all E experts.
-// The z tile [16 x E] is built from LDS-staged h and e slices (fp32 FMA), then
-// each wave ranks four tokens: K rounds of a wave-wide arg-max over v = s + b
-// (equal v -> lower expert id), a sort of the K picks by expert id, and the
-// gate denominator summed in that order, so the gates depend only on the
-// picked set.
+// bf16 tokens (the large workloads): the logits run on the matrix cores.  The
+// fp32 centroids are split exactly into three bf16 parts, e = e_hi + e_mid +
+// e_lo (truncate, truncate, remainder: 8 + 8 + 8 significant bits), so every
+// product h * e_part is exact in fp32 and the MFMA accumulates in fp32 --
+// fp32 accuracy at bf16 matrix-core rate (the bf16x3 split of Henry, Tang and
+// Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype For
+// Higher-Precision Computations", 2019).  The d_model loop is split S ways
+// across workgroups into fixed partial sums; the top-K kernel adds them in a
+// fixed order, so z is deterministic.
+// fp32 tokens (the tiny workload): one fused kernel with fp32 FMA.
+//
+// Selection (both paths): one wave per token, E/64 experts per lane, K rounds
+// of a wave-wide arg-max over v = s + b (equal v -> lower expert id), a sort of
+// the K picks by expert id, and the gate denominator summed in that order, so
+// the gates depend only on the picked set.
 #include "common.h"
 
 #include <math.h>
@@ -19,28 +28,16 @@
 namespace moe {
 namespace {
 
-constexpr int kBT = 16;       // tokens per workgroup
-constexpr int kBK = 32;       // d_model slice per LDS stage
-constexpr int kThreads = 256;
-constexpr int kTokPerWave = kBT / 4;
+constexpr int kSent = 0x7fffffff;  // "no expert"
 
-template <typename TIn>
-__device__ __forceinline__ float load_in(const TIn* p, size_t i);
-template <>
-__device__ __forceinline__ float load_in<float>(const float* p, size_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p, size_t i) {
-  return bf16_to_f32(p[i]);
-}
-
-// Arg-max over the wave: larger v wins, equal v -> smaller expert id.
+// Arg-max over the wave: larger v wins, equal v -> smaller expert id; a real
+// expert id always beats the sentinel.
 __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     float ov = __shfl_xor(v, m, kWave);
     int oid = __shfl_xor(id, m, kWave);
-    // a real expert id always beats the "none" sentinel
-    if (oid != 0x7fffffff && (id == 0x7fffffff || ov > v || (ov == v && oid < id))) {
+    if (oid != kSent && (id == kSent || ov > v || (ov == v && oid < id))) {
       v = ov;
       id = oid;
     }
@@ -59,15 +56,117 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <typename TIn, int EJ>
-__global__ __launch_bounds__(kThreads) void route_kernel(
-    int T, int d, int E, int K, int fn, const TIn* __restrict__ h,
-    const float* __restrict__ e, const float* __restrict__ b, int32_t* __restrict__ idx_out,
-    float* __restrict__ gate_out, int32_t* __restrict__ loads) {
+// Scores, biased top-K, gates and load counts of token t; z[j] is the logit of
+// expert lane + 64 j (ignored for experts >= E).  Called by a whole wave.
+template <int EJ>
+__device__ __forceinline__ void select_token(int t, int E, int K, int fn, const float (&z)[EJ],
+                                             const float (&bias)[EJ], int32_t* __restrict__ idx_out,
+                                             float* __restrict__ gate_out,
+                                             int32_t* __restrict__ loads) {
+  const int lane = threadIdx.x % kWave;
+  float s[EJ], v[EJ];
+  if (fn == 0) {
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) s[j] = 1.0f / (1.0f + expf(-z[j]));
+  } else {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EJ; ++j)
+      if (lane + kWave * j < E) m = fmaxf(m, z[j]);
+    m = wave_max(m);
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+      s[j] = (lane + kWave * j < E) ? expf(z[j] - m) : 0.0f;
+      part += s[j];
+    }
+    const float tot = wave_sum(part);
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) s[j] = s[j] / tot;
+  }
+#pragma unroll
+  for (int j = 0; j < EJ; ++j) v[j] = s[j] + bias[j];
+
+  // K rounds of arg-max; sel / sv hold the picks (wave-uniform).
+  int sel[MOE_MAX_TOPK_DEV];
+  float sv[MOE_MAX_TOPK_DEV];
+  unsigned taken = 0u;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    sel[k] = kSent;
+    sv[k] = 0.0f;
+    if (k < K) {
+      float bv = -INFINITY;
+      int be = kSent;
+#pragma unroll
+      for (int j = 0; j < EJ; ++j) {
+        const int ex = lane + kWave * j;
+        const bool ok = ex < E && !((taken >> j) & 1u);
+        // the first free candidate is always taken, so a NaN score cannot
+        // leave the pick without an expert id
+        if (ok && (be == kSent || v[j] > bv || (v[j] == bv && ex < be))) {
+          bv = v[j];
+          be = ex;
+        }
+      }
+      wave_argmax(bv, be);
+      if (be < 0 || be >= E) be = 0;  // only reachable with non-finite scores
+      const int jw = be / kWave;      // wave-uniform
+      float sj = 0.0f;
+#pragma unroll
+      for (int j = 0; j < EJ; ++j)
+        if (j == jw) sj = s[j];
+      sj = __shfl(sj, be % kWave, kWave);
+      if (lane == be % kWave) taken |= 1u << jw;
+      sel[k] = be;
+      sv[k] = sj;
+    }
+  }
+  // ascending expert id (sentinel ids sort last)
+#pragma unroll
+  for (int a = 0; a < MOE_MAX_TOPK_DEV - 1; ++a)
+#pragma unroll
+    for (int c = 0; c < MOE_MAX_TOPK_DEV - 1 - a; ++c)
+      if (sel[c] > sel[c + 1]) {
+        int ti = sel[c]; sel[c] = sel[c + 1]; sel[c + 1] = ti;
+        float tf = sv[c]; sv[c] = sv[c + 1]; sv[c + 1] = tf;
+      }
+  float den = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (k < K) den += sv[k];
+  den = fmaxf(den, 1e-12f);
+  int my_id = 0;
+  float my_s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (k == lane) {
+      my_id = sel[k];
+      my_s = sv[k];
+    }
+  if (lane < K) {
+    idx_out[static_cast<size_t>(t) * K + lane] = my_id;
+    gate_out[static_cast<size_t>(t) * K + lane] = my_s / den;
+    if (my_id >= 0 && my_id < E) atomicAdd(&loads[my_id], 1);
+  }
+}
+
+// ------------------------------------------------------------ fp32 tokens: fused
+
+constexpr int kBT = 16;       // tokens per workgroup
+constexpr int kBK = 32;       // d_model slice per LDS stage
+constexpr int kThreads = 256;
+constexpr int kTokPerWave = kBT / 4;
+
+template <int EJ>
+__global__ __launch_bounds__(kThreads) void route_f32_kernel(
+    int T, int d, int E, int K, int fn, const float* __restrict__ h, const float* __restrict__ e,
+    const float* __restrict__ b, int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+    int32_t* __restrict__ loads) {
   extern __shared__ float smem[];
   float* hs = smem;                       // [kBT][kBK]
   float* es = smem + kBT * kBK;           // [E][kBK + 1]
-  float* zs = es;                         // reused after the K loop: [kBT][E]
+  float* zs = es;                         // reused after the d loop: [kBT][E]
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -84,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     for (int q = tid; q < kBT * kBK; q += kThreads) {
       int r = q / kBK, c = q % kBK;
       int t = t0 + r, k = k0 + c;
-      hs[q] = (t < T && k < d) ? load_in<TIn>(h, static_cast<size_t>(t) * d + k) : 0.0f;
+      hs[q] = (t < T && k < d) ? h[static_cast<size_t>(t) * d + k] : 0.0f;
     }
     for (int q = tid; q < E * kBK; q += kThreads) {
       int r = q / kBK, c = q % kBK;
@@ -108,7 +207,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     __syncthreads();
   }
 
-  // z tile to LDS (the e slice is no longer needed).
 #pragma unroll
   for (int i = 0; i < kTokPerWave; ++i)
 #pragma unroll
@@ -124,104 +222,154 @@ __global__ __launch_bounds__(kThreads) void route_kernel(
     int ex = lane + kWave * j;
     bias[j] = (b != nullptr && ex < E) ? b[ex] : 0.0f;
   }
-
   for (int i = 0; i < kTokPerWave; ++i) {
     const int r = wave * kTokPerWave + i;
     const int t = t0 + r;
     if (t >= T) break;  // wave-uniform
-    float s[EJ], v[EJ];
-    if (fn == 0) {
+    float z[EJ];
 #pragma unroll
-      for (int j = 0; j < EJ; ++j) {
-        int ex = lane + kWave * j;
-        float z = (ex < E) ? zs[r * E + ex] : 0.0f;
-        s[j] = 1.0f / (1.0f + expf(-z));
-      }
-    } else {
-      float m = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < EJ; ++j) {
-        int ex = lane + kWave * j;
-        if (ex < E) m = fmaxf(m, zs[r * E + ex]);
-      }
-      m = wave_max(m);
-      float part = 0.0f;
-#pragma unroll
-      for (int j = 0; j < EJ; ++j) {
-        int ex = lane + kWave * j;
-        s[j] = (ex < E) ? expf(zs[r * E + ex] - m) : 0.0f;
-        part += s[j];
-      }
-      float tot = wave_sum(part);
-#pragma unroll
-      for (int j = 0; j < EJ; ++j) s[j] = s[j] / tot;
+    for (int j = 0; j < EJ; ++j) {
+      int ex = lane + kWave * j;
+      z[j] = (ex < E) ? zs[r * E + ex] : 0.0f;
     }
-#pragma unroll
-    for (int j = 0; j < EJ; ++j) v[j] = s[j] + bias[j];
-
-    // K rounds of arg-max; sel/sv hold the picks (wave-uniform).
-    int sel[MOE_MAX_TOPK_DEV];
-    float sv[MOE_MAX_TOPK_DEV];
-    unsigned taken = 0u;
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
-      sel[k] = 0x7fffffff;
-      sv[k] = 0.0f;
-      if (k < K) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int j = 0; j < EJ; ++j) {
-          int ex = lane + kWave * j;
-          bool ok = ex < E && !((taken >> j) & 1u);
-          // the first free candidate is always taken, so a NaN score cannot
-          // leave the pick without an expert id
-          if (ok && (be == 0x7fffffff || v[j] > bv || (v[j] == bv && ex < be))) {
-            bv = v[j];
-            be = ex;
-          }
-        }
-        wave_argmax(bv, be);
-        if (be < 0 || be >= E) be = 0;      // only reachable with non-finite scores
-        const int jw = be / kWave;          // uniform
-        float sj = 0.0f;
-#pragma unroll
-        for (int j = 0; j < EJ; ++j)
-          if (j == jw) sj = s[j];
-        sj = __shfl(sj, be % kWave, kWave);
-        if (lane == be % kWave) taken |= 1u << jw;
-        sel[k] = be;
-        sv[k] = sj;
-      }
-    }
-    // ascending expert id (sentinel ids sort last)
-#pragma unroll
-    for (int a = 0; a < MOE_MAX_TOPK_DEV - 1; ++a)
-#pragma unroll
-      for (int c = 0; c < MOE_MAX_TOPK_DEV - 1 - a; ++c)
-        if (sel[c] > sel[c + 1]) {
-          int ti = sel[c]; sel[c] = sel[c + 1]; sel[c + 1] = ti;
-          float tf = sv[c]; sv[c] = sv[c + 1]; sv[c + 1] = tf;
-        }
-    float den = 0.0f;
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
-      if (k < K) den += sv[k];
-    den = fmaxf(den, 1e-12f);
-    int my_id = 0;
-    float my_s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
-      if (k == lane) {
-        my_id = sel[k];
-        my_s = sv[k];
-      }
-    if (lane < K) {
-      idx_out[static_cast<size_t>(t) * K + lane] = my_id;
-      gate_out[static_cast<size_t>(t) * K + lane] = my_s / den;
-      if (my_id >= 0 && my_id < E) atomicAdd(&loads[my_id], 1);
-    }
+    select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads);
   }
+}
+
+// ------------------------------------------------------------ bf16 tokens: MFMA
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kZT = 128;   // tokens per workgroup tile
+constexpr int kZE = 128;   // experts per workgroup tile
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo_bits, uint32_t hi_bits) {
+  return (lo_bits >> 16) | (hi_bits & 0xffff0000u);
+}
+
+// Exact three-way bf16 split of 8 fp32 values: x = hi + mid + lo.
+__device__ __forceinline__ void split3(const float4& p, const float4& q, bf16x8_t& hi,
+                                       bf16x8_t& mid, bf16x8_t& lo) {
+  const float x[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t xb = __float_as_uint(x[i]);
+    h[i] = xb & 0xffff0000u;                                  // truncate: top 8 bits
+    const float r1 = x[i] - __uint_as_float(h[i]);            // exact
+    m[i] = __float_as_uint(r1) & 0xffff0000u;                 // next 8 bits
+    const float r2 = r1 - __uint_as_float(m[i]);              // exact, <= 8 bits left
+    l[i] = __float_as_uint(r2);                               // exact in bf16
+  }
+  uint4 hv, mv, lv;
+  hv.x = pack2(h[0], h[1]); hv.y = pack2(h[2], h[3]); hv.z = pack2(h[4], h[5]); hv.w = pack2(h[6], h[7]);
+  mv.x = pack2(m[0], m[1]); mv.y = pack2(m[2], m[3]); mv.z = pack2(m[4], m[5]); mv.w = pack2(m[6], m[7]);
+  lv.x = pack2(l[0], l[1]); lv.y = pack2(l[2], l[3]); lv.z = pack2(l[4], l[5]); lv.w = pack2(l[6], l[7]);
+  hi = __builtin_bit_cast(bf16x8_t, hv);
+  mid = __builtin_bit_cast(bf16x8_t, mv);
+  lo = __builtin_bit_cast(bf16x8_t, lv);
+}
+
+// zpart[s][t][i] = sum over k in split s of h[t][k] * e[i][k].
+// Workgroup: 128 tokens x 128 experts, four waves in 2 x 2, each 64 x 64 as
+// 2 x 2 blocks of 32 x 32; operands straight from global memory (h rows and
+// e rows are both k-contiguous: one 16-byte / two 16-byte loads per lane).
+__global__ __launch_bounds__(256) void route_logits_mfma_kernel(int T, int d, int E, int klen,
+                                                                const uint16_t* __restrict__ h,
+                                                                const float* __restrict__ e,
+                                                                float* __restrict__ zpart) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int t_base = blockIdx.x * kZT + (wave >> 1) * 64;
+  const int e_base = blockIdx.y * kZE + (wave & 1) * 64;
+  const int split = blockIdx.z;
+  const int k_begin = split * klen;
+
+  const uint16_t* hp[2];
+  const float* ep[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = t_base + b * 32 + fr;
+    const int ex = e_base + b * 32 + fr;
+    hp[b] = (t < T) ? h + static_cast<size_t>(t) * d + k_begin + fh * 8 : nullptr;
+    ep[b] = (ex < E) ? e + static_cast<size_t>(ex) * d + k_begin + fh * 8 : nullptr;
+  }
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
+
+  uint4 ha[2];
+  float4 e0[2], e1[2];
+#define MOE_FETCH(K)                                                                         \
+  do {                                                                                       \
+    _Pragma("unroll") for (int b = 0; b < 2; ++b) {                                          \
+      ha[b] = hp[b] ? *reinterpret_cast<const uint4*>(hp[b] + (K)) : make_uint4(0, 0, 0, 0);  \
+      e0[b] = ep[b] ? *reinterpret_cast<const float4*>(ep[b] + (K)) : make_float4(0, 0, 0, 0); \
+      e1[b] = ep[b] ? *reinterpret_cast<const float4*>(ep[b] + (K) + 4) : make_float4(0, 0, 0, 0); \
+    }                                                                                        \
+  } while (0)
+  MOE_FETCH(0);
+  for (int k = 0; k < klen; k += 16) {
+    bf16x8_t af[2], bh[2], bm[2], bl[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      af[b] = __builtin_bit_cast(bf16x8_t, ha[b]);
+      split3(e0[b], e1[b], bh[b], bm[b], bl[b]);
+    }
+    if (k + 16 < klen) MOE_FETCH(k + 16);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bl[b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bm[b], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bh[b], acc[a][b], 0, 0, 0);
+      }
+  }
+#undef MOE_FETCH
+  // D[row = token][col = expert]: lane (col + 32*((row/4)%2)), register (row%4) + 4*(row/8)
+  float* zs = zpart + static_cast<size_t>(split) * T * E;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int ex = e_base + b * 32 + fr;
+      if (ex >= E) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int t = t_base + a * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
+        if (t < T) zs[static_cast<size_t>(t) * E + ex] = acc[a][b][q];
+      }
+    }
+}
+
+// One wave per token: z = sum_s zpart[s] (fixed order), then selection.
+template <int EJ>
+__global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int K, int fn, int S,
+                                                         const float* __restrict__ zpart,
+                                                         const float* __restrict__ b,
+                                                         int32_t* __restrict__ idx_out,
+                                                         float* __restrict__ gate_out,
+                                                         int32_t* __restrict__ loads) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (t >= T) return;  // wave-uniform
+  float z[EJ], bias[EJ];
+#pragma unroll
+  for (int j = 0; j < EJ; ++j) {
+    const int ex = lane + kWave * j;
+    float acc = 0.0f;
+    if (ex < E)
+      for (int s = 0; s < S; ++s) acc += zpart[(static_cast<size_t>(s) * T + t) * E + ex];
+    z[j] = acc;
+    bias[j] = (b != nullptr && ex < E) ? b[ex] : 0.0f;
+  }
+  select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
@@ -229,48 +377,52 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
   if (i < n) p[i] = v;
 }
 
-template <typename TIn>
-hipError_t launch_typed(int T, int d, int E, int K, int fn, const TIn* h, const float* e,
-                        const float* b, int32_t* idx, float* gates, int32_t* loads,
-                        hipStream_t s) {
+// ------------------------------------------------------------ launch helpers
+
+template <int EJ>
+const void* f32_kernel_ptr() { return reinterpret_cast<const void*>(route_f32_kernel<EJ>); }
+
+hipError_t launch_route_f32(int T, int d, int E, int K, int fn, const float* h, const float* e,
+                            const float* b, int32_t* idx, float* gates, int32_t* loads,
+                            hipStream_t s) {
   dim3 grid((T + kBT - 1) / kBT), block(kThreads);
-  size_t es_floats = static_cast<size_t>(E) * (kBK + 1);
-  size_t zs_floats = static_cast<size_t>(kBT) * E;
-  size_t shmem = (kBT * kBK + (es_floats > zs_floats ? es_floats : zs_floats)) * sizeof(float);
-  int ej = (E + kWave - 1) / kWave;
+  const size_t es_floats = static_cast<size_t>(E) * (kBK + 1);
+  const size_t zs_floats = static_cast<size_t>(kBT) * E;
+  const size_t shmem = (kBT * kBK + (es_floats > zs_floats ? es_floats : zs_floats)) * sizeof(float);
+  const int ej = (E + kWave - 1) / kWave;
   if (shmem > 64 * 1024) {
-    hipError_t err = hipSuccess;
-    if (ej <= 1)
-      err = hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<TIn, 1>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    else if (ej <= 2)
-      err = hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<TIn, 2>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    else if (ej <= 4)
-      err = hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<TIn, 4>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    else
-      err = hipFuncSetAttribute(reinterpret_cast<const void*>(route_kernel<TIn, 8>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    const void* f = ej <= 1 ? f32_kernel_ptr<1>() : ej <= 2 ? f32_kernel_ptr<2>()
+                  : ej <= 4 ? f32_kernel_ptr<4>() : f32_kernel_ptr<8>();
+    hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (err != hipSuccess) return err;
   }
-  ProfScope prof_(s, "route");
+  ProfScope prof_(s, "route_f32");
   if (ej <= 1)
-    hipLaunchKernelGGL((route_kernel<TIn, 1>), grid, block, shmem, s, T, d, E, K, fn, h, e, b,
-                       idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<1>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
   else if (ej <= 2)
-    hipLaunchKernelGGL((route_kernel<TIn, 2>), grid, block, shmem, s, T, d, E, K, fn, h, e, b,
-                       idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<2>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
   else if (ej <= 4)
-    hipLaunchKernelGGL((route_kernel<TIn, 4>), grid, block, shmem, s, T, d, E, K, fn, h, e, b,
-                       idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<4>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
   else
-    hipLaunchKernelGGL((route_kernel<TIn, 8>), grid, block, shmem, s, T, d, E, K, fn, h, e, b,
-                       idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<8>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// Number of d_model splits of the matrix-core logits (0: that path is not used).
+int route_splits(int T, int d, int E, int h_bf16) {
+  if (!h_bf16 || d % 32 != 0) return 0;
+  const int tiles = ((T + kZT - 1) / kZT) * ((E + kZE - 1) / kZE);
+  int S = 1;
+  while (tiles * S < 256 && S < 8 && d % (32 * 2 * S) == 0) S *= 2;
+  return S;
+}
+
+size_t route_workspace_bytes(int T, int d, int E, int h_bf16) {
+  const int S = route_splits(T, d, E, h_bf16);
+  return align_up(static_cast<size_t>(S) * T * E * sizeof(float), 256);
+}
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
@@ -283,14 +435,39 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
 
 hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h_bf16,
                         const float* e, const float* b, int32_t* idx, float* gates,
-                        int32_t* loads, hipStream_t s) {
+                        int32_t* loads, void* ws, hipStream_t s) {
   hipError_t err = launch_fill_i32(loads, 0, static_cast<size_t>(E), s);
   if (err != hipSuccess) return err;
-  if (h_bf16)
-    return launch_typed<uint16_t>(T, d, E, K, fn, static_cast<const uint16_t*>(h), e, b, idx,
-                                  gates, loads, s);
-  return launch_typed<float>(T, d, E, K, fn, static_cast<const float*>(h), e, b, idx, gates,
-                             loads, s);
+  const int S = route_splits(T, d, E, h_bf16);
+  if (S == 0) {
+    if (h_bf16) return hipErrorInvalidValue;  // rejected on the host before this point
+    return launch_route_f32(T, d, E, K, fn, static_cast<const float*>(h), e, b, idx, gates,
+                            loads, s);
+  }
+  float* zpart = static_cast<float*>(ws);
+  {
+    ProfScope prof_(s, "route_logits");
+    dim3 grid((T + kZT - 1) / kZT, (E + kZE - 1) / kZE, S);
+    hipLaunchKernelGGL(route_logits_mfma_kernel, grid, dim3(256), 0, s, T, d, E, d / S,
+                       static_cast<const uint16_t*>(h), e, zpart);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    ProfScope prof_(s, "route_topk");
+    const int ej = (E + kWave - 1) / kWave;
+    dim3 grid((T + 3) / 4), block(256);
+    const float* zp = zpart;
+    if (ej <= 1)
+      hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+    else if (ej <= 2)
+      hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+    else if (ej <= 4)
+      hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+    else
+      hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

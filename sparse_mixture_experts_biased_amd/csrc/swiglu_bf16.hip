@@ -7,19 +7,23 @@
 // Two launches over the device-built tile list:
 //   gate/up: act[r, n] = SiLU(x_r . Wg[n]) * (x_r . Wu[n])     K = d_model
 //            x rows gathered on load through row_index (no x_perm copy);
-//            the B tile stacks 128 W_gate rows over the same 128 W_up rows,
+//            the B tile stacks 64 W_gate rows over the same 64 W_up rows,
 //            so each lane holds matching gate and up accumulators.
 //   down:    y[r, n] = (act_r . Wd[n]) * row_scale[r]          K = d_ffn
-// Tile: 128 rows x 256 weight rows x 64 k, four waves in a 2 x 2 layout, each
-// wave 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Global
-// 16-byte loads for the next k-slice are in flight while the current slice is
-// multiplied out of LDS (two LDS stages, XOR-swizzled 16-byte chunks so the
-// fragment reads are bank-conflict free).
 //
-// Work order: (group, column tile, row tile), and block ids are remapped so
-// each XCD takes a contiguous run of that order: the row tiles of one
-// (expert, column tile) run side by side on one XCD and share the weight
-// slice through its L2, and the column tiles of one expert share its x rows.
+// Tile: 256 grouped rows x 128 weight rows x 64 k.  A row tile of 256 covers
+// a whole expert whenever it has <= 256 rows (the DeepSeek-V3 prefill and
+// decode shapes), so each weight slice is streamed from HBM exactly once.
+// Four waves, each owning 64 rows (2 x 4 blocks of v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation); a wave skips the MFMAs of 32-row blocks that hold no
+// row of the group.  The global loads of the next two 64-k slices are in
+// flight while the current slice is multiplied out of LDS (two LDS stages,
+// 16-byte chunks XOR-swizzled per row so fragment reads are conflict free).
+//
+// Work order: (group, column tile, row tile); block ids are remapped so each
+// XCD walks a contiguous run of it: row tiles of one (expert, column tile) run
+// side by side on one XCD and share the weight slice through its L2, and the
+// column tiles of one expert reuse its gathered x rows from that L2.
 #include "swiglu_tiles.h"
 
 namespace moe {
@@ -28,18 +32,21 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;        // grouped rows per tile
-constexpr int kBNW = 256;       // weight rows per tile
+constexpr int kBM = 256;        // grouped rows per tile
+constexpr int kBNW = 128;       // weight rows per tile
 constexpr int kBK = 64;         // k per LDS stage (8 chunks of 16 B per row)
 constexpr int kThreads = 256;
 constexpr int kRowBytes = kBK * 2;                     // 128 B
+constexpr int kABytes = kBM * kRowBytes;               // 32 KB
 constexpr int kStageBytes = (kBM + kBNW) * kRowBytes;  // 48 KB
 constexpr int kNumXcd = 8;
+constexpr int kALoads = kBM * 8 / kThreads;            // 8 x 16 B per thread
+constexpr int kBLoads = kBNW * 8 / kThreads;           // 4 x 16 B per thread
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
-// GATEUP: columns per tile = 128 (act columns), W0 = W_gate, W1 = W_up
-// DOWN:   columns per tile = 256 (y columns),   W0 = W_down
+// GATEUP: 64 act columns per tile, W0 = W_gate, W1 = W_up
+// DOWN:   128 y columns per tile,  W0 = W_down
 template <bool GATEUP>
 __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
     int Kdim, int N, int x_rows, int n_groups, int NT, const TileInfo* __restrict__ tiles,
@@ -56,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
   const int w = xcd * per_xcd + slot;
   if (slot >= per_xcd || w >= total) return;
-  int lo = 0, hi = n_groups;  // largest g with gts[g] * NT <= w
+  int lo = 0, hi = n_groups;  // largest g with gts[g] * NT <= w (that group has tiles)
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
     if (gts[mid] * NT <= w) lo = mid; else hi = mid;
@@ -67,67 +74,64 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   const int local = w - gstart * NT;
   const int ntile = local / nmt;
   const TileInfo ti = tiles[gstart + local % nmt];
+  const int nrows = min(ti.m1 - ti.m0, kBM);
 
-  constexpr int kCols = GATEUP ? 128 : 256;
+  constexpr int kCols = GATEUP ? 64 : 128;
   const int n0 = ntile * kCols;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- per-thread load slots: 4 A chunks, 8 B chunks per k-slice
-  const int lc = tid & 7;          // 16-byte chunk within the 128-byte k-slice row
-  const int lr = tid >> 3;         // 0..31
-  const uint16_t* a_src[4];
+  // ---- per-thread load slots (row lr + 32 i, 16-byte chunk lc of the k-slice)
+  const int lc = tid & 7;
+  const int lr = tid >> 3;  // 0..31
+  const uint16_t* a_src[kALoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int gr = ti.m0 + lr + 32 * i;
+  for (int i = 0; i < kALoads; ++i) {
+    const int r = lr + 32 * i;
     int sr = -1;
-    if (gr < ti.m1) {
+    if (r < nrows) {
+      const int gr = ti.m0 + r;
       sr = row_index ? row_index[gr] : gr;
       if (sr < 0 || sr >= x_rows) sr = -1;
     }
     a_src[i] = (sr >= 0) ? A + static_cast<size_t>(sr) * Kdim + lc * 8 : nullptr;
   }
-  const size_t wexp = static_cast<size_t>(g) * N * Kdim;
-  const uint16_t* b_src[8];
+  const uint16_t* wexp0 = W0 + static_cast<size_t>(g) * N * Kdim;
+  const uint16_t* wexp1 = GATEUP ? W1 + static_cast<size_t>(g) * N * Kdim : nullptr;
+  const uint16_t* b_src[kBLoads];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int r = lr + 32 * i;  // 0..255
+  for (int i = 0; i < kBLoads; ++i) {
+    const int r = lr + 32 * i;  // 0..127
     const uint16_t* base;
     int n;
     if (GATEUP) {
-      base = (r < 128) ? W0 : W1;
-      n = n0 + (r & 127);
+      base = (r < 64) ? wexp0 : wexp1;
+      n = n0 + (r & 63);
     } else {
-      base = W0;
+      base = wexp0;
       n = n0 + r;
     }
-    b_src[i] = (n < N) ? base + wexp + static_cast<size_t>(n) * Kdim + lc * 8 : nullptr;
+    b_src[i] = (n < N) ? base + static_cast<size_t>(n) * Kdim + lc * 8 : nullptr;
   }
 
-  uint4 ra[4], rb[8];
-  auto load_slice = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_slice = [&](int stage) {
-    char* as = smem + stage * kStageBytes;
-    char* bs = as + kBM * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(as + swz(lr + 32 * i, lc)) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(bs + swz(lr + 32 * i, lc)) = rb[i];
-  };
-
-  // B-tile rows of this wave's four 32-wide column blocks
-  int brow[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    brow[nb] = GATEUP ? ((nb >> 1) * 128 + wn * 64 + (nb & 1) * 32) : (wn * 128 + nb * 32);
+#define MOE_LOAD_SLICE(SA, SB, K0)                                                      \
+  do {                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) if (a_src[i]) SA[i] =          \
+        *reinterpret_cast<const uint4*>(a_src[i] + (K0));                              \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i) SB[i] =                        \
+        b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + (K0)) : make_uint4(0, 0, 0, 0); \
+  } while (0)
+  // Rows past the group are never loaded or stored: their LDS rows hold stale
+  // values, which only reach output rows that are masked at the store.
+#define MOE_STORE_SLICE(SA, SB, STAGE)                                                  \
+  do {                                                                                 \
+    char* as_ = smem + (STAGE) * kStageBytes;                                          \
+    char* bs_ = as_ + kABytes;                                                         \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) if (a_src[i])                  \
+        *reinterpret_cast<uint4*>(as_ + swz(lr + 32 * i, lc)) = SA[i];                 \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                \
+        *reinterpret_cast<uint4*>(bs_ + swz(lr + 32 * i, lc)) = SB[i];                 \
+  } while (0)
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -137,40 +141,61 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
 
-  const int nk = Kdim / kBK;
-  load_slice(0);
-  store_slice(0);
-  __syncthreads();
-  const int fr = lane & 31;        // fragment row within a 32-block
-  const int fh = lane >> 5;        // which 8-wide k half of the 16-k step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_slice((kt + 1) * kBK);
-    const char* as = smem + cur * kStageBytes;
-    const char* bs = as + kBM * kRowBytes;
+  // wave-uniform: which of this wave's two 32-row blocks hold rows of the group
+  const bool mb0 = wave * 64 < nrows;
+  const bool mb1 = wave * 64 + 32 < nrows;
+  const int fr = lane & 31;  // fragment row within a 32-block
+  const int fh = lane >> 5;  // which 8-wide k half of a 16-k step
+
+  auto compute = [&](int stage) {
+    const char* as = smem + stage * kStageBytes;
+    const char* bs = as + kABytes;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = kk * 2 + fh;
       bf16x8_t af[2], bfr[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        int r = wm * 64 + mb * 32 + fr;
-        af[mb] = *reinterpret_cast<const bf16x8_t*>(as + swz(r, c));
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        int r = brow[nb] + fr;
-        bfr[nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(r, c));
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int nb = 0; nb < 4; ++nb)
+        bfr[nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(nb * 32 + fr, c));
+      af[0] = *reinterpret_cast<const bf16x8_t*>(as + swz(wave * 64 + fr, c));
+      af[1] = *reinterpret_cast<const bf16x8_t*>(as + swz(wave * 64 + 32 + fr, c));
+      if (mb0) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[nb], acc[0][nb], 0, 0, 0);
+      }
+      if (mb1) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bfr[nb], acc[1][nb], 0, 0, 0);
+      }
     }
-    if (kt + 1 < nk) store_slice(cur ^ 1);
+  };
+
+  // ---- main loop: slices kt+1 and kt+2 are in flight while slice kt is multiplied
+  const int nk = Kdim / kBK;
+  uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) sa0[i] = sa1[i] = make_uint4(0, 0, 0, 0);
+  MOE_LOAD_SLICE(sa0, sb0, 0);
+  if (nk > 1) MOE_LOAD_SLICE(sa1, sb1, kBK);
+  MOE_STORE_SLICE(sa0, sb0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    // even step: compute stage 0 (slice kt); set 0 takes slice kt+2; set 1 holds kt+1
+    if (kt + 2 < nk) MOE_LOAD_SLICE(sa0, sb0, (kt + 2) * kBK);
+    compute(0);
+    if (kt + 1 < nk) MOE_STORE_SLICE(sa1, sb1, 1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    // odd step: compute stage 1 (slice kt+1); set 1 takes slice kt+3; set 0 holds kt+2
+    if (kt + 3 < nk) MOE_LOAD_SLICE(sa1, sb1, (kt + 3) * kBK);
+    compute(1);
+    if (kt + 2 < nk) MOE_STORE_SLICE(sa0, sb0, 0);
     __syncthreads();
   }
+#undef MOE_LOAD_SLICE
+#undef MOE_STORE_SLICE
 
   // ---- epilogue: D[row][col] of a 32x32 block sits in lane (col + 32*((row/4)%2)),
   // register (row%4) + 4*(row/8).
@@ -178,15 +203,15 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = wm * 64 + mb * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
+      const int row = wave * 64 + mb * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
+      if (row >= nrows) continue;
       const int gr = ti.m0 + row;
-      if (gr >= ti.m1) continue;
       if (GATEUP) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int col = n0 + wn * 64 + nb * 32 + fr;
+          const int col = n0 + nb * 32 + fr;
           if (col < N) {
-            float v = silu(acc[mb][nb][q]) * acc[mb][nb + 2][q];
+            const float v = silu(acc[mb][nb][q]) * acc[mb][nb + 2][q];
             out[static_cast<size_t>(gr) * N + col] = f32_to_bf16(v);
           }
         }
@@ -194,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
         const float sc = row_scale ? row_scale[gr] : 1.0f;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int col = n0 + wn * 128 + nb * 32 + fr;
+          const int col = n0 + nb * 32 + fr;
           if (col < N) out[static_cast<size_t>(gr) * N + col] = f32_to_bf16(acc[mb][nb][q] * sc);
         }
       }
@@ -215,7 +240,7 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
   const int max_tiles = max_tiles_for(rows, n_groups, kBM);
   uint16_t* act = static_cast<uint16_t*>(w.act);
 
-  const int nt1 = (d_ffn + 127) / 128;
+  const int nt1 = (d_ffn + 63) / 64;
   long blocks1 = static_cast<long>(max_tiles) * nt1;
   blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
   {
@@ -227,7 +252,7 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  const int nt2 = (d_model + 255) / 256;
+  const int nt2 = (d_model + 127) / 128;
   long blocks2 = static_cast<long>(max_tiles) * nt2;
   blocks2 = (blocks2 + kNumXcd - 1) / kNumXcd * kNumXcd;
   {

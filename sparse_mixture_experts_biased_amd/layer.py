@@ -47,6 +47,9 @@ class MoELayer:
         self.topk_idx = torch.empty((T, K), **i32)
         self.gates = torch.empty((T, K), dtype=torch.float32, device=device)
         self.loads = torch.empty((E,), **i32)
+        self.route_ws_bytes = L.moe_route_workspace_size(T, d, E, self.dt)
+        self.route_ws = torch.empty((max(self.route_ws_bytes, 1),), dtype=torch.uint8,
+                                    device=device)
         self.offsets = torch.empty((E + 1,), **i32)
         self.row_token = torch.empty((TK,), **i32)
         self.slot_row = torch.empty((TK,), **i32)
@@ -71,7 +74,7 @@ class MoELayer:
     def route(self, h, b, stream=None):
         s = self.shape
         L.moe_route(s.T, s.d_model, s.E_r, s.K, self.fn, h, self.dt, self.e, b, self.topk_idx,
-                    self.gates, self.loads, stream)
+                    self.gates, self.loads, self.route_ws, self.route_ws_bytes, stream)
 
     def permute(self, h=None, x_perm=None, stream=None):
         s = self.shape

@@ -44,15 +44,23 @@ def _st(rc):
 def test_route_rejects_bad_arguments():
     lib = L.load()
     P = ctypes.c_void_p(16)  # never dereferenced: validation fails first
-    assert _st(lib.moe_route(0, 128, 8, 2, 0, P, 1, P, None, P, P, P, None))[0] == L.MOE_ERR_INVALID_ARG
-    rc, msg = _st(lib.moe_route(64, 128, 8, 9, 0, P, 1, P, None, P, P, P, None))
+    assert _st(lib.moe_route(0, 128, 8, 2, 0, P, 1, P, None, P, P, P, P, 1 << 30, None))[0] == L.MOE_ERR_INVALID_ARG
+    rc, msg = _st(lib.moe_route(64, 128, 8, 9, 0, P, 1, P, None, P, P, P, P, 1 << 30, None))
     assert rc == L.MOE_ERR_INVALID_ARG and "K=9 > E_r=8" in msg
-    assert lib.moe_route(64, 128, 32, 17, 0, P, 1, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(64, 128, 8, 2, 0, None, 1, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(64, 100, 8, 2, 0, P, 1, P, None, P, P, P, None) == L.MOE_ERR_UNSUPPORTED
-    assert lib.moe_route(64, 128, 1024, 2, 0, P, 1, P, None, P, P, P, None) == L.MOE_ERR_UNSUPPORTED
-    assert lib.moe_route(64, 128, 8, 2, 7, P, 1, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(64, 128, 8, 2, 0, P, 5, P, None, P, P, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 128, 32, 17, 0, P, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 128, 8, 2, 0, None, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 100, 8, 2, 0, P, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(64, 128, 1024, 2, 0, P, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(64, 128, 8, 2, 7, P, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(64, 128, 8, 2, 0, P, 5, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
+    # bf16 tokens run the matrix-core logits: d_model % 32 and a workspace are required
+    assert lib.moe_route(64, 136, 8, 2, 0, P, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    need = L.moe_route_workspace_size(4096, 7168, 256, L.MOE_BF16)
+    assert need >= 4096 * 256 * 4
+    rc, msg = _st(lib.moe_route(4096, 7168, 256, 8, 0, P, 1, P, None, P, P, P, P, need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    assert lib.moe_route(4096, 7168, 256, 8, 0, P, 1, P, None, P, P, P, None, need, None) == L.MOE_ERR_INVALID_ARG
+    assert L.moe_route_workspace_size(64, 128, 8, L.MOE_F32) == 0
 
 
 def test_permute_rejects_bad_arguments():

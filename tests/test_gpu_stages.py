@@ -48,7 +48,9 @@ def _route_gpu(h, e, b, K, fn):
     gates = torch.empty((T, K), dtype=torch.float32, device=DEV)
     loads = torch.empty((E,), dtype=torch.int32, device=DEV)
     dt = L.MOE_BF16 if h.dtype == torch.bfloat16 else L.MOE_F32
-    L.moe_route(T, d, E, K, fn, h, dt, e, b, idx, gates, loads)
+    wsb = L.moe_route_workspace_size(T, d, E, dt)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    L.moe_route(T, d, E, K, fn, h, dt, e, b, idx, gates, loads, ws, wsb)
     torch.cuda.synchronize()
     return idx, gates, loads
 
