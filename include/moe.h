@@ -152,8 +152,9 @@ moe_status moe_permute(int T, int d_model, int E_r, int K, const int32_t* topk_i
  *              bytes (the SiLU(gate)*up activations and the tile list)
  * bf16: fp32 accumulation on the matrix cores; the activation is rounded to
  * bf16 before W_down and y to bf16 (round to nearest even).
- * Limits: bf16 needs d_model % 64 == 0 and d_ffn % 64 == 0; fp32 needs
- * d_model % 16 == 0 and d_ffn % 16 == 0.
+ * Limits: bf16 needs d_model % 64 == 0, d_ffn % 64 == 0 and each of x, the
+ * activations [rows, d_ffn] and one expert's weight matrix under 2 GiB; fp32
+ * needs d_model % 16 == 0 and d_ffn % 16 == 0.
  */
 size_t moe_grouped_swiglu_workspace_size(int n_groups, int d_model, int d_ffn, int rows,
                                          moe_dtype dtype);

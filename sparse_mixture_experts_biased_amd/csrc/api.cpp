@@ -150,6 +150,15 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
   if (static_cast<long long>(rows) * d_ffn > (1LL << 40) ||
       static_cast<long long>(d_model) * d_ffn > INT32_MAX)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: sizes overflow");
+  if (dtype == MOE_BF16) {
+    // the matrix-core path addresses each operand with 32-bit buffer offsets
+    const long long lim = (1LL << 31) - 1;
+    if (2LL * x_rows * d_model > lim || 2LL * rows * d_ffn > lim || 2LL * d_model * d_ffn > lim)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "moe_grouped_swiglu: bf16 operands must each be under 2 GiB "
+                  "(x %lld, activations %lld, one weight matrix %lld bytes)",
+                  2LL * x_rows * d_model, 2LL * rows * d_ffn, 2LL * d_model * d_ffn);
+  }
   const size_t need = moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
   if (workspace_bytes < need)
     return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: workspace %zu < %zu bytes",

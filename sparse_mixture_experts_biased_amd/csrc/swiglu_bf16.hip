@@ -42,6 +42,7 @@ constexpr int kStageBytes = (kBM + kBNW) * kRowBytes;  // 48 KB
 constexpr int kNumXcd = 8;
 constexpr int kALoads = kBM * 8 / kThreads;            // 8 x 16 B per thread
 constexpr int kBLoads = kBNW * 8 / kThreads;           // 4 x 16 B per thread
+constexpr int kBufferFlags = 0x00020000;               // raw buffer, 32-bit data format
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
@@ -81,10 +82,19 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
 
-  // ---- per-thread load slots (row lr + 32 i, 16-byte chunk lc of the k-slice)
+  // ---- per-thread load slots (row lr + 32 i, 16-byte chunk lc of the k-slice).
+  // Buffer loads: an offset past the end of the buffer reads zeros without a
+  // memory access, so rows past the group, rows with an out-of-range source
+  // and columns past N need no branch -- the loop stays straight-line and the
+  // loads of later slices stay in flight across the LDS stores.  The per-lane
+  // offsets are loop-invariant; the k position goes in the uniform soffset.
   const int lc = tid & 7;
   const int lr = tid >> 3;  // 0..31
-  const uint16_t* a_src[kALoads];
+  constexpr uint32_t kOff = 0x80000000u;  // beyond every buffer (sizes < 2 GiB)
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(x_rows) * Kdim * 2u),
+      kBufferFlags);
+  uint32_t a_off[kALoads];
 #pragma unroll
   for (int i = 0; i < kALoads; ++i) {
     const int r = lr + 32 * i;
@@ -94,40 +104,36 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
       sr = row_index ? row_index[gr] : gr;
       if (sr < 0 || sr >= x_rows) sr = -1;
     }
-    a_src[i] = (sr >= 0) ? A + static_cast<size_t>(sr) * Kdim + lc * 8 : nullptr;
+    a_off[i] = (sr >= 0) ? (static_cast<uint32_t>(sr) * Kdim + lc * 8) * 2u : kOff;
   }
-  const uint16_t* wexp0 = W0 + static_cast<size_t>(g) * N * Kdim;
-  const uint16_t* wexp1 = GATEUP ? W1 + static_cast<size_t>(g) * N * Kdim : nullptr;
-  const uint16_t* b_src[kBLoads];
+  const int wbytes = static_cast<int>(static_cast<uint32_t>(N) * Kdim * 2u);
+  const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W0 + static_cast<size_t>(g) * N * Kdim), 0, wbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(GATEUP ? W1 + static_cast<size_t>(g) * N * Kdim : W0), 0, wbytes,
+      kBufferFlags);
+  uint32_t b_off[kBLoads];
 #pragma unroll
   for (int i = 0; i < kBLoads; ++i) {
     const int r = lr + 32 * i;  // 0..127
-    const uint16_t* base;
-    int n;
-    if (GATEUP) {
-      base = (r < 64) ? wexp0 : wexp1;
-      n = n0 + (r & 63);
-    } else {
-      base = wexp0;
-      n = n0 + r;
-    }
-    b_src[i] = (n < N) ? base + static_cast<size_t>(n) * Kdim + lc * 8 : nullptr;
+    const int n = GATEUP ? n0 + (r & 63) : n0 + r;
+    b_off[i] = (n < N) ? (static_cast<uint32_t>(n) * Kdim + lc * 8) * 2u : kOff;
   }
 
 #define MOE_LOAD_SLICE(SA, SB, K0)                                                      \
   do {                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) if (a_src[i]) SA[i] =          \
-        *reinterpret_cast<const uint4*>(a_src[i] + (K0));                              \
-    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i) SB[i] =                        \
-        b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + (K0)) : make_uint4(0, 0, 0, 0); \
+    const uint32_t kb_ = static_cast<uint32_t>(K0) * 2u;                               \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) SA[i] =                        \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb_, 0)); \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i) SB[i] = __builtin_bit_cast(     \
+        uint4, __builtin_amdgcn_raw_buffer_load_b128((!GATEUP || i < kBLoads / 2) ? rsB0 : rsB1, \
+                                                     b_off[i], kb_, 0));               \
   } while (0)
-  // Rows past the group are never loaded or stored: their LDS rows hold stale
-  // values, which only reach output rows that are masked at the store.
 #define MOE_STORE_SLICE(SA, SB, STAGE)                                                  \
   do {                                                                                 \
     char* as_ = smem + (STAGE) * kStageBytes;                                          \
     char* bs_ = as_ + kABytes;                                                         \
-    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) if (a_src[i])                  \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                \
         *reinterpret_cast<uint4*>(as_ + swz(lr + 32 * i, lc)) = SA[i];                 \
     _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                \
         *reinterpret_cast<uint4*>(bs_ + swz(lr + 32 * i, lc)) = SB[i];                 \
@@ -175,23 +181,25 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   // ---- main loop: slices kt+1 and kt+2 are in flight while slice kt is multiplied
   const int nk = Kdim / kBK;
   uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads];
-#pragma unroll
-  for (int i = 0; i < kALoads; ++i) sa0[i] = sa1[i] = make_uint4(0, 0, 0, 0);
+  // Every step issues its prefetch unconditionally (past the end it re-reads
+  // the last slice, an L2 hit), so the wait before each LDS store counts only
+  // the slice being stored and the newer slice stays in flight.
   MOE_LOAD_SLICE(sa0, sb0, 0);
-  if (nk > 1) MOE_LOAD_SLICE(sa1, sb1, kBK);
+  MOE_LOAD_SLICE(sa1, sb1, min(1, nk - 1) * kBK);
   MOE_STORE_SLICE(sa0, sb0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    // even step: compute stage 0 (slice kt); set 0 takes slice kt+2; set 1 holds kt+1
-    if (kt + 2 < nk) MOE_LOAD_SLICE(sa0, sb0, (kt + 2) * kBK);
+  for (int kt = 0;; kt += 2) {
+    // even step: multiply stage 0 (slice kt); set 0 takes slice kt+2
+    MOE_LOAD_SLICE(sa0, sb0, min(kt + 2, nk - 1) * kBK);
     compute(0);
-    if (kt + 1 < nk) MOE_STORE_SLICE(sa1, sb1, 1);
-    __syncthreads();
     if (kt + 1 >= nk) break;
-    // odd step: compute stage 1 (slice kt+1); set 1 takes slice kt+3; set 0 holds kt+2
-    if (kt + 3 < nk) MOE_LOAD_SLICE(sa1, sb1, (kt + 3) * kBK);
+    MOE_STORE_SLICE(sa1, sb1, 1);
+    __syncthreads();
+    // odd step: multiply stage 1 (slice kt+1); set 1 takes slice kt+3
+    MOE_LOAD_SLICE(sa1, sb1, min(kt + 3, nk - 1) * kBK);
     compute(1);
-    if (kt + 2 < nk) MOE_STORE_SLICE(sa0, sb0, 0);
+    if (kt + 2 >= nk) break;
+    MOE_STORE_SLICE(sa0, sb0, 0);
     __syncthreads();
   }
 #undef MOE_LOAD_SLICE

@@ -91,6 +91,11 @@ def test_grouped_swiglu_rejects_bad_arguments():
                                   need, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_grouped_swiglu(8, 256, 512, 1000, 500, None, P, P, 1, P, P, P, None, P, P,
                                   need, None) == L.MOE_ERR_INVALID_ARG
+    # the matrix-core path needs every bf16 operand under 2 GiB
+    big = L.moe_grouped_swiglu_workspace_size(8, 7168, 2048, 1 << 19, L.MOE_BF16)
+    rc, msg = _st(lib.moe_grouped_swiglu(8, 7168, 2048, 1 << 19, 1 << 18, P, P, P, 1, P, P, P,
+                                         None, P, P, big, None))
+    assert rc == L.MOE_ERR_UNSUPPORTED and "2 GiB" in msg
     # zero rows is a valid no-op
     assert lib.moe_grouped_swiglu(8, 256, 512, 0, 500, P, P, P, 1, P, P, P, None, P, P,
                                   need, None) == L.MOE_OK
