@@ -11,14 +11,19 @@
 //            so each lane holds matching gate and up accumulators.
 //   down:    y[r, n] = (act_r . Wd[n]) * row_scale[r]          K = d_ffn
 //
-// Tile: 256 grouped rows x 128 weight rows x 64 k.  A row tile of 256 covers
-// a whole expert whenever it has <= 256 rows (the DeepSeek-V3 prefill and
-// decode shapes), so each weight slice is streamed from HBM exactly once.
-// Four waves, each owning 64 rows (2 x 4 blocks of v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation); a wave skips the MFMAs of 32-row blocks that hold no
-// row of the group.  The global loads of the next two 64-k slices are in
-// flight while the current slice is multiplied out of LDS (two LDS stages,
-// 16-byte chunks XOR-swizzled per row so fragment reads are conflict free).
+// Tiles: BM grouped rows x 128 weight rows x 64 k, four waves, each wave
+// 64 rows x (128 / (4 / (BM/64))) weight rows as 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation); a wave skips the MFMAs of
+// 32-row blocks that hold no row of the group.  Two shapes:
+//   BM = 128 ("stream"): 64 KB of LDS and <= 256 registers per lane, so two
+//       workgroups share a CU -- used when groups are small (few rows per
+//       expert), where the kernel streams weights and is bound by the bytes
+//       it keeps in flight;
+//   BM = 256 ("compute"): 96 KB of LDS, one workgroup per CU, fewer LDS reads
+//       per MFMA -- used for large groups, where the matrix cores bound it.
+// The global loads of the next two 64-k slices are in flight while the
+// current slice is multiplied out of LDS (two LDS stages, 16-byte chunks
+// XOR-swizzled per row so fragment reads are conflict free).
 //
 // Work order: (group, column tile, row tile); block ids are remapped so each
 // XCD walks a contiguous run of it: row tiles of one (expert, column tile) run
@@ -32,30 +37,42 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256;        // grouped rows per tile
 constexpr int kBNW = 128;       // weight rows per tile
 constexpr int kBK = 64;         // k per LDS stage (8 chunks of 16 B per row)
 constexpr int kThreads = 256;
 constexpr int kRowBytes = kBK * 2;                     // 128 B
-constexpr int kABytes = kBM * kRowBytes;               // 32 KB
-constexpr int kStageBytes = (kBM + kBNW) * kRowBytes;  // 48 KB
 constexpr int kNumXcd = 8;
-constexpr int kALoads = kBM * 8 / kThreads;            // 8 x 16 B per thread
 constexpr int kBLoads = kBNW * 8 / kThreads;           // 4 x 16 B per thread
 constexpr int kBufferFlags = 0x00020000;               // raw buffer, 32-bit data format
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
+template <int BM>
+struct Tile {
+  static constexpr int kWavesM = BM / 64;              // waves along rows
+  static constexpr int kWavesN = 4 / kWavesM;          // waves along weight rows
+  static constexpr int kNB = kBNW / kWavesN / 32;      // 32-wide weight blocks per wave
+  static constexpr int kABytes = BM * kRowBytes;
+  static constexpr int kStageBytes = (BM + kBNW) * kRowBytes;
+  static constexpr int kALoads = BM * 8 / kThreads;
+  static constexpr int kOccupancy = BM == 128 ? 2 : 1;  // workgroups per CU
+};
+
 // GATEUP: 64 act columns per tile, W0 = W_gate, W1 = W_up
 // DOWN:   128 y columns per tile,  W0 = W_down
-template <bool GATEUP>
-__global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
+template <bool GATEUP, int BM>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Tile<BM>::kOccupancy, Tile<BM>::kOccupancy)))
+void bf16_tile_kernel(
     int Kdim, int N, int x_rows, int n_groups, int NT, const TileInfo* __restrict__ tiles,
     const int32_t* __restrict__ gts, const int32_t* __restrict__ meta,
     const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     const float* __restrict__ row_scale, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  using TL = Tile<BM>;
+  constexpr int kALoads = TL::kALoads;
+  constexpr int kNB = TL::kNB;
+  __shared__ __attribute__((aligned(16))) char smem[2 * TL::kStageBytes];
 
   // ---- block -> (group, column tile, row tile), XCD-contiguous
   const int total = meta[0] * NT;
@@ -75,12 +92,13 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   const int local = w - gstart * NT;
   const int ntile = local / nmt;
   const TileInfo ti = tiles[gstart + local % nmt];
-  const int nrows = min(ti.m1 - ti.m0, kBM);
+  const int nrows = min(ti.m1 - ti.m0, BM);
 
   constexpr int kCols = GATEUP ? 64 : 128;
   const int n0 = ntile * kCols;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave / TL::kWavesN, wn = wave % TL::kWavesN;
 
   // ---- per-thread load slots (row lr + 32 i, 16-byte chunk lc of the k-slice).
   // Buffer loads: an offset past the end of the buffer reads zeros without a
@@ -131,48 +149,61 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   } while (0)
 #define MOE_STORE_SLICE(SA, SB, STAGE)                                                  \
   do {                                                                                 \
-    char* as_ = smem + (STAGE) * kStageBytes;                                          \
-    char* bs_ = as_ + kABytes;                                                         \
+    char* as_ = smem + (STAGE) * TL::kStageBytes;                                      \
+    char* bs_ = as_ + TL::kABytes;                                                     \
     _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                \
         *reinterpret_cast<uint4*>(as_ + swz(lr + 32 * i, lc)) = SA[i];                 \
     _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                \
         *reinterpret_cast<uint4*>(bs_ + swz(lr + 32 * i, lc)) = SB[i];                 \
   } while (0)
 
-  f32x16_t acc[2][4];
+  // B-tile rows of this wave's 32-wide weight blocks.  GATEUP: the first half
+  // of the blocks are W_gate rows, the second half the matching W_up rows.
+  int brow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (GATEUP) {
+      const int half = kNB / 2;
+      const int base = wn * (64 / TL::kWavesN);
+      brow[nb] = (nb < half) ? base + nb * 32 : 64 + base + (nb - half) * 32;
+    } else {
+      brow[nb] = wn * (kBNW / TL::kWavesN) + nb * 32;
+    }
+  }
+
+  f32x16_t acc[2][kNB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
 
   // wave-uniform: which of this wave's two 32-row blocks hold rows of the group
-  const bool mb0 = wave * 64 < nrows;
-  const bool mb1 = wave * 64 + 32 < nrows;
+  const bool mb0 = wm * 64 < nrows;
+  const bool mb1 = wm * 64 + 32 < nrows;
   const int fr = lane & 31;  // fragment row within a 32-block
   const int fh = lane >> 5;  // which 8-wide k half of a 16-k step
 
   auto compute = [&](int stage) {
-    const char* as = smem + stage * kStageBytes;
-    const char* bs = as + kABytes;
+    if (!mb0) return;
+    const char* as = smem + stage * TL::kStageBytes;
+    const char* bs = as + TL::kABytes;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = kk * 2 + fh;
-      bf16x8_t af[2], bfr[4];
+      bf16x8_t af[2], bfr[kNB];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        bfr[nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(nb * 32 + fr, c));
-      af[0] = *reinterpret_cast<const bf16x8_t*>(as + swz(wave * 64 + fr, c));
-      af[1] = *reinterpret_cast<const bf16x8_t*>(as + swz(wave * 64 + 32 + fr, c));
-      if (mb0) {
+      for (int nb = 0; nb < kNB; ++nb)
+        bfr[nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(brow[nb] + fr, c));
+      af[0] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + fr, c));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[nb], acc[0][nb], 0, 0, 0);
-      }
+      for (int nb = 0; nb < kNB; ++nb)
+        acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0], bfr[nb], acc[0][nb], 0, 0, 0);
       if (mb1) {
+        af[1] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + 32 + fr, c));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
           acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1], bfr[nb], acc[1][nb], 0, 0, 0);
       }
     }
@@ -211,23 +242,23 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = wave * 64 + mb * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
+      const int row = wm * 64 + mb * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
       if (row >= nrows) continue;
       const int gr = ti.m0 + row;
       if (GATEUP) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int col = n0 + nb * 32 + fr;
+        for (int nb = 0; nb < kNB / 2; ++nb) {
+          const int col = n0 + brow[nb] + fr;
           if (col < N) {
-            const float v = silu(acc[mb][nb][q]) * acc[mb][nb + 2][q];
+            const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
             out[static_cast<size_t>(gr) * N + col] = f32_to_bf16(v);
           }
         }
       } else {
         const float sc = row_scale ? row_scale[gr] : 1.0f;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = n0 + nb * 32 + fr;
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int col = n0 + brow[nb] + fr;
           if (col < N) out[static_cast<size_t>(gr) * N + col] = f32_to_bf16(acc[mb][nb][q] * sc);
         }
       }
@@ -235,17 +266,15 @@ __global__ __launch_bounds__(kThreads) void bf16_tile_kernel(
   }
 }
 
-}  // namespace
-
-hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
-                              const int32_t* offsets, const int32_t* row_index,
-                              const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
-                              const uint16_t* wd, const float* row_scale, uint16_t* y,
-                              void* ws, hipStream_t s) {
-  SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
-  hipError_t err = launch_build_tiles(n_groups, rows, kBM, offsets, w, s);
+template <int BM>
+hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                        const int32_t* offsets, const int32_t* row_index, const uint16_t* x,
+                        const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                        const float* row_scale, uint16_t* y, const SwigluWorkspace& w,
+                        hipStream_t s) {
+  hipError_t err = launch_build_tiles(n_groups, rows, BM, offsets, w, s);
   if (err != hipSuccess) return err;
-  const int max_tiles = max_tiles_for(rows, n_groups, kBM);
+  const int max_tiles = max_tiles_for(rows, n_groups, BM);
   uint16_t* act = static_cast<uint16_t*>(w.act);
 
   const int nt1 = (d_ffn + 63) / 64;
@@ -253,7 +282,7 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
   blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
   {
     ProfScope prof_(s, "gateup_bf16");
-    hipLaunchKernelGGL((bf16_tile_kernel<true>), dim3(static_cast<unsigned>(blocks1)),
+    hipLaunchKernelGGL((bf16_tile_kernel<true, BM>), dim3(static_cast<unsigned>(blocks1)),
                        dim3(kThreads), 0, s, d_model, d_ffn, x_rows, n_groups, nt1, w.tiles,
                        w.group_tile_start, w.meta, row_index, x, wg, wu, nullptr, act);
   }
@@ -265,11 +294,28 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
   blocks2 = (blocks2 + kNumXcd - 1) / kNumXcd * kNumXcd;
   {
     ProfScope prof_(s, "down_bf16");
-    hipLaunchKernelGGL((bf16_tile_kernel<false>), dim3(static_cast<unsigned>(blocks2)),
+    hipLaunchKernelGGL((bf16_tile_kernel<false, BM>), dim3(static_cast<unsigned>(blocks2)),
                        dim3(kThreads), 0, s, d_ffn, d_model, rows, n_groups, nt2, w.tiles,
                        w.group_tile_start, w.meta, nullptr, act, wd, nullptr, row_scale, y);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                              const int32_t* offsets, const int32_t* row_index,
+                              const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                              const uint16_t* wd, const float* row_scale, uint16_t* y,
+                              void* ws, hipStream_t s) {
+  SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
+  // Few rows per group: weight streaming, keep bytes in flight (two
+  // workgroups per CU).  Many rows per group: matrix-core bound.
+  if (rows <= 256 * n_groups)
+    return launch_tiles<128>(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, wg,
+                             wu, wd, row_scale, y, w, s);
+  return launch_tiles<256>(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, wg, wu,
+                           wd, row_scale, y, w, s);
 }
 
 }  // namespace moe
