@@ -21,9 +21,10 @@
 //       it keeps in flight;
 //   BM = 256 ("compute"): 96 KB of LDS, one workgroup per CU, fewer LDS reads
 //       per MFMA -- used for large groups, where the matrix cores bound it.
-// The global loads of the next two 64-k slices are in flight while the
-// current slice is multiplied out of LDS (two LDS stages, 16-byte chunks
-// XOR-swizzled per row so fragment reads are conflict free).
+// The global loads of the next three 64-k slices are in flight while the
+// current slice is multiplied out of LDS (three register sets, two LDS
+// stages, 16-byte chunks XOR-swizzled per row so fragment reads are conflict
+// free).
 //
 // Work order: (group, column tile, row tile); block ids are remapped so each
 // XCD walks a contiguous run of it: row tiles of one (expert, column tile) run
@@ -209,30 +210,35 @@ void bf16_tile_kernel(
     }
   };
 
-  // ---- main loop: slices kt+1 and kt+2 are in flight while slice kt is multiplied
+  // ---- main loop: slices kt+1, kt+2 and kt+3 are in flight while slice kt is
+  // multiplied.  Three register sets rotate through the loads; two LDS stages
+  // alternate.  Every step issues its prefetch unconditionally (past the end
+  // it re-reads the last slice, an L2 hit), so the wait before each LDS store
+  // counts only the slice being stored and the newer slices stay in flight.
   const int nk = Kdim / kBK;
-  uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads];
-  // Every step issues its prefetch unconditionally (past the end it re-reads
-  // the last slice, an L2 hit), so the wait before each LDS store counts only
-  // the slice being stored and the newer slice stays in flight.
+  uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads], sa2[kALoads], sb2[kBLoads];
   MOE_LOAD_SLICE(sa0, sb0, 0);
   MOE_LOAD_SLICE(sa1, sb1, min(1, nk - 1) * kBK);
+  MOE_LOAD_SLICE(sa2, sb2, min(2, nk - 1) * kBK);
   MOE_STORE_SLICE(sa0, sb0, 0);
   __syncthreads();
-  for (int kt = 0;; kt += 2) {
-    // even step: multiply stage 0 (slice kt); set 0 takes slice kt+2
-    MOE_LOAD_SLICE(sa0, sb0, min(kt + 2, nk - 1) * kBK);
-    compute(0);
-    if (kt + 1 >= nk) break;
-    MOE_STORE_SLICE(sa1, sb1, 1);
-    __syncthreads();
-    // odd step: multiply stage 1 (slice kt+1); set 1 takes slice kt+3
-    MOE_LOAD_SLICE(sa1, sb1, min(kt + 3, nk - 1) * kBK);
-    compute(1);
-    if (kt + 2 >= nk) break;
-    MOE_STORE_SLICE(sa0, sb0, 0);
-    __syncthreads();
+#define MOE_STEP(J, LA, LB, STAGE, SA, SB)                                              \
+  MOE_LOAD_SLICE(LA, LB, min((J) + 3, nk - 1) * kBK);                                  \
+  compute(STAGE);                                                                      \
+  if ((J) + 1 >= nk) break;                                                            \
+  MOE_STORE_SLICE(SA, SB, (STAGE) ^ 1);                                                \
+  __syncthreads();
+  for (int kt = 0;; kt += 6) {
+    // step j multiplies slice j (stage j % 2), refills set j % 3 with slice
+    // j + 3 and stores slice j + 1 (set (j + 1) % 3) to stage (j + 1) % 2
+    MOE_STEP(kt + 0, sa0, sb0, 0, sa1, sb1)
+    MOE_STEP(kt + 1, sa1, sb1, 1, sa2, sb2)
+    MOE_STEP(kt + 2, sa2, sb2, 0, sa0, sb0)
+    MOE_STEP(kt + 3, sa0, sb0, 1, sa1, sb1)
+    MOE_STEP(kt + 4, sa1, sb1, 0, sa2, sb2)
+    MOE_STEP(kt + 5, sa2, sb2, 1, sa0, sb0)
   }
+#undef MOE_STEP
 #undef MOE_LOAD_SLICE
 #undef MOE_STORE_SLICE
 
