@@ -114,6 +114,19 @@ def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256):
     )
 
 
+def copy_probe(nbytes: int) -> int:
+    """A plain device-to-device copy of known size: the reference that scales
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {nbytes} bytes 3 times")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,7 +136,11 @@ def main(argv=None):
                     choices=["dsv3_prefill", "dsv3_decode", "dsv3_skewed", "mixtral_8x7b"])
     ap.add_argument("--rotate", type=int, default=10, help="token batches cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy a BYTES-sized buffer 3 times (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py measures the single-GPU layer forward only: this build has no "

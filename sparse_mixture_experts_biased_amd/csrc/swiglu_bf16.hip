@@ -11,20 +11,20 @@
 //            so each lane holds matching gate and up accumulators.
 //   down:    y[r, n] = (act_r . Wd[n]) * row_scale[r]          K = d_ffn
 //
-// Tiles: BM grouped rows x 128 weight rows x 64 k, four waves, each wave
-// 64 rows x (128 / (4 / (BM/64))) weight rows as 32 x 32 blocks of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation); a wave skips the MFMAs of
-// 32-row blocks that hold no row of the group.  Two shapes:
-//   BM = 128 ("stream"): 64 KB of LDS and <= 256 registers per lane, so two
-//       workgroups share a CU -- used when groups are small (few rows per
-//       expert), where the kernel streams weights and is bound by the bytes
-//       it keeps in flight;
-//   BM = 256 ("compute"): 96 KB of LDS, one workgroup per CU, fewer LDS reads
-//       per MFMA -- used for large groups, where the matrix cores bound it.
-// The global loads of the next three 64-k slices are in flight while the
-// current slice is multiplied out of LDS (three register sets, two LDS
-// stages, 16-byte chunks XOR-swizzled per row so fragment reads are conflict
-// free).
+// Tile: 256 grouped rows x 256 weight rows x 64 k, eight waves (two per
+// SIMD) in a 4 x 2 layout, each wave 64 rows x 128 weight rows as 2 x 4
+// blocks of v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  A 256-row tile
+// covers a whole expert whenever it has <= 256 rows (the DeepSeek-V3 prefill
+// and decode shapes), so each weight slice is streamed from HBM once; a wave
+// skips the MFMAs of 32-row blocks that hold no row of the group, and rows
+// past the group are neither loaded nor staged.  256 weight rows per tile
+// halve the re-reads of the gathered x rows (once per column tile) compared
+// with 128.  The global loads of the next 64-k slice stay in flight while the
+// current one is multiplied out of LDS (two register sets, two 64 KB LDS
+// stages; 16-byte chunks XOR-swizzled per row so fragment reads and staging
+// writes are bank-conflict free).  The kernel is templated on the tile shape
+// and the number of register sets; this shape measured fastest for both the
+// weight-streaming (few rows per expert) and the matrix-core-bound shapes.
 //
 // Work order: (group, column tile, row tile); block ids are remapped so each
 // XCD walks a contiguous run of it: row tiles of one (expert, column tile) run
@@ -38,40 +38,50 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBNW = 128;       // weight rows per tile
 constexpr int kBK = 64;         // k per LDS stage (8 chunks of 16 B per row)
-constexpr int kThreads = 256;
 constexpr int kRowBytes = kBK * 2;                     // 128 B
 constexpr int kNumXcd = 8;
-constexpr int kBLoads = kBNW * 8 / kThreads;           // 4 x 16 B per thread
 constexpr int kBufferFlags = 0x00020000;               // raw buffer, 32-bit data format
 
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
+// LDS byte offset of 16-byte chunk c of tile row r.  The chunk index is XORed
+// with (r & 7) ^ ((r >> 3) & 1): a fragment read (32 consecutive rows, one
+// chunk) and a staging write (8 lanes per row) then hit distinct banks whether
+// the LDS serves 8 lanes x 16 B or 16 lanes x 16 B per cycle.
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * kRowBytes + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+}
 
-template <int BM>
+template <int BM, int BNW, int NTHR>
 struct Tile {
+  static constexpr int kThreads = NTHR;
+  static constexpr int kWaves = NTHR / 64;
   static constexpr int kWavesM = BM / 64;              // waves along rows
-  static constexpr int kWavesN = 4 / kWavesM;          // waves along weight rows
-  static constexpr int kNB = kBNW / kWavesN / 32;      // 32-wide weight blocks per wave
+  static constexpr int kWavesN = kWaves / kWavesM;     // waves along weight rows
+  static constexpr int kNB = BNW / kWavesN / 32;       // 32-wide weight blocks per wave
   static constexpr int kABytes = BM * kRowBytes;
-  static constexpr int kStageBytes = (BM + kBNW) * kRowBytes;
-  static constexpr int kALoads = BM * 8 / kThreads;
-  static constexpr int kOccupancy = BM == 128 ? 2 : 1;  // workgroups per CU
+  static constexpr int kStageBytes = (BM + BNW) * kRowBytes;
+  static constexpr int kRowsPerPass = NTHR / 8;        // rows one load pass covers
+  static constexpr int kALoads = BM / kRowsPerPass;
+  static constexpr int kBLoads = BNW / kRowsPerPass;
+  // waves per SIMD: workgroups per CU x waves per workgroup / 4 SIMDs
+  static constexpr int kWavesPerEU = ((BM + BNW <= 256) ? 2 : 1) * kWaves / 4;
 };
 
 // GATEUP: 64 act columns per tile, W0 = W_gate, W1 = W_up
 // DOWN:   128 y columns per tile,  W0 = W_down
-template <bool GATEUP, int BM>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Tile<BM>::kOccupancy, Tile<BM>::kOccupancy)))
+template <bool GATEUP, int BM, int BNW, int NTHR, int NSETS>
+__global__ __launch_bounds__(NTHR)
+__attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
+                                   Tile<BM, BNW, NTHR>::kWavesPerEU)))
 void bf16_tile_kernel(
     int Kdim, int N, int x_rows, int n_groups, int NT, const TileInfo* __restrict__ tiles,
     const int32_t* __restrict__ gts, const int32_t* __restrict__ meta,
     const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
     const float* __restrict__ row_scale, uint16_t* __restrict__ out) {
-  using TL = Tile<BM>;
+  using TL = Tile<BM, BNW, NTHR>;
   constexpr int kALoads = TL::kALoads;
+  constexpr int kBLoads = TL::kBLoads;
   constexpr int kNB = TL::kNB;
   __shared__ __attribute__((aligned(16))) char smem[2 * TL::kStageBytes];
 
@@ -95,7 +105,7 @@ void bf16_tile_kernel(
   const TileInfo ti = tiles[gstart + local % nmt];
   const int nrows = min(ti.m1 - ti.m0, BM);
 
-  constexpr int kCols = GATEUP ? 64 : 128;
+  constexpr int kCols = GATEUP ? BNW / 2 : BNW;
   const int n0 = ntile * kCols;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -108,7 +118,8 @@ void bf16_tile_kernel(
   // loads of later slices stay in flight across the LDS stores.  The per-lane
   // offsets are loop-invariant; the k position goes in the uniform soffset.
   const int lc = tid & 7;
-  const int lr = tid >> 3;  // 0..31
+  const int lr = tid >> 3;  // 0 .. kRowsPerPass-1
+  constexpr int kRP = TL::kRowsPerPass;
   constexpr uint32_t kOff = 0x80000000u;  // beyond every buffer (sizes < 2 GiB)
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A), 0, static_cast<int>(static_cast<uint32_t>(x_rows) * Kdim * 2u),
@@ -116,7 +127,7 @@ void bf16_tile_kernel(
   uint32_t a_off[kALoads];
 #pragma unroll
   for (int i = 0; i < kALoads; ++i) {
-    const int r = lr + 32 * i;
+    const int r = lr + kRP * i;
     int sr = -1;
     if (r < nrows) {
       const int gr = ti.m0 + r;
@@ -134,8 +145,8 @@ void bf16_tile_kernel(
   uint32_t b_off[kBLoads];
 #pragma unroll
   for (int i = 0; i < kBLoads; ++i) {
-    const int r = lr + 32 * i;  // 0..127
-    const int n = GATEUP ? n0 + (r & 63) : n0 + r;
+    const int r = lr + kRP * i;  // 0..BNW-1
+    const int n = GATEUP ? n0 + (r % (BNW / 2)) : n0 + r;
     b_off[i] = (n < N) ? (static_cast<uint32_t>(n) * Kdim + lc * 8) * 2u : kOff;
   }
 
@@ -153,9 +164,10 @@ void bf16_tile_kernel(
     char* as_ = smem + (STAGE) * TL::kStageBytes;                                      \
     char* bs_ = as_ + TL::kABytes;                                                     \
     _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                \
-        *reinterpret_cast<uint4*>(as_ + swz(lr + 32 * i, lc)) = SA[i];                 \
+        if (lr + kRP * i < nrows)                                                      \
+          *reinterpret_cast<uint4*>(as_ + swz(lr + kRP * i, lc)) = SA[i];              \
     _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                \
-        *reinterpret_cast<uint4*>(bs_ + swz(lr + 32 * i, lc)) = SB[i];                 \
+        *reinterpret_cast<uint4*>(bs_ + swz(lr + kRP * i, lc)) = SB[i];                \
   } while (0)
 
   // B-tile rows of this wave's 32-wide weight blocks.  GATEUP: the first half
@@ -165,10 +177,10 @@ void bf16_tile_kernel(
   for (int nb = 0; nb < kNB; ++nb) {
     if (GATEUP) {
       const int half = kNB / 2;
-      const int base = wn * (64 / TL::kWavesN);
-      brow[nb] = (nb < half) ? base + nb * 32 : 64 + base + (nb - half) * 32;
+      const int base = wn * (BNW / 2 / TL::kWavesN);
+      brow[nb] = (nb < half) ? base + nb * 32 : BNW / 2 + base + (nb - half) * 32;
     } else {
-      brow[nb] = wn * (kBNW / TL::kWavesN) + nb * 32;
+      brow[nb] = wn * (BNW / TL::kWavesN) + nb * 32;
     }
   }
 
@@ -210,33 +222,52 @@ void bf16_tile_kernel(
     }
   };
 
-  // ---- main loop: slices kt+1, kt+2 and kt+3 are in flight while slice kt is
-  // multiplied.  Three register sets rotate through the loads; two LDS stages
-  // alternate.  Every step issues its prefetch unconditionally (past the end
-  // it re-reads the last slice, an L2 hit), so the wait before each LDS store
-  // counts only the slice being stored and the newer slices stay in flight.
+  // ---- main loop: NSETS register sets rotate through the global loads, so
+  // slices kt+1 .. kt+NSETS are in flight while slice kt is multiplied out of
+  // one of two LDS stages.  Every step issues its prefetch unconditionally
+  // (past the end it re-reads the last slice, an L2 hit), so the wait before
+  // each LDS store counts only the slice being stored and the newer slices
+  // stay in flight.  Rows past the group are neither loaded nor stored: their
+  // LDS rows hold stale values, which only reach output rows masked at the end.
   const int nk = Kdim / kBK;
-  uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads], sa2[kALoads], sb2[kBLoads];
+  uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads];
+  uint4 sa2[NSETS > 2 ? kALoads : 1], sb2[NSETS > 2 ? kBLoads : 1];
+  uint4 sa3[NSETS > 3 ? kALoads : 1], sb3[NSETS > 3 ? kBLoads : 1];
   MOE_LOAD_SLICE(sa0, sb0, 0);
   MOE_LOAD_SLICE(sa1, sb1, min(1, nk - 1) * kBK);
-  MOE_LOAD_SLICE(sa2, sb2, min(2, nk - 1) * kBK);
+  if constexpr (NSETS > 2) MOE_LOAD_SLICE(sa2, sb2, min(2, nk - 1) * kBK);
+  if constexpr (NSETS > 3) MOE_LOAD_SLICE(sa3, sb3, min(3, nk - 1) * kBK);
   MOE_STORE_SLICE(sa0, sb0, 0);
   __syncthreads();
+  // step J multiplies slice J (stage J % 2), refills its register set with
+  // slice J + NSETS and stores slice J + 1 (the next set) to the other stage
 #define MOE_STEP(J, LA, LB, STAGE, SA, SB)                                              \
-  MOE_LOAD_SLICE(LA, LB, min((J) + 3, nk - 1) * kBK);                                  \
+  MOE_LOAD_SLICE(LA, LB, min((J) + NSETS, nk - 1) * kBK);                              \
   compute(STAGE);                                                                      \
   if ((J) + 1 >= nk) break;                                                            \
   MOE_STORE_SLICE(SA, SB, (STAGE) ^ 1);                                                \
   __syncthreads();
-  for (int kt = 0;; kt += 6) {
-    // step j multiplies slice j (stage j % 2), refills set j % 3 with slice
-    // j + 3 and stores slice j + 1 (set (j + 1) % 3) to stage (j + 1) % 2
-    MOE_STEP(kt + 0, sa0, sb0, 0, sa1, sb1)
-    MOE_STEP(kt + 1, sa1, sb1, 1, sa2, sb2)
-    MOE_STEP(kt + 2, sa2, sb2, 0, sa0, sb0)
-    MOE_STEP(kt + 3, sa0, sb0, 1, sa1, sb1)
-    MOE_STEP(kt + 4, sa1, sb1, 0, sa2, sb2)
-    MOE_STEP(kt + 5, sa2, sb2, 1, sa0, sb0)
+  if constexpr (NSETS == 2) {
+    for (int kt = 0;; kt += 2) {
+      MOE_STEP(kt + 0, sa0, sb0, 0, sa1, sb1)
+      MOE_STEP(kt + 1, sa1, sb1, 1, sa0, sb0)
+    }
+  } else if constexpr (NSETS == 3) {
+    for (int kt = 0;; kt += 6) {
+      MOE_STEP(kt + 0, sa0, sb0, 0, sa1, sb1)
+      MOE_STEP(kt + 1, sa1, sb1, 1, sa2, sb2)
+      MOE_STEP(kt + 2, sa2, sb2, 0, sa0, sb0)
+      MOE_STEP(kt + 3, sa0, sb0, 1, sa1, sb1)
+      MOE_STEP(kt + 4, sa1, sb1, 0, sa2, sb2)
+      MOE_STEP(kt + 5, sa2, sb2, 1, sa0, sb0)
+    }
+  } else {
+    for (int kt = 0;; kt += 4) {
+      MOE_STEP(kt + 0, sa0, sb0, 0, sa1, sb1)
+      MOE_STEP(kt + 1, sa1, sb1, 1, sa2, sb2)
+      MOE_STEP(kt + 2, sa2, sb2, 0, sa3, sb3)
+      MOE_STEP(kt + 3, sa3, sb3, 1, sa0, sb0)
+    }
   }
 #undef MOE_STEP
 #undef MOE_LOAD_SLICE
@@ -272,7 +303,7 @@ void bf16_tile_kernel(
   }
 }
 
-template <int BM>
+template <int BM, int BNW, int NTHR, int NSETS>
 hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                         const int32_t* offsets, const int32_t* row_index, const uint16_t* x,
                         const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
@@ -283,25 +314,25 @@ hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_ro
   const int max_tiles = max_tiles_for(rows, n_groups, BM);
   uint16_t* act = static_cast<uint16_t*>(w.act);
 
-  const int nt1 = (d_ffn + 63) / 64;
+  const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
   long blocks1 = static_cast<long>(max_tiles) * nt1;
   blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
   {
     ProfScope prof_(s, "gateup_bf16");
-    hipLaunchKernelGGL((bf16_tile_kernel<true, BM>), dim3(static_cast<unsigned>(blocks1)),
-                       dim3(kThreads), 0, s, d_model, d_ffn, x_rows, n_groups, nt1, w.tiles,
+    hipLaunchKernelGGL((bf16_tile_kernel<true, BM, BNW, NTHR, NSETS>),
+                       dim3(static_cast<unsigned>(blocks1)), dim3(NTHR), 0, s, d_model, d_ffn, x_rows, n_groups, nt1, w.tiles,
                        w.group_tile_start, w.meta, row_index, x, wg, wu, nullptr, act);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  const int nt2 = (d_model + 127) / 128;
+  const int nt2 = (d_model + BNW - 1) / BNW;
   long blocks2 = static_cast<long>(max_tiles) * nt2;
   blocks2 = (blocks2 + kNumXcd - 1) / kNumXcd * kNumXcd;
   {
     ProfScope prof_(s, "down_bf16");
-    hipLaunchKernelGGL((bf16_tile_kernel<false, BM>), dim3(static_cast<unsigned>(blocks2)),
-                       dim3(kThreads), 0, s, d_ffn, d_model, rows, n_groups, nt2, w.tiles,
+    hipLaunchKernelGGL((bf16_tile_kernel<false, BM, BNW, NTHR, NSETS>),
+                       dim3(static_cast<unsigned>(blocks2)), dim3(NTHR), 0, s, d_ffn, d_model, rows, n_groups, nt2, w.tiles,
                        w.group_tile_start, w.meta, nullptr, act, wd, nullptr, row_scale, y);
   }
   return hipGetLastError();
@@ -315,13 +346,8 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
                               const uint16_t* wd, const float* row_scale, uint16_t* y,
                               void* ws, hipStream_t s) {
   SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
-  // Few rows per group: weight streaming, keep bytes in flight (two
-  // workgroups per CU).  Many rows per group: matrix-core bound.
-  if (rows <= 256 * n_groups)
-    return launch_tiles<128>(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, wg,
-                             wu, wd, row_scale, y, w, s);
-  return launch_tiles<256>(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, wg, wu,
-                           wd, row_scale, y, w, s);
+  return launch_tiles<256, 256, 512, 2>(n_groups, d_model, d_ffn, rows, x_rows, offsets,
+                                        row_index, x, wg, wu, wd, row_scale, y, w, s);
 }
 
 }  // namespace moe
