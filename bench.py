@@ -48,6 +48,28 @@ def algorithmic(cfg, n_touched, n_touched_shared):
     return gateup_bytes, gateup_flops, layer_bytes, layer_flops
 
 
+def recorded_traffic(workload: str):
+    """HBM bytes per routed gate/up launch from the FETCH_SIZE / WRITE_SIZE
+    counter runs summarised in profiles/hbm_traffic_<workload>.md, already
+    scaled by the copy calibration.  None when no such record exists or the
+    kernel sources changed since the counters were taken (their hash differs)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ("swiglu_bf16.hip", "swiglu_tiles.h", "common.h"):
+        with open(os.path.join(ROOT, "sparse_mixture_experts_biased_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"traffic routed\.gateup_bf16 (\S+) bytes=(\d+) .*sources=([0-9a-f]+)", line)
+            if m and m.group(1) == workload and h.hexdigest().startswith(m.group(3)):
+                return int(m.group(2))
+    return None
+
+
 def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256):
     """Time the oracle on a bounded sample of the same workload on host cores.
 
@@ -217,6 +239,8 @@ def main(argv=None):
     else:
         roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
+    traffic = recorded_traffic(cfg.name)
+    roofline["traffic"] = traffic
     roofline.update(kernel="gateup_bf16 (routed experts)", avg_ms=round(routed_ms, 4),
                     algorithmic_bytes=gu_bytes, algorithmic_flops=gu_flops,
                     hbm_gbs=round(gbs, 1), mfma_tflops=round(tfs, 1),
