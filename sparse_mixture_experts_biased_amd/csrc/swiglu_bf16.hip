@@ -92,12 +92,9 @@ void bf16_tile_kernel(
   const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
   const int w = xcd * per_xcd + slot;
   if (slot >= per_xcd || w >= total) return;
-  int lo = 0, hi = n_groups;  // largest g with gts[g] * NT <= w (that group has tiles)
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (gts[mid] * NT <= w) lo = mid; else hi = mid;
-  }
-  const int g = lo;
+  // gts[g] * NT <= w < gts[g + 1] * NT implies gts[g] <= w / NT < gts[g + 1]:
+  // tile w / NT belongs to the group of work item w.
+  const int g = tiles[w / NT].group;
   const int gstart = gts[g];
   const int nmt = gts[g + 1] - gstart;
   const int local = w - gstart * NT;
@@ -273,34 +270,470 @@ void bf16_tile_kernel(
 #undef MOE_LOAD_SLICE
 #undef MOE_STORE_SLICE
 
-  // ---- epilogue: D[row][col] of a 32x32 block sits in lane (col + 32*((row/4)%2)),
-  // register (row%4) + 4*(row/8).
+  // ---- epilogue: the bf16 tile is staged in LDS (both stages are free now)
+  // and written as whole 16-byte chunks of each output row; the MFMA layout
+  // alone would give 2-byte stores scattered over 32 rows per instruction.
+  // D[row][col] of a 32x32 block sits in lane (col + 32*((row/4)%2)),
+  // register (row%4) + 4*(row/8).  Staging layout: row-major bf16 rows of
+  // kCols, the 16-byte chunk index XORed with (row & 4) so the two half-waves
+  // (rows r and r+4) write disjoint banks.
+  static_assert(BM * kCols * 2 <= 2 * TL::kStageBytes, "output tile exceeds LDS");
+  constexpr int kOutRowBytes = kCols * 2;
+  constexpr int kOutChunks = kCols / 8;
+  __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = wm * 64 + mb * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
       if (row >= nrows) continue;
-      const int gr = ti.m0 + row;
+      char* orow = smem + row * kOutRowBytes;
+      const int sw = row & 4;
       if (GATEUP) {
 #pragma unroll
         for (int nb = 0; nb < kNB / 2; ++nb) {
-          const int col = n0 + brow[nb] + fr;
-          if (col < N) {
-            const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
-            out[static_cast<size_t>(gr) * N + col] = f32_to_bf16(v);
-          }
+          const int c = brow[nb] + fr;
+          const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
+          *reinterpret_cast<uint16_t*>(orow + (((c >> 3) ^ sw) << 4) + (c & 7) * 2) =
+              f32_to_bf16(v);
         }
       } else {
-        const float sc = row_scale ? row_scale[gr] : 1.0f;
+        const float sc = row_scale ? row_scale[ti.m0 + row] : 1.0f;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
-          const int col = n0 + brow[nb] + fr;
-          if (col < N) out[static_cast<size_t>(gr) * N + col] = f32_to_bf16(acc[mb][nb][q] * sc);
+          const int c = brow[nb] + fr;
+          *reinterpret_cast<uint16_t*>(orow + (((c >> 3) ^ sw) << 4) + (c & 7) * 2) =
+              f32_to_bf16(acc[mb][nb][q] * sc);
         }
       }
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < BM * kOutChunks / NTHR; ++it) {
+    const int idx = it * NTHR + tid;
+    const int r = idx / kOutChunks;
+    const int c = idx % kOutChunks;
+    if (r < nrows && n0 + c * 8 < N) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kOutRowBytes +
+                                                     ((c ^ (r & 4)) << 4));
+      *reinterpret_cast<uint4*>(out + static_cast<size_t>(ti.m0 + r) * N + n0 + c * 8) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- streaming variant
+//
+// One workgroup per CU, each walking a fixed list of work items: the items of
+// an XCD (the same XCD-contiguous runs as above) are dealt round-robin to its
+// workgroups.  A workgroup streams the k-slices of its items back to back
+// through the same two register sets and two LDS stages, so the first slices
+// of the next item are in flight while the last slice of the current one is
+// multiplied and its output tile written: no CU idles through an item's
+// set-up loads or its epilogue, and there is no launch gap between items.
+// The next item's tile records and gathered row indices are fetched a few
+// slices ahead by loads issued on every step (branch-free, so the compiler's
+// wait counts stay exact).  Used when K is an even number of at least
+// kMinStreamSlices slices and N is a multiple of the column tile.
+constexpr int kMinStreamSlices = 8;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+template <bool GATEUP, int BM, int BNW, int NTHR>
+__global__ __launch_bounds__(NTHR)
+__attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
+                                   Tile<BM, BNW, NTHR>::kWavesPerEU)))
+void bf16_stream_kernel(
+    int Kdim, int N, int x_rows, int rows, int max_tiles, int NT,
+    const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
+    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    const float* __restrict__ row_scale, uint16_t* __restrict__ out) {
+  using TL = Tile<BM, BNW, NTHR>;
+  constexpr int kALoads = TL::kALoads;
+  constexpr int kBLoads = TL::kBLoads;
+  constexpr int kNB = TL::kNB;
+  constexpr int kRP = TL::kRowsPerPass;
+  constexpr int kCols = GATEUP ? BNW / 2 : BNW;
+  constexpr uint32_t kOff = 0x80000000u;  // beyond every buffer (sizes < 2 GiB)
+  static_assert(kCols % kRP == 0, "a load pass must not straddle the gate/up halves");
+  __shared__ __attribute__((aligned(16))) char smem[2 * TL::kStageBytes];
+
+  // ---- this workgroup's items: first, first + nslot, ... below end
+  const int total = meta[0] * NT;
+  const int nslot = gridDim.x / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int first = xcd * per_xcd + static_cast<int>(blockIdx.x) / kNumXcd;
+  const int end = min(total, (xcd + 1) * per_xcd);
+  if (first >= end) return;
+  const int n_items = (end - first + nslot - 1) / nslot;
+  const int nk = Kdim / kBK;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar
+  const int lane = tid % kWave;
+  const int wm = wave / TL::kWavesN, wn = wave % TL::kWavesN;
+  const int lc = tid & 7;
+  const int lr = tid >> 3;  // 0 .. kRP-1
+  const uint32_t rowbytes = static_cast<uint32_t>(Kdim) * 2u;
+  const uint32_t wbytes = static_cast<uint32_t>(N) * rowbytes;
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(A, static_cast<uint32_t>(x_rows) * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsT =
+      buffer_rsrc(tiles, static_cast<uint32_t>(max_tiles) * sizeof(TileInfo));
+  // gate/up gathers x rows through row_index (NULL: grouped row r is x row r);
+  // without it every row-index load is out of range and reads nothing
+  const bool gather = GATEUP && row_index != nullptr;
+  const __amdgpu_buffer_rsrc_t rsR =
+      buffer_rsrc(row_index, gather ? static_cast<uint32_t>(rows) * 4u : 0u);
+
+  // A-tile offset of load slot i (tile row lr + kRP * i, source row sr) of an
+  // item with nrows rows; the row test is written as lr < nrows - kRP * i so
+  // that no per-slot row value has to stay in a register.
+  auto a_offset = [&](int i, int nrows, int sr) -> uint32_t {
+    return (lr < nrows - kRP * i && sr >= 0 && sr < x_rows)
+               ? static_cast<uint32_t>(sr) * rowbytes + static_cast<uint32_t>(lc) * 16u
+               : kOff;
+  };
+
+  // ---- load-side item: its group, column tile, rows and per-lane offsets
+  int l_item = 0, l_g, l_ntile, l_m0, l_nrows;
+  {
+    const int w = first;
+    const TileInfo t0 = tiles[w / NT];
+    const int local = w - t0.gstart * NT;
+    const TileInfo ti = tiles[t0.gstart + local % t0.ntiles];
+    l_g = t0.group;
+    l_ntile = local / t0.ntiles;
+    l_m0 = ti.m0;
+    l_nrows = min(ti.m1 - ti.m0, BM);
+  }
+  uint32_t a_off[kALoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) {
+    const int r = lr + kRP * i;
+    int sr = l_m0 + r;
+    if (gather) sr = (r < l_nrows) ? row_index[l_m0 + r] : -1;
+    a_off[i] = a_offset(i, l_nrows, sr);
+  }
+  // B-tile row of load slot i is lr + boff(i); GATEUP stacks gate rows over
+  // the matching up rows, so slots of the second half repeat the first's rows.
+  auto b_row_add = [&](int i) -> uint32_t {
+    const int add = GATEUP ? (kRP * i) % (BNW / 2) : kRP * i;
+    return static_cast<uint32_t>(add) * rowbytes;
+  };
+
+  // Weights of the load-side item and the byte offset of its column tile
+  // (set per item); the lane's own B row and chunk stay in bb.
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  uint32_t bcol;
+  const uint32_t bb = static_cast<uint32_t>(lr) * rowbytes + static_cast<uint32_t>(lc) * 16u;
+  auto set_weights = [&]() {
+    rb0 = buffer_rsrc(W0 + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    rb1 = buffer_rsrc((GATEUP ? W1 : W0) + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
+  };
+  set_weights();
+  const uint32_t kb_end = static_cast<uint32_t>(nk) * kBK * 2u;
+  uint32_t kb = 0;  // byte offset of the load side's next k-slice
+
+#define MOE_LOAD_SLICE(SA, SB)                                                               \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) SA[i] =                             \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0)); \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i) SB[i] = __builtin_bit_cast(          \
+        uint4, __builtin_amdgcn_raw_buffer_load_b128((!GATEUP || i < kBLoads / 2) ? rb0 : rb1, \
+                                                     bb, bcol + kb + b_row_add(i), 0));     \
+    kb += kBK * 2;                                                                          \
+  } while (0)
+#define MOE_STORE_SLICE(SA, SB, STAGE)                                                      \
+  do {                                                                                      \
+    char* as_ = smem + (STAGE) * TL::kStageBytes;                                           \
+    char* bs_ = as_ + TL::kABytes;                                                          \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                     \
+        *reinterpret_cast<uint4*>(as_ + swz(lr + kRP * i, lc)) = SA[i];                     \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                     \
+        *reinterpret_cast<uint4*>(bs_ + swz(lr + kRP * i, lc)) = SB[i];                     \
+  } while (0)
+  // ---- next item, fetched ahead.  p holds, in lane l, dword (l & 7) of the
+  // tile record of the next item's group start (lanes with l & 8 == 0) or of
+  // its row tile (l & 8 != 0); ri holds, in lane j + 8 i, the source row of
+  // tile row 8 * wave + j + kRP * i (the rows this wave's load slots need).
+  // Both are refetched on every other step, after that step's slice loads,
+  // and read back two steps later: a wait for them then covers only slices
+  // that were due anyway, and the loop stays branch-free around its loads
+  // (so the compiler's wait counts stay exact).  After the next item changes,
+  // the group record is read one fetch later, the row-tile record two and the
+  // row indices three.
+  static_assert(kALoads * 8 <= kWave, "one lane per gathered row of the wave");
+  int p = 0, ri = -1;
+  int n_g = 0, n_ntile = 0, n_m0 = 0, n_nrows = 0;
+  int nw = first + min(1, n_items - 1) * nslot;  // next item
+  int t0rec = nw / NT;                           // a tile of its group
+  int rec = 0;                                   // its row tile
+  int fa = 0;                                    // fetches since nw changed
+
+  // Read the records fetched two steps ago, and move the load side to the
+  // next item once all slices of the current one are issued.
+#define MOE_ADVANCE()                                                                       \
+  do {                                                                                      \
+    if (fa == 1) { /* the group record just arrived: locate the row tile */                 \
+      const int gstart_ = __builtin_amdgcn_readlane(p, 3);                                  \
+      const int gnt_ = max(__builtin_amdgcn_readlane(p, 4), 1);                             \
+      const int local_ = nw - gstart_ * NT;                                                 \
+      n_g = __builtin_amdgcn_readlane(p, 0);                                                \
+      n_ntile = local_ / gnt_;                                                              \
+      rec = gstart_ + local_ - n_ntile * gnt_;                                              \
+    }                                                                                       \
+    n_m0 = __builtin_amdgcn_readlane(p, 9);                                                 \
+    n_nrows = min(__builtin_amdgcn_readlane(p, 10) - n_m0, BM);                             \
+    if (kb == kb_end) {                                                                     \
+      if (l_item + 1 < n_items) {                                                           \
+        ++l_item;                                                                           \
+        kb = 0;                                                                             \
+        l_g = n_g; l_ntile = n_ntile; l_m0 = n_m0; l_nrows = n_nrows;                       \
+        set_weights();                                                                      \
+        _Pragma("unroll") for (int i = 0; i < kALoads; ++i) {                               \
+          const int sr_ = gather ? __builtin_amdgcn_ds_bpermute(((lane >> 3) + 8 * i) * 4, ri) \
+                                 : l_m0 + kRP * i + lr;                                     \
+          a_off[i] = a_offset(i, l_nrows, sr_);                                             \
+        }                                                                                   \
+        nw = first + min(l_item + 1, n_items - 1) * nslot;                                  \
+        t0rec = nw / NT;                                                                    \
+        fa = 0;                                                                             \
+      } else {                                                                              \
+        kb = kb_end - kBK * 2; /* past the last item: re-read its last slice (an L2 hit) */ \
+      }                                                                                     \
+    }                                                                                       \
+  } while (0)
+  // Refetch the next item's records and row indices (the lane id is
+  // recomputed rather than kept in a register through the loop).
+#define MOE_FETCH()                                                                         \
+  do {                                                                                      \
+    int z_ = 0;                                                                             \
+    asm volatile("" : "+v"(z_));                                                            \
+    const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z_));     \
+    if (GATEUP) { /* without row_index every load is out of range: no branch */             \
+      const int r_ = wave * 8 + (ln_ & 7) + kRP * ((ln_ >> 3) & (kALoads - 1));             \
+      ri = __builtin_amdgcn_raw_buffer_load_b32(                                            \
+          rsR, r_ < n_nrows ? static_cast<uint32_t>(n_m0 + r_) * 4u : kOff, 0, 0);          \
+    }                                                                                       \
+    p = __builtin_amdgcn_raw_buffer_load_b32(                                               \
+        rsT, static_cast<uint32_t>((ln_ & 8) ? rec : t0rec) * 32u + (ln_ & 7) * 4u, 0, 0);  \
+    fa = min(fa + 1, 3);                                                                    \
+  } while (0)
+
+  // ---- compute-side item (trails the load side by two slices)
+  int c_m0 = l_m0, c_nrows = l_nrows, c_n0 = l_ntile * kCols;
+
+  int brow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (GATEUP) {
+      const int half = kNB / 2;
+      const int base = wn * (BNW / 2 / TL::kWavesN);
+      brow[nb] = (nb < half) ? base + nb * 32 : BNW / 2 + base + (nb - half) * 32;
+    } else {
+      brow[nb] = wn * (BNW / TL::kWavesN) + nb * 32;
+    }
+  }
+
+  f32x16_t acc[2][kNB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
+
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+
+  // Wave (wm, wn) multiplies the 32-row blocks 2 wm and 2 wm + 1.  The LDS
+  // fragments of k-step kk + 1 are read while the MFMAs of kk run (two
+  // fragment buffers), so the LDS latency is not exposed per k-step.
+  auto compute = [&](int stage) {
+    const bool mb0 = wm * 64 < c_nrows;
+    const bool mb1 = wm * 64 + 32 < c_nrows;
+    if (!mb0) return;
+    const char* as = smem + stage * TL::kStageBytes;
+    const char* bs = as + TL::kABytes;
+    bf16x8_t bq[2][kNB], aq[2][2];
+#define MOE_FRAGS(KK, BUF)                                                                  \
+  do {                                                                                      \
+    const int c_ = (KK) * 2 + fh;                                                           \
+    _Pragma("unroll") for (int nb = 0; nb < kNB; ++nb) bq[BUF][nb] =                        \
+        *reinterpret_cast<const bf16x8_t*>(bs + swz(brow[nb] + fr, c_));                    \
+    aq[BUF][0] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + fr, c_));            \
+    if (mb1) aq[BUF][1] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + 32 + fr, c_)); \
+  } while (0)
+    MOE_FRAGS(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < kBK / 16) MOE_FRAGS(kk + 1, cur ^ 1);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        acc[0][nb] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cur][0], bq[cur][nb], acc[0][nb], 0, 0, 0);
+      if (mb1) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[cur][1], bq[cur][nb],
+                                                               acc[1][nb], 0, 0, 0);
+      }
+    }
+#undef MOE_FRAGS
+  };
+
+  // Output tile of the compute-side item, staged through LDS stage `stage`
+  // (free once every wave has multiplied it) in rounds of kRoundRows rows:
+  // bf16 rows of kCols with the 16-byte chunk index XORed with (row & 4), then
+  // written as whole 16-byte chunks.  D[row][col] of a 32x32 block sits in
+  // lane (col + 32*((row/4)%2)), register (row%4) + 4*(row/8).
+  constexpr int kOutRowBytes = kCols * 2;
+  constexpr int kRoundRows = (BM * kOutRowBytes <= TL::kStageBytes) ? BM
+                                                                    : TL::kStageBytes / kOutRowBytes;
+  constexpr int kOutChunks = kCols / 8;
+  static_assert(kRoundRows % 64 == 0 && BM % kRoundRows == 0, "rounds hold whole waves' rows");
+  // Row of (mb, q) is wm*64 + mb*32 + 8*(q/4) + 4*fh + q%4, so (row & 4) is
+  // 4*fh in every register and each LDS write is a per-lane base plus a
+  // constant; the read-out rows of iteration `it` are it * (NTHR / kOutChunks)
+  // + tid / kOutChunks, again a per-lane base plus a constant.
+  auto epilogue = [&](int stage) {
+    // Lane constants are rederived here from the hardware lane id: hoisted
+    // out of the item loop they would stay live through the inner loop, which
+    // needs every register.
+    int ez = 0;  // opaque zero: keeps the lane-id computation inside the loop
+    asm volatile("" : "+v"(ez));
+    const int e_lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, ez));
+    const int e_wave = wave;
+    const int etid = e_wave * kWave + e_lane;
+    const int e_wm = e_wave / TL::kWavesN, e_wn = e_wave % TL::kWavesN;
+    const int e_fr = e_lane & 31, e_fh = e_lane >> 5;
+    char* ot = smem + stage * TL::kStageBytes;
+    constexpr int kReadRows = NTHR / kOutChunks;
+    static_assert(NTHR % kOutChunks == 0 && kReadRows % 8 == 0, "read-out rows keep row & 4");
+    static_assert(kRoundRows % 64 == 0 && BM % kRoundRows == 0, "rounds hold whole waves' rows");
+#pragma unroll
+    for (int r0 = 0; r0 < BM; r0 += kRoundRows) {
+      if (r0 >= c_nrows) break;
+      {
+        int cofs[kNB];
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int c = (GATEUP ? (nb < kNB / 2 ? e_wn * (BNW / 2 / TL::kWavesN) + nb * 32
+                                                : BNW / 2 + e_wn * (BNW / 2 / TL::kWavesN) +
+                                                      (nb - kNB / 2) * 32)
+                                : e_wn * (BNW / TL::kWavesN) + nb * 32) +
+                        e_fr;
+          cofs[nb] = (((c >> 3) ^ (4 * e_fh)) << 4) + (c & 7) * 2;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if (e_wm * 64 < r0 || e_wm * 64 >= r0 + kRoundRows) break;  // rows of another round
+          // block row base, relative to the round, plus this lane's half (4 * fh)
+          const int base = e_wm * 64 + mb * 32 - r0 + 4 * e_fh;
+          char* ob = ot + base * kOutRowBytes;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            // rows past the item are staged too (never written out)
+            const int rr = 8 * (q >> 2) + (q & 3);
+            char* orow = ob + rr * kOutRowBytes;
+            if (GATEUP) {
+#pragma unroll
+              for (int nb = 0; nb < kNB / 2; ++nb) {
+                const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
+                *reinterpret_cast<uint16_t*>(orow + cofs[nb]) = f32_to_bf16(v);
+              }
+            } else if (row_scale == nullptr) {
+#pragma unroll
+              for (int nb = 0; nb < kNB; ++nb)
+                *reinterpret_cast<uint16_t*>(orow + cofs[nb]) = f32_to_bf16(acc[mb][nb][q]);
+            } else {  // waits on its loads, so stalls the stream once per item
+              // (row < c_nrows) as (lane base < c_nrows - rr): no per-row registers
+              const int row0 = base + r0;
+              const float sc = row0 < c_nrows - rr ? row_scale[c_m0 + row0 + rr] : 1.0f;
+#pragma unroll
+              for (int nb = 0; nb < kNB; ++nb)
+                *reinterpret_cast<uint16_t*>(orow + cofs[nb]) = f32_to_bf16(acc[mb][nb][q] * sc);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int rl = etid / kOutChunks, cl = etid % kOutChunks;
+      const char* src = ot + rl * kOutRowBytes + ((cl ^ (rl & 4)) << 4);
+      uint16_t* dst = out + static_cast<size_t>(c_m0 + r0 + rl) * N + c_n0 + cl * 8;
+#pragma unroll
+      for (int it = 0; it < kRoundRows / kReadRows; ++it) {
+        if (rl < c_nrows - r0 - it * kReadRows)
+          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(it) * kReadRows * N) =
+              *reinterpret_cast<const uint4*>(src + it * kReadRows * kOutRowBytes);
+      }
+      __syncthreads();
+    }
+  };
+
+  // ---- stream: each step loads the slice two ahead into the register set
+  // stored by the previous step, stores the next slice (loaded one step ago)
+  // to the other LDS stage, and multiplies one slice out of its stage; the LDS
+  // writes drain under the MFMAs, and the stored set is free during them.  nk is even, so every item starts on
+  // stage 1 and ends on stage 0, where its output tile is then staged (at LDS
+  // offset 0, so the staging offsets fit the instructions' 16-bit immediate).
+  uint4 sa0[kALoads], sb0[kBLoads], sa1[kALoads], sb1[kBLoads];
+  MOE_LOAD_SLICE(sa0, sb0);
+  MOE_LOAD_SLICE(sa1, sb1);
+  MOE_STORE_SLICE(sa0, sb0, 1);
+  __syncthreads();
+  // The load side changes item only on the first step of a pair (nk is even),
+  // so that step also advances and refetches the fetch-ahead.
+  for (int j = 0; j < n_items; ++j) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      MOE_ADVANCE();
+      MOE_LOAD_SLICE(sa0, sb0);
+      MOE_FETCH();
+      MOE_STORE_SLICE(sa1, sb1, 0);
+      compute(1);
+      __syncthreads();
+      MOE_LOAD_SLICE(sa1, sb1);
+      MOE_STORE_SLICE(sa0, sb0, 1);
+      compute(0);
+      __syncthreads();
+    }
+    epilogue(0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;
+    c_m0 = l_m0;
+    c_nrows = l_nrows;
+    c_n0 = l_ntile * kCols;
+  }
+#undef MOE_ADVANCE
+#undef MOE_FETCH
+#undef MOE_LOAD_SLICE
+#undef MOE_STORE_SLICE
+}
+
+// Workgroups of the streaming kernels: one per CU, a multiple of the XCD count.
+int stream_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < kNumXcd)
+      cus = 256;
+    cached[dev] = cus / kNumXcd * kNumXcd;
+  }
+  return cached[dev];
 }
 
 template <int BM, int BNW, int NTHR, int NSETS>
@@ -315,25 +748,37 @@ hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_ro
   uint16_t* act = static_cast<uint16_t*>(w.act);
 
   const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
-  long blocks1 = static_cast<long>(max_tiles) * nt1;
-  blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
-  {
+  if (d_model / kBK >= kMinStreamSlices && d_model % (2 * kBK) == 0 && d_ffn % (BNW / 2) == 0) {
+    ProfScope prof_(s, "gateup_bf16");
+    hipLaunchKernelGGL((bf16_stream_kernel<true, BM, BNW, NTHR>), dim3(stream_grid()),
+                       dim3(NTHR), 0, s, d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles,
+                       w.meta, row_index, x, wg, wu, nullptr, act);
+  } else {
+    long blocks1 = static_cast<long>(max_tiles) * nt1;
+    blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     ProfScope prof_(s, "gateup_bf16");
     hipLaunchKernelGGL((bf16_tile_kernel<true, BM, BNW, NTHR, NSETS>),
-                       dim3(static_cast<unsigned>(blocks1)), dim3(NTHR), 0, s, d_model, d_ffn, x_rows, n_groups, nt1, w.tiles,
-                       w.group_tile_start, w.meta, row_index, x, wg, wu, nullptr, act);
+                       dim3(static_cast<unsigned>(blocks1)), dim3(NTHR), 0, s, d_model, d_ffn,
+                       x_rows, n_groups, nt1, w.tiles, w.group_tile_start, w.meta, row_index, x,
+                       wg, wu, nullptr, act);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   const int nt2 = (d_model + BNW - 1) / BNW;
-  long blocks2 = static_cast<long>(max_tiles) * nt2;
-  blocks2 = (blocks2 + kNumXcd - 1) / kNumXcd * kNumXcd;
-  {
+  if (d_ffn / kBK >= kMinStreamSlices && d_ffn % (2 * kBK) == 0 && d_model % BNW == 0) {
+    ProfScope prof_(s, "down_bf16");
+    hipLaunchKernelGGL((bf16_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
+                       dim3(NTHR), 0, s, d_ffn, d_model, rows, rows, max_tiles, nt2, w.tiles,
+                       w.meta, nullptr, act, wd, nullptr, row_scale, y);
+  } else {
+    long blocks2 = static_cast<long>(max_tiles) * nt2;
+    blocks2 = (blocks2 + kNumXcd - 1) / kNumXcd * kNumXcd;
     ProfScope prof_(s, "down_bf16");
     hipLaunchKernelGGL((bf16_tile_kernel<false, BM, BNW, NTHR, NSETS>),
-                       dim3(static_cast<unsigned>(blocks2)), dim3(NTHR), 0, s, d_ffn, d_model, rows, n_groups, nt2, w.tiles,
-                       w.group_tile_start, w.meta, nullptr, act, wd, nullptr, row_scale, y);
+                       dim3(static_cast<unsigned>(blocks2)), dim3(NTHR), 0, s, d_ffn, d_model,
+                       rows, n_groups, nt2, w.tiles, w.group_tile_start, w.meta, nullptr, act,
+                       wd, nullptr, row_scale, y);
   }
   return hipGetLastError();
 }

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(int n_groups, int row
     if (g < n_groups) {
       gts[g] = min(start, max_tiles);
       for (int i = 0; i < nt && start + i < max_tiles; ++i)
-        tiles[start + i] = TileInfo{g, lo + i * bm, hi, 0};
+        tiles[start + i] = TileInfo{g, lo + i * bm, hi, start, min(nt, max_tiles - start), {0, 0, 0}};
     }
     __syncthreads();
     if (threadIdx.x == 1023) carry_s = carry + part[1023];

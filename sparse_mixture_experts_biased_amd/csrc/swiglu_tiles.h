@@ -12,10 +12,13 @@ namespace moe {
 
 struct TileInfo {
   int32_t group;
-  int32_t m0;    // first grouped row of the tile
-  int32_t m1;    // one past the group's last row (rows >= m1 are masked)
-  int32_t pad;
+  int32_t m0;      // first grouped row of the tile
+  int32_t m1;      // one past the group's last row (rows >= m1 are masked)
+  int32_t gstart;  // index of the group's first tile
+  int32_t ntiles;  // number of tiles of the group
+  int32_t pad[3];
 };
+static_assert(sizeof(TileInfo) == 32, "TileInfo is read as eight dwords");
 
 struct SwigluWorkspace {
   void* act;                  // [rows, d_ffn] SiLU(gate) * up

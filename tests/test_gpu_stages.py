@@ -215,6 +215,12 @@ SWIGLU_CASES = [
     (1000, 256, 128, 4, 1, torch.bfloat16),    # big groups: many row tiles
     (97, 64, 64, 3, 3, torch.bfloat16),        # K = E_r, smallest aligned sizes
     (150, 96, 80, 6, 2, torch.float32),
+    # K spans >= 8 even 64-wide slices and N is a multiple of the column tile
+    # in both GEMMs: the one-workgroup-per-CU streaming kernels
+    (600, 512, 512, 8, 2, torch.bfloat16),
+    (5, 512, 512, 64, 2, torch.bfloat16),      # nearly all experts empty
+    (2000, 512, 512, 4, 2, torch.bfloat16),    # 1000-row groups: four row tiles each
+    (4000, 1024, 1024, 48, 4, torch.bfloat16),  # several work items per workgroup
 ]
 
 
@@ -252,6 +258,31 @@ def test_grouped_swiglu_row_scale_and_direct_rows():
                            (host_array(wg), host_array(wu), host_array(wd)))
     ref = ref * scale.cpu().numpy().astype(np.float64)[:, None]
     assert rel_err(to_host_f64(y), ref) <= out_tol("bf16")
+
+
+def test_grouped_swiglu_streaming_row_scale_direct_rows_and_bad_rows():
+    """The streaming kernels (d, f >= 512) with a per-row scale, identity rows
+    (row_index NULL) and gathered rows with out-of-range entries."""
+    T, d, f, E = 700, 512, 512, 5
+    x = _tokens(T, d, torch.bfloat16, 81)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, 82)
+    w_host = (host_array(wg), host_array(wu), host_array(wd))
+    off = np.array([0, 300, 300, 301, 590, 700], dtype=np.int32)  # empty and 1-row groups
+    scale = torch.rand(T, generator=_gen(83), device=DEV)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), None, wg, wu, wd, T, scale)
+    ref = O.grouped_swiglu(host_array(x), off, None, w_host)
+    ref = ref * scale.cpu().numpy().astype(np.float64)[:, None]
+    assert rel_err(to_host_f64(y), ref) <= out_tol("bf16")
+    ri = (np.arange(T, dtype=np.int32) * 7) % T
+    ri[[0, 299, 450]] = [-1, T, 1 << 30]
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(ri).to(DEV), wg, wu, wd,
+                    T)
+    yh = to_host_f64(y)
+    assert np.all(yh[[0, 299, 450]] == 0)
+    ok = np.ones(T, bool)
+    ok[[0, 299, 450]] = False
+    ref = O.grouped_swiglu(host_array(x), off, np.where(ok, ri, 0).astype(np.int32), w_host)
+    assert rel_err(yh[ok], ref[ok]) <= out_tol("bf16")
 
 
 def test_grouped_swiglu_bad_row_index_reads_zero_row():
