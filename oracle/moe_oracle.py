@@ -18,7 +18,11 @@ Plain NumPy, written from the method's definitions, one function per step:
   * Same page, section 4, item 2: router matmul and score function in fp32.
   * Same page, section 4, item 1: MaxVio = (max_i c_i - cbar) / cbar.
   * Same page, section 3: sort token copies by expert, run each expert on its
-    rows, weight by the gate, add back.
+    rows, weight by the gate, add back; with a capacity factor CF, expert
+    buffers hold C = ceil(CF * T * K / E_r) rows and a copy routed to a full
+    expert is dropped (the token keeps only its residual and other experts).
+  * Routing-and-load-balancing page (yiqiao-yin.github.io), section 5: tokens
+    are admitted to an expert in the order they appear.
 
 Precision.  The pages fix the router at fp32: z is the fp64 dot product of
 the exact inputs rounded once to fp32, s = sigma(z) is evaluated in fp64 and
@@ -36,6 +40,7 @@ Readings where the pages are silent (each listed in the design notes):
 """
 from __future__ import annotations
 
+import math
 from typing import Callable, Optional, Sequence, Tuple, Union
 
 import numpy as np
@@ -158,6 +163,41 @@ def permute(idx: np.ndarray, E_r: int):
     return offsets.astype(np.int32), row_token.astype(np.int32), slot_row.astype(np.int32)
 
 
+def expert_capacity(T: int, K: int, E_r: int, cf: float) -> int:
+    """C = ceil(CF * T * K / E_r), evaluated as ceil((cf * (T*K)) / E_r) in
+    IEEE double."""
+    return int(math.ceil(float(cf) * float(T * K) / float(E_r)))
+
+
+def permute_capacity(idx: np.ndarray, E_r: int, C: int):
+    """Capacity-bounded dispatch: expert i admits its copies in ascending token
+    order until it holds C rows; later copies are dropped.
+
+    Returns (offsets over the kept rows, row_token of the kept rows, slot_row
+    with -1 for a dropped copy, kept count per expert).
+    """
+    T, K = idx.shape
+    kept = np.zeros(E_r, dtype=np.int64)
+    lists = [[] for _ in range(E_r)]           # admitted (t, k) per expert
+    slot_row = np.full(T * K, -1, dtype=np.int64)
+    for t in range(T):                          # arrival order
+        for k in range(K):
+            i = int(idx[t, k])
+            if kept[i] < C:
+                lists[i].append(t * K + k)
+                kept[i] += 1
+    offsets = np.zeros(E_r + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    row_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    for i in range(E_r):
+        for j, q in enumerate(lists[i]):
+            r = offsets[i] + j
+            row_token[r] = q // K
+            slot_row[q] = r
+    return (offsets.astype(np.int32), row_token.astype(np.int32), slot_row.astype(np.int32),
+            kept.astype(np.int32))
+
+
 # ---------------------------------------------------------------- experts
 
 def silu(x: np.ndarray) -> np.ndarray:
@@ -218,7 +258,9 @@ def shared_experts(h: np.ndarray, weights: Optional[ExpertSource], E_s: int) -> 
 
 def combine(h: np.ndarray, y_shared: Optional[np.ndarray], y_perm: np.ndarray,
             slot_row: np.ndarray, g: np.ndarray) -> np.ndarray:
-    """y_t = h_t + y_shared_t + sum_k g_{t,k} * y_perm[slot_row[t,k]], fp64."""
+    """y_t = h_t + y_shared_t + sum_k g_{t,k} * y_perm[slot_row[t,k]], fp64.
+
+    A dropped copy (slot_row < 0, capacity dispatch) contributes nothing."""
     h64 = to_f64(h)
     T = h64.shape[0]
     K = g.shape[1]
@@ -227,7 +269,8 @@ def combine(h: np.ndarray, y_shared: Optional[np.ndarray], y_perm: np.ndarray,
         y += y_shared
     sr = slot_row.reshape(T, K).astype(np.int64)
     for k in range(K):
-        y += g[:, k:k + 1].astype(np.float64) * y_perm[sr[:, k]]
+        keep = sr[:, k] >= 0
+        y[keep] += g[keep, k:k + 1].astype(np.float64) * y_perm[sr[keep, k]]
     return y
 
 
@@ -259,13 +302,18 @@ def load_stats(loads: np.ndarray, T: int, K: int):
 
 def layer_forward(h, e, b, K: int, fn: str, routed: ExpertSource,
                   shared: Optional[ExpertSource] = None, E_s: int = 0,
-                  gamma: Optional[float] = None):
-    """One full layer call: route, dispatch, routed + shared experts, combine,
-    and (when gamma is given) the per-step bias update after counting."""
+                  gamma: Optional[float] = None, capacity: Optional[int] = None):
+    """One full layer call: route, dispatch (capacity-bounded when `capacity`
+    is given), routed + shared experts, combine, and (when gamma is given) the
+    per-step bias update after counting.  The bias update counts the router's
+    choices (before any drop)."""
     E_r = e.shape[0]
     T = h.shape[0]
     r = route(h, e, b, K, fn)
-    offsets, row_token, slot_row = permute(r["idx"], E_r)
+    if capacity is None:
+        offsets, row_token, slot_row = permute(r["idx"], E_r)
+    else:
+        offsets, row_token, slot_row, _ = permute_capacity(r["idx"], E_r, capacity)
     y_perm = grouped_swiglu(h, offsets, row_token, routed)
     y_sh = shared_experts(h, shared, E_s) if E_s else None
     y = combine(h, y_sh, y_perm, slot_row, r["gates"])

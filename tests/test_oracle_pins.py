@@ -423,3 +423,101 @@ def test_grouped_swiglu_is_per_expert_dense():
         rows = [t for t in range(T) if i in r["idx"][t]]
         ref = O.swiglu(h[rows], w[0][i], w[1][i], w[2][i])
         assert np.allclose(y[off[i]:off[i + 1]], ref, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------ capacity dispatch
+# Routing-math page, section 3: C = ceil(CF * T * K / E_r); a copy routed to a
+# full expert is dropped.  Routing-and-load-balancing page, section 5: tokens
+# are admitted in the order they appear, so capacity is order-dependent by
+# design while the router is not.
+
+@pytest.mark.parametrize("T,K,E,cf,C", [(4096, 8, 256, 1.0, 128), (4096, 8, 256, 1.25, 160),
+                                        (10, 1, 4, 1.0, 3), (64, 2, 8, 1.0, 16),
+                                        (64, 2, 8, 1.25, 20), (7, 3, 5, 1.1, 5)])
+def test_capacity_closed_form(T, K, E, cf, C):
+    assert O.expert_capacity(T, K, E, cf) == C
+
+
+def test_capacity_admission_is_rank_in_token_order():
+    # a copy (t, k) routed to expert i is kept iff fewer than C earlier tokens
+    # picked i -- a counting statement independent of the dispatch loop
+    rng = np.random.default_rng(40)
+    T, E, K = 300, 9, 3
+    idx = np.sort(np.stack([rng.choice(E, K, replace=False, p=np.arange(1, E + 1) / 45)
+                            for _ in range(T)]), axis=1)
+    for C in (0, 1, 17, 60, 100, T):
+        off, rt, sr, kept = O.permute_capacity(idx, E, C)
+        before = np.zeros(E, dtype=np.int64)
+        for t in range(T):
+            for k in range(K):
+                i = idx[t, k]
+                assert (sr[t * K + k] >= 0) == (before[i] < C)
+            for k in range(K):
+                before[idx[t, k]] += 1
+        c = O.load_count(idx, E)
+        assert np.array_equal(kept, np.minimum(c, C))
+        assert np.array_equal(np.diff(off), kept)
+        # kept copies: inverse maps, ascending token inside each expert segment
+        q = np.nonzero(sr >= 0)[0]
+        assert np.array_equal(rt[sr[q]], q // K)
+        assert sorted(sr[q].tolist()) == list(range(int(off[-1])))
+        for i in range(E):
+            assert np.all(np.diff(rt[off[i]:off[i + 1]]) > 0)
+            assert np.all(np.any(idx[rt[off[i]:off[i + 1]]] == i, axis=1))
+
+
+def test_capacity_at_or_above_max_load_drops_nothing():
+    rng = np.random.default_rng(41)
+    idx = np.sort(np.stack([rng.choice(16, 4, replace=False) for _ in range(200)]), axis=1)
+    c = O.load_count(idx, 16)
+    a = O.permute(idx, 16)
+    for C in (int(c.max()), int(c.max()) + 5):
+        b = O.permute_capacity(idx, 16, C)
+        for x, y in zip(a, b[:3]):
+            assert np.array_equal(x, y)
+
+
+def test_capacity_zero_keeps_only_residual_and_shared():
+    rng = np.random.default_rng(42)
+    T, d, f, E, K = 24, 12, 10, 5, 2
+    h, e, w, ws = _small_layer(rng, T, d, f, E, 1)
+    out = O.layer_forward(h, e, None, K, "sigmoid", w, ws, 1, capacity=0)
+    ref = h.astype(np.float64) + O.swiglu(h, ws[0][0], ws[1][0], ws[2][0])
+    assert np.all(out["slot_row"] == -1) and out["offsets"][-1] == 0
+    assert np.array_equal(out["y"], ref)
+
+
+def test_capacity_dropped_copies_lose_their_gate_share():
+    # identical experts: y_t - h_t = (sum of the kept gates of t) * SwiGLU(h_t);
+    # gates are not renormalised over the kept experts
+    rng = np.random.default_rng(43)
+    T, d, f, E, K = 60, 16, 24, 4, 2
+    h, e, w, _ = _small_layer(rng, T, d, f, E, 0)
+    w = tuple(np.repeat(m[:1], E, axis=0) for m in w)
+    C = O.expert_capacity(T, K, E, 1.0) // 2            # forces drops
+    out = O.layer_forward(h, e, None, K, "sigmoid", w, capacity=C)
+    kept = (out["slot_row"].reshape(T, K) >= 0)
+    assert 0 < kept.sum() < T * K
+    gsum = (out["gates"].astype(np.float64) * kept).sum(1)
+    ref = h.astype(np.float64) + gsum[:, None] * O.swiglu(h, w[0][0], w[1][0], w[2][0])
+    assert np.allclose(out["y"], ref, rtol=0, atol=1e-12)
+
+
+def test_capacity_is_order_dependent_router_is_not():
+    # the same tokens in another order: the router's picks follow the tokens,
+    # but which copies an over-full expert drops changes
+    rng = np.random.default_rng(44)
+    T, d, E, K = 64, 16, 8, 2
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    e = (rng.standard_normal((E, d)) / 4).astype(np.float32)
+    e[0] += 2 * h.mean(0) / np.linalg.norm(h.mean(0))     # expert 0 over-subscribed
+    C = O.expert_capacity(T, K, E, 1.0)
+    r0 = O.route(h, e, None, K, "sigmoid")
+    assert r0["loads"][0] > C
+    perm = rng.permutation(T)
+    r1 = O.route(h[perm], e, None, K, "sigmoid")
+    assert np.array_equal(r1["idx"], r0["idx"][perm])        # router: equivariant
+    kept0 = O.permute_capacity(r0["idx"], E, C)[2].reshape(T, K) >= 0
+    kept1 = O.permute_capacity(r1["idx"], E, C)[2].reshape(T, K) >= 0
+    assert not np.array_equal(kept1, kept0[perm])             # capacity: not equivariant
+    assert kept1.sum() == kept0.sum()                         # same number of drops
