@@ -30,21 +30,23 @@ def log(msg):
     sys.stderr.flush()
 
 
-def algorithmic(cfg, n_touched, n_touched_shared):
+def algorithmic(cfg, n_touched, n_touched_shared, rows=None):
     """Algorithmic bytes / flops of the gate/up launch and of the whole layer.
 
     Per touched routed or shared expert: W_gate + W_up = 2 * d * f bf16 words
     (gate/up launch) and W_down = d * f words (down launch).  Per token: h read
     once (d words) and y written once (d words).  Per assignment row: the
     activation (f words) written by gate/up.  Expert flops: 6 d f per row
-    (2 d f each for gate, up and down), rows = T*K routed + T*E_s shared.
+    (2 d f each for gate, up and down), rows = T*K routed (the kept copies
+    under a capacity) + T*E_s shared.
     """
     d, f, T, K = cfg.d_model, cfg.d_ffn, cfg.T, cfg.K
+    rows = T * K if rows is None else rows
     eb = 2 if cfg.dtype == "bf16" else 4
-    gateup_bytes = n_touched * 2 * d * f * eb + T * d * eb + T * K * f * eb
-    gateup_flops = 4.0 * d * f * T * K
+    gateup_bytes = n_touched * 2 * d * f * eb + T * d * eb + rows * f * eb
+    gateup_flops = 4.0 * d * f * rows
     layer_bytes = (n_touched + n_touched_shared) * 3 * d * f * eb + 2 * T * d * eb
-    layer_flops = 6.0 * d * f * T * (K + cfg.E_s) + 2.0 * T * d * cfg.E_r
+    layer_flops = 6.0 * d * f * (rows + T * cfg.E_s) + 2.0 * T * d * cfg.E_r
     return gateup_bytes, gateup_flops, layer_bytes, layer_flops
 
 
@@ -70,7 +72,7 @@ def recorded_traffic(workload: str):
     return None
 
 
-def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256):
+def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256, capacity=None):
     """Time the oracle on a bounded sample of the same workload on host cores.
 
     Sample: routing of all T tokens; the routed experts 0..sample_experts-1 on
@@ -98,7 +100,10 @@ def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256):
 
     t0 = time.perf_counter()
     r = O.route(h, e, b_host, cfg.K, cfg.score)
-    off, rt, sr = O.permute(r["idx"], cfg.E_r)
+    if capacity is None:
+        off, rt, sr = O.permute(r["idx"], cfg.E_r)
+    else:
+        off, rt, sr, _ = O.permute_capacity(r["idx"], cfg.E_r, capacity)
     t_route = time.perf_counter() - t0
 
     t0 = time.perf_counter()
@@ -158,6 +163,8 @@ def main(argv=None):
                     choices=["dsv3_prefill", "dsv3_decode", "dsv3_skewed", "mixtral_8x7b"])
     ap.add_argument("--rotate", type=int, default=10, help="token batches cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--capacity-factor", type=float, default=None, metavar="CF",
+                    help="cap every expert at ceil(CF*T*K/E_r) rows (token dropping)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-sized buffer 3 times (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
@@ -194,7 +201,7 @@ def main(argv=None):
     shape = LayerShape(cfg.T, cfg.d_model, cfg.E_r, cfg.K, cfg.E_s, cfg.d_ffn, cfg.dtype,
                        cfg.score)
     run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
-                   lay.ws_down)
+                   lay.ws_down, capacity_factor=args.capacity_factor)
     b = lay.b.clone() if lay.b is not None else None
     b_host0 = host_array(lay.b) if lay.b is not None else None
     gamma = cfg.gamma if b is not None else None
@@ -223,7 +230,8 @@ def main(argv=None):
     tokens_per_s = cfg.T / (ms_per_step / 1000.0)
     loads = run.loads.cpu().numpy()
     n_touched = int((loads > 0).sum())
-    gu_bytes, gu_flops, layer_bytes, layer_flops = algorithmic(cfg, n_touched, cfg.E_s)
+    kept_rows = int(run.offsets[-1].item())
+    gu_bytes, gu_flops, layer_bytes, layer_flops = algorithmic(cfg, n_touched, cfg.E_s, kept_rows)
     stages = {k: round(v[1] / v[0], 5) for k, v in prof.items()}
     log("per-kernel average ms: " + json.dumps(stages))
     log(f"wall {wall * 1000:.2f} ms, events {ev_ms:.2f} ms over {args.steps} steps")
@@ -239,7 +247,8 @@ def main(argv=None):
     else:
         roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
-    traffic = recorded_traffic(cfg.name)
+    # the counter record covers the dispatch without a capacity limit
+    traffic = recorded_traffic(cfg.name) if run.capacity is None else None
     roofline["traffic"] = traffic
     roofline.update(kernel="gateup_bf16 (routed experts)", avg_ms=round(routed_ms, 4),
                     algorithmic_bytes=gu_bytes, algorithmic_flops=gu_flops,
@@ -254,7 +263,7 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, lay, b_host0)
+        cpu = cpu_baseline(cfg, lay, b_host0, capacity=run.capacity)
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -263,7 +272,11 @@ def main(argv=None):
         "data": "synthetic (seeded Gaussian tokens and weights, random-init experts)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d_model} E_r={cfg.E_r} "
                                f"K={cfg.K} E_s={cfg.E_s} d_ffn={cfg.d_ffn} {cfg.score} router, "
-                               f"bias update gamma={cfg.gamma}",
+                               f"bias update gamma={cfg.gamma}" +
+                               ("" if run.capacity is None else
+                                f", capacity factor {args.capacity_factor} (C={run.capacity} "
+                                f"rows per expert, {cfg.T * cfg.K - kept_rows} of "
+                                f"{cfg.T * cfg.K} copies dropped)"),
                    "tokens_per_step": cfg.T, "parallelism": "single GPU"},
         "roofline": roofline, "layer": layer, "stages_ms": stages, "cpu_baseline": cpu,
     }

@@ -128,6 +128,42 @@ moe_status moe_permute(int T, int d_model, int E_r, int K, const int32_t* topk_i
                        size_t workspace_bytes, void* stream);
 
 /*
+ * moe_expert_capacity -- host helper: C = ceil(CF * T * K / E_r), the number
+ * of rows one expert's buffer holds (Sparse MoE routing-math page, section 3,
+ * expert buffer capacity equation), evaluated as ceil((CF * (T*K)) / E_r) in
+ * IEEE double.  Returns -1 for T, K or E_r < 1, a negative or NaN factor, or a
+ * result beyond INT32_MAX.  No device work.
+ */
+int moe_expert_capacity(int T, int K, int E_r, double capacity_factor);
+
+/*
+ * moe_permute_capacity -- moe_permute with a per-expert capacity: expert i
+ * admits its copies in ascending token order until it holds `capacity` rows;
+ * a later copy is dropped (the token keeps its residual, its shared experts
+ * and its other routed experts; gates are not renormalised).
+ *
+ * Defined by: Sparse MoE routing-math page, section 3 (capacity C and token
+ * dropping; the layer listing keeps the first C of each expert's token list)
+ * and the Routing-and-Load-Balancing page, section 5 (admission in token
+ * order, so the result depends on the batch order by design).
+ *
+ *   capacity  rows per expert, >= 0 (see moe_expert_capacity); otherwise
+ *             MOE_ERR_INVALID_ARG
+ *   offsets   [E_r + 1] int32 out: exclusive scan of min(c_i, capacity);
+ *             offsets[E_r] = number of kept copies
+ *   slot_row  [T*K] int32 out: permuted row of copy (t, k), or -1 when the
+ *             copy was dropped (or its id is outside [0, E_r))
+ * Every other argument, the outputs' layout, ownership and error behaviour
+ * are those of moe_permute; the loads from moe_route stay the router's
+ * counts (before any drop), which is what the bias update uses.
+ */
+moe_status moe_permute_capacity(int T, int d_model, int E_r, int K, int capacity,
+                                const int32_t* topk_idx, const void* h, moe_dtype dtype,
+                                int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                                void* x_perm, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * moe_grouped_swiglu -- one grouped SwiGLU over variable-size row groups:
  * group g runs expert g on rows offsets[g] .. offsets[g+1]-1.
  *

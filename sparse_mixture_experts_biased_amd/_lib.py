@@ -16,6 +16,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SIGMOID, MOE_SOFTMAX = 0, 1
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
+            "moe_expert_capacity", "moe_permute_capacity",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "moe_bias_update", "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -51,6 +52,9 @@ def load() -> ctypes.CDLL:
         "moe_route": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _sz, _p], _i),
         "moe_permute_workspace_size": ([_i, _i], _sz),
         "moe_permute": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
+        "moe_expert_capacity": ([_i, _i, _i, ctypes.c_double], _i),
+        "moe_permute_capacity": ([_i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p],
+                                 _i),
         "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
         "moe_grouped_swiglu": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
                                 _sz, _p], _i),
@@ -126,6 +130,18 @@ def moe_permute(T, d_model, E_r, K, topk_idx, h, dtype, offsets, row_token, slot
     _check(load().moe_permute(T, d_model, E_r, K, _ptr(topk_idx), _ptr(h), dtype, _ptr(offsets),
                               _ptr(row_token), _ptr(slot_row), _ptr(x_perm), _ptr(workspace),
                               workspace_bytes, _stream(stream)))
+
+
+def moe_expert_capacity(T, K, E_r, capacity_factor) -> int:
+    return int(load().moe_expert_capacity(T, K, E_r, float(capacity_factor)))
+
+
+def moe_permute_capacity(T, d_model, E_r, K, capacity, topk_idx, h, dtype, offsets, row_token,
+                         slot_row, x_perm, workspace, workspace_bytes, stream=None):
+    _check(load().moe_permute_capacity(T, d_model, E_r, K, capacity, _ptr(topk_idx), _ptr(h),
+                                       dtype, _ptr(offsets), _ptr(row_token), _ptr(slot_row),
+                                       _ptr(x_perm), _ptr(workspace), workspace_bytes,
+                                       _stream(stream)))
 
 
 def moe_grouped_swiglu_workspace_size(n_groups, d_model, d_ffn, rows, dtype) -> int:

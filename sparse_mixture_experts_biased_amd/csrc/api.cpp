@@ -1,6 +1,7 @@
 // C ABI of the MoE layer library: host-side argument validation, then the
 // asynchronous kernel launches.  Nothing here allocates device memory,
 // synchronises with the device or copies data back to the host.
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -87,34 +88,65 @@ size_t moe_permute_workspace_size(int T, int E_r) {
   return moe::permute_workspace_bytes(T, E_r);
 }
 
+namespace {
+
+moe_status permute_checked(const char* fn, int T, int d_model, int E_r, int K, int cap,
+                           const int32_t* topk_idx, const void* h, moe_dtype dtype,
+                           int32_t* offsets, int32_t* row_token, int32_t* slot_row, void* x_perm,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 1 || E_r < 1 || K < 1 || d_model < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T=%d d_model=%d E_r=%d K=%d must be >= 1", fn, T,
+                d_model, E_r, K);
+  if (K > E_r || K > MOE_MAX_TOPK) return fail(MOE_ERR_INVALID_ARG, "%s: K=%d out of range", fn, K);
+  if (E_r > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E_r=%d > %d", fn, E_r, MOE_MAX_EXPERTS);
+  if (static_cast<long long>(T) * K > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T*K overflows int32", fn);
+  if (!topk_idx || !offsets || !row_token || !slot_row || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (workspace_bytes < moe::permute_workspace_bytes(T, E_r))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes,
+                moe::permute_workspace_bytes(T, E_r));
+  if (x_perm) {
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "%s: x_perm needs h", fn);
+    if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: bad dtype", fn);
+    if (d_model % 8 != 0)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: d_model=%d not a multiple of 8", fn, d_model);
+  }
+  const int eb = dtype == MOE_BF16 ? 2 : 4;
+  return hip_status(moe::launch_permute(T, d_model, E_r, K, cap, topk_idx, h, eb, offsets,
+                                        row_token, slot_row, x_perm, workspace,
+                                        as_stream(stream)),
+                    fn);
+}
+
+}  // namespace
+
 moe_status moe_permute(int T, int d_model, int E_r, int K, const int32_t* topk_idx,
                        const void* h, moe_dtype dtype, int32_t* offsets, int32_t* row_token,
                        int32_t* slot_row, void* x_perm, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (T < 1 || E_r < 1 || K < 1 || d_model < 1)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: T=%d d_model=%d E_r=%d K=%d must be >= 1", T,
-                d_model, E_r, K);
-  if (K > E_r || K > MOE_MAX_TOPK)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: K=%d out of range", K);
-  if (E_r > MOE_MAX_EXPERTS)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_permute: E_r=%d > %d", E_r, MOE_MAX_EXPERTS);
-  if (static_cast<long long>(T) * K > INT32_MAX)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: T*K overflows int32");
-  if (!topk_idx || !offsets || !row_token || !slot_row || !workspace)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
-  if (workspace_bytes < moe::permute_workspace_bytes(T, E_r))
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: workspace %zu < %zu bytes", workspace_bytes,
-                moe::permute_workspace_bytes(T, E_r));
-  if (x_perm) {
-    if (!h) return fail(MOE_ERR_INVALID_ARG, "moe_permute: x_perm needs h");
-    if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_permute: bad dtype");
-    if (d_model % 8 != 0)
-      return fail(MOE_ERR_UNSUPPORTED, "moe_permute: d_model=%d not a multiple of 8", d_model);
-  }
-  const int eb = dtype == MOE_BF16 ? 2 : 4;
-  return hip_status(moe::launch_permute(T, d_model, E_r, K, topk_idx, h, eb, offsets, row_token,
-                                        slot_row, x_perm, workspace, as_stream(stream)),
-                    "moe_permute");
+  return permute_checked("moe_permute", T, d_model, E_r, K, -1, topk_idx, h, dtype, offsets,
+                         row_token, slot_row, x_perm, workspace, workspace_bytes, stream);
+}
+
+int moe_expert_capacity(int T, int K, int E_r, double capacity_factor) {
+  if (T < 1 || K < 1 || E_r < 1 || !(capacity_factor >= 0.0)) return -1;
+  const double c = std::ceil(capacity_factor * static_cast<double>(static_cast<long long>(T) * K) /
+                             static_cast<double>(E_r));
+  if (c > static_cast<double>(INT32_MAX)) return -1;
+  return static_cast<int>(c);
+}
+
+moe_status moe_permute_capacity(int T, int d_model, int E_r, int K, int capacity,
+                                const int32_t* topk_idx, const void* h, moe_dtype dtype,
+                                int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                                void* x_perm, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (capacity < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute_capacity: capacity=%d must be >= 0", capacity);
+  return permute_checked("moe_permute_capacity", T, d_model, E_r, K, capacity, topk_idx, h, dtype,
+                         offsets, row_token, slot_row, x_perm, workspace, workspace_bytes, stream);
 }
 
 size_t moe_grouped_swiglu_workspace_size(int n_groups, int d_model, int d_ffn, int rows,

@@ -45,8 +45,9 @@ hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h
 // dispatch
 constexpr int kPermChunk = 256;  // tokens per histogram / rank chunk
 size_t permute_workspace_bytes(int T, int E);
-hipError_t launch_permute(int T, int d, int E, int K, const int32_t* idx, const void* h,
-                          int elem_bytes, int32_t* offsets, int32_t* row_token,
+// cap < 0: every copy is kept; cap >= 0: at most cap rows per expert.
+hipError_t launch_permute(int T, int d, int E, int K, int cap, const int32_t* idx,
+                          const void* h, int elem_bytes, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, void* x_perm, void* ws, hipStream_t s);
 
 // grouped SwiGLU

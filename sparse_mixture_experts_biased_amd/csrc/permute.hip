@@ -13,6 +13,11 @@
 //      experts -> offsets, and per-chunk segment bases
 //   3. per chunk, an LDS bitmap bits[e][token in chunk]; the rank of token t
 //      inside expert e's segment is the popcount of the bits below t.
+//
+// With a capacity C (routing-math page, section 3: C = ceil(CF*T*K/E_r)
+// rows per expert; admission in token order per the routing-and-load-
+// balancing page, section 5) the scan sums min(c_e, C) and a copy whose rank
+// inside its expert is C or more is dropped (slot -1, no row).
 #include "common.h"
 
 namespace moe {
@@ -40,7 +45,8 @@ __global__ __launch_bounds__(kChunk) void hist_kernel(int T, int E, int K,
 }
 
 // One workgroup of 1024 threads (E <= 1024).
-__global__ __launch_bounds__(1024) void scan_kernel(int E, int n_chunks, int TK,
+// cap < 0: no capacity limit.
+__global__ __launch_bounds__(1024) void scan_kernel(int E, int n_chunks, int TK, int cap,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ row_token) {
@@ -50,6 +56,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int E, int n_chunks, int TK,
   int tot = 0;
   if (e < E)
     for (int c = 0; c < n_chunks; ++c) tot += counts[static_cast<size_t>(c) * E + e];
+  if (cap >= 0) tot = min(tot, cap);  // kept rows of expert e
   // inclusive Hillis-Steele scan over experts
   part[e] = (e < E) ? tot : 0;
   __syncthreads();
@@ -78,8 +85,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(int E, int n_chunks, int TK,
   for (int r = total_s + e; r < TK; r += 1024) row_token[r] = -1;
 }
 
-__global__ __launch_bounds__(kChunk) void assign_kernel(int T, int E, int K,
+__global__ __launch_bounds__(kChunk) void assign_kernel(int T, int E, int K, int cap,
                                                         const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ offsets,
                                                         const int32_t* __restrict__ base,
                                                         int32_t* __restrict__ row_token,
                                                         int32_t* __restrict__ slot_row) {
@@ -109,6 +117,10 @@ __global__ __launch_bounds__(kChunk) void assign_kernel(int T, int E, int K,
     int rank = __popc(row[w] & (bit - 1u));
     for (int ww = 0; ww < w; ++ww) rank += __popc(row[ww]);
     int slot = base[static_cast<size_t>(blockIdx.x) * E + ex] + rank;
+    if (cap >= 0 && slot - offsets[ex] >= cap) {  // expert full: dropped
+      slot_row[q] = -1;
+      continue;
+    }
     slot_row[q] = slot;
     row_token[slot] = t;
   }
@@ -142,8 +154,8 @@ size_t permute_workspace_bytes(int T, int E) {
   return align_up(n_chunks * E * sizeof(int32_t), 256);
 }
 
-hipError_t launch_permute(int T, int d, int E, int K, const int32_t* idx, const void* h,
-                          int elem_bytes, int32_t* offsets, int32_t* row_token,
+hipError_t launch_permute(int T, int d, int E, int K, int cap, const int32_t* idx,
+                          const void* h, int elem_bytes, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, void* x_perm, void* ws, hipStream_t s) {
   const int n_chunks = (T + kChunk - 1) / kChunk;
   const int TK = T * K;
@@ -155,14 +167,14 @@ hipError_t launch_permute(int T, int d, int E, int K, const int32_t* idx, const 
   }
   {
     ProfScope prof_(s, "perm_scan");
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, E, n_chunks, TK, counts, offsets,
-                       row_token);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, E, n_chunks, TK, cap, counts,
+                       offsets, row_token);
   }
   {
     ProfScope prof_(s, "perm_assign");
     hipLaunchKernelGGL(assign_kernel, dim3(n_chunks), dim3(kChunk),
-                       static_cast<size_t>(E) * kWords * sizeof(uint32_t), s, T, E, K, idx,
-                       counts, row_token, slot_row);
+                       static_cast<size_t>(E) * kWords * sizeof(uint32_t), s, T, E, K, cap, idx,
+                       offsets, counts, row_token, slot_row);
   }
   if (x_perm != nullptr) {
     const int row_vecs = d * elem_bytes / 16;

@@ -3,7 +3,7 @@
 MoELayer owns the intermediate device buffers (allocated once, with torch, at
 construction) and calls the five entry points in order on one stream:
 
-    moe_route -> moe_permute -> moe_grouped_swiglu (routed experts)
+    moe_route -> moe_permute (or moe_permute_capacity) -> moe_grouped_swiglu (routed experts)
     -> moe_grouped_swiglu (shared experts) -> moe_combine -> moe_bias_update
 
 Layer output (Sparse MoE routing-math page, section 0):
@@ -33,8 +33,14 @@ class LayerShape:
 
 class MoELayer:
     def __init__(self, shape: LayerShape, e, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
-                 ws_down=None, device="cuda"):
+                 ws_down=None, device="cuda", capacity_factor: Optional[float] = None):
+        """capacity_factor: None dispatches every copy; a factor CF caps each
+        expert at C = ceil(CF*T*K/E_r) rows, admitted in token order."""
         s = self.shape = shape
+        self.capacity = (None if capacity_factor is None else
+                         L.moe_expert_capacity(s.T, s.K, s.E_r, capacity_factor))
+        if self.capacity is not None and self.capacity < 0:
+            raise ValueError(f"bad capacity factor {capacity_factor}")
         self.profile_tags = False   # label routed / shared launches in the kernel timing
         self.dt = L.MOE_BF16 if s.dtype == "bf16" else L.MOE_F32
         self.tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
@@ -78,9 +84,14 @@ class MoELayer:
 
     def permute(self, h=None, x_perm=None, stream=None):
         s = self.shape
-        L.moe_permute(s.T, s.d_model, s.E_r, s.K, self.topk_idx, h, self.dt, self.offsets,
-                      self.row_token, self.slot_row, x_perm, self.perm_ws, self.perm_ws_bytes,
-                      stream)
+        if self.capacity is None:
+            L.moe_permute(s.T, s.d_model, s.E_r, s.K, self.topk_idx, h, self.dt, self.offsets,
+                          self.row_token, self.slot_row, x_perm, self.perm_ws,
+                          self.perm_ws_bytes, stream)
+        else:
+            L.moe_permute_capacity(s.T, s.d_model, s.E_r, s.K, self.capacity, self.topk_idx, h,
+                                   self.dt, self.offsets, self.row_token, self.slot_row, x_perm,
+                                   self.perm_ws, self.perm_ws_bytes, stream)
 
     def routed_experts(self, h, stream=None):
         s = self.shape

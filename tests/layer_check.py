@@ -15,11 +15,11 @@ from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
 from synthetic import host_array
 
 
-def runner_for(lay, T=None):
+def runner_for(lay, T=None, capacity_factor=None):
     c = lay.cfg
     shape = LayerShape(T or c.T, c.d_model, c.E_r, c.K, c.E_s, c.d_ffn, c.dtype, c.score)
     return MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
-                    lay.ws_down)
+                    lay.ws_down, capacity_factor=capacity_factor)
 
 
 def _expert_source(w_gate, w_up, w_down):
@@ -44,7 +44,9 @@ def check_permutation_valid(idx, offsets, row_token, slot_row, E):
 
 def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=0,
                 check_all_tokens=False):
-    """Run one layer forward on the GPU and compare with the oracle.
+    """Run one layer forward on the GPU and compare with the oracle.  With a
+    capacity (run.capacity), the oracle's capacity dispatch of the whole batch
+    decides which copies are kept.
 
     Returns a dict with near-tie / flip counts and the observed errors."""
     c = lay.cfg
@@ -60,13 +62,24 @@ def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=
     n_near, n_flip, r = check_route(h, lay.e, b_in, K, c.score, run.topk_idx, run.gates,
                                     run.loads, E)
     flipped = np.nonzero(~np.all(idx == r["idx"], axis=1))[0]
-    if n_flip == 0:
+    cap = run.capacity
+    kept = np.ones((T, K), dtype=bool)
+    if cap is not None:
+        # which copies survive depends on every earlier token: decided on the
+        # GPU's own picks (teacher forcing; equal to the oracle's without flips)
+        o_off, o_rt, o_sr, o_kept = O.permute_capacity(idx, E, cap)
+        assert np.array_equal(off, o_off)
+        assert np.array_equal(rt[:int(o_off[-1])], o_rt) and np.array_equal(sr, o_sr)
+        assert np.all(rt[int(o_off[-1]):] == -1)
+        kept = (o_sr >= 0).reshape(T, K)
+        say(f"capacity {cap}: {int((~kept).sum())} of {T * K} copies dropped")
+    elif n_flip == 0:
         o_off, o_rt, o_sr = O.permute(r["idx"], E)
         assert np.array_equal(off, o_off)
         assert np.array_equal(rt, o_rt) and np.array_equal(sr, o_sr)
     else:
         check_permutation_valid(idx, off, rt, sr, E)
-    res = dict(near_ties=n_near, flipped=n_flip, b_new=b_dev)
+    res = dict(near_ties=n_near, flipped=n_flip, b_new=b_dev, dropped=int((~kept).sum()))
 
     # bias update after counting (bit-exact when the loads agree)
     if gamma is not None and b_in is not None:
@@ -93,6 +106,7 @@ def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=
         rng.choice(cand, n_tok_sample, replace=False))
     idx_s, g_s = r["idx"][toks], r["gates"][toks]
     off_s, rt_s, sr_s = O.permute(idx_s, E)
+    sr_s = np.where(kept[toks].reshape(-1), sr_s, -1).astype(np.int32)   # dropped copies
     y_perm_s = O.grouped_swiglu(h_host[toks], off_s, rt_s, experts)
     y_sh_s = O.shared_experts(h_host[toks], shared, c.E_s) if c.E_s else None
     y_ref = O.combine(h_host[toks], y_sh_s, y_perm_s, sr_s, g_s)
@@ -109,7 +123,7 @@ def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=
     res["y_minus_h_rel_err"] = err_delta
 
     # routed expert outputs (y_perm) of a sample of non-empty experts, all their rows
-    if n_flip == 0:
+    if n_flip == 0 or cap is not None:
         nonempty = np.nonzero(np.diff(off) > 0)[0]
         ex = nonempty if len(nonempty) <= n_exp_sample else np.sort(
             rng.choice(nonempty, n_exp_sample, replace=False))

@@ -75,6 +75,28 @@ def test_permute_rejects_bad_arguments():
     assert lib.moe_permute(100, 64, 8, 0, P, None, 1, P, P, P, None, P, need, None) == L.MOE_ERR_INVALID_ARG
 
 
+def test_expert_capacity_and_capacity_permute_arguments():
+    # C = ceil(CF*T*K/E_r) on the host, no device work
+    assert L.moe_expert_capacity(4096, 8, 256, 1.0) == 128
+    assert L.moe_expert_capacity(4096, 8, 256, 1.25) == 160
+    assert L.moe_expert_capacity(10, 1, 4, 1.0) == 3
+    assert L.moe_expert_capacity(10, 1, 4, 0.0) == 0
+    assert L.moe_expert_capacity(10, 1, 4, -0.5) == -1
+    assert L.moe_expert_capacity(10, 1, 4, float("nan")) == -1
+    assert L.moe_expert_capacity(0, 1, 4, 1.0) == -1
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    need = L.moe_permute_workspace_size(100, 8)
+    rc, msg = _st(lib.moe_permute_capacity(100, 64, 8, 2, -1, P, None, 1, P, P, P, None, P, need,
+                                           None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "capacity" in msg
+    rc, msg = _st(lib.moe_permute_capacity(100, 64, 8, 2, 5, P, None, 1, P, P, P, None, P,
+                                           need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    assert lib.moe_permute_capacity(100, 64, 8, 9, 5, P, None, 1, P, P, P, None, P, need,
+                                    None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_grouped_swiglu_rejects_bad_arguments():
     lib = L.load()
     P = ctypes.c_void_p(16)

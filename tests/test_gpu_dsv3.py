@@ -37,6 +37,19 @@ def test_dsv3_prefill_full_size(dsv3):
     say(str(res))
 
 
+@pytest.mark.parametrize("cf", [1.0, 1.25])
+def test_dsv3_prefill_capacity_factor(dsv3, cf):
+    """Capacity-bounded dispatch at full size: C = ceil(CF*T*K/E_r) = 128 / 160
+    rows per expert (the loads reach about 167, so copies are dropped)."""
+    cfg = dsv3.cfg
+    run = runner_for(dsv3, capacity_factor=cf)
+    assert run.capacity == O.expert_capacity(cfg.T, cfg.K, cfg.E_r, cf)
+    res = check_layer(dsv3, dsv3.h, dsv3.b, cfg.gamma, run, n_tok_sample=12, n_exp_sample=4,
+                      seed=5)
+    assert res["dropped"] > 0
+    say(str(res))
+
+
 def test_dsv3_decode_full_size(dsv3):
     cfg = CONFIGS["dsv3_decode"]
     h = make_tokens(cfg, device="cuda")

@@ -152,6 +152,67 @@ def test_permute_parity(T, E, K):
     assert np.array_equal(sr.cpu().numpy(), o_sr)
 
 
+def _permute_capacity_gpu(idx, E, C, h=None):
+    T, K = idx.shape
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    row_token = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    slot_row = torch.empty(T * K, dtype=torch.int32, device=DEV)
+    wsb = L.moe_permute_workspace_size(T, E)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    x_perm = None if h is None else torch.empty((T * K, h.shape[1]), dtype=h.dtype, device=DEV)
+    L.moe_permute_capacity(T, h.shape[1] if h is not None else 8, E, K, C, idx, h, L.MOE_BF16,
+                           offsets, row_token, slot_row, x_perm, ws, wsb)
+    torch.cuda.synchronize()
+    return offsets, row_token, slot_row, x_perm
+
+
+@pytest.mark.parametrize("T,E,K,cf", [(1, 4, 2, 1.0), (300, 8, 2, 1.0), (1000, 64, 4, 0.5),
+                                      (4096, 256, 8, 1.0), (4096, 256, 8, 1.25),
+                                      (16384, 256, 8, 1.0), (513, 1024, 3, 2.0)])
+def test_permute_capacity_parity(T, E, K, cf):
+    C = L.moe_expert_capacity(T, K, E, cf)
+    assert C == O.expert_capacity(T, K, E, cf)
+    say(f"moe_permute_capacity T={T} E={E} K={K} C={C}")
+    rng = np.random.default_rng(T + 11 * E)
+    # skewed picks so that some experts overflow
+    v = rng.random((T, E)).astype(np.float32) * np.linspace(1.0, 2.0, E, dtype=np.float32)
+    idx = O.biased_topk(v, None, K)
+    off, rt, sr, _ = _permute_capacity_gpu(torch.from_numpy(idx).to(DEV), E, C)
+    o_off, o_rt, o_sr, kept = O.permute_capacity(idx, E, C)
+    n = int(o_off[-1])
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    assert np.array_equal(rt.cpu().numpy()[:n], o_rt)
+    assert np.all(rt.cpu().numpy()[n:] == -1)
+    assert np.array_equal(sr.cpu().numpy(), o_sr)
+
+
+def test_permute_capacity_edges_and_order_dependence():
+    T, E, K, d = 500, 8, 2, 64
+    rng = np.random.default_rng(12)
+    v = rng.random((T, E)).astype(np.float32)
+    v[:, 2] += 0.5                                   # expert 2 over-subscribed
+    idx = O.biased_topk(v, None, K)
+    h = _tokens(T, d, torch.bfloat16, 13)
+    # C = 0: everything dropped; C >= max load: identical to moe_permute
+    off, rt, sr, _ = _permute_capacity_gpu(torch.from_numpy(idx).to(DEV), E, 0)
+    assert int(off[-1]) == 0 and torch.all(sr == -1) and torch.all(rt == -1)
+    c = O.load_count(idx, E)
+    a = _permute_gpu(torch.from_numpy(idx).to(DEV), E, h)
+    b = _permute_capacity_gpu(torch.from_numpy(idx).to(DEV), E, int(c.max()), h)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # the same copies in another token order: the dropped set changes
+    C = O.expert_capacity(T, K, E, 1.0)
+    assert c[2] > C
+    perm = rng.permutation(T)
+    _, _, sr0, _ = _permute_capacity_gpu(torch.from_numpy(idx).to(DEV), E, C)
+    _, _, sr1, _ = _permute_capacity_gpu(torch.from_numpy(idx[perm]).to(DEV), E, C)
+    k0 = (sr0.cpu().numpy() >= 0).reshape(T, K)
+    k1 = (sr1.cpu().numpy() >= 0).reshape(T, K)
+    assert not np.array_equal(k1, k0[perm]) and k1.sum() == k0.sum()
+    assert np.array_equal(sr1.cpu().numpy(), O.permute_capacity(idx[perm], E, C)[2])
+
+
 def test_permute_total_collapse_and_gather():
     T, E, K, d = 700, 16, 2, 64
     idx = np.tile(np.array([[3, 9]], dtype=np.int32), (T, 1))
