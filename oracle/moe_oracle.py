@@ -23,6 +23,11 @@ Plain NumPy, written from the method's definitions, one function per step:
     expert is dropped (the token keeps only its residual and other experts).
   * Routing-and-load-balancing page (yiqiao-yin.github.io), section 5: tokens
     are admitted to an expert in the order they appear.
+  * Router diagnostics (forward values): routing-math page, section 1 (Switch
+    auxiliary loss f_i P_i with f_i = E_r/(K T) * #{t : i in I_t} and
+    P_i = mean_t p_{t,i}; router z-loss = mean_t logsumexp(z_t)^2) and the
+    designs page (raminaeye.github.io), per-layer log: MaxVio, dropped-copy
+    rate and the entropy of the load share (share clamped at 1e-9 in the log).
 
 Precision.  The pages fix the router at fp32: z is the fp64 dot product of
 the exact inputs rounded once to fp32, s = sigma(z) is evaluated in fp64 and
@@ -296,6 +301,32 @@ def max_vio(loads: np.ndarray, T: int, K: int) -> float:
 def load_stats(loads: np.ndarray, T: int, K: int):
     return dict(max_load=int(loads.max()), min_load=int(loads.min()),
                 max_vio=max_vio(loads, T, K))
+
+
+# ---------------------------------------------------------------- diagnostics
+
+def router_diagnostics(z: np.ndarray, idx: np.ndarray, E_r: int,
+                       kept: Optional[np.ndarray] = None) -> dict:
+    """Forward values of the router's balance diagnostics, fp64.
+
+    z: [T, E_r] logits; idx: [T, K] picked experts; kept: [T, K] bool mask of
+    the copies a capacity dispatch kept (None: all kept).
+    """
+    z64 = np.asarray(z, dtype=np.float64)
+    T, K = idx.shape
+    m = z64.max(axis=1, keepdims=True)
+    ez = np.exp(z64 - m)
+    lse = m[:, 0] + np.log(ez.sum(axis=1))              # logsumexp per token
+    p = ez / ez.sum(axis=1, keepdims=True)               # softmax probabilities
+    P = p.mean(axis=0)                                   # P_i
+    c = load_count(idx, E_r).astype(np.float64)
+    f = c * E_r / (K * T)                                # f_i
+    share = c / c.sum()
+    entropy = float(-(share * np.log(np.maximum(share, 1e-9))).sum())
+    cbar = K * T / E_r
+    return dict(P=P, f=f, switch_fP=float((f * P).sum()), z_loss=float((lse ** 2).mean()),
+                load_entropy=entropy, max_vio=float((c.max() - cbar) / cbar),
+                dropped=0.0 if kept is None else float(1.0 - kept.mean()))
 
 
 # ---------------------------------------------------------------- layer

@@ -521,3 +521,50 @@ def test_capacity_is_order_dependent_router_is_not():
     kept1 = O.permute_capacity(r1["idx"], E, C)[2].reshape(T, K) >= 0
     assert not np.array_equal(kept1, kept0[perm])             # capacity: not equivariant
     assert kept1.sum() == kept0.sum()                         # same number of drops
+
+
+# ------------------------------------------------------------------ router diagnostics
+# Routing-math page, section 1: f_i = E_r/(K T) #{t : i in I_t}, P_i = mean_t p_ti,
+# sum_i f_i P_i is minimised at 1 by uniform load; z-loss = mean_t lse(z_t)^2.
+# Designs page: MaxVio, dropped rate, entropy of the load share.
+
+def test_diagnostics_uniform_load_and_zero_logits():
+    E, K = 8, 2
+    T = 4 * E
+    idx = np.array([[(2 * t) % E, (2 * t + 1) % E] for t in range(T)])   # every expert 8 times
+    idx.sort(axis=1)
+    d = O.router_diagnostics(np.zeros((T, E), np.float32), idx, E)
+    assert np.allclose(d["f"], 1.0) and np.allclose(d["P"], 1.0 / E)
+    assert abs(d["switch_fP"] - 1.0) < 1e-15          # the page's minimum
+    assert abs(d["z_loss"] - math.log(E) ** 2) < 1e-12
+    assert abs(d["load_entropy"] - math.log(E)) < 1e-12
+    assert d["max_vio"] == 0.0 and d["dropped"] == 0.0
+
+
+def test_diagnostics_collapse_and_library_logsumexp():
+    rng = np.random.default_rng(50)
+    T, E, K = 100, 16, 4
+    z = (rng.standard_normal((T, E)) * 3).astype(np.float32)
+    idx = np.tile(np.array([[2, 5, 7, 11]]), (T, 1))      # every token picks the same 4
+    d = O.router_diagnostics(z, idx, E)
+    assert abs(d["load_entropy"] - math.log(K)) < 1e-12
+    assert abs(d["max_vio"] - (E / K - 1)) < 1e-12
+    lse = scipy.special.logsumexp(z.astype(np.float64), axis=1)
+    assert abs(d["z_loss"] - float(np.mean(lse ** 2))) < 1e-9 * d["z_loss"]
+    P = scipy.special.softmax(z.astype(np.float64), axis=1).mean(0)
+    assert np.allclose(d["P"], P, rtol=1e-12, atol=0)
+    assert abs(d["P"].sum() - 1.0) < 1e-12 and abs(d["f"].sum() - E) < 1e-12
+    # the Switch product on a collapse: f = E/K on the picked 4, so sum f P = (E/K) P_picked
+    assert abs(d["switch_fP"] - (E / K) * P[[2, 5, 7, 11]].sum()) < 1e-12
+
+
+def test_diagnostics_dropped_rate_from_capacity():
+    rng = np.random.default_rng(51)
+    T, E, K = 200, 8, 2
+    v = rng.random((T, E)).astype(np.float32)
+    v[:, 0] += 1.0
+    idx = O.biased_topk(v, None, K)
+    C = O.expert_capacity(T, K, E, 1.0)
+    _, _, sr, kept = O.permute_capacity(idx, E, C)
+    d = O.router_diagnostics(np.log(v), idx, E, kept=(sr >= 0).reshape(T, K))
+    assert abs(d["dropped"] - (sr < 0).sum() / (T * K)) < 1e-15 and d["dropped"] > 0
