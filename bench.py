@@ -165,6 +165,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--capacity-factor", type=float, default=None, metavar="CF",
                     help="cap every expert at ceil(CF*T*K/E_r) rows (token dropping)")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="route with the router statistics and compute the balance diagnostics "
+                         "(Switch f.P, z-loss, load entropy, MaxVio, dropped rate) every step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-sized buffer 3 times (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
@@ -201,7 +204,8 @@ def main(argv=None):
     shape = LayerShape(cfg.T, cfg.d_model, cfg.E_r, cfg.K, cfg.E_s, cfg.d_ffn, cfg.dtype,
                        cfg.score)
     run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
-                   lay.ws_down, capacity_factor=args.capacity_factor)
+                   lay.ws_down, capacity_factor=args.capacity_factor,
+                   diagnostics=args.diagnostics)
     b = lay.b.clone() if lay.b is not None else None
     b_host0 = host_array(lay.b) if lay.b is not None else None
     gamma = cfg.gamma if b is not None else None
@@ -280,6 +284,8 @@ def main(argv=None):
                    "tokens_per_step": cfg.T, "parallelism": "single GPU"},
         "roofline": roofline, "layer": layer, "stages_ms": stages, "cpu_baseline": cpu,
     }
+    if args.diagnostics:
+        out["router_diag"] = {k: round(v, 6) for k, v in run.diag_host().items()}
     print(json.dumps(out), flush=True)
     return 0
 

@@ -64,6 +64,16 @@ typedef struct {
   int32_t reserved;
 } moe_bias_stats;
 
+/* Router balance diagnostics (forward values), filled by moe_router_diag. */
+typedef struct {
+  float switch_fP;     /* sum_i f_i P_i (times alpha_aux: the Switch auxiliary loss) */
+  float z_loss;        /* (1/T) sum_t logsumexp(z_t)^2 (times c_z: the router z-loss) */
+  float load_entropy;  /* -sum_i share_i log(max(share_i, 1e-9)), share = c / sum c  */
+  float max_vio;       /* (max_i c_i - cbar) / cbar, cbar = K T / E_r              */
+  float dropped;       /* 1 - kept copies / (T K); 0 when no dispatch is given     */
+  float reserved[3];
+} moe_router_diag_values;
+
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -98,6 +108,53 @@ moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn,
                      const void* h, moe_dtype h_dtype, const float* e, const float* b,
                      int32_t* topk_idx, float* gates, int32_t* loads, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_stats -- moe_route plus the per-batch router statistics the
+ * diagnostics need, computed by the same kernels from the same fp32 logits.
+ *
+ * Defined by: Sparse MoE routing-math page, section 1 (Switch auxiliary loss:
+ * P_i = (1/T) sum_t p_{t,i} with p = softmax(z); router z-loss: the mean of
+ * logsumexp(z_t)^2).  For a sigmoid router p is still the softmax of z (the
+ * Switch definition); the selection itself is unchanged.
+ *
+ *   p_mean    [E_r] fp32 out: P_i
+ *   zsq_mean  [1] fp32 out: (1/T) sum_t logsumexp(z_t)^2
+ *   workspace at least moe_route_stats_workspace_size() bytes (the routing
+ *             scratch plus T*E_r + T floats of per-token values)
+ * Every other argument is that of moe_route, with the same outputs and
+ * errors; NULL p_mean or zsq_mean -> MOE_ERR_INVALID_ARG.  The token sums
+ * run in a fixed order (deterministic).
+ */
+size_t moe_route_stats_workspace_size(int T, int d_model, int E_r, moe_dtype h_dtype);
+moe_status moe_route_stats(int T, int d_model, int E_r, int K, moe_score_fn fn,
+                           const void* h, moe_dtype h_dtype, const float* e, const float* b,
+                           int32_t* topk_idx, float* gates, int32_t* loads, float* p_mean,
+                           float* zsq_mean, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * moe_router_diag -- the router's balance diagnostics for one batch.
+ *
+ * Defined by: Sparse MoE routing-math page, section 1 (f_i = E_r/(K T) c_i,
+ * the Switch product sum_i f_i P_i, minimised at 1 by uniform load; router
+ * z-loss) and section 4 item 1 (MaxVio); the Mixture of Experts designs page,
+ * router log (entropy of the load share, share clamped at 1e-9 in the log;
+ * dropped-copy rate).
+ *
+ *   loads     [E_r] int32: c_i from moe_route / moe_route_stats
+ *   p_mean, zsq_mean      from moe_route_stats
+ *   offsets   [E_r + 1] int32 from moe_permute / moe_permute_capacity, or
+ *             NULL (dropped = 0)
+ *   f         [E_r] fp32 out f_i, or NULL
+ *   diag      device moe_router_diag_values out
+ * Errors: T, E_r, K < 1, K > E_r, E_r > MOE_MAX_EXPERTS or a NULL required
+ * pointer -> MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED before any launch.
+ * Deterministic (fixed-order reductions in one workgroup).
+ */
+moe_status moe_router_diag(int T, int E_r, int K, const int32_t* loads, const float* p_mean,
+                           const float* zsq_mean, const int32_t* offsets, float* f,
+                           moe_router_diag_values* diag, void* stream);
 
 /*
  * moe_permute -- dispatch: expert histogram, exclusive scan, stable

@@ -16,7 +16,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SIGMOID, MOE_SOFTMAX = 0, 1
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
-            "moe_expert_capacity", "moe_permute_capacity",
+            "moe_expert_capacity", "moe_permute_capacity", "moe_route_stats_workspace_size",
+            "moe_route_stats", "moe_router_diag",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "moe_bias_update", "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -26,6 +27,12 @@ class MoeError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"[status {status}] {msg}")
         self.status = status
+
+
+class MoeRouterDiag(ctypes.Structure):
+    _fields_ = [("switch_fP", ctypes.c_float), ("z_loss", ctypes.c_float),
+                ("load_entropy", ctypes.c_float), ("max_vio", ctypes.c_float),
+                ("dropped", ctypes.c_float), ("reserved", ctypes.c_float * 3)]
 
 
 class MoeBiasStats(ctypes.Structure):
@@ -53,6 +60,10 @@ def load() -> ctypes.CDLL:
         "moe_permute_workspace_size": ([_i, _i], _sz),
         "moe_permute": ([_i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p], _i),
         "moe_expert_capacity": ([_i, _i, _i, ctypes.c_double], _i),
+        "moe_route_stats_workspace_size": ([_i, _i, _i, _i], _sz),
+        "moe_route_stats": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+                            _i),
+        "moe_router_diag": ([_i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
         "moe_permute_capacity": ([_i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p],
                                  _i),
         "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
@@ -119,6 +130,27 @@ def moe_route(T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx, gates, loads, 
     _check(load().moe_route(T, d_model, E_r, K, fn, _ptr(h), h_dtype, _ptr(e), _ptr(b),
                             _ptr(topk_idx), _ptr(gates), _ptr(loads), _ptr(workspace),
                             workspace_bytes, _stream(stream)))
+
+
+def moe_route_stats_workspace_size(T, d_model, E_r, h_dtype) -> int:
+    return int(load().moe_route_stats_workspace_size(T, d_model, E_r, h_dtype))
+
+
+def moe_route_stats(T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx, gates, loads, p_mean,
+                    zsq_mean, workspace, workspace_bytes, stream=None):
+    _check(load().moe_route_stats(T, d_model, E_r, K, fn, _ptr(h), h_dtype, _ptr(e), _ptr(b),
+                                  _ptr(topk_idx), _ptr(gates), _ptr(loads), _ptr(p_mean),
+                                  _ptr(zsq_mean), _ptr(workspace), workspace_bytes,
+                                  _stream(stream)))
+
+
+def moe_router_diag(T, E_r, K, loads, p_mean, zsq_mean, offsets, f, diag, stream=None):
+    """diag: a device tensor of at least 8 float32 (the moe_router_diag_values layout)."""
+    _check(load().moe_router_diag(T, E_r, K, _ptr(loads), _ptr(p_mean), _ptr(zsq_mean),
+                                  _ptr(offsets), _ptr(f), _ptr(diag), _stream(stream)))
+
+
+DIAG_FIELDS = ("switch_fP", "z_loss", "load_entropy", "max_vio", "dropped")
 
 
 def moe_permute_workspace_size(T, E_r) -> int:

@@ -52,35 +52,84 @@ size_t moe_route_workspace_size(int T, int d_model, int E_r, moe_dtype h_dtype) 
   return moe::route_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16);
 }
 
+namespace {
+
+moe_status route_checked(const char* name, int T, int d_model, int E_r, int K, moe_score_fn fn,
+                         const void* h, moe_dtype h_dtype, const float* e, const float* b,
+                         int32_t* topk_idx, float* gates, int32_t* loads, float* p_mean,
+                         float* zsq_mean, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (T < 1 || d_model < 1 || E_r < 1 || K < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T=%d d_model=%d E_r=%d K=%d must be >= 1", name, T,
+                d_model, E_r, K);
+  if (K > E_r) return fail(MOE_ERR_INVALID_ARG, "%s: K=%d > E_r=%d", name, K, E_r);
+  if (K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID_ARG, "%s: K=%d > %d", name, K, MOE_MAX_TOPK);
+  if (E_r > 512) return fail(MOE_ERR_UNSUPPORTED, "%s: E_r=%d > 512", name, E_r);
+  if (fn != MOE_SIGMOID && fn != MOE_SOFTMAX)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown score function %d", name, (int)fn);
+  if (!valid_dtype(h_dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: bad dtype", name);
+  if (d_model % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d_model=%d not a multiple of 8", name, d_model);
+  if (h_dtype == MOE_BF16 && d_model % 32 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 tokens need d_model %% 32 == 0 (got %d)", name,
+                d_model);
+  if (!h || !e || !topk_idx || !gates || !loads)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  const bool stats = p_mean != nullptr;
+  const size_t need = stats ? moe::route_stats_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16)
+                            : moe::route_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", name, workspace_bytes, need);
+  if (static_cast<long long>(T) * K > INT32_MAX || static_cast<long long>(T) * d_model > (1LL << 40) ||
+      static_cast<long long>(T) * E_r > (1LL << 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: sizes overflow", name);
+  return hip_status(moe::launch_route(T, d_model, E_r, K, (int)fn, h, h_dtype == MOE_BF16, e, b,
+                                      topk_idx, gates, loads, workspace, p_mean, zsq_mean,
+                                      as_stream(stream)),
+                    name);
+}
+
+}  // namespace
+
 moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
                      moe_dtype h_dtype, const float* e, const float* b, int32_t* topk_idx,
                      float* gates, int32_t* loads, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  if (T < 1 || d_model < 1 || E_r < 1 || K < 1)
-    return fail(MOE_ERR_INVALID_ARG, "moe_route: T=%d d_model=%d E_r=%d K=%d must be >= 1", T,
-                d_model, E_r, K);
-  if (K > E_r) return fail(MOE_ERR_INVALID_ARG, "moe_route: K=%d > E_r=%d", K, E_r);
-  if (K > MOE_MAX_TOPK)
-    return fail(MOE_ERR_INVALID_ARG, "moe_route: K=%d > %d", K, MOE_MAX_TOPK);
-  if (E_r > 512) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E_r=%d > 512", E_r);
-  if (fn != MOE_SIGMOID && fn != MOE_SOFTMAX)
-    return fail(MOE_ERR_INVALID_ARG, "moe_route: unknown score function %d", (int)fn);
-  if (!valid_dtype(h_dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_route: bad dtype");
-  if (d_model % 8 != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_route: d_model=%d not a multiple of 8", d_model);
-  if (h_dtype == MOE_BF16 && d_model % 32 != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_route: bf16 tokens need d_model %% 32 == 0 (got %d)",
-                d_model);
-  if (!h || !e || !topk_idx || !gates || !loads)
-    return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
-  const size_t need = moe::route_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace %zu < %zu bytes", workspace_bytes, need);
-  if (static_cast<long long>(T) * K > INT32_MAX || static_cast<long long>(T) * d_model > (1LL << 40))
-    return fail(MOE_ERR_INVALID_ARG, "moe_route: sizes overflow");
-  return hip_status(moe::launch_route(T, d_model, E_r, K, (int)fn, h, h_dtype == MOE_BF16, e, b,
-                                      topk_idx, gates, loads, workspace, as_stream(stream)),
-                    "moe_route");
+  return route_checked("moe_route", T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx, gates,
+                       loads, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+size_t moe_route_stats_workspace_size(int T, int d_model, int E_r, moe_dtype h_dtype) {
+  if (T < 1 || d_model < 1 || E_r < 1 || !valid_dtype(h_dtype)) return 0;
+  return moe::route_stats_workspace_bytes(T, d_model, E_r, h_dtype == MOE_BF16);
+}
+
+moe_status moe_route_stats(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
+                           moe_dtype h_dtype, const float* e, const float* b, int32_t* topk_idx,
+                           float* gates, int32_t* loads, float* p_mean, float* zsq_mean,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p_mean || !zsq_mean) return fail(MOE_ERR_INVALID_ARG, "moe_route_stats: null pointer");
+  return route_checked("moe_route_stats", T, d_model, E_r, K, fn, h, h_dtype, e, b, topk_idx,
+                       gates, loads, p_mean, zsq_mean, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_router_diag(int T, int E_r, int K, const int32_t* loads, const float* p_mean,
+                           const float* zsq_mean, const int32_t* offsets, float* f,
+                           moe_router_diag_values* diag, void* stream) {
+  if (T < 1 || E_r < 1 || K < 1 || K > E_r)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_diag: T=%d E_r=%d K=%d", T, E_r, K);
+  if (E_r > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_router_diag: E_r=%d > %d", E_r, MOE_MAX_EXPERTS);
+  if (static_cast<long long>(T) * K > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_diag: T*K overflows int32");
+  if (!loads || !p_mean || !zsq_mean || !diag)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_diag: null pointer");
+  static_assert(sizeof(moe_router_diag_values) == sizeof(moe::RouterDiag), "diag layout");
+  return hip_status(moe::launch_router_diag(T, E_r, K, loads, p_mean, zsq_mean, offsets, f,
+                                            reinterpret_cast<moe::RouterDiag*>(diag),
+                                            as_stream(stream)),
+                    "moe_router_diag");
 }
 
 size_t moe_permute_workspace_size(int T, int E_r) {

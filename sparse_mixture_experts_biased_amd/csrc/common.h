@@ -38,9 +38,21 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // router
 int route_splits(int T, int d, int E, int h_bf16);
 size_t route_workspace_bytes(int T, int d, int E, int h_bf16);
+// p_mean / zsq_mean non-NULL: also the diagnostics (workspace of
+// route_stats_workspace_bytes); else the workspace of route_workspace_bytes.
 hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h_bf16,
                         const float* e, const float* b, int32_t* idx, float* gates,
-                        int32_t* loads, void* ws, hipStream_t s);
+                        int32_t* loads, void* ws, float* p_mean, float* zsq_mean,
+                        hipStream_t s);
+size_t route_stats_workspace_bytes(int T, int d, int E, int h_bf16);
+hipError_t launch_route_stats(int T, int E, const float* prow, const float* lsq, float* part,
+                              float* p_mean, float* zsq_mean, hipStream_t s);
+struct RouterDiag {  // layout of moe_router_diag
+  float switch_fP, z_loss, load_entropy, max_vio, dropped, reserved[3];
+};
+hipError_t launch_router_diag(int T, int E, int K, const int32_t* loads, const float* p_mean,
+                              const float* zsq_mean, const int32_t* offsets, float* f,
+                              RouterDiag* diag, hipStream_t s);
 
 // dispatch
 constexpr int kPermChunk = 256;  // tokens per histogram / rank chunk

@@ -21,6 +21,11 @@
 // of a wave-wide arg-max over v = s + b (equal v -> lower expert id), a sort of
 // the K picks by expert id, and the gate denominator summed in that order, so
 // the gates depend only on the picked set.
+//
+// Diagnostics (optional, same page, section 1: Switch P_i and the router
+// z-loss): the selection wave also writes the token's softmax row p_t and
+// logsumexp(z_t)^2; two reduction kernels average them over the tokens in a
+// fixed order (deterministic).
 #include "common.h"
 
 #include <math.h>
@@ -62,8 +67,31 @@ template <int EJ>
 __device__ __forceinline__ void select_token(int t, int E, int K, int fn, const float (&z)[EJ],
                                              const float (&bias)[EJ], int32_t* __restrict__ idx_out,
                                              float* __restrict__ gate_out,
-                                             int32_t* __restrict__ loads) {
+                                             int32_t* __restrict__ loads,
+                                             float* __restrict__ prow,
+                                             float* __restrict__ lsq) {
   const int lane = threadIdx.x % kWave;
+  if (prow != nullptr) {  // diagnostics: softmax row and logsumexp^2 of token t
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EJ; ++j)
+      if (lane + kWave * j < E) m = fmaxf(m, z[j]);
+    m = wave_max(m);
+    float ez[EJ], part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EJ; ++j) {
+      ez[j] = (lane + kWave * j < E) ? expf(z[j] - m) : 0.0f;
+      part += ez[j];
+    }
+    const float tot = wave_sum(part);
+#pragma unroll
+    for (int j = 0; j < EJ; ++j)
+      if (lane + kWave * j < E) prow[static_cast<size_t>(t) * E + lane + kWave * j] = ez[j] / tot;
+    if (lane == 0) {
+      const float lse = m + logf(tot);
+      lsq[t] = lse * lse;
+    }
+  }
   float s[EJ], v[EJ];
   if (fn == 0) {
 #pragma unroll
@@ -162,7 +190,7 @@ template <int EJ>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     int T, int d, int E, int K, int fn, const float* __restrict__ h, const float* __restrict__ e,
     const float* __restrict__ b, int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
-    int32_t* __restrict__ loads) {
+    int32_t* __restrict__ loads, float* __restrict__ prow, float* __restrict__ lsq) {
   extern __shared__ float smem[];
   float* hs = smem;                       // [kBT][kBK]
   float* es = smem + kBT * kBK;           // [E][kBK + 1]
@@ -232,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
       int ex = lane + kWave * j;
       z[j] = (ex < E) ? zs[r * E + ex] : 0.0f;
     }
-    select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads);
+    select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, prow, lsq);
   }
 }
 
@@ -355,7 +383,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int K, in
                                                          const float* __restrict__ b,
                                                          int32_t* __restrict__ idx_out,
                                                          float* __restrict__ gate_out,
-                                                         int32_t* __restrict__ loads) {
+                                                         int32_t* __restrict__ loads,
+                                                         float* __restrict__ prow,
+                                                         float* __restrict__ lsq) {
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   if (t >= T) return;  // wave-uniform
@@ -369,7 +399,42 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int K, in
     z[j] = acc;
     bias[j] = (b != nullptr && ex < E) ? b[ex] : 0.0f;
   }
-  select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads);
+  select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, prow, lsq);
+}
+
+// ------------------------------------------------------------ diagnostics
+
+constexpr int kStatChunk = 64;  // tokens per partial sum
+
+// part[c][e] = sum of p_te over tokens of chunk c (e < E); part[c][E] = sum of
+// logsumexp^2 over the chunk.  Grid (ceil((E + 1) / 256), chunks).
+__global__ __launch_bounds__(256) void stats_partial_kernel(int T, int E,
+                                                            const float* __restrict__ prow,
+                                                            const float* __restrict__ lsq,
+                                                            float* __restrict__ part) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int t0 = blockIdx.y * kStatChunk;
+  const int t1 = min(T, t0 + kStatChunk);
+  if (e > E) return;
+  float acc = 0.0f;
+  if (e < E)
+    for (int t = t0; t < t1; ++t) acc += prow[static_cast<size_t>(t) * E + e];
+  else
+    for (int t = t0; t < t1; ++t) acc += lsq[t];
+  part[static_cast<size_t>(blockIdx.y) * (E + 1) + e] = acc;
+}
+
+// p_mean[e] = (1/T) sum_c part[c][e]; zsq_mean = (1/T) sum_c part[c][E].
+__global__ __launch_bounds__(1024) void stats_final_kernel(int T, int E, int n_chunks,
+                                                           const float* __restrict__ part,
+                                                           float* __restrict__ p_mean,
+                                                           float* __restrict__ zsq_mean) {
+  for (int e = threadIdx.x; e <= E; e += 1024) {
+    float acc = 0.0f;
+    for (int c = 0; c < n_chunks; ++c) acc += part[static_cast<size_t>(c) * (E + 1) + e];
+    const float v = acc / static_cast<float>(T);
+    if (e < E) p_mean[e] = v; else *zsq_mean = v;
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
@@ -384,7 +449,7 @@ const void* f32_kernel_ptr() { return reinterpret_cast<const void*>(route_f32_ke
 
 hipError_t launch_route_f32(int T, int d, int E, int K, int fn, const float* h, const float* e,
                             const float* b, int32_t* idx, float* gates, int32_t* loads,
-                            hipStream_t s) {
+                            float* prow, float* lsq, hipStream_t s) {
   dim3 grid((T + kBT - 1) / kBT), block(kThreads);
   const size_t es_floats = static_cast<size_t>(E) * (kBK + 1);
   const size_t zs_floats = static_cast<size_t>(kBT) * E;
@@ -398,13 +463,13 @@ hipError_t launch_route_f32(int T, int d, int E, int K, int fn, const float* h, 
   }
   ProfScope prof_(s, "route_f32");
   if (ej <= 1)
-    hipLaunchKernelGGL(route_f32_kernel<1>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<1>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads, prow, lsq);
   else if (ej <= 2)
-    hipLaunchKernelGGL(route_f32_kernel<2>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<2>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads, prow, lsq);
   else if (ej <= 4)
-    hipLaunchKernelGGL(route_f32_kernel<4>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<4>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads, prow, lsq);
   else
-    hipLaunchKernelGGL(route_f32_kernel<8>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads);
+    hipLaunchKernelGGL(route_f32_kernel<8>, grid, block, shmem, s, T, d, E, K, fn, h, e, b, idx, gates, loads, prow, lsq);
   return hipGetLastError();
 }
 
@@ -424,6 +489,29 @@ size_t route_workspace_bytes(int T, int d, int E, int h_bf16) {
   return align_up(static_cast<size_t>(S) * T * E * sizeof(float), 256);
 }
 
+// Diagnostics scratch after the logits: p rows [T][E], logsumexp^2 [T],
+// partial sums [chunks][E + 1].
+size_t route_stats_workspace_bytes(int T, int d, int E, int h_bf16) {
+  const size_t n_chunks = (static_cast<size_t>(T) + kStatChunk - 1) / kStatChunk;
+  return route_workspace_bytes(T, d, E, h_bf16) +
+         align_up(static_cast<size_t>(T) * E * sizeof(float), 256) +
+         align_up(static_cast<size_t>(T) * sizeof(float), 256) +
+         align_up(n_chunks * (E + 1) * sizeof(float), 256);
+}
+
+hipError_t launch_route_stats(int T, int E, const float* prow, const float* lsq, float* part,
+                              float* p_mean, float* zsq_mean, hipStream_t s) {
+  const int n_chunks = (T + kStatChunk - 1) / kStatChunk;
+  {
+    ProfScope prof_(s, "route_stats");
+    hipLaunchKernelGGL(stats_partial_kernel, dim3((E + 1 + 255) / 256, n_chunks), dim3(256), 0, s,
+                       T, E, prow, lsq, part);
+    hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(1024), 0, s, T, E, n_chunks, part, p_mean,
+                       zsq_mean);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   {
@@ -435,14 +523,27 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s) {
 
 hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h_bf16,
                         const float* e, const float* b, int32_t* idx, float* gates,
-                        int32_t* loads, void* ws, hipStream_t s) {
+                        int32_t* loads, void* ws, float* p_mean, float* zsq_mean,
+                        hipStream_t s) {
   hipError_t err = launch_fill_i32(loads, 0, static_cast<size_t>(E), s);
   if (err != hipSuccess) return err;
   const int S = route_splits(T, d, E, h_bf16);
+  float* prow = nullptr;
+  float* lsq = nullptr;
+  float* part = nullptr;
+  if (p_mean != nullptr) {
+    char* base = static_cast<char*>(ws) + route_workspace_bytes(T, d, E, h_bf16);
+    prow = reinterpret_cast<float*>(base);
+    lsq = reinterpret_cast<float*>(base + align_up(static_cast<size_t>(T) * E * sizeof(float), 256));
+    part = reinterpret_cast<float*>(reinterpret_cast<char*>(lsq) +
+                                    align_up(static_cast<size_t>(T) * sizeof(float), 256));
+  }
   if (S == 0) {
     if (h_bf16) return hipErrorInvalidValue;  // rejected on the host before this point
-    return launch_route_f32(T, d, E, K, fn, static_cast<const float*>(h), e, b, idx, gates,
-                            loads, s);
+    err = launch_route_f32(T, d, E, K, fn, static_cast<const float*>(h), e, b, idx, gates,
+                           loads, prow, lsq, s);
+    if (err != hipSuccess || p_mean == nullptr) return err;
+    return launch_route_stats(T, E, prow, lsq, part, p_mean, zsq_mean, s);
   }
   float* zpart = static_cast<float*>(ws);
   {
@@ -459,15 +560,17 @@ hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h
     dim3 grid((T + 3) / 4), block(256);
     const float* zp = zpart;
     if (ej <= 1)
-      hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+      hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
     else if (ej <= 2)
-      hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+      hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
     else if (ej <= 4)
-      hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+      hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
     else
-      hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads);
+      hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
   }
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (err != hipSuccess || p_mean == nullptr) return err;
+  return launch_route_stats(T, E, prow, lsq, part, p_mean, zsq_mean, s);
 }
 
 }  // namespace moe

@@ -33,9 +33,12 @@ class LayerShape:
 
 class MoELayer:
     def __init__(self, shape: LayerShape, e, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
-                 ws_down=None, device="cuda", capacity_factor: Optional[float] = None):
+                 ws_down=None, device="cuda", capacity_factor: Optional[float] = None,
+                 diagnostics: bool = False):
         """capacity_factor: None dispatches every copy; a factor CF caps each
-        expert at C = ceil(CF*T*K/E_r) rows, admitted in token order."""
+        expert at C = ceil(CF*T*K/E_r) rows, admitted in token order.
+        diagnostics: route with moe_route_stats and fill the router's balance
+        diagnostics (moe_router_diag) after the dispatch of every forward."""
         s = self.shape = shape
         self.capacity = (None if capacity_factor is None else
                          L.moe_expert_capacity(s.T, s.K, s.E_r, capacity_factor))
@@ -53,7 +56,16 @@ class MoELayer:
         self.topk_idx = torch.empty((T, K), **i32)
         self.gates = torch.empty((T, K), dtype=torch.float32, device=device)
         self.loads = torch.empty((E,), **i32)
-        self.route_ws_bytes = L.moe_route_workspace_size(T, d, E, self.dt)
+        self.diagnostics = diagnostics
+        if diagnostics:
+            f32 = dict(dtype=torch.float32, device=device)
+            self.p_mean = torch.empty((E,), **f32)
+            self.zsq_mean = torch.empty((1,), **f32)
+            self.f = torch.empty((E,), **f32)
+            self.diag = torch.zeros((8,), **f32)
+            self.route_ws_bytes = L.moe_route_stats_workspace_size(T, d, E, self.dt)
+        else:
+            self.route_ws_bytes = L.moe_route_workspace_size(T, d, E, self.dt)
         self.route_ws = torch.empty((max(self.route_ws_bytes, 1),), dtype=torch.uint8,
                                     device=device)
         self.offsets = torch.empty((E + 1,), **i32)
@@ -79,8 +91,23 @@ class MoELayer:
     # individual stages -------------------------------------------------
     def route(self, h, b, stream=None):
         s = self.shape
-        L.moe_route(s.T, s.d_model, s.E_r, s.K, self.fn, h, self.dt, self.e, b, self.topk_idx,
-                    self.gates, self.loads, self.route_ws, self.route_ws_bytes, stream)
+        if self.diagnostics:
+            L.moe_route_stats(s.T, s.d_model, s.E_r, s.K, self.fn, h, self.dt, self.e, b,
+                              self.topk_idx, self.gates, self.loads, self.p_mean, self.zsq_mean,
+                              self.route_ws, self.route_ws_bytes, stream)
+        else:
+            L.moe_route(s.T, s.d_model, s.E_r, s.K, self.fn, h, self.dt, self.e, b,
+                        self.topk_idx, self.gates, self.loads, self.route_ws,
+                        self.route_ws_bytes, stream)
+
+    def router_diag(self, stream=None):
+        s = self.shape
+        L.moe_router_diag(s.T, s.E_r, s.K, self.loads, self.p_mean, self.zsq_mean, self.offsets,
+                          self.f, self.diag, stream)
+
+    def diag_host(self):
+        v = self.diag.cpu().tolist()
+        return dict(zip(L.DIAG_FIELDS, v[:len(L.DIAG_FIELDS)]))
 
     def permute(self, h=None, x_perm=None, stream=None):
         s = self.shape
@@ -131,6 +158,8 @@ class MoELayer:
         the loads are counted (the update affects the next call)."""
         self.route(h, b, stream)
         self.permute(stream=stream)
+        if self.diagnostics:
+            self.router_diag(stream)
         self.routed_experts(h, stream)
         self.shared_experts(h, stream)
         self.combine(h, stream)

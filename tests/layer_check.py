@@ -15,11 +15,11 @@ from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
 from synthetic import host_array
 
 
-def runner_for(lay, T=None, capacity_factor=None):
+def runner_for(lay, T=None, capacity_factor=None, diagnostics=False):
     c = lay.cfg
     shape = LayerShape(T or c.T, c.d_model, c.E_r, c.K, c.E_s, c.d_ffn, c.dtype, c.score)
     return MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
-                    lay.ws_down, capacity_factor=capacity_factor)
+                    lay.ws_down, capacity_factor=capacity_factor, diagnostics=diagnostics)
 
 
 def _expert_source(w_gate, w_up, w_down):

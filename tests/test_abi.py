@@ -97,6 +97,28 @@ def test_expert_capacity_and_capacity_permute_arguments():
                                     None) == L.MOE_ERR_INVALID_ARG
 
 
+def test_route_stats_and_router_diag_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    base = L.moe_route_workspace_size(4096, 7168, 256, L.MOE_BF16)
+    need = L.moe_route_stats_workspace_size(4096, 7168, 256, L.MOE_BF16)
+    assert need >= base + 4096 * 256 * 4 + 4096 * 4
+    assert L.moe_route_stats_workspace_size(64, 128, 8, L.MOE_F32) >= 64 * 8 * 4 + 64 * 4
+    rc, msg = _st(lib.moe_route_stats(4096, 7168, 256, 8, 0, P, 1, P, None, P, P, P, P, P, P,
+                                      need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    rc, msg = _st(lib.moe_route_stats(4096, 7168, 256, 8, 0, P, 1, P, None, P, P, P, None, P, P,
+                                      need, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "null" in msg
+    assert lib.moe_route_stats(64, 128, 8, 9, 0, P, 0, P, None, P, P, P, P, P, P, 1 << 20,
+                               None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_diag(64, 8, 9, P, P, P, None, None, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_diag(64, 8, 2, P, None, P, None, None, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_diag(64, 8, 2, P, P, P, None, None, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_diag(64, 2048, 2, P, P, P, None, None, P, None) == L.MOE_ERR_UNSUPPORTED
+    assert ctypes.sizeof(L.MoeRouterDiag) == 32
+
+
 def test_grouped_swiglu_rejects_bad_arguments():
     lib = L.load()
     P = ctypes.c_void_p(16)

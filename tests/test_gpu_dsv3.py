@@ -50,6 +50,26 @@ def test_dsv3_prefill_capacity_factor(dsv3, cf):
     say(str(res))
 
 
+def test_dsv3_prefill_with_router_diagnostics(dsv3):
+    """The layer with diagnostics on (moe_route_stats + moe_router_diag after
+    a CF = 1.0 dispatch): same outputs as without, diagnostics vs the oracle."""
+    cfg = dsv3.cfg
+    run = runner_for(dsv3, capacity_factor=1.0)
+    run_d = runner_for(dsv3, capacity_factor=1.0, diagnostics=True)
+    y0 = run.forward(dsv3.h, dsv3.b.clone()).clone()
+    y1 = run_d.forward(dsv3.h, dsv3.b.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    dv = run_d.diag_host()
+    idx = run_d.topk_idx.cpu().numpy()
+    kept = (run_d.slot_row.cpu().numpy() >= 0).reshape(cfg.T, cfg.K)
+    z = O.router_logits(host_array(dsv3.h), host_array(dsv3.e))
+    ref = O.router_diagnostics(z, idx, cfg.E_r, kept=kept)
+    say(f"diagnostics {dv} vs oracle { {k: ref[k] for k in dv} }")
+    for k, v in dv.items():
+        assert abs(v - ref[k]) <= 1e-4 * max(1.0, abs(ref[k])), k
+
+
 def test_dsv3_decode_full_size(dsv3):
     cfg = CONFIGS["dsv3_decode"]
     h = make_tokens(cfg, device="cuda")

@@ -120,6 +120,63 @@ def test_route_worked_example_bias_moves_pick():
     assert np.allclose(g2.cpu().numpy()[0], s / s.sum(), atol=GATE_TOL)
 
 
+DIAG_REL = 1e-4   # fp32 sums over up to T tokens in a fixed chunked order vs fp64
+
+
+@pytest.mark.parametrize("T,d,E,K,fn,dtype,cf", [
+    (64, 128, 8, 2, "sigmoid", torch.float32, None),
+    (300, 256, 16, 4, "softmax", torch.bfloat16, None),
+    (1000, 512, 64, 6, "sigmoid", torch.bfloat16, 1.0),
+    (4096, 7168, 256, 8, "sigmoid", torch.bfloat16, 1.0),
+    (2000, 1024, 512, 8, "softmax", torch.float32, 1.25)])
+def test_route_stats_and_router_diag(T, d, E, K, fn, dtype, cf):
+    say(f"moe_route_stats / moe_router_diag T={T} d={d} E={E} K={K} {fn} {dtype} cf={cf}")
+    h = _tokens(T, d, dtype, 90 + T)
+    g = _gen(91 + E)
+    e = (torch.randn((E, d), generator=g, device=DEV) / math.sqrt(d)).float()
+    b = (torch.rand(E, generator=g, device=DEV) * 0.02 - 0.01).float() if fn == "sigmoid" else None
+    dt = L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32
+    fnc = L.MOE_SIGMOID if fn == "sigmoid" else L.MOE_SOFTMAX
+    i32 = dict(dtype=torch.int32, device=DEV)
+    idx0, idx1 = torch.empty((T, K), **i32), torch.empty((T, K), **i32)
+    g0 = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    g1 = torch.empty_like(g0)
+    l0, l1 = torch.empty(E, **i32), torch.empty(E, **i32)
+    wsb0 = L.moe_route_workspace_size(T, d, E, dt)
+    ws0 = torch.empty(max(wsb0, 1), dtype=torch.uint8, device=DEV)
+    L.moe_route(T, d, E, K, fnc, h, dt, e, b, idx0, g0, l0, ws0, wsb0)
+    wsb = L.moe_route_stats_workspace_size(T, d, E, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    p_mean = torch.empty(E, dtype=torch.float32, device=DEV)
+    zsq = torch.empty(1, dtype=torch.float32, device=DEV)
+    L.moe_route_stats(T, d, E, K, fnc, h, dt, e, b, idx1, g1, l1, p_mean, zsq, ws, wsb)
+    torch.cuda.synchronize()
+    # the statistics leave the routing untouched: bit-identical outputs
+    assert torch.equal(idx0, idx1) and torch.equal(g0.view(torch.int32), g1.view(torch.int32))
+    assert torch.equal(l0, l1)
+    idx = idx1.cpu().numpy()
+    offsets = None
+    kept = None
+    if cf is not None:
+        C = L.moe_expert_capacity(T, K, E, cf)
+        offsets, _, sr, _ = _permute_capacity_gpu(idx1, E, C)
+        kept = (sr.cpu().numpy() >= 0).reshape(T, K)
+    f = torch.empty(E, dtype=torch.float32, device=DEV)
+    diag = torch.zeros(8, dtype=torch.float32, device=DEV)
+    L.moe_router_diag(T, E, K, l1, p_mean, zsq, offsets, f, diag)
+    torch.cuda.synchronize()
+    z = O.router_logits(host_array(h), host_array(e))
+    ref = O.router_diagnostics(z, idx, E, kept=kept)   # teacher-forced on the GPU's picks
+    pm = p_mean.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(pm - ref["P"]) / ref["P"]) <= DIAG_REL
+    assert np.allclose(f.cpu().numpy(), ref["f"], rtol=1e-6, atol=0)
+    dv = dict(zip(L.DIAG_FIELDS, diag.cpu().tolist()))
+    say(str(dv))
+    for k in ("switch_fP", "z_loss", "load_entropy", "max_vio", "dropped"):
+        assert abs(dv[k] - ref[k]) <= DIAG_REL * max(1.0, abs(ref[k])), (k, dv[k], ref[k])
+    assert (dv["dropped"] > 0) == (cf is not None and kept is not None and not kept.all())
+
+
 def _permute_gpu(idx, E, h=None):
     T, K = idx.shape
     offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
