@@ -23,6 +23,11 @@ Plain NumPy, written from the method's definitions, one function per step:
     expert is dropped (the token keeps only its residual and other experts).
   * Routing-and-load-balancing page (yiqiao-yin.github.io), section 5: tokens
     are admitted to an expert in the order they appear.
+  * Backward pass of the layer (gradients of a loss through y, with the
+    routing decisions I_t fixed): the chain rule applied to the layer-output,
+    SwiGLU, gate and score equations above.  The gate gradient reaches the
+    router only through the unbiased scores s (routing-math page, section 2:
+    the bias decides the selection only, so it receives no gradient).
   * Router diagnostics (forward values): routing-math page, section 1 (Switch
     auxiliary loss f_i P_i with f_i = E_r/(K T) * #{t : i in I_t} and
     P_i = mean_t p_{t,i}; router z-loss = mean_t logsumexp(z_t)^2) and the
@@ -327,6 +332,132 @@ def router_diagnostics(z: np.ndarray, idx: np.ndarray, E_r: int,
     return dict(P=P, f=f, switch_fP=float((f * P).sum()), z_loss=float((lse ** 2).mean()),
                 load_entropy=entropy, max_vio=float((c.max() - cbar) / cbar),
                 dropped=0.0 if kept is None else float(1.0 - kept.mean()))
+
+
+# ---------------------------------------------------------------- backward
+
+def combine_backward(dy: np.ndarray, y_perm: np.ndarray, slot_row: np.ndarray,
+                     g: np.ndarray):
+    """Gradients of y_t = h_t + y_shared_t + sum_k g_{t,k} y_perm[slot_row[t,k]].
+
+    Returns (dy_perm [rows, d]: g_{t,k} dy_t on row slot_row[t,k]; dg [T, K]:
+    <dy_t, y_perm[slot_row[t,k]]>, 0 for a dropped copy).  The residual and the
+    shared experts receive dy itself.
+    """
+    dy64 = to_f64(dy)
+    T, K = g.shape
+    sr = slot_row.reshape(T, K).astype(np.int64)
+    dy_perm = np.zeros_like(y_perm, dtype=np.float64)
+    dg = np.zeros((T, K), dtype=np.float64)
+    for k in range(K):
+        keep = sr[:, k] >= 0
+        dy_perm[sr[keep, k]] = g[keep, k:k + 1].astype(np.float64) * dy64[keep]
+        dg[keep, k] = np.einsum("td,td->t", dy64[keep], y_perm[sr[keep, k]])
+    return dy_perm, dg
+
+
+def swiglu_backward(x, w_gate, w_up, w_down, dy):
+    """Gradients of (SiLU(x W_gate^T) * (x W_up^T)) W_down^T, fp64.
+
+    With a = x W_gate^T, u = x W_up^T, act = SiLU(a) u and SiLU'(a) =
+    sigma(a) (1 + a (1 - sigma(a))): d act = dy W_down, dW_down = dy^T act,
+    da = d act * u * SiLU'(a), du = d act * SiLU(a), dx = da W_gate + du W_up,
+    dW_gate = da^T x, dW_up = du^T x.  Returns (dx, dW_gate, dW_up, dW_down).
+    """
+    x64 = to_f64(x) if x.dtype != np.float64 else x
+    wg, wu, wd = to_f64(w_gate), to_f64(w_up), to_f64(w_down)
+    dy64 = to_f64(dy) if dy.dtype != np.float64 else dy
+    a = x64 @ wg.T
+    u = x64 @ wu.T
+    sa = 1.0 / (1.0 + np.exp(-a))
+    act = a * sa * u
+    dact = dy64 @ wd
+    dwd = dy64.T @ act
+    da = dact * u * sa * (1.0 + a * (1.0 - sa))
+    du = dact * a * sa
+    dx = da @ wg + du @ wu
+    return dx, da.T @ x64, du.T @ x64, dwd
+
+
+def grouped_swiglu_backward(x: np.ndarray, offsets: np.ndarray, row_index: Optional[np.ndarray],
+                            weights: ExpertSource, dy_rows: np.ndarray,
+                            groups: Optional[Sequence[int]] = None):
+    """Backward of grouped_swiglu: dx_rows [rows, d] (gradient of each grouped
+    row's input) and {g: (dW_gate, dW_up, dW_down)} for the groups with rows."""
+    x64 = to_f64(x)
+    rows = int(offsets[-1])
+    src = np.arange(rows) if row_index is None else row_index.astype(np.int64)
+    dx = np.zeros((rows, x64.shape[1]), dtype=np.float64)
+    dw = {}
+    n_groups = len(offsets) - 1
+    for gi in (range(n_groups) if groups is None else groups):
+        lo, hi = int(offsets[gi]), int(offsets[gi + 1])
+        if hi == lo:
+            continue
+        wg, wu, wd = _expert(weights, gi)
+        dx[lo:hi], dwg, dwu, dwd = swiglu_backward(x64[src[lo:hi]], wg, wu, wd, dy_rows[lo:hi])
+        dw[gi] = (dwg, dwu, dwd)
+    return dx, dw
+
+
+def router_backward(h: np.ndarray, e: np.ndarray, idx: np.ndarray, fn: str,
+                    dg: np.ndarray):
+    """Gradient of the gates g_{t,k} (the picks I_t fixed) w.r.t. the logits of
+    the picked experts, the tokens and the centroids, fp64.
+
+    sigmoid: g_i = s_i / S, S = sum_{j in I_t} s_j, s = sigma(z): ds_i =
+    (dg_i - sum_j g_j dg_j) / S and dz_i = ds_i s_i (1 - s_i).
+    softmax renormalised over the picks: g_i = exp(z_i) / sum_{j in I_t}
+    exp(z_j) (the full normaliser cancels), so dz_i = g_i (dg_i - sum_j g_j dg_j).
+    Returns (dz [T, K], dh [T, d] = sum_k dz_{t,k} e_{idx[t,k]}, de [E_r, d] =
+    sum over picks of dz h_t).  The bias gets no gradient.
+    """
+    h64, e64 = to_f64(h), to_f64(e)
+    ii = idx.astype(np.int64)
+    z = np.einsum("td,tkd->tk", h64, e64[ii])             # logits of the picks
+    dg64 = dg.astype(np.float64)
+    if fn == "sigmoid":
+        sv = 1.0 / (1.0 + np.exp(-z))
+        S = sv.sum(axis=1, keepdims=True)
+        g = sv / S
+        ds = (dg64 - (g * dg64).sum(axis=1, keepdims=True)) / S
+        dz = ds * sv * (1.0 - sv)
+    elif fn == "softmax":
+        ez = np.exp(z - z.max(axis=1, keepdims=True))
+        g = ez / ez.sum(axis=1, keepdims=True)
+        dz = g * (dg64 - (g * dg64).sum(axis=1, keepdims=True))
+    else:
+        raise ValueError(fn)
+    dh = np.einsum("tk,tkd->td", dz, e64[ii])
+    de = np.zeros_like(e64)
+    np.add.at(de, ii.reshape(-1), dz.reshape(-1, 1) * np.repeat(h64, idx.shape[1], axis=0))
+    return dz, dh, de
+
+
+def layer_backward(h, e, b, K: int, fn: str, routed: ExpertSource, dy,
+                   shared: Optional[ExpertSource] = None, E_s: int = 0,
+                   capacity: Optional[int] = None):
+    """Gradients of sum_t <dy_t, y_t> for one layer call (the routing decisions
+    of the forward pass held fixed): dh, de and the expert weight gradients."""
+    out = layer_forward(h, e, b, K, fn, routed, shared, E_s, capacity=capacity)
+    dy_perm, dg = combine_backward(dy, out["y_perm"], out["slot_row"], out["gates"])
+    dx_perm, dw = grouped_swiglu_backward(h, out["offsets"], out["row_token"], routed, dy_perm)
+    dh = to_f64(dy).copy()
+    T = dh.shape[0]
+    sr = out["slot_row"].reshape(T, K).astype(np.int64)
+    for k in range(K):
+        keep = sr[:, k] >= 0
+        dh[keep] += dx_perm[sr[keep, k]]
+    dw_shared = {}
+    for j in range(E_s):
+        wg, wu, wd = _expert(shared, j)
+        dxs, dwg, dwu, dwd = swiglu_backward(to_f64(h), wg, wu, wd, to_f64(dy))
+        dh += dxs
+        dw_shared[j] = (dwg, dwu, dwd)
+    dz, dh_r, de = router_backward(h, e, out["idx"], fn, dg)
+    dh += dh_r
+    return dict(out, dy_perm=dy_perm, dg=dg, dx_perm=dx_perm, dz=dz, dh=dh, de=de,
+                dw=dw, dw_shared=dw_shared)
 
 
 # ---------------------------------------------------------------- layer

@@ -568,3 +568,95 @@ def test_diagnostics_dropped_rate_from_capacity():
     _, _, sr, kept = O.permute_capacity(idx, E, C)
     d = O.router_diagnostics(np.log(v), idx, E, kept=(sr >= 0).reshape(T, K))
     assert abs(d["dropped"] - (sr < 0).sum() / (T * K)) < 1e-15 and d["dropped"] > 0
+
+
+# ------------------------------------------------------------------ backward
+# The backward oracle is pinned by central finite differences of the forward
+# (fp64, the picks I_t and the capacity drops held fixed).
+
+def _fd_loss(h, e, w, ws, idx, fn, kept, dy):
+    """sum_t <dy_t, y_t> of the layer forward, everything in fp64."""
+    z = h @ e.T
+    if fn == "sigmoid":
+        sel = np.take_along_axis(1.0 / (1.0 + np.exp(-z)), idx, axis=1)
+        g = sel / sel.sum(axis=1, keepdims=True)
+    else:
+        g = scipy.special.softmax(np.take_along_axis(z, idx, axis=1), axis=1)
+    y = h.copy()
+    if ws is not None:
+        y += O.swiglu(h, ws[0][0], ws[1][0], ws[2][0])
+    for t in range(h.shape[0]):
+        for k in range(idx.shape[1]):
+            if kept[t, k]:
+                i = idx[t, k]
+                y[t] += g[t, k] * O.swiglu(h[t:t + 1], w[0][i], w[1][i], w[2][i])[0]
+    return float((dy * y).sum())
+
+
+@pytest.mark.parametrize("fn,cap", [("sigmoid", None), ("softmax", None), ("sigmoid", 3)])
+def test_layer_backward_matches_finite_differences(fn, cap):
+    rng = np.random.default_rng(60)
+    T, d, f, E, K = 12, 6, 5, 4, 2
+    h, e, w, ws = _small_layer(rng, T, d, f, E, 1, dtype=np.float64)
+    e = e.astype(np.float64)
+    b = (rng.random(E) * 0.05).astype(np.float32) if fn == "sigmoid" else None
+    dy = rng.standard_normal((T, d))
+    bw = O.layer_backward(h, e, b, K, fn, w, dy, ws, 1, capacity=cap)
+    idx = bw["idx"].astype(np.int64)
+    kept = (bw["slot_row"].reshape(T, K) >= 0)
+    if cap is not None:
+        assert not kept.all()
+    L = lambda hh, ee, ww, wws: _fd_loss(hh, ee, ww, wws, idx, fn, kept, dy)
+    eps = 1e-5
+
+    def fd(fun, x, grad):
+        v = rng.standard_normal(x.shape)
+        num = (fun(x + eps * v) - fun(x - eps * v)) / (2 * eps)
+        ana = float((grad * v).sum())
+        assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (num, ana)
+
+    fd(lambda hh: L(hh, e, w, ws), h, bw["dh"])
+    fd(lambda ee: L(h, ee, w, ws), e, bw["de"])
+    for i in sorted(bw["dw"]):
+        for m in range(3):
+            def fw(x, i=i, m=m):
+                ww = [a.copy() for a in w]
+                ww[m][i] = x
+                return L(h, e, tuple(ww), ws)
+            fd(fw, w[m][i], bw["dw"][i][m])
+    for m in range(3):
+        def fs(x, m=m):
+            wws = [a.copy() for a in ws]
+            wws[m][0] = x
+            return L(h, e, w, tuple(wws))
+        fd(fs, ws[m][0], bw["dw_shared"][0][m])
+    # experts without rows get no gradient entry; the bias gets none at all
+    assert set(bw["dw"]) == set(np.unique(idx[kept]).tolist())
+
+
+def test_swiglu_backward_closed_form_linear_limit():
+    # W_gate = 0: a = 0, SiLU(0) = 0, SiLU'(0) = 1/2 -> act = 0, d act = dy W_down,
+    # du = 0, da = d act * u / 2, dx = da W_gate + 0 = 0, dW_up = 0, dW_down = 0,
+    # dW_gate = (d act * u / 2)^T x
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((7, 5))
+    wg = np.zeros((3, 5))
+    wu = rng.standard_normal((3, 5))
+    wd = rng.standard_normal((5, 3))
+    dy = rng.standard_normal((7, 5))
+    dx, dwg, dwu, dwd = O.swiglu_backward(x, wg, wu, wd, dy)
+    assert np.all(dx == 0) and np.all(dwu == 0) and np.all(dwd == 0)
+    assert np.allclose(dwg, ((dy @ wd) * (x @ wu.T) / 2).T @ x, rtol=1e-14, atol=1e-14)
+
+
+def test_router_backward_gates_sum_to_one_direction():
+    # sum_k g_k = 1 for every token, so a gate gradient dg = c (constant per
+    # token) moves nothing: dz = 0, dh = 0, de = 0 (both score functions)
+    rng = np.random.default_rng(62)
+    h = rng.standard_normal((9, 4))
+    e = rng.standard_normal((6, 4))
+    idx = np.sort(np.stack([rng.choice(6, 3, replace=False) for _ in range(9)]), axis=1)
+    dg = np.repeat(rng.standard_normal((9, 1)), 3, axis=1)
+    for fn in ("sigmoid", "softmax"):
+        dz, dh, de = O.router_backward(h, e, idx, fn, dg)
+        assert np.abs(dz).max() < 1e-14 and np.abs(dh).max() < 1e-13 and np.abs(de).max() < 1e-13
