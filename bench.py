@@ -165,6 +165,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--capacity-factor", type=float, default=None, metavar="CF",
                     help="cap every expert at ceil(CF*T*K/E_r) rows (token dropping)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step: the forward pass plus the backward pass of the "
+                         "layer (gradients of tokens, centroids and every expert weight)")
     ap.add_argument("--diagnostics", action="store_true",
                     help="route with the router statistics and compute the balance diagnostics "
                          "(Switch f.P, z-loss, load entropy, MaxVio, dropped rate) every step")
@@ -211,9 +214,18 @@ def main(argv=None):
     gamma = cfg.gamma if b is not None else None
     stream = torch.cuda.current_stream()
     run.profile_tags = True
+    dy = None
+    if args.backward:
+        run.prepare_backward(stream)     # transposed weight copies: outside the timed steps
+        dy = make_tokens(cfg, step=10_000, device="cuda")
+
+    def step(i):
+        run.forward(hs[i % len(hs)], b, gamma, stream)
+        if dy is not None:
+            run.backward(hs[i % len(hs)], dy, stream)
 
     for i in range(args.warmup):
-        run.forward(hs[i % len(hs)], b, gamma, stream)
+        step(i)
     torch.cuda.synchronize()
     moe_profile_report()  # drop warm-up records
     moe_profile_enable(True)
@@ -222,7 +234,7 @@ def main(argv=None):
     t_start = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        run.forward(hs[i % len(hs)], b, gamma, stream)
+        step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -286,6 +298,19 @@ def main(argv=None):
     }
     if args.diagnostics:
         out["router_diag"] = {k: round(v, 6) for k, v in run.diag_host().items()}
+    if args.backward:
+        # per touched expert: W_gate, W_up (recomputed a, u), W_down^T, [W_gate^T | W_up^T]
+        # read, three gradients written: 8 d f words; per assignment row dy_perm, dx
+        # (2 d words) and the staged a|u, da|du (4 f words) are overhead
+        d, f = cfg.d_model, cfg.d_ffn
+        bw_bytes = (n_touched + cfg.E_s) * 8 * d * f * 2
+        bw_ms = sum(v[1] for k, v in prof.items() if "backward" in k) / args.steps
+        out["mode"] = "forward+backward"
+        out["backward"] = dict(ms_per_step=round(bw_ms, 4), algorithmic_bytes=bw_bytes,
+                               hbm_gbs=round(bw_bytes / (bw_ms / 1000.0) / 1e9, 1),
+                               hbm_frac=round(bw_bytes / (bw_ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                               flops=6.0 * 2 * d * f * (kept_rows + cfg.T * cfg.E_s))
+        out["config"]["workload"] += ", training step (forward + backward)"
     print(json.dumps(out), flush=True)
     return 0
 

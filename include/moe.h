@@ -318,6 +318,94 @@ const char* moe_last_error(void);
 /* Library version string (host memory, static). */
 const char* moe_version(void);
 
+/* ================================================================ backward
+ *
+ * Gradients of a loss L through the layer output y (dy = dL/dy), with the
+ * routing decisions of the forward pass fixed.  Defined by the chain rule on
+ * the Sparse MoE routing-math page's layer-output, SwiGLU, gate and score
+ * equations (sections 0 and 2); the gate gradient reaches the router only
+ * through the unbiased scores s, and the bias b gets none (section 2: it
+ * decides the selection only).  bf16 operands, fp32 accumulation; gradients
+ * are written in bf16 (weights) or fp32 (centroids, gates, logits).
+ *
+ * One backward step, after a forward with the same buffers:
+ *   moe_combine_backward          dy -> dy_perm (g * dy per copy), dgates
+ *   moe_grouped_swiglu_backward   routed experts: dy_perm -> dx_perm, dW
+ *   moe_grouped_swiglu_backward   shared experts: dy -> dx_shared, dW_shared
+ *   moe_combine (gates = 1)       dh = dy + sum dx_shared + sum_k dx_perm
+ *   moe_route_backward            dh += router term; de
+ */
+
+/*
+ * moe_transpose_experts -- dst[i][c][col_offset + r] = src[i][r][c] for n
+ * matrices [rows, cols] (bf16).  Builds the transposed weight copies the
+ * backward takes: W_down^T [E, d_ffn, d_model] (rows = d_model, cols = d_ffn,
+ * ld_dst = d_model, col_offset 0) and [W_gate^T | W_up^T] [E, d_model,
+ * 2 d_ffn] (two calls, ld_dst = 2 d_ffn, col_offset 0 and d_ffn).
+ * ld_dst >= rows + col_offset, else MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_transpose_experts(int n, int rows, int cols, const void* src, moe_dtype dtype,
+                                 void* dst, int ld_dst, int col_offset, void* stream);
+
+/*
+ * moe_combine_backward -- gradients of y_t = h_t + sum_j y_shared[j, t] +
+ * sum_k g_{t,k} y_perm[slot_row[t,k]] (routing-math page, section 0):
+ *   dy_perm [T*K, d_model] out: row slot_row[t,k] = g_{t,k} dy_t (rows of
+ *           dropped copies are not written)
+ *   dgates  [T, K] fp32 out: <dy_t, y_perm[slot_row[t,k]]> (0 when dropped)
+ * The residual and the shared experts receive dy itself.  bf16 only.
+ */
+moe_status moe_combine_backward(int T, int d_model, int K, const void* dy, const void* y_perm,
+                                const int32_t* slot_row, const float* gates, moe_dtype dtype,
+                                void* dy_perm, float* dgates, void* stream);
+
+/*
+ * moe_grouped_swiglu_backward -- backward of moe_grouped_swiglu (without a
+ * row scale): with a = x W_gate^T, u = x W_up^T, act = SiLU(a) u per group,
+ *   d act = dy W_down;  da = d act * u * SiLU'(a);  du = d act * SiLU(a)
+ *   dx = da W_gate + du W_up;  dW_down = dy^T act;  dW_gate = da^T x;
+ *   dW_up = du^T x,   SiLU'(a) = sigma(a) (1 + a (1 - sigma(a))).
+ *
+ *   offsets, row_index, x, w_gate, w_up  as in the forward call
+ *   w_gu_t    [n_groups, d_model, 2 d_ffn] [W_gate^T | W_up^T]
+ *   w_down_t  [n_groups, d_ffn, d_model] W_down^T
+ *   dy        [rows, d_model] gradient of the grouped outputs
+ *   dx        [rows, d_model] out: gradient of each grouped row's input
+ *   dw_gate, dw_up [n_groups, d_ffn, d_model] out; dw_down [n_groups,
+ *             d_model, d_ffn] out; groups without rows get zeros
+ *   workspace at least moe_grouped_swiglu_backward_workspace_size() bytes
+ * bf16 only; d_model and d_ffn multiples of 64; every operand addressed
+ * through one buffer descriptor under 2 GiB (else MOE_ERR_UNSUPPORTED).
+ */
+size_t moe_grouped_swiglu_backward_workspace_size(int n_groups, int d_model, int d_ffn,
+                                                  int rows);
+moe_status moe_grouped_swiglu_backward(int n_groups, int d_model, int d_ffn, int rows,
+                                       int x_rows, const int32_t* offsets,
+                                       const int32_t* row_index, const void* x, moe_dtype dtype,
+                                       const void* w_gate, const void* w_up, const void* w_gu_t,
+                                       const void* w_down_t, const void* dy, void* dx,
+                                       void* dw_gate, void* dw_up, void* dw_down,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_backward -- gradient of the gates g_{t,k} w.r.t. the router:
+ * sigmoid: g_i = s_i / S, S = sum_{j in I_t} s_j: dz_i = (dg_i - sum_j g_j
+ * dg_j) / S * s_i (1 - s_i); softmax renormalised over the picks: dz_i =
+ * g_i (dg_i - sum_j g_j dg_j).  The logits of the picks are recomputed in fp32.
+ *
+ *   topk_idx, h, e   as in the forward moe_route call (bf16 tokens)
+ *   dgates    [T, K] fp32 from moe_combine_backward
+ *   offsets, row_token  the dispatch of every pick (moe_permute, no capacity)
+ *   dz        [T, K] fp32 out: dL/dz of the picks
+ *   dh        [T, d_model] in/out (bf16): dh_t += sum_k dz_{t,k} e_{idx[t,k]}
+ *   de        [E_r, d_model] fp32 out: sum over picks of dz h_t (fixed order)
+ */
+moe_status moe_route_backward(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
+                              moe_dtype h_dtype, const float* e, const int32_t* topk_idx,
+                              const float* dgates, const int32_t* offsets,
+                              const int32_t* row_token, float* dz, void* dh, float* de,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

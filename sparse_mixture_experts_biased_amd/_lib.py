@@ -17,7 +17,9 @@ MOE_SIGMOID, MOE_SOFTMAX = 0, 1
 
 EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size", "moe_permute",
             "moe_expert_capacity", "moe_permute_capacity", "moe_route_stats_workspace_size",
-            "moe_route_stats", "moe_router_diag",
+            "moe_route_stats", "moe_router_diag", "moe_transpose_experts",
+            "moe_combine_backward", "moe_grouped_swiglu_backward_workspace_size",
+            "moe_grouped_swiglu_backward", "moe_route_backward",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
             "moe_bias_update", "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -64,6 +66,13 @@ def load() -> ctypes.CDLL:
         "moe_route_stats": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
                             _i),
         "moe_router_diag": ([_i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
+        "moe_transpose_experts": ([_i, _i, _i, _p, _i, _p, _i, _i, _p], _i),
+        "moe_combine_backward": ([_i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _p], _i),
+        "moe_grouped_swiglu_backward_workspace_size": ([_i, _i, _i, _i], _sz),
+        "moe_grouped_swiglu_backward": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p,
+                                         _p, _p, _p, _p, _p, _sz, _p], _i),
+        "moe_route_backward": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p],
+                               _i),
         "moe_permute_capacity": ([_i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p],
                                  _i),
         "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
@@ -217,3 +226,38 @@ def moe_profile_report() -> dict:
         name, n, tot, mn, mx = line.split()
         out[name] = (int(n), float(tot), float(mn), float(mx))
     return out
+
+
+def moe_transpose_experts(n, rows, cols, src, dtype, dst, ld_dst, col_offset, stream=None):
+    _check(load().moe_transpose_experts(n, rows, cols, _ptr(src), dtype, _ptr(dst), ld_dst,
+                                        col_offset, _stream(stream)))
+
+
+def moe_combine_backward(T, d_model, K, dy, y_perm, slot_row, gates, dtype, dy_perm, dgates,
+                         stream=None):
+    _check(load().moe_combine_backward(T, d_model, K, _ptr(dy), _ptr(y_perm), _ptr(slot_row),
+                                       _ptr(gates), dtype, _ptr(dy_perm), _ptr(dgates),
+                                       _stream(stream)))
+
+
+def moe_grouped_swiglu_backward_workspace_size(n_groups, d_model, d_ffn, rows) -> int:
+    return int(load().moe_grouped_swiglu_backward_workspace_size(n_groups, d_model, d_ffn, rows))
+
+
+def moe_grouped_swiglu_backward(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x,
+                                dtype, w_gate, w_up, w_gu_t, w_down_t, dy, dx, dw_gate, dw_up,
+                                dw_down, workspace, workspace_bytes, stream=None):
+    _check(load().moe_grouped_swiglu_backward(
+        n_groups, d_model, d_ffn, rows, x_rows, _ptr(offsets), _ptr(row_index), _ptr(x), dtype,
+        _ptr(w_gate), _ptr(w_up), _ptr(w_gu_t), _ptr(w_down_t), _ptr(dy), _ptr(dx),
+        _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def moe_route_backward(T, d_model, E_r, K, fn, h, h_dtype, e, topk_idx, dgates, offsets,
+                       row_token, dz, dh, de, stream=None):
+    _check(load().moe_route_backward(T, d_model, E_r, K, fn, _ptr(h), h_dtype, _ptr(e),
+                                     _ptr(topk_idx), _ptr(dgates), _ptr(offsets),
+                                     _ptr(row_token), _ptr(dz), _ptr(dh), _ptr(de),
+                                     _stream(stream)))
+

@@ -406,3 +406,116 @@ size_t swiglu_workspace_bytes(int n_groups, int d_model, int d_ffn, int rows, in
   return swiglu_layout(nullptr, n_groups, d_ffn, rows, bf16 ? 2 : 4, 32).bytes;
 }
 }  // namespace moe
+
+// ---------------------------------------------------------------- backward
+
+moe_status moe_transpose_experts(int n, int rows, int cols, const void* src, moe_dtype dtype,
+                                 void* dst, int ld_dst, int col_offset, void* stream) {
+  if (n < 1 || rows < 1 || cols < 1 || col_offset < 0 || ld_dst < rows + col_offset)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_transpose_experts: n=%d rows=%d cols=%d ld_dst=%d col_offset=%d", n, rows,
+                cols, ld_dst, col_offset);
+  if (n > 65535) return fail(MOE_ERR_UNSUPPORTED, "moe_transpose_experts: n=%d > 65535", n);
+  if (dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_transpose_experts: bf16 only");
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "moe_transpose_experts: null pointer");
+  return hip_status(moe::launch_transpose_experts(n, rows, cols, static_cast<const uint16_t*>(src),
+                                                  static_cast<uint16_t*>(dst), ld_dst, col_offset,
+                                                  as_stream(stream)),
+                    "moe_transpose_experts");
+}
+
+moe_status moe_combine_backward(int T, int d_model, int K, const void* dy, const void* y_perm,
+                                const int32_t* slot_row, const float* gates, moe_dtype dtype,
+                                void* dy_perm, float* dgates, void* stream) {
+  if (T < 1 || d_model < 1 || K < 1 || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_backward: T=%d d_model=%d K=%d", T, d_model, K);
+  if (static_cast<long long>(T) * K > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_backward: T*K overflows int32");
+  if (dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_combine_backward: bf16 only");
+  if (!dy || !y_perm || !slot_row || !gates || !dy_perm || !dgates)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_backward: null pointer");
+  return hip_status(moe::launch_combine_backward(T, d_model, K, static_cast<const uint16_t*>(dy),
+                                                 static_cast<const uint16_t*>(y_perm), slot_row,
+                                                 gates, static_cast<uint16_t*>(dy_perm), dgates,
+                                                 as_stream(stream)),
+                    "moe_combine_backward");
+}
+
+size_t moe_grouped_swiglu_backward_workspace_size(int n_groups, int d_model, int d_ffn,
+                                                  int rows) {
+  if (n_groups < 1 || d_model < 1 || d_ffn < 1 || rows < 0) return 0;
+  return moe::bwd_workspace_bytes(n_groups, d_model, d_ffn, rows);
+}
+
+moe_status moe_grouped_swiglu_backward(int n_groups, int d_model, int d_ffn, int rows,
+                                       int x_rows, const int32_t* offsets,
+                                       const int32_t* row_index, const void* x, moe_dtype dtype,
+                                       const void* w_gate, const void* w_up, const void* w_gu_t,
+                                       const void* w_down_t, const void* dy, void* dx,
+                                       void* dw_gate, void* dw_up, void* dw_down,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_grouped_swiglu_backward";
+  if (n_groups < 1 || d_model < 1 || d_ffn < 1 || rows < 0 || x_rows < 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: n_groups=%d d_model=%d d_ffn=%d rows=%d x_rows=%d", fn,
+                n_groups, d_model, d_ffn, rows, x_rows);
+  if (n_groups > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_groups=%d > %d", fn, n_groups, MOE_MAX_EXPERTS);
+  if (dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (d_model % 64 != 0 || d_ffn % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d_model and d_ffn must be multiples of 64", fn);
+  if (!offsets || !x || !w_gate || !w_up || !w_gu_t || !w_down_t || !dy || !dx || !dw_gate ||
+      !dw_up || !dw_down || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (row_index == nullptr && x_rows < rows)
+    return fail(MOE_ERR_INVALID_ARG, "%s: x_rows=%d < rows=%d without row_index", fn, x_rows,
+                rows);
+  const size_t need = moe::bwd_workspace_bytes(n_groups, d_model, d_ffn, rows);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  // every operand the kernels address through one buffer descriptor stays under
+  // 2 GiB; one expert's transposed block holds at most d_model x (rows + 64)
+  const long long two_gib = 1LL << 31;
+  const long long mx = std::max(d_model, d_ffn);
+  if (static_cast<long long>(rows) * 2 * d_ffn * 2 >= two_gib ||
+      static_cast<long long>(rows) * d_model * 2 >= two_gib ||
+      static_cast<long long>(x_rows) * d_model * 2 >= two_gib ||
+      static_cast<long long>(d_model) * 2 * d_ffn * 2 >= two_gib ||
+      mx * (static_cast<long long>(rows) + 64) * 2 >= two_gib)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: an operand is 2 GiB or larger", fn);
+  if (rows == 0) return MOE_OK;
+  return hip_status(
+      moe::launch_swiglu_backward(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index,
+                                  static_cast<const uint16_t*>(x),
+                                  static_cast<const uint16_t*>(w_gate),
+                                  static_cast<const uint16_t*>(w_up),
+                                  static_cast<const uint16_t*>(w_gu_t),
+                                  static_cast<const uint16_t*>(w_down_t),
+                                  static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dx),
+                                  static_cast<uint16_t*>(dw_gate), static_cast<uint16_t*>(dw_up),
+                                  static_cast<uint16_t*>(dw_down), workspace, as_stream(stream)),
+      fn);
+}
+
+moe_status moe_route_backward(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
+                              moe_dtype h_dtype, const float* e, const int32_t* topk_idx,
+                              const float* dgates, const int32_t* offsets,
+                              const int32_t* row_token, float* dz, void* dh, float* de,
+                              void* stream) {
+  const char* nm = "moe_route_backward";
+  if (T < 1 || d_model < 1 || E_r < 1 || K < 1 || K > E_r || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T=%d d_model=%d E_r=%d K=%d", nm, T, d_model, E_r, K);
+  if (E_r > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "%s: E_r=%d", nm, E_r);
+  if (fn != MOE_SIGMOID && fn != MOE_SOFTMAX)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown score function %d", nm, (int)fn);
+  if (h_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 tokens only", nm);
+  if (!h || !e || !topk_idx || !dgates || !offsets || !row_token || !dz || !dh || !de)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", nm);
+  if (static_cast<long long>(T) * K > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T*K overflows int32", nm);
+  return hip_status(moe::launch_route_backward(T, d_model, E_r, K, (int)fn,
+                                               static_cast<const uint16_t*>(h), e, topk_idx,
+                                               dgates, offsets, row_token, dz,
+                                               static_cast<uint16_t*>(dh), de, as_stream(stream)),
+                    nm);
+}
+

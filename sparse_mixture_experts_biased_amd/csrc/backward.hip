@@ -1,0 +1,625 @@
+// Backward pass of the layer (bf16 operands, fp32 accumulation).
+//
+// Method: the chain rule applied to the layer-output, SwiGLU, gate and score
+// equations of the Sparse MoE routing-math page (arman1o1.github.io),
+// sections 0 and 2, with the routing decisions of the forward pass fixed.
+// With a = x W_gate^T, u = x W_up^T, act = SiLU(a) u, per expert:
+//   d act = dy W_down;  da = d act * u * SiLU'(a);  du = d act * SiLU(a)
+//   dx = da W_gate + du W_up
+//   dW_down = dy^T act;  dW_gate = da^T x;  dW_up = du^T x
+// SiLU'(a) = sigma(a) (1 + a (1 - sigma(a))).  The gate gradient reaches the
+// router only through the unbiased scores s (section 2: the bias picks, it
+// gets no gradient).
+//
+// Every product is an "NT" grouped GEMM (both operands K-contiguous) on
+// v_mfma_f32_32x32x16_bf16: transposed weight copies W_down^T [f, d] and
+// [W_gate^T | W_up^T] [d, 2f] (built once per weight update) serve the
+// activation gradients, and per-expert transposed activations (each expert's
+// rows padded to a multiple of 64 and laid out as its own [C, rows] block)
+// serve the weight gradients, whose K is the expert's row count.
+#include "swiglu_tiles.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;  // tile
+constexpr int kThreads = 256;                   // 4 waves, 2 x 2, 64 x 64 each
+constexpr int kRowBytes = kBK * 2;
+constexpr int kStage = (kBM + kBN) * kRowBytes;  // 32 KB
+constexpr int kBufferFlags = 0x00020000;
+constexpr uint32_t kOff = 0x80000000u;          // beyond every buffer (< 2 GiB)
+constexpr int kPad = 64;                         // expert rows padded to this in the
+                                                 // transposed layouts
+
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * kRowBytes + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+enum { kModeRows = 0, kModeKvar = 1 };
+enum { kEpiStore = 0, kEpiSwigluBwd = 1 };
+
+struct GemmArgs {
+  int M, N, K;             // Rows: N, K used (rows from the tile list); Kvar: M, N
+  int NT, MT;              // column / row tiles per group
+  int n_groups;
+  const TileInfo* tiles;   // Rows
+  const int32_t* meta;     // Rows: meta[0] = tiles
+  const int32_t* kpad;     // Kvar: padded row offsets [n_groups + 1]
+  const int32_t* row_index;  // Rows: A row gather (NULL: grouped row itself)
+  int a_rows;              // Rows: rows of A (bound of the gather)
+  const uint16_t* A;       // Rows: [a_rows, lda]; Kvar: per-group blocks [M, mpad]
+  int lda;
+  const uint16_t* B;       // Rows: per-group [N, ldb] at B + g * b_stride; Kvar: blocks [N, mpad]
+  int ldb;
+  size_t b_stride;
+  uint16_t* C;             // Rows: [rows, ldc]; Kvar: per group [M, ldc] at C + g * c_stride
+  int ldc;
+  size_t c_stride;
+  const uint16_t* aux;     // SwigluBwd: [rows, 2f] holding a | u
+  int f;
+};
+
+// C = A B^T over one 128 x 128 tile; K in 64-wide slices, one register set of
+// global loads in flight while the previous slice is multiplied out of LDS.
+template <int MODE, int EPI>
+__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  const int lc = tid & 7, lr = tid >> 3;  // 32 rows per load pass
+
+  int g, m0, nrows, n0, kbeg, nk;
+  if (MODE == kModeRows) {
+    const int w = blockIdx.x;
+    if (w >= p.meta[0] * p.NT) return;
+    const TileInfo ti = p.tiles[w / p.NT];
+    g = ti.group;
+    m0 = ti.m0;
+    nrows = min(ti.m1 - ti.m0, kBM);
+    n0 = (w % p.NT) * kBN;
+    kbeg = 0;
+    nk = p.K / kBK;
+  } else {
+    const int w = blockIdx.x;
+    if (w >= p.n_groups * p.MT * p.NT) return;
+    g = w / (p.MT * p.NT);
+    const int rem = w % (p.MT * p.NT);
+    m0 = (rem / p.NT) * kBM;
+    nrows = min(p.M - m0, kBM);
+    n0 = (rem % p.NT) * kBN;
+    kbeg = p.kpad[g];
+    nk = (p.kpad[g + 1] - kbeg) / kBK;
+  }
+
+  // ---- operand sources
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  uint32_t a_off[4], b_off[4];
+  if (MODE == kModeRows) {
+    rsA = rsrc(p.A, static_cast<uint32_t>(p.a_rows) * p.lda * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lr + 32 * i;
+      int sr = -1;
+      if (r < nrows) {
+        sr = p.row_index ? p.row_index[m0 + r] : m0 + r;
+        if (sr < 0 || sr >= p.a_rows) sr = -1;
+      }
+      a_off[i] = sr >= 0 ? (static_cast<uint32_t>(sr) * p.lda + lc * 8) * 2u : kOff;
+    }
+    rsB = rsrc(p.B + static_cast<size_t>(g) * p.b_stride,
+               static_cast<uint32_t>(p.N) * p.ldb * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + lr + 32 * i;
+      b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * p.ldb + lc * 8) * 2u : kOff;
+    }
+  } else {
+    const int mpad = p.kpad[g + 1] - kbeg;
+    rsA = rsrc(p.A + static_cast<size_t>(kbeg) * p.M, static_cast<uint32_t>(p.M) * mpad * 2u);
+    rsB = rsrc(p.B + static_cast<size_t>(kbeg) * p.N, static_cast<uint32_t>(p.N) * mpad * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + lr + 32 * i;
+      const int n = n0 + lr + 32 * i;
+      a_off[i] = m < p.M ? (static_cast<uint32_t>(m) * mpad + lc * 8) * 2u : kOff;
+      b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * mpad + lc * 8) * 2u : kOff;
+    }
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
+
+  uint4 sa[4], sb[4];
+  auto load = [&](int kt) {
+    const uint32_t kb = static_cast<uint32_t>(kt) * kBK * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0));
+      sb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, b_off[i], kb, 0));
+    }
+  };
+  auto store = [&](int stage) {
+    char* as = smem + stage * kStage;
+    char* bs = as + kBM * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(as + swz(lr + 32 * i, lc)) = sa[i];
+      *reinterpret_cast<uint4*>(bs + swz(lr + 32 * i, lc)) = sb[i];
+    }
+  };
+  const int fr = lane & 31, fh = lane >> 5;
+  const bool busy = wm * 64 < nrows;
+  auto compute = [&](int stage) {
+    if (!busy) return;
+    const char* as = smem + stage * kStage;
+    const char* bs = as + kBM * kRowBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = kk * 2 + fh;
+      bf16x8_t af[2], bq[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        af[x] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + x * 32 + fr, c));
+        bq[x] = *reinterpret_cast<const bf16x8_t*>(bs + swz(wn * 64 + x * 32 + fr, c));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bq[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  if (nk > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) load(kt + 1);
+      compute(kt & 1);
+      if (kt + 1 < nk) store((kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: D[row][col] of a 32x32 block is in lane col + 32*((row/4)%2),
+  // register (row%4) + 4*(row/8)
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = wm * 64 + a * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
+      if (row >= nrows) continue;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int col = n0 + wn * 64 + b * 32 + fr;
+        if (col >= p.N) continue;
+        const float v = acc[a][b][q];
+        if (MODE == kModeRows) {
+          const size_t r = static_cast<size_t>(m0 + row);
+          if (EPI == kEpiSwigluBwd) {
+            const float av = bf16_to_f32(p.aux[r * (2 * p.f) + col]);
+            const float uv = bf16_to_f32(p.aux[r * (2 * p.f) + p.f + col]);
+            const float sg = sigm(av);
+            p.C[r * p.ldc + col] = f32_to_bf16(v * uv * sg * (1.0f + av * (1.0f - sg)));
+            p.C[r * p.ldc + p.f + col] = f32_to_bf16(v * av * sg);
+          } else {
+            p.C[r * p.ldc + col] = f32_to_bf16(v);
+          }
+        } else {
+          p.C[static_cast<size_t>(g) * p.c_stride + static_cast<size_t>(m0 + row) * p.ldc + col] =
+              f32_to_bf16(v);
+        }
+      }
+    }
+}
+
+// kpad[g] = sum over groups before g of their rows rounded up to kPad.
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(int n_groups, int rows,
+                                                           const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ kpad) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry_s;
+  if (threadIdx.x == 0) carry_s = 0;
+  __syncthreads();
+  for (int g0 = 0; g0 < n_groups; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int m = 0;
+    if (g < n_groups) {
+      const int lo = min(max(offsets[g], 0), rows);
+      const int hi = min(max(offsets[g + 1], lo), rows);
+      m = (hi - lo + kPad - 1) / kPad * kPad;
+    }
+    part[threadIdx.x] = m;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = threadIdx.x >= static_cast<unsigned>(off) ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const int carry = carry_s;
+    if (g < n_groups) kpad[g] = carry + part[threadIdx.x] - m;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry_s = carry + part[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) kpad[n_groups] = carry_s;
+}
+
+enum { kTrCopy = 0, kTrAct = 1 };
+
+// Transposes the rows of one row tile (<= 128 grouped rows of one expert) and
+// 64 source columns into the expert's [C, mpad] block: dst column = the row's
+// position inside its expert.  The expert's last tile also writes the zero
+// padding columns.  kTrAct: the source value is SiLU(a) * u from src = [a | u]
+// (ld 2C).  Grid (tiles, C / 64), 256 threads.
+template <int TR>
+__global__ __launch_bounds__(256) void pad_transpose_kernel(
+    int C, int rows, int src_rows, const TileInfo* __restrict__ tiles,
+    const int32_t* __restrict__ meta, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ kpad, const int32_t* __restrict__ row_index,
+    const uint16_t* __restrict__ src, int ld_src, uint16_t* __restrict__ dst) {
+  __shared__ uint16_t t[64][kBM + 2];
+  if (static_cast<int>(blockIdx.x) >= meta[0]) return;
+  const TileInfo ti = tiles[blockIdx.x];
+  const int g = ti.group;
+  const int m0 = ti.m0;
+  const int nr = min(ti.m1 - ti.m0, kBM);
+  const int c0 = blockIdx.y * 64;
+  const int gstart = offsets[g];
+  const int mpad = kpad[g + 1] - kpad[g];
+  uint16_t* blk = dst + static_cast<size_t>(kpad[g]) * C;  // [C, mpad]
+  // load: rows m0..m0+nr, columns c0..c0+63
+  for (int q = threadIdx.x; q < kBM * 64; q += 256) {
+    const int r = q / 64, c = q % 64;
+    uint16_t v = 0;
+    if (r < nr && c0 + c < C) {
+      const int gr = m0 + r;
+      int sr = row_index ? row_index[gr] : gr;
+      if (sr >= 0 && sr < src_rows) {
+        if (TR == kTrAct) {
+          const float a = bf16_to_f32(src[static_cast<size_t>(sr) * ld_src + c0 + c]);
+          const float u = bf16_to_f32(src[static_cast<size_t>(sr) * ld_src + C + c0 + c]);
+          v = f32_to_bf16(silu(a) * u);
+        } else {
+          v = src[static_cast<size_t>(sr) * ld_src + c0 + c];
+        }
+      }
+    }
+    t[c][r] = v;
+  }
+  __syncthreads();
+  const int p0 = m0 - gstart;  // first column of this tile inside the expert block
+  const bool last = ti.m1 - m0 <= kBM;
+  const int width = last ? mpad - p0 : nr;  // the last tile also writes the padding
+  for (int q = threadIdx.x; q < 64 * width; q += 256) {
+    const int c = q / width, r = q % width;
+    if (c0 + c >= C) continue;
+    blk[static_cast<size_t>(c0 + c) * mpad + p0 + r] = r < nr ? t[c][r] : 0;
+  }
+}
+
+// Combine backward, one wave per token: dy_perm[slot] = g * dy_t (output
+// dtype), dgates = <dy_t, y_perm[slot]> in fp32 (0 for a dropped copy).
+__global__ __launch_bounds__(256) void combine_bwd_kernel(int T, int d, int K, int TK,
+                                                          const uint16_t* __restrict__ dy,
+                                                          const uint16_t* __restrict__ yp,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ gates,
+                                                          uint16_t* __restrict__ dyp,
+                                                          float* __restrict__ dg) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (t >= T) return;
+  const uint16_t* dyt = dy + static_cast<size_t>(t) * d;
+  for (int k = 0; k < K; ++k) {
+    const int s = slot_row[static_cast<size_t>(t) * K + k];
+    if (s < 0 || s >= TK) {
+      if (lane == 0) dg[static_cast<size_t>(t) * K + k] = 0.0f;
+      continue;
+    }
+    const float gk = gates[static_cast<size_t>(t) * K + k];
+    const uint16_t* ys = yp + static_cast<size_t>(s) * d;
+    uint16_t* out = dyp + static_cast<size_t>(s) * d;
+    float dot = 0.0f;
+    for (int c = lane; c < d; c += kWave) {
+      const float v = bf16_to_f32(dyt[c]);
+      dot += v * bf16_to_f32(ys[c]);
+      out[c] = f32_to_bf16(gk * v);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+    if (lane == 0) dg[static_cast<size_t>(t) * K + k] = dot;
+  }
+}
+
+// Router backward, one wave per token: logits of the K picks, dz, and
+// dh_t += sum_k dz_k e_k (dh in the tokens' dtype).
+__global__ __launch_bounds__(256) void route_bwd_token_kernel(
+    int T, int d, int E, int K, int fn, const uint16_t* __restrict__ h, const float* __restrict__ e,
+    const int32_t* __restrict__ idx, const float* __restrict__ dg, float* __restrict__ dz_out,
+    uint16_t* __restrict__ dh) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (t >= T) return;
+  const uint16_t* ht = h + static_cast<size_t>(t) * d;
+  float z[MOE_MAX_TOPK_DEV], w[MOE_MAX_TOPK_DEV], dgk[MOE_MAX_TOPK_DEV];
+  int id[MOE_MAX_TOPK_DEV];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    z[k] = 0.0f;
+    id[k] = -1;
+    dgk[k] = 0.0f;
+    if (k < K) {
+      int i = idx[static_cast<size_t>(t) * K + k];
+      if (i < 0 || i >= E) continue;
+      id[k] = i;
+      dgk[k] = dg[static_cast<size_t>(t) * K + k];
+      const float* ei = e + static_cast<size_t>(i) * d;
+      float acc = 0.0f;
+      for (int c = lane; c < d; c += kWave) acc += bf16_to_f32(ht[c]) * ei[c];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+      z[k] = acc;
+    }
+  }
+  // g over the picks and dz (wave-uniform scalars)
+  float gsum = 0.0f, zmax = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (id[k] >= 0) zmax = fmaxf(zmax, z[k]);
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    w[k] = 0.0f;
+    if (id[k] >= 0) w[k] = fn == 0 ? sigm(z[k]) : __expf(z[k] - zmax);
+    gsum += w[k];
+  }
+  gsum = fmaxf(gsum, 1e-12f);
+  float gdg = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) gdg += (w[k] / gsum) * dgk[k];
+  float dz[MOE_MAX_TOPK_DEV];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    dz[k] = 0.0f;
+    if (id[k] < 0) continue;
+    const float gk = w[k] / gsum;
+    dz[k] = fn == 0 ? (dgk[k] - gdg) / gsum * w[k] * (1.0f - w[k]) : gk * (dgk[k] - gdg);
+  }
+  if (lane < K) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (k == lane) v = dz[k];
+    dz_out[static_cast<size_t>(t) * K + lane] = v;
+  }
+  uint16_t* dht = dh + static_cast<size_t>(t) * d;
+  for (int c = lane; c < d; c += kWave) {
+    float acc = bf16_to_f32(dht[c]);
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (id[k] >= 0) acc += dz[k] * e[static_cast<size_t>(id[k]) * d + c];
+    dht[c] = f32_to_bf16(acc);
+  }
+}
+
+// de_i = sum over expert i's copies (uncapped dispatch, ascending token) of
+// dz * h_t; one workgroup per expert, fixed order: deterministic.
+__global__ __launch_bounds__(256) void route_bwd_de_kernel(int T, int d, int E, int K,
+                                                           const uint16_t* __restrict__ h,
+                                                           const int32_t* __restrict__ idx,
+                                                           const float* __restrict__ dz,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ row_token,
+                                                           float* __restrict__ de) {
+  const int i = blockIdx.x;
+  const int lo = offsets[i], hi = offsets[i + 1];
+  for (int c0 = threadIdx.x; c0 < d; c0 += 256) {
+    float acc = 0.0f;
+    for (int r = lo; r < hi; ++r) {
+      const int t = row_token[r];
+      if (t < 0 || t >= T) continue;
+      float w = 0.0f;
+      for (int k = 0; k < K; ++k)
+        if (idx[static_cast<size_t>(t) * K + k] == i) w = dz[static_cast<size_t>(t) * K + k];
+      acc += w * bf16_to_f32(h[static_cast<size_t>(t) * d + c0]);
+    }
+    de[static_cast<size_t>(i) * d + c0] = acc;
+  }
+}
+
+// out[n][c][ld * ? ] : dst[e * cols * ld + c * ld + col_off + r] = src[e][r][c]
+__global__ __launch_bounds__(256) void transpose_experts_kernel(int rows, int cols,
+                                                                const uint16_t* __restrict__ src,
+                                                                uint16_t* __restrict__ dst, int ld,
+                                                                int col_off) {
+  __shared__ uint16_t t[64][65];
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const uint16_t* s = src + static_cast<size_t>(e) * rows * cols;
+  uint16_t* o = dst + static_cast<size_t>(e) * cols * ld;
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int r = q / 64, c = q % 64;
+    t[c][r] = (r0 + r < rows && c0 + c < cols) ? s[static_cast<size_t>(r0 + r) * cols + c0 + c] : 0;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * 64; q += 256) {
+    const int c = q / 64, r = q % 64;
+    if (r0 + r < rows && c0 + c < cols)
+      o[static_cast<size_t>(c0 + c) * ld + col_off + r0 + r] = t[c][r];
+  }
+}
+
+template <int MODE, int EPI>
+hipError_t gemm(const GemmArgs& a, unsigned blocks, hipStream_t s) {
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, EPI>), dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- workspace
+
+BwdWorkspace bwd_layout(void* base, int n_groups, int d, int f, int rows) {
+  BwdWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    size_t at = off;
+    off = align_up(off + n, 256);
+    return base ? static_cast<char*>(base) + at : nullptr;
+  };
+  const size_t rpad = static_cast<size_t>(rows) + static_cast<size_t>(kPad) * n_groups;
+  w.tiles.tiles = reinterpret_cast<TileInfo*>(
+      take(static_cast<size_t>(max_tiles_for(rows, n_groups, kBM)) * sizeof(TileInfo)));
+  w.tiles.group_tile_start = reinterpret_cast<int32_t*>(take((n_groups + 1) * sizeof(int32_t)));
+  w.tiles.meta = reinterpret_cast<int32_t*>(take(4 * sizeof(int32_t)));
+  w.kpad = reinterpret_cast<int32_t*>(take((n_groups + 1) * sizeof(int32_t)));
+  w.au = reinterpret_cast<uint16_t*>(take(static_cast<size_t>(rows) * 2 * f * 2));
+  w.dadu = reinterpret_cast<uint16_t*>(take(static_cast<size_t>(rows) * 2 * f * 2));
+  w.xT = reinterpret_cast<uint16_t*>(take(rpad * d * 2));
+  w.dyT = reinterpret_cast<uint16_t*>(take(rpad * d * 2));
+  w.actT = reinterpret_cast<uint16_t*>(take(rpad * f * 2));
+  w.daT = reinterpret_cast<uint16_t*>(take(rpad * f * 2));
+  w.duT = reinterpret_cast<uint16_t*>(take(rpad * f * 2));
+  w.bytes = off;
+  return w;
+}
+
+size_t bwd_workspace_bytes(int n_groups, int d, int f, int rows) {
+  return bwd_layout(nullptr, n_groups, d, f, rows).bytes;
+}
+
+size_t bwd_rpad_max(int n_groups, int rows) {
+  return static_cast<size_t>(rows) + static_cast<size_t>(kPad) * n_groups;
+}
+
+hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_rows,
+                                  const int32_t* offsets, const int32_t* row_index,
+                                  const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                                  const uint16_t* wgu_t, const uint16_t* wd_t,
+                                  const uint16_t* dy, uint16_t* dx, uint16_t* dwg,
+                                  uint16_t* dwu, uint16_t* dwd, void* ws, hipStream_t s) {
+  BwdWorkspace w = bwd_layout(ws, n_groups, d, f, rows);
+  SwigluWorkspace tl{};
+  tl.tiles = w.tiles.tiles;
+  tl.group_tile_start = w.tiles.group_tile_start;
+  tl.meta = w.tiles.meta;
+  hipError_t err = launch_build_tiles(n_groups, rows, kBM, offsets, tl, s);
+  if (err != hipSuccess) return err;
+  const int max_tiles = max_tiles_for(rows, n_groups, kBM);
+  ProfScope prof_(s, "swiglu_backward");
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, n_groups, rows, offsets,
+                     w.kpad);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  GemmArgs a{};
+  a.tiles = tl.tiles;
+  a.meta = tl.meta;
+  a.n_groups = n_groups;
+  a.row_index = row_index;
+  a.a_rows = x_rows;
+  // 1. a = x W_gate^T, u = x W_up^T  -> au [rows, 2f]
+  a.N = f; a.K = d; a.NT = (f + kBN - 1) / kBN;
+  a.A = x; a.lda = d;
+  a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
+  a.ldc = 2 * f;
+  a.B = wg; a.C = w.au;
+  if ((err = gemm<kModeRows, kEpiStore>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  a.B = wu; a.C = w.au + f;
+  if ((err = gemm<kModeRows, kEpiStore>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  // 2. d act = dy W_down (B = W_down^T [f, d]) -> da, du into dadu [rows, 2f]
+  a.row_index = nullptr; a.a_rows = rows;
+  a.A = dy; a.lda = d;
+  a.B = wd_t; a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
+  a.C = w.dadu; a.ldc = 2 * f; a.aux = w.au; a.f = f;
+  if ((err = gemm<kModeRows, kEpiSwigluBwd>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  // 3. dx = [da | du] [W_gate^T | W_up^T]^T  (K = 2f, B = [d, 2f]) -> dx [rows, d]
+  a.N = d; a.K = 2 * f; a.NT = (d + kBN - 1) / kBN;
+  a.A = w.dadu; a.lda = 2 * f;
+  a.B = wgu_t; a.ldb = 2 * f; a.b_stride = static_cast<size_t>(d) * 2 * f;
+  a.C = dx; a.ldc = d;
+  if ((err = gemm<kModeRows, kEpiStore>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  // 4. per-expert transposed activations (rows padded to 64 per expert)
+  {
+    dim3 gd(max_tiles, (d + 63) / 64), gf(max_tiles, (f + 63) / 64);
+    hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gd, dim3(256), 0, s, d, rows, x_rows,
+                       tl.tiles, tl.meta, offsets, w.kpad, row_index, x, d, w.xT);
+    hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gd, dim3(256), 0, s, d, rows, rows,
+                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, dy, d, w.dyT);
+    hipLaunchKernelGGL(pad_transpose_kernel<kTrAct>, gf, dim3(256), 0, s, f, rows, rows,
+                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.au, 2 * f, w.actT);
+    hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gf, dim3(256), 0, s, f, rows, rows,
+                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.dadu, 2 * f, w.daT);
+    hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gf, dim3(256), 0, s, f, rows, rows,
+                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.dadu + f, 2 * f, w.duT);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  // 5. weight gradients, K = the expert's (padded) rows
+  GemmArgs k{};
+  k.n_groups = n_groups;
+  k.kpad = w.kpad;
+  //    dW_gate [f, d] = da^T x ; dW_up = du^T x
+  k.M = f; k.N = d; k.MT = (f + kBM - 1) / kBM; k.NT = (d + kBN - 1) / kBN;
+  k.B = w.xT; k.ldc = d; k.c_stride = static_cast<size_t>(f) * d;
+  const unsigned gb = static_cast<unsigned>(n_groups) * k.MT * k.NT;
+  k.A = w.daT; k.C = dwg;
+  if ((err = gemm<kModeKvar, kEpiStore>(k, gb, s)) != hipSuccess) return err;
+  k.A = w.duT; k.C = dwu;
+  if ((err = gemm<kModeKvar, kEpiStore>(k, gb, s)) != hipSuccess) return err;
+  //    dW_down [d, f] = dy^T act
+  k.M = d; k.N = f; k.MT = (d + kBM - 1) / kBM; k.NT = (f + kBN - 1) / kBN;
+  k.A = w.dyT; k.B = w.actT; k.C = dwd; k.ldc = f; k.c_stride = static_cast<size_t>(d) * f;
+  return gemm<kModeKvar, kEpiStore>(k, static_cast<unsigned>(n_groups) * k.MT * k.NT, s);
+}
+
+hipError_t launch_combine_backward(int T, int d, int K, const uint16_t* dy, const uint16_t* yp,
+                                   const int32_t* slot_row, const float* gates, uint16_t* dyp,
+                                   float* dg, hipStream_t s) {
+  ProfScope prof_(s, "combine_backward");
+  hipLaunchKernelGGL(combine_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, d, K, T * K, dy,
+                     yp, slot_row, gates, dyp, dg);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_backward(int T, int d, int E, int K, int fn, const uint16_t* h,
+                                 const float* e, const int32_t* idx, const float* dg,
+                                 const int32_t* offsets, const int32_t* row_token, float* dz,
+                                 uint16_t* dh, float* de, hipStream_t s) {
+  ProfScope prof_(s, "route_backward");
+  hipLaunchKernelGGL(route_bwd_token_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, d, E, K, fn,
+                     h, e, idx, dg, dz, dh);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_bwd_de_kernel, dim3(E), dim3(256), 0, s, T, d, E, K, h, idx, dz,
+                     offsets, row_token, de);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_experts(int n, int rows, int cols, const uint16_t* src,
+                                    uint16_t* dst, int ld, int col_off, hipStream_t s) {
+  dim3 grid((cols + 63) / 64, (rows + 63) / 64, n);
+  hipLaunchKernelGGL(transpose_experts_kernel, grid, dim3(256), 0, s, rows, cols, src, dst, ld,
+                     col_off);
+  return hipGetLastError();
+}
+
+}  // namespace moe

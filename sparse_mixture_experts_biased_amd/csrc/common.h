@@ -13,8 +13,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// fp32 -> bf16, round to nearest even (quiet NaN kept quiet).
-// Round to nearest even; gfx950 converts in hardware (v_cvt_pk_bf16_f32).
+// fp32 -> bf16, round to nearest even; gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }

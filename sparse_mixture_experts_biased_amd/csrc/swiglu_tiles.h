@@ -49,6 +49,39 @@ inline SwigluWorkspace swiglu_layout(void* base, int n_groups, int d_ffn, int ro
   return w;
 }
 
+// Backward pass (backward.hip): scratch layout and launches (bf16 only).
+struct BwdWorkspace {
+  struct {
+    TileInfo* tiles;
+    int32_t* group_tile_start;
+    int32_t* meta;
+  } tiles;                  // 128-row tiles of the grouped rows
+  int32_t* kpad;            // [n_groups + 1] expert rows padded to 64, prefix sums
+  uint16_t* au;             // [rows, 2f]  a | u recomputed
+  uint16_t* dadu;           // [rows, 2f]  da | du
+  uint16_t *xT, *dyT;       // per-expert [d, mpad] blocks
+  uint16_t *actT, *daT, *duT;  // per-expert [f, mpad] blocks
+  size_t bytes;
+};
+BwdWorkspace bwd_layout(void* base, int n_groups, int d, int f, int rows);
+size_t bwd_workspace_bytes(int n_groups, int d, int f, int rows);
+size_t bwd_rpad_max(int n_groups, int rows);
+hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_rows,
+                                  const int32_t* offsets, const int32_t* row_index,
+                                  const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
+                                  const uint16_t* wgu_t, const uint16_t* wd_t,
+                                  const uint16_t* dy, uint16_t* dx, uint16_t* dwg,
+                                  uint16_t* dwu, uint16_t* dwd, void* ws, hipStream_t s);
+hipError_t launch_combine_backward(int T, int d, int K, const uint16_t* dy, const uint16_t* yp,
+                                   const int32_t* slot_row, const float* gates, uint16_t* dyp,
+                                   float* dg, hipStream_t s);
+hipError_t launch_route_backward(int T, int d, int E, int K, int fn, const uint16_t* h,
+                                 const float* e, const int32_t* idx, const float* dg,
+                                 const int32_t* offsets, const int32_t* row_token, float* dz,
+                                 uint16_t* dh, float* de, hipStream_t s);
+hipError_t launch_transpose_experts(int n, int rows, int cols, const uint16_t* src,
+                                    uint16_t* dst, int ld, int col_off, hipStream_t s);
+
 hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* offsets,
                               const SwigluWorkspace& w, hipStream_t s);
 

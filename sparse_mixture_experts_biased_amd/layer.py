@@ -167,6 +167,90 @@ class MoELayer:
             self.bias_update(b, gamma, stream)
         return self.y
 
+    # backward -----------------------------------------------------------
+    def prepare_backward(self, stream=None):
+        """Allocate the backward buffers and build the transposed weight copies
+        ([W_gate^T | W_up^T] and W_down^T); call again after the weights change."""
+        s = self.shape
+        if s.dtype != "bf16":
+            raise NotImplementedError("the backward pass runs on bf16 layers")
+        if s.E_s > 1:
+            raise NotImplementedError("the backward pass takes at most one shared expert")
+        dev = self.y.device
+        T, K, E, d, f = s.T, s.K, s.E_r, s.d_model, s.d_ffn
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+
+        def transposed(wg, wu, wd, n):
+            gu_t = torch.empty((n, d, 2 * f), **bf)
+            d_t = torch.empty((n, f, d), **bf)
+            L.moe_transpose_experts(n, f, d, wg, self.dt, gu_t, 2 * f, 0, stream)
+            L.moe_transpose_experts(n, f, d, wu, self.dt, gu_t, 2 * f, f, stream)
+            L.moe_transpose_experts(n, d, f, wd, self.dt, d_t, d, 0, stream)
+            return gu_t, d_t
+
+        self.w_gu_t, self.w_down_t = transposed(self.w_gate, self.w_up, self.w_down, E)
+        self.dy_perm = torch.zeros((T * K, d), **bf)
+        self.dx_perm = torch.zeros((T * K, d), **bf)
+        self.dgates = torch.empty((T, K), **f32)
+        self.dz = torch.empty((T, K), **f32)
+        self.dh = torch.empty((T, d), **bf)
+        self.de = torch.empty((E, d), **f32)
+        self.ones = torch.ones((T, K), **f32)
+        self.dw_gate = torch.empty_like(self.w_gate)
+        self.dw_up = torch.empty_like(self.w_up)
+        self.dw_down = torch.empty_like(self.w_down)
+        bw = L.moe_grouped_swiglu_backward_workspace_size(E, d, f, T * K)
+        if s.E_s:
+            self.ws_gu_t, self.ws_down_t = transposed(self.ws_gate, self.ws_up, self.ws_down,
+                                                      s.E_s)
+            self.dx_shared = torch.empty((T, d), **bf)
+            self.dws_gate = torch.empty_like(self.ws_gate)
+            self.dws_up = torch.empty_like(self.ws_up)
+            self.dws_down = torch.empty_like(self.ws_down)
+            bw = max(bw, L.moe_grouped_swiglu_backward_workspace_size(s.E_s, d, f, T))
+        else:
+            self.dx_shared = None
+        self.bw_ws_bytes = bw
+        self.bw_ws = torch.empty((bw,), dtype=torch.uint8, device=dev)
+        if self.capacity is not None:   # the router's gradient covers every pick
+            self.all_offsets = torch.empty((E + 1,), **i32)
+            self.all_row_token = torch.empty((T * K,), **i32)
+            self.all_slot_row = torch.empty((T * K,), **i32)
+
+    def backward(self, h, dy, stream=None):
+        """Gradients of sum_t <dy_t, y_t> after forward(h): dh, de and the
+        expert weight gradients (routed: dw_*, shared: dws_*), with the
+        forward's routing decisions fixed.  Requires prepare_backward()."""
+        s = self.shape
+        T, K, E, d, f = s.T, s.K, s.E_r, s.d_model, s.d_ffn
+        L.moe_combine_backward(T, d, K, dy, self.y_perm, self.slot_row, self.gates, self.dt,
+                               self.dy_perm, self.dgates, stream)
+        L.moe_grouped_swiglu_backward(E, d, f, T * K, T, self.offsets, self.row_token, h, self.dt,
+                                      self.w_gate, self.w_up, self.w_gu_t, self.w_down_t,
+                                      self.dy_perm, self.dx_perm, self.dw_gate, self.dw_up,
+                                      self.dw_down, self.bw_ws, self.bw_ws_bytes, stream)
+        if s.E_s:
+            L.moe_grouped_swiglu_backward(s.E_s, d, f, T, T, self.sh_offsets, self.sh_rows, h,
+                                          self.dt, self.ws_gate, self.ws_up, self.ws_gu_t,
+                                          self.ws_down_t, dy, self.dx_shared, self.dws_gate,
+                                          self.dws_up, self.dws_down, self.bw_ws,
+                                          self.bw_ws_bytes, stream)
+        # dh = dy + dx_shared + sum_k dx_perm[slot] (the combine with unit gates)
+        L.moe_combine(T, d, K, s.E_s, dy, self.dx_shared, self.dx_perm, self.slot_row,
+                      self.ones, self.dt, self.dh, stream)
+        if self.capacity is None:
+            offs, rtok = self.offsets, self.row_token
+        else:
+            L.moe_permute(T, d, E, K, self.topk_idx, None, self.dt, self.all_offsets,
+                          self.all_row_token, self.all_slot_row, None, self.perm_ws,
+                          self.perm_ws_bytes, stream)
+            offs, rtok = self.all_offsets, self.all_row_token
+        L.moe_route_backward(T, d, E, K, self.fn, h, self.dt, self.e, self.topk_idx,
+                             self.dgates, offs, rtok, self.dz, self.dh, self.de, stream)
+        return self.dh
+
     def stats_host(self):
         st = self.stats.cpu()
         return dict(max_load=int(st[0]), min_load=int(st[1]),

@@ -119,6 +119,30 @@ def test_route_stats_and_router_diag_arguments():
     assert ctypes.sizeof(L.MoeRouterDiag) == 32
 
 
+def test_backward_entry_points_reject_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    need = L.moe_grouped_swiglu_backward_workspace_size(8, 256, 512, 1000)
+    assert need >= 1000 * 4 * 512 * 2            # a|u and da|du at least
+    args = [8, 256, 512, 1000, 500, P, P, P, 1, P, P, P, P, P, P, P, P, P, P]
+    rc, msg = _st(lib.moe_grouped_swiglu_backward(*args, need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    bad = list(args); bad[8] = 0                   # fp32
+    assert lib.moe_grouped_swiglu_backward(*bad, need, None) == L.MOE_ERR_UNSUPPORTED
+    bad = list(args); bad[1] = 200                 # d_model % 64
+    assert lib.moe_grouped_swiglu_backward(*bad, need, None) == L.MOE_ERR_UNSUPPORTED
+    bad = list(args); bad[11] = None               # w_gu_t
+    assert lib.moe_grouped_swiglu_backward(*bad, need, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(10, 64, 2, P, P, P, P, 0, P, P, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_backward(10, 64, 2, P, P, P, P, 1, None, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(10, 64, 8, 9, 0, P, 1, P, P, P, P, P, P, P, P, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(10, 64, 8, 2, 0, P, 0, P, P, P, P, P, P, P, P, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_transpose_experts(2, 10, 20, P, 1, P, 9, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_transpose_experts(2, 10, 20, P, 0, P, 10, 0, None) == L.MOE_ERR_UNSUPPORTED
+
+
 def test_grouped_swiglu_rejects_bad_arguments():
     lib = L.load()
     P = ctypes.c_void_p(16)
