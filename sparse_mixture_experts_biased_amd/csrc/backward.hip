@@ -199,36 +199,69 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     }
   }
 
-  // ---- epilogue: D[row][col] of a 32x32 block is in lane col + 32*((row/4)%2),
-  // register (row%4) + 4*(row/8)
+  // ---- epilogue through LDS (both stages are free after the last barrier):
+  // the tile is staged as bf16 rows of 128 columns (16-byte chunk index XORed
+  // with row & 4, which separates the two half-waves) and written as whole
+  // 16-byte row chunks.  D[row][col] of a 32x32 block is in lane
+  // col + 32*((row/4)%2), register (row%4) + 4*(row/8).
+  constexpr int kORow = kBN * 2;                  // 256 B per staged row
+  char* o0 = smem;                                // [128][128] bf16
+  char* o1 = smem + kBM * kORow;                  // second tile (du) for kEpiSwigluBwd
+  auto opos = [&](int row, int col) {
+    return row * kORow + ((((col >> 3) ^ (row & 4))) << 4) + (col & 7) * 2;
+  };
+  const int rl = tid / 16, cl = tid % 16;          // read-out: 16 chunks per row, 16 rows per pass
+  const size_t cbase = MODE == kModeRows ? 0 : static_cast<size_t>(g) * p.c_stride;
+  if (EPI == kEpiSwigluBwd) {
+    // a | u of the tile's rows into the two staging tiles (16-byte loads)
+#pragma unroll
+    for (int it = 0; it < kBM / 16; ++it) {
+      const int row = it * 16 + rl;
+      uint4 av = make_uint4(0, 0, 0, 0), uv = av;
+      if (row < nrows && n0 + cl * 8 < p.N) {
+        const size_t r = static_cast<size_t>(m0 + row) * (2 * p.f);
+        av = *reinterpret_cast<const uint4*>(p.aux + r + n0 + cl * 8);
+        uv = *reinterpret_cast<const uint4*>(p.aux + r + p.f + n0 + cl * 8);
+      }
+      *reinterpret_cast<uint4*>(o0 + row * kORow + ((cl ^ (row & 4)) << 4)) = av;
+      *reinterpret_cast<uint4*>(o1 + row * kORow + ((cl ^ (row & 4)) << 4)) = uv;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = wm * 64 + a * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
-      if (row >= nrows) continue;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int col = n0 + wn * 64 + b * 32 + fr;
-        if (col >= p.N) continue;
+        const int col = wn * 64 + b * 32 + fr;
         const float v = acc[a][b][q];
-        if (MODE == kModeRows) {
-          const size_t r = static_cast<size_t>(m0 + row);
-          if (EPI == kEpiSwigluBwd) {
-            const float av = bf16_to_f32(p.aux[r * (2 * p.f) + col]);
-            const float uv = bf16_to_f32(p.aux[r * (2 * p.f) + p.f + col]);
-            const float sg = sigm(av);
-            p.C[r * p.ldc + col] = f32_to_bf16(v * uv * sg * (1.0f + av * (1.0f - sg)));
-            p.C[r * p.ldc + p.f + col] = f32_to_bf16(v * av * sg);
-          } else {
-            p.C[r * p.ldc + col] = f32_to_bf16(v);
-          }
+        uint16_t* p0 = reinterpret_cast<uint16_t*>(o0 + opos(row, col));
+        if (EPI == kEpiSwigluBwd) {
+          uint16_t* p1 = reinterpret_cast<uint16_t*>(o1 + opos(row, col));
+          const float av = bf16_to_f32(*p0), uv = bf16_to_f32(*p1);
+          const float sg = sigm(av);
+          *p0 = f32_to_bf16(v * uv * sg * (1.0f + av * (1.0f - sg)));
+          *p1 = f32_to_bf16(v * av * sg);
         } else {
-          p.C[static_cast<size_t>(g) * p.c_stride + static_cast<size_t>(m0 + row) * p.ldc + col] =
-              f32_to_bf16(v);
+          *p0 = f32_to_bf16(v);
         }
       }
     }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kBM / 16; ++it) {
+    const int row = it * 16 + rl;
+    if (row >= nrows || n0 + cl * 8 >= p.N) continue;
+    const size_t r = static_cast<size_t>(m0 + row);
+    const int sw = (cl ^ (row & 4)) << 4;
+    *reinterpret_cast<uint4*>(p.C + cbase + r * p.ldc + n0 + cl * 8) =
+        *reinterpret_cast<const uint4*>(o0 + row * kORow + sw);
+    if (EPI == kEpiSwigluBwd)
+      *reinterpret_cast<uint4*>(p.C + cbase + r * p.ldc + p.f + n0 + cl * 8) =
+          *reinterpret_cast<const uint4*>(o1 + row * kORow + sw);
+  }
 }
 
 // kpad[g] = sum over groups before g of their rows rounded up to kPad.
@@ -422,7 +455,9 @@ __global__ __launch_bounds__(256) void route_bwd_token_kernel(
 }
 
 // de_i = sum over expert i's copies (uncapped dispatch, ascending token) of
-// dz * h_t; one workgroup per expert, fixed order: deterministic.
+// dz * h_t; one workgroup per expert: the copies' weights dz are looked up
+// once into LDS, then each thread accumulates 8 columns of h rows (16-byte
+// loads) in the segment's order -- a fixed order, so deterministic.
 __global__ __launch_bounds__(256) void route_bwd_de_kernel(int T, int d, int E, int K,
                                                            const uint16_t* __restrict__ h,
                                                            const int32_t* __restrict__ idx,
@@ -430,19 +465,45 @@ __global__ __launch_bounds__(256) void route_bwd_de_kernel(int T, int d, int E, 
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ row_token,
                                                            float* __restrict__ de) {
+  constexpr int kRows = 512;                 // copies staged per pass
+  __shared__ float wr[kRows];
+  __shared__ int tr[kRows];
   const int i = blockIdx.x;
   const int lo = offsets[i], hi = offsets[i + 1];
-  for (int c0 = threadIdx.x; c0 < d; c0 += 256) {
-    float acc = 0.0f;
-    for (int r = lo; r < hi; ++r) {
-      const int t = row_token[r];
-      if (t < 0 || t >= T) continue;
-      float w = 0.0f;
-      for (int k = 0; k < K; ++k)
-        if (idx[static_cast<size_t>(t) * K + k] == i) w = dz[static_cast<size_t>(t) * K + k];
-      acc += w * bf16_to_f32(h[static_cast<size_t>(t) * d + c0]);
+  const int nv = d / 8;                      // 16-byte vectors per row
+  for (int v0 = 0; v0 < nv; v0 += 256) {
+    const int v = v0 + threadIdx.x;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r0 = lo; r0 < hi; r0 += kRows) {
+      const int n = min(kRows, hi - r0);
+      __syncthreads();
+      for (int q = threadIdx.x; q < n; q += 256) {
+        const int t = row_token[r0 + q];
+        float w = 0.0f;
+        if (t >= 0 && t < T)
+          for (int k = 0; k < K; ++k)
+            if (idx[static_cast<size_t>(t) * K + k] == i) w = dz[static_cast<size_t>(t) * K + k];
+        wr[q] = w;
+        tr[q] = (t >= 0 && t < T) ? t : -1;
+      }
+      __syncthreads();
+      if (v < nv)
+        for (int q = 0; q < n; ++q) {
+          if (tr[q] < 0) continue;
+          const uint4 hv = *reinterpret_cast<const uint4*>(h + static_cast<size_t>(tr[q]) * d + v * 8);
+          const uint32_t u[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[2 * c] += wr[q] * __uint_as_float(u[c] << 16);
+            acc[2 * c + 1] += wr[q] * __uint_as_float(u[c] & 0xffff0000u);
+          }
+        }
     }
-    de[static_cast<size_t>(i) * d + c0] = acc;
+    if (v < nv) {
+      float4* out = reinterpret_cast<float4*>(de + static_cast<size_t>(i) * d + v * 8);
+      out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
   }
 }
 
