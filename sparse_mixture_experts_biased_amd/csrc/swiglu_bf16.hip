@@ -322,7 +322,445 @@ void bf16_tile_kernel(
   }
 }
 
-// ---------------------------------------------------------------- streaming variant
+// ---------------------------------------------------------------- streaming kernel
+//
+// One workgroup per CU, each walking a fixed list of work items: the items of
+// an XCD (the same XCD-contiguous runs as above) are dealt round-robin to its
+// workgroups, and a workgroup streams the k-slices of its items back to back,
+// so the first slices of the next item are already in flight while the last
+// one of the current item is multiplied and its output tile written.
+//
+// Operand slices go from HBM/L2 straight into LDS (buffer loads with the LDS
+// destination: no staging registers, no LDS store instructions).  Four LDS
+// stages of 32 k x (256 A rows + 256 B rows) rotate with three slices in
+// flight: step j waits for its own slice, meets the other waves at one
+// barrier (after which the stage multiplied at step j - 1 is free in every
+// wave), sends the loads of slice j + 3 into that stage and multiplies slice
+// j.  The stages are separate LDS objects and the stage of a step is a
+// compile-time choice (the step loop is unrolled by four), which lets the
+// compiler count the loads each LDS read waits for exactly.  The wait before
+// the barrier counts only the two newer slices' loads (8 per lane), so it is
+// exact whatever else was issued in between: loads complete in order, and any
+// extra newer load only makes the wait longer.
+//
+// The next item's tile records arrive through scalar loads two steps apart,
+// its gathered row indices (gate/up) through a small LDS DMA, so the loop has
+// no vector loads besides the slices.  Down: each item's row scales are sent
+// into LDS (by item parity) when its loads start and read by its epilogue.
+// Used when K is a multiple of 128 with at least kMinStreamSlices 32-k slices
+// and N is a multiple of the column tile.
+// Stage geometry of the streaming kernel for k-slices of BK (32 or 64): tile
+// rows of 2 BK bytes, 256 A rows + 256 B rows per stage, 4 stages of 32 KB or 2
+// of 64 KB.  A slice load covers RPI whole rows per wave instruction.
+template <int BK>
+struct StreamGeom {
+  static_assert(BK == 32 || BK == 64, "32 or 64 k per stage");
+  static constexpr int kRow = BK * 2;               // bytes per tile row
+  static constexpr int kChunks = BK / 8;            // 16-byte chunks per row
+  static constexpr int kTileBytes = 256 * kRow;     // one operand tile
+  static constexpr int kStageBytes = 2 * kTileBytes;
+  static constexpr int kStages = BK == 32 ? 4 : 2;
+  static constexpr int kRPI = 64 / kChunks;         // rows per load instruction
+  static constexpr int kNI = 256 / kRPI / 8;        // load instructions per wave and operand
+  // LDS byte offset of 16-byte k chunk c of tile row r.  64-byte rows: the
+  // chunk is XORed with ((r >> 1) & 3) ^ ((r >> 3) & 1), 128-byte rows with
+  // (r & 7) ^ ((r >> 3) & 1): a fragment read (32 consecutive rows, one chunk)
+  // then puts any 8 consecutive rows in distinct 16-byte bank groups of a
+  // 128-byte window and any 16 in distinct groups of a 256-byte one.
+  static __device__ __forceinline__ int swz(int r, int c) {
+    const int x = BK == 32 ? ((r >> 1) & 3) ^ ((r >> 3) & 1) : (r & 7) ^ ((r >> 3) & 1);
+    return r * kRow + ((c ^ x) << 4);
+  }
+};
+constexpr int kMinStreamSlices = 8;
+constexpr int kStreamBK = 64;             // k per stage of the LDS-fed streaming kernel
+constexpr int kDmaMinRowsPerGroup = 256;  // average rows per group that select it
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes),
+                                           kBufferFlags);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer load of BYTES per lane into LDS: lane l's data lands at lds + l * BYTES
+// (lds is wave-uniform).  Only voffset takes part in the range check, so an
+// out-of-range voffset reads zeros while the uniform soffset moves along k.
+template <int BYTES>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                    uint32_t soff) {
+  static_assert(BYTES == 4 || BYTES == 16, "dword or 16-byte loads");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+}
+
+template <bool GATEUP, int BK>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bf16_stream_kernel(
+    int Kdim, int N, int x_rows, int rows, int NT, const TileInfo* __restrict__ tiles,
+    const int32_t* __restrict__ meta, const int32_t* __restrict__ row_index,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
+    const uint16_t* __restrict__ W1, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ out) {
+  using G = StreamGeom<BK>;
+  constexpr int BM = 256, BNW = 256, NTHR = 512;
+  constexpr int kWavesN = 2;                  // waves: 4 along rows x 2 along weight rows
+  constexpr int kNB = BNW / kWavesN / 32;     // 32-wide weight blocks per wave
+  constexpr int kCols = GATEUP ? BNW / 2 : BNW;
+  constexpr int kNI = G::kNI, kRPI = G::kRPI;
+  constexpr uint32_t kOff = 0x80000000u;      // beyond every buffer (sizes < 2 GiB)
+  constexpr int kS0 = G::kStageBytes;
+  constexpr int kS2 = G::kStages == 4 ? G::kStageBytes : 16;
+  __shared__ __attribute__((aligned(16))) char st0[kS0];
+  __shared__ __attribute__((aligned(16))) char st1[kS0];
+  __shared__ __attribute__((aligned(16))) char st2[kS2];
+  __shared__ __attribute__((aligned(16))) char st3[kS2];
+  __shared__ __attribute__((aligned(16))) int32_t ri_lds[8 * 64];     // next item's source rows
+  __shared__ __attribute__((aligned(16))) float sc_lds[2 * 8 * 64];   // row scales by item parity
+  char* const st_last = G::kStages == 4 ? st3 : st1;
+
+  // ---- this workgroup's items: first, first + nslot, ... below end
+  const int total = meta[0] * NT;
+  const int nslot = gridDim.x / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int first = xcd * per_xcd + static_cast<int>(blockIdx.x) / kNumXcd;
+  const int end = min(total, (xcd + 1) * per_xcd);
+  if (first >= end) return;
+  const int n_items = (end - first + nslot - 1) / nslot;
+  const int nk = Kdim / BK;  // a multiple of 4 / BK * 32 stages... a multiple of the stage count
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar
+  const int lane = tid % kWave;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  // Slice loads: load instruction i of a wave sends tile rows kRPI (wave + 8 i)
+  // + drow of A and of B; lane l lands at LDS chunk l % kChunks of its row, so
+  // it loads the k chunk that the swizzle stores there.
+  const int drow = lane / G::kChunks;
+  const int dchunk =
+      (lane % G::kChunks) ^ (BK == 32 ? ((drow >> 1) & 3) ^ ((drow >> 3) & 1) : drow ^ (wave & 1));
+  const uint32_t rowbytes = static_cast<uint32_t>(Kdim) * 2u;
+  const uint32_t wbytes = static_cast<uint32_t>(N) * rowbytes;
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(A, static_cast<uint32_t>(x_rows) * rowbytes);
+  // gate/up gathers x rows through row_index (NULL: grouped row r is x row r)
+  const bool gather = GATEUP && row_index != nullptr;
+  const __amdgpu_buffer_rsrc_t rsR =
+      buffer_rsrc(row_index, gather ? static_cast<uint32_t>(rows) * 4u : 0u);
+  const bool has_scale = !GATEUP && row_scale != nullptr;
+  const __amdgpu_buffer_rsrc_t rsS =
+      buffer_rsrc(row_scale, has_scale ? static_cast<uint32_t>(rows) * 4u : 0u);
+
+  auto a_offset = [&](int i, int nrows, int sr) -> uint32_t {
+    return (kRPI * (wave + 8 * i) + drow < nrows && sr >= 0 && sr < x_rows)
+               ? static_cast<uint32_t>(sr) * rowbytes + static_cast<uint32_t>(dchunk) * 16u
+               : kOff;
+  };
+
+  // ---- load-side item
+  int l_item = 0, l_g, l_ntile, l_m0, l_nrows;
+  {
+    const TileInfo t0 = tiles[first / NT];
+    const int local = first - t0.gstart * NT;
+    const TileInfo ti = tiles[t0.gstart + local % t0.ntiles];
+    l_g = t0.group;
+    l_ntile = local / t0.ntiles;
+    l_m0 = ti.m0;
+    l_nrows = min(ti.m1 - ti.m0, BM);
+  }
+  uint32_t a_off[kNI];
+#pragma unroll
+  for (int i = 0; i < kNI; ++i) {
+    const int r = kRPI * (wave + 8 * i) + drow;
+    const int sr = gather ? (r < l_nrows ? row_index[l_m0 + r] : -1) : l_m0 + r;
+    a_off[i] = a_offset(i, l_nrows, sr);
+  }
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  uint32_t bcol;
+  const uint32_t b_off = static_cast<uint32_t>(kRPI * wave + drow) * rowbytes +
+                         static_cast<uint32_t>(dchunk) * 16u;
+  auto set_weights = [&]() {
+    rb0 = buffer_rsrc(W0 + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    rb1 = buffer_rsrc((GATEUP ? W1 : W0) + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
+  };
+  set_weights();
+  const uint32_t kb_end = static_cast<uint32_t>(nk) * G::kRow;
+  uint32_t kb = 0;  // byte offset of the load side's next k-slice
+
+  // ---- next item, fetched ahead: group record at slice 0 of the current
+  // load-side item, row-tile record at slice 2, row indices sent at slice 4
+  int nw = first + min(1, n_items - 1) * nslot;
+  int f_group = 0, f_gstart = 0, f_ntiles = 1, f_m0 = 0, f_m1 = 0;
+  int n_g = l_g, n_ntile = l_ntile, n_m0 = l_m0, n_nrows = l_nrows;
+
+  // Moves the load side on by one slice into stage st.
+  auto issue = [&](char* st) {
+    if (kb == kb_end) {
+      if (l_item + 1 < n_items) {
+        ++l_item;
+        kb = 0;
+        l_g = n_g; l_ntile = n_ntile; l_m0 = n_m0; l_nrows = n_nrows;
+        set_weights();
+#pragma unroll
+        for (int i = 0; i < kNI; ++i) {
+          const int sr = gather ? ri_lds[wave * 64 + kRPI * i + drow]
+                                : l_m0 + kRPI * (wave + 8 * i) + drow;
+          a_off[i] = a_offset(i, l_nrows, sr);
+        }
+        nw = first + min(l_item + 1, n_items - 1) * nslot;
+      } else {
+        kb = kb_end - G::kRow;  // past the last item: re-read its last slice (an L2 hit)
+      }
+    }
+    const uint32_t lk = kb / G::kRow;
+    if (lk == 0) {
+      const TileInfo t = tiles[nw / NT];
+      f_group = t.group;
+      f_gstart = t.gstart;
+      f_ntiles = max(t.ntiles, 1);
+    } else if (lk == 2) {
+      const int local = nw - f_gstart * NT;
+      n_ntile = local / f_ntiles;
+      n_g = f_group;
+      const TileInfo u = tiles[f_gstart + local - n_ntile * f_ntiles];
+      f_m0 = u.m0;
+      f_m1 = u.m1;
+    } else if (lk == 4) {
+      n_m0 = f_m0;
+      n_nrows = min(f_m1 - f_m0, BM);
+      if (GATEUP) {
+        // lane l < 32: row kRPI * (wave + 8 * (l / kRPI)) + l % kRPI
+        const int r = kRPI * (wave + 8 * (lane / kRPI)) + lane % kRPI;
+        dma<4>(rsR, ri_lds + wave * 64,
+               (lane < 32 && r < n_nrows) ? static_cast<uint32_t>(n_m0 + r) * 4u : kOff, 0);
+      } else {
+        const int r = wm * 64 + lane;
+        dma<4>(rsS, sc_lds + (l_item & 1) * 512 + wave * 64,
+               r < l_nrows ? static_cast<uint32_t>(l_m0 + r) * 4u : kOff, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kNI; ++i)
+      dma<16>(rsA, st + kRPI * (wave + 8 * i) * G::kRow, a_off[i], kb);
+    // B tile row kRPI (wave + 8 i) + drow: W_gate rows over the matching W_up
+    // rows (gate/up), or 256 consecutive W_down rows
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      const int add = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;
+      dma<16>((GATEUP && i >= kNI / 2) ? rb1 : rb0,
+              st + G::kTileBytes + kRPI * (wave + 8 * i) * G::kRow, b_off,
+              bcol + static_cast<uint32_t>(add) * rowbytes + kb);
+    }
+    kb += G::kRow;
+  };
+
+  // ---- compute side (trails the load side by kStages - 1 slices)
+  int c_item = 0, c_m0 = l_m0, c_nrows = l_nrows, c_n0 = l_ntile * kCols;
+
+  int brow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (GATEUP) {
+      const int half = kNB / 2;
+      const int base = wn * (BNW / 2 / kWavesN);
+      brow[nb] = (nb < half) ? base + nb * 32 : BNW / 2 + base + (nb - half) * 32;
+    } else {
+      brow[nb] = wn * (BNW / kWavesN) + nb * 32;
+    }
+  }
+
+  f32x16_t acc[2][kNB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
+
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+
+  // Wave (wm, wn) multiplies the 32-row blocks 2 wm and 2 wm + 1 (a block
+  // with no row of the item is skipped) against its kNB weight blocks.
+  auto compute = [&](const char* st) {
+    const bool mb0 = wm * 64 < c_nrows;
+    const bool mb1 = wm * 64 + 32 < c_nrows;
+    if (!mb0) return;
+    const char* bs = st + G::kTileBytes;
+#pragma unroll
+    for (int kh = 0; kh < BK / 32; ++kh) {
+      bf16x8_t bq[2][kNB], aq[2][2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = kh * 4 + kk * 2 + fh;
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          bq[kk][nb] = *reinterpret_cast<const bf16x8_t*>(bs + G::swz(brow[nb] + fr, c));
+        aq[kk][0] = *reinterpret_cast<const bf16x8_t*>(st + G::swz(wm * 64 + fr, c));
+        if (mb1) aq[kk][1] = *reinterpret_cast<const bf16x8_t*>(st + G::swz(wm * 64 + 32 + fr, c));
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          acc[0][nb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk][0], bq[kk][nb], acc[0][nb], 0, 0, 0);
+        if (mb1) {
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb)
+            acc[1][nb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk][1], bq[kk][nb], acc[1][nb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Output tile of the compute-side item, staged through the last stage (free
+  // once every wave has multiplied it; the next slice into it is sent only
+  // after the next step's barrier) in rounds of kRoundRows rows: bf16 rows of
+  // kCols with the 16-byte chunk index XORed with (row & 4), then written as
+  // whole 16-byte chunks.  D[row][col] of a 32x32 block sits in lane
+  // (col + 32*((row/4)%2)), register (row%4) + 4*(row/8).
+  constexpr int kOutRowBytes = kCols * 2;
+  constexpr int kRoundRows =
+      G::kStageBytes / kOutRowBytes < BM ? G::kStageBytes / kOutRowBytes : BM;
+  constexpr int kOutChunks = kCols / 8;
+  constexpr int kReadRows = NTHR / kOutChunks;
+  static_assert(kRoundRows % 64 == 0 && BM % kRoundRows == 0, "rounds hold whole waves' rows");
+  static_assert(NTHR % kOutChunks == 0 && kReadRows % 8 == 0, "read-out rows keep row & 4");
+  auto epilogue = [&]() {
+    // Lane constants are rederived here from the hardware lane id: hoisted
+    // out of the item loop they would stay live through the inner loop.
+    int ez = 0;  // opaque zero: keeps the lane-id computation inside the loop
+    asm volatile("" : "+v"(ez));
+    const int e_lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, ez));
+    const int etid = wave * kWave + e_lane;
+    const int e_fr = e_lane & 31, e_fh = e_lane >> 5;
+    const float* sc = sc_lds + (c_item & 1) * 512 + wave * 64;
+    char* const ot = st_last;
+    // every wave has multiplied the last stage
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int r0 = 0; r0 < BM; r0 += kRoundRows) {
+      if (r0 >= c_nrows) break;
+      {
+        int cofs[kNB];
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) {
+          const int c = (GATEUP ? (nb < kNB / 2 ? wn * (BNW / 2 / kWavesN) + nb * 32
+                                                : BNW / 2 + wn * (BNW / 2 / kWavesN) +
+                                                      (nb - kNB / 2) * 32)
+                                : wn * (BNW / kWavesN) + nb * 32) +
+                        e_fr;
+          cofs[nb] = (((c >> 3) ^ (4 * e_fh)) << 4) + (c & 7) * 2;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if (wm * 64 < r0 || wm * 64 >= r0 + kRoundRows) break;  // rows of another round
+          // block row base, relative to the round, plus this lane's half (4 * fh)
+          const int base = wm * 64 + mb * 32 - r0 + 4 * e_fh;
+          char* ob = ot + base * kOutRowBytes;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float4 s4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (has_scale)
+              s4 = *reinterpret_cast<const float4*>(sc + mb * 32 + 8 * q4 + 4 * e_fh);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int q1 = 0; q1 < 4; ++q1) {
+              const int q = 4 * q4 + q1;
+              // rows past the item are staged too (never written out)
+              char* orow = ob + (8 * q4 + q1) * kOutRowBytes;
+              if (GATEUP) {
+#pragma unroll
+                for (int nb = 0; nb < kNB / 2; ++nb) {
+                  const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
+                  *reinterpret_cast<uint16_t*>(orow + cofs[nb]) = f32_to_bf16(v);
+                }
+              } else {
+#pragma unroll
+                for (int nb = 0; nb < kNB; ++nb)
+                  *reinterpret_cast<uint16_t*>(orow + cofs[nb]) =
+                      f32_to_bf16(acc[mb][nb][q] * sv[q1]);
+              }
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const int rl = etid / kOutChunks, cl = etid % kOutChunks;
+      const char* src = ot + rl * kOutRowBytes + ((cl ^ (rl & 4)) << 4);
+      uint16_t* dst = out + static_cast<size_t>(c_m0 + r0 + rl) * N + c_n0 + cl * 8;
+#pragma unroll
+      for (int it = 0; it < kRoundRows / kReadRows; ++it) {
+        if (rl < c_nrows - r0 - it * kReadRows)
+          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(it) * kReadRows * N) =
+              *reinterpret_cast<const uint4*>(src + it * kReadRows * kOutRowBytes);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+
+  // ---- stream: the first kStages - 1 slices in flight, then per step: wait
+  // for this step's slice (the newer slices, 2 kNI loads per lane each, may
+  // stay in flight), barrier, send the next slice into the stage freed by the
+  // previous step, multiply.  nk is a multiple of the stage count, so every
+  // item starts on stage 0 and ends on the last.
+#define MOE_STEP(CUR, NEXT)                                                                 \
+  if constexpr (G::kStages == 4)                                                            \
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(4 * kNI) : "memory");             \
+  else                                                                                      \
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");                           \
+  issue(NEXT);                                                                              \
+  compute(CUR);
+  if constexpr (G::kStages == 4) {
+    issue(st0);
+    issue(st1);
+    issue(st2);
+  } else {
+    issue(st0);
+  }
+  for (int j = 0; j < n_items; ++j) {
+    if constexpr (G::kStages == 4) {
+      for (int kt = 0; kt < nk; kt += 4) {
+        MOE_STEP(st0, st3)
+        MOE_STEP(st1, st0)
+        MOE_STEP(st2, st1)
+        MOE_STEP(st3, st2)
+      }
+    } else {
+      for (int kt = 0; kt < nk; kt += 2) {
+        MOE_STEP(st0, st1)
+        MOE_STEP(st1, st0)
+      }
+    }
+    epilogue();
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;
+    ++c_item;
+    c_m0 = l_m0;
+    c_nrows = l_nrows;
+    c_n0 = l_ntile * kCols;
+  }
+#undef MOE_STEP
+  // the re-read slices of the last steps must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Shapes the streaming kernel takes: K a multiple of 128 with at least
+// kMinStreamSlices slices, N a multiple of its column tile.
+bool stream_shape(int K, int N, int cols) {
+  return K % 128 == 0 && K / kStreamBK >= kMinStreamSlices && N % cols == 0;
+}
+
+// ---------------------------------------------------------------- streaming, register-staged
 //
 // One workgroup per CU, each walking a fixed list of work items: the items of
 // an XCD (the same XCD-contiguous runs as above) are dealt round-robin to its
@@ -335,18 +773,12 @@ void bf16_tile_kernel(
 // slices ahead by loads issued on every step (branch-free, so the compiler's
 // wait counts stay exact).  Used when K is an even number of at least
 // kMinStreamSlices slices and N is a multiple of the column tile.
-constexpr int kMinStreamSlices = 8;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes),
-                                           kBufferFlags);
-}
 
 template <bool GATEUP, int BM, int BNW, int NTHR>
 __global__ __launch_bounds__(NTHR)
 __attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
                                    Tile<BM, BNW, NTHR>::kWavesPerEU)))
-void bf16_stream_kernel(
+void bf16_regs_stream_kernel(
     int Kdim, int N, int x_rows, int rows, int max_tiles, int NT,
     const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
     const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
@@ -748,9 +1180,18 @@ hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_ro
   uint16_t* act = static_cast<uint16_t*>(w.act);
 
   const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
-  if (d_model / kBK >= kMinStreamSlices && d_model % (2 * kBK) == 0 && d_ffn % (BNW / 2) == 0) {
+  // Groups of at least a full row tile on average make the products matrix-core
+  // bound: LDS-fed kernel.  Fewer rows make them weight-streaming bound:
+  // register-staged kernel, which keeps more weight bytes in flight per CU.
+  const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
+  if (stream_shape(d_model, d_ffn, 128) && mfma_bound) {
     ProfScope prof_(s, "gateup_bf16");
-    hipLaunchKernelGGL((bf16_stream_kernel<true, BM, BNW, NTHR>), dim3(stream_grid()),
+    hipLaunchKernelGGL((bf16_stream_kernel<true, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
+                       s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, wg,
+                       wu, nullptr, act);
+  } else if (stream_shape(d_model, d_ffn, BNW / 2)) {
+    ProfScope prof_(s, "gateup_bf16");
+    hipLaunchKernelGGL((bf16_regs_stream_kernel<true, BM, BNW, NTHR>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles,
                        w.meta, row_index, x, wg, wu, nullptr, act);
   } else {
@@ -766,9 +1207,14 @@ hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_ro
   if (err != hipSuccess) return err;
 
   const int nt2 = (d_model + BNW - 1) / BNW;
-  if (d_ffn / kBK >= kMinStreamSlices && d_ffn % (2 * kBK) == 0 && d_model % BNW == 0) {
+  if (stream_shape(d_ffn, d_model, 256) && mfma_bound) {
     ProfScope prof_(s, "down_bf16");
-    hipLaunchKernelGGL((bf16_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
+    hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
+                       s, d_ffn, d_model, rows, rows, nt2, w.tiles, w.meta, nullptr, act, wd,
+                       nullptr, row_scale, y);
+  } else if (stream_shape(d_ffn, d_model, BNW)) {
+    ProfScope prof_(s, "down_bf16");
+    hipLaunchKernelGGL((bf16_regs_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, d_ffn, d_model, rows, rows, max_tiles, nt2, w.tiles,
                        w.meta, nullptr, act, wd, nullptr, row_scale, y);
   } else {

@@ -339,6 +339,8 @@ SWIGLU_CASES = [
     (5, 512, 512, 64, 2, torch.bfloat16),      # nearly all experts empty
     (2000, 512, 512, 4, 2, torch.bfloat16),    # 1000-row groups: four row tiles each
     (4000, 1024, 1024, 48, 4, torch.bfloat16),  # several work items per workgroup
+    # >= 256 rows per expert on average: the LDS-fed streaming kernel
+    (1500, 512, 512, 6, 2, torch.bfloat16),    # ragged groups of ~500 rows
 ]
 
 
@@ -378,14 +380,22 @@ def test_grouped_swiglu_row_scale_and_direct_rows():
     assert rel_err(to_host_f64(y), ref) <= out_tol("bf16")
 
 
-def test_grouped_swiglu_streaming_row_scale_direct_rows_and_bad_rows():
+@pytest.mark.parametrize("T,off", [
+    # < 256 rows per group on average: the register-staged streaming kernel
+    (700, [0, 300, 300, 301, 590, 700]),
+    # >= 256 rows per group on average: the LDS-fed one (a 589-row group spans three row tiles)
+    (1300, [0, 600, 600, 601, 1190, 1300]),
+])
+def test_grouped_swiglu_streaming_row_scale_direct_rows_and_bad_rows(T, off):
     """The streaming kernels (d, f >= 512) with a per-row scale, identity rows
-    (row_index NULL) and gathered rows with out-of-range entries."""
-    T, d, f, E = 700, 512, 512, 5
+    (row_index NULL) and gathered rows with out-of-range entries; empty and
+    1-row groups."""
+    say(f"streaming swiglu T={T} groups={off}")
+    d, f, E = 512, 512, 5
     x = _tokens(T, d, torch.bfloat16, 81)
     wg, wu, wd = _weights(E, d, f, torch.bfloat16, 82)
     w_host = (host_array(wg), host_array(wu), host_array(wd))
-    off = np.array([0, 300, 300, 301, 590, 700], dtype=np.int32)  # empty and 1-row groups
+    off = np.array(off, dtype=np.int32)
     scale = torch.rand(T, generator=_gen(83), device=DEV)
     y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), None, wg, wu, wd, T, scale)
     ref = O.grouped_swiglu(host_array(x), off, None, w_host)
