@@ -7,7 +7,7 @@
 // Two launches over the device-built tile list:
 //   gate/up: act[r, n] = SiLU(x_r . Wg[n]) * (x_r . Wu[n])     K = d_model
 //            x rows gathered on load through row_index (no x_perm copy);
-//            the B tile stacks 64 W_gate rows over the same 64 W_up rows,
+//            the B tile stacks 128 W_gate rows over the same 128 W_up rows,
 //            so each lane holds matching gate and up accumulators.
 //   down:    y[r, n] = (act_r . Wd[n]) * row_scale[r]          K = d_ffn
 //
@@ -22,9 +22,15 @@
 // with 128.  The global loads of the next 64-k slice stay in flight while the
 // current one is multiplied out of LDS (two register sets, two 64 KB LDS
 // stages; 16-byte chunks XOR-swizzled per row so fragment reads and staging
-// writes are bank-conflict free).  The kernel is templated on the tile shape
-// and the number of register sets; this shape measured fastest for both the
+// writes are bank-conflict free).  This shape measured fastest for both the
 // weight-streaming (few rows per expert) and the matrix-core-bound shapes.
+//
+// Three kernels share the tile: a one-tile-per-workgroup kernel (any shape),
+// and two persistent streaming kernels for K and N that fit whole slices and
+// column tiles: an LDS-fed one (operands loaded straight into LDS) for groups
+// of at least 256 rows on average, where the matrix cores bound the products,
+// and a register-staged one for smaller groups, where streaming the weights
+// from HBM bounds them and more bytes in flight per CU pay.
 //
 // Work order: (group, column tile, row tile); block ids are remapped so each
 // XCD walks a contiguous run of it: row tiles of one (expert, column tile) run
@@ -322,7 +328,7 @@ void bf16_tile_kernel(
   }
 }
 
-// ---------------------------------------------------------------- streaming kernel
+// ---------------------------------------------------------------- streaming, LDS-fed
 //
 // One workgroup per CU, each walking a fixed list of work items: the items of
 // an XCD (the same XCD-contiguous runs as above) are dealt round-robin to its
@@ -330,25 +336,30 @@ void bf16_tile_kernel(
 // so the first slices of the next item are already in flight while the last
 // one of the current item is multiplied and its output tile written.
 //
-// Operand slices go from HBM/L2 straight into LDS (buffer loads with the LDS
-// destination: no staging registers, no LDS store instructions).  Four LDS
-// stages of 32 k x (256 A rows + 256 B rows) rotate with three slices in
-// flight: step j waits for its own slice, meets the other waves at one
-// barrier (after which the stage multiplied at step j - 1 is free in every
-// wave), sends the loads of slice j + 3 into that stage and multiplies slice
-// j.  The stages are separate LDS objects and the stage of a step is a
-// compile-time choice (the step loop is unrolled by four), which lets the
-// compiler count the loads each LDS read waits for exactly.  The wait before
-// the barrier counts only the two newer slices' loads (8 per lane), so it is
-// exact whatever else was issued in between: loads complete in order, and any
-// extra newer load only makes the wait longer.
+// Operand slices go from HBM/L2 straight into LDS (buffer loads with an LDS
+// destination: no staging registers, no LDS store instructions).  The stages
+// rotate with kStages - 1 slices in flight: step j waits for its own slice,
+// meets the other waves at one barrier (after which the stage multiplied at
+// step j - 1 is free in every wave), sends the loads of the next slice into
+// that stage and multiplies slice j.  The wait and the barrier are one asm
+// statement, so every wave's share of the slice has landed before any wave
+// reads it.  The stages are separate LDS objects and the stage of a step is a
+// compile-time choice (the step loop is unrolled by the stage count), which
+// lets the compiler count the loads each LDS read waits for exactly.  The
+// explicit wait counts only the newer slices' loads, so it is exact whatever
+// else was issued in between: loads complete in order, and any extra newer
+// load only makes the wait longer.
 //
 // The next item's tile records arrive through scalar loads two steps apart,
 // its gathered row indices (gate/up) through a small LDS DMA, so the loop has
 // no vector loads besides the slices.  Down: each item's row scales are sent
 // into LDS (by item parity) when its loads start and read by its epilogue.
-// Used when K is a multiple of 128 with at least kMinStreamSlices 32-k slices
-// and N is a multiple of the column tile.
+// Used when K is a multiple of 128 with at least kMinStreamSlices slices and N
+// is a multiple of the column tile, for groups of at least a full row tile on
+// average (matrix-core-bound products).  With 64-k slices a stage holds 64 KB,
+// so one slice is in flight per step: enough where the products are bound by
+// the matrix cores, too little for weight streaming, which the register-staged
+// kernel below handles with two slices in flight.
 // Stage geometry of the streaming kernel for k-slices of BK (32 or 64): tile
 // rows of 2 BK bytes, 256 A rows + 256 B rows per stage, 4 stages of 32 KB or 2
 // of 64 KB.  A slice load covers RPI whole rows per wave instruction.
