@@ -55,21 +55,34 @@ def recorded_traffic(workload: str):
     counter runs summarised in profiles/hbm_traffic_<workload>.md, already
     scaled by the copy calibration.  None when no such record exists or the
     kernel sources changed since the counters were taken (their hash differs)."""
-    import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
-    h = hashlib.sha256()
-    for f in ("swiglu_bf16.hip", "swiglu_tiles.h", "common.h"):
-        with open(os.path.join(ROOT, "sparse_mixture_experts_biased_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    digest = kernel_source_hash()
     with open(path) as fh:
         for line in fh:
             m = re.match(r"traffic routed\.gateup_bf16 (\S+) bytes=(\d+) .*sources=([0-9a-f]+)", line)
-            if m and m.group(1) == workload and h.hexdigest().startswith(m.group(3)):
+            if m and m.group(1) == workload and digest.startswith(m.group(3)):
                 return int(m.group(2))
     return None
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the grouped-SwiGLU kernel sources with comments and blank
+    lines removed (a comment edit leaves the kernel, and its counters, as they
+    were)."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in ("swiglu_bf16.hip", "swiglu_tiles.h", "common.h"):
+        with open(os.path.join(ROOT, "sparse_mixture_experts_biased_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.split("\n"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256, capacity=None):
