@@ -167,6 +167,84 @@ def copy_probe(nbytes: int) -> int:
     return 0
 
 
+def calibrate() -> int:
+    """Achievable peaks on this GPU, the references the roofline fractions are
+    also read against: a plain device copy of 2 GiB (HBM), the matrix-core
+    loop moe_calib_mfma_loop (bf16 MFMA with no memory traffic), and the vendor
+    GEMM library (hipBLASLt, through torch.matmul) on dense bf16 products of
+    the expert GEMMs' sizes.  Random operands throughout (the core clock
+    depends on the data).  Prints one JSON line."""
+    import torch
+    import sparse_mixture_experts_biased_amd._lib as L
+    torch.manual_seed(0)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    n = 1 << 31
+    src = torch.randint(-(1 << 30), 1 << 30, (n // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), 10)
+    out["copy_2GiB"] = {"ms": round(ms, 4), "GB/s (read + write)": round(2 * n / ms / 1e6, 1)}
+    del dst
+    log(f"copy: {out['copy_2GiB']}")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * cus * 256, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: L.moe_calib_stream_read(8 * cus, src, sink), 10)
+    out["read_2GiB"] = {"ms": round(ms, 4), "GB/s": round(n / ms / 1e6, 1)}
+    del src, sink
+    log(f"streaming read: {out['read_2GiB']}")
+
+    wg, iters = 4 * cus, 512
+    ops = torch.randn(wg * 256 * 96, device="cuda").to(torch.bfloat16)
+    res = torch.empty(wg * 256, device="cuda")
+    fl = [0.0]
+
+    def loop():
+        fl[0] = L.moe_calib_mfma_loop(wg, iters, ops, res)
+
+    ms = timed(loop, 10)
+    out["mfma_loop"] = {"workgroups": wg, "iters": iters, "ms": round(ms, 4),
+                        "TFLOP/s": round(fl[0] / ms / 1e9, 1)}
+    log(f"mfma loop: {out['mfma_loop']}")
+
+    # dense equivalents of the expert GEMMs (M rows x N outputs x K), and one
+    # DeepSeek-V3 prefill expert as the library would see it without grouping
+    shapes = {
+        "mixtral gate/up 8192x28672x4096": (8192, 28672, 4096),
+        "mixtral down 8192x4096x14336": (8192, 4096, 14336),
+        "dsv3 hot expert gate/up 8192x4096x7168": (8192, 4096, 7168),
+        "dsv3 hot expert down 8192x7168x2048": (8192, 7168, 2048),
+        "dsv3 prefill one expert gate/up 128x4096x7168": (128, 4096, 7168),
+    }
+    lib = {}
+    for name, (M, N, K) in shapes.items():
+        # weights [N, K] as the layer stores them (K-contiguous, like the kernels'
+        # operands); a 2-D product with the transposed view is one library GEMM
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        w = torch.randn(N, K, device="cuda").to(torch.bfloat16)
+        ms = timed(lambda: torch.mm(a, w.t()), 10)
+        lib[name] = {"ms": round(ms, 4), "TFLOP/s": round(2.0 * M * N * K / ms / 1e9, 1),
+                     "GB/s (operands + output)": round(2.0 * (M * K + K * N + M * N) / ms / 1e6, 1)}
+        log(f"hipBLASLt {name}: {lib[name]}")
+        del a, w
+    out["hipblaslt"] = lib
+    print(json.dumps({"calibration": out, "device": torch.cuda.get_device_name(0), "cus": cus}),
+          flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,9 +264,14 @@ def main(argv=None):
                          "(Switch f.P, z-loss, load entropy, MaxVio, dropped rate) every step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-sized buffer 3 times (calibrates HBM byte counters)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure the achievable peaks (device copy, matrix-core loop, "
+                         "hipBLASLt on the expert GEMM sizes) and print them as one JSON line")
     args = ap.parse_args(argv)
     if args.copy_probe:
         return copy_probe(args.copy_probe)
+    if args.calibrate:
+        return calibrate()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("bench.py measures the single-GPU layer forward only: this build has no "

@@ -312,6 +312,37 @@ moe_status moe_profile_enable(int on);
 moe_status moe_profile_tag(const char* tag);
 moe_status moe_profile_report(char* buf, size_t buf_bytes);
 
+/*
+ * Measurement aid, not part of the layer: the bf16 matrix-core rate with no
+ * memory traffic, against which the grouped SwiGLU's matrix-core fraction is
+ * read.  `workgroups` workgroups of 256 threads; every wave issues, `iters`
+ * times, the MFMA sequence of one wave of the grouped SwiGLU tile over two
+ * k-steps (2 x 4 blocks of v_mfma_f32_32x32x16_bf16 each, 8 independent
+ * accumulators) on two sets of fragments held in registers.
+ *   operands  device, workgroups * 256 * 96 bf16 values (random in practice;
+ *             each thread loads its own 192 bytes once)
+ *   out       device, workgroups * 256 floats (sums of the accumulators, so the
+ *             work cannot be dropped)
+ *   flops     host, or NULL: receives the FLOPs the launch performs
+ * Asynchronous on `stream`; time it with events on that stream.
+ * MOE_ERR_INVALID_ARG for workgroups or iters < 1, workgroups > 2^20 or a
+ * null device pointer.
+ */
+moe_status moe_calib_mfma_loop(int workgroups, int iters, const void* operands, float* out,
+                               double* flops, void* stream);
+
+/*
+ * Measurement aid, not part of the layer: the HBM read rate a plain streaming
+ * kernel reaches, against which the weight-streaming kernels are read.
+ * `workgroups` workgroups of 256 threads read the `bytes` at device pointer
+ * `src` once in 16-byte vectors (grid-stride, eight loads in flight per thread)
+ * and write one folded word per thread to `out` (device, workgroups * 256
+ * uint32).  MOE_ERR_INVALID_ARG for workgroups outside 1..2^20, a null
+ * pointer, or bytes / src not non-zero multiples of 16.
+ */
+moe_status moe_calib_stream_read(int workgroups, const void* src, size_t bytes, uint32_t* out,
+                                 void* stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* moe_last_error(void);
 

@@ -21,7 +21,8 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size
             "moe_combine_backward", "moe_grouped_swiglu_backward_workspace_size",
             "moe_grouped_swiglu_backward", "moe_route_backward",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
-            "moe_bias_update", "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
+            "moe_bias_update", "moe_calib_mfma_loop", "moe_calib_stream_read",
+            "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
 
 
@@ -80,6 +81,8 @@ def load() -> ctypes.CDLL:
                                 _sz, _p], _i),
         "moe_combine": ([_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p], _i),
         "moe_bias_update": ([_i, _i, _i, _f, _p, _p, _p, _p], _i),
+        "moe_calib_mfma_loop": ([_i, _i, _p, _p, ctypes.POINTER(ctypes.c_double), _p], _i),
+        "moe_calib_stream_read": ([_i, _p, _sz, _p, _p], _i),
         "moe_profile_enable": ([_i], _i),
         "moe_profile_tag": ([ctypes.c_char_p], _i),
         "moe_profile_report": ([ctypes.c_char_p, _sz], _i),
@@ -207,6 +210,21 @@ def moe_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates, dtype,
 def moe_bias_update(T, E_r, K, gamma, loads, b, stats, stream=None):
     _check(load().moe_bias_update(T, E_r, K, float(gamma), _ptr(loads), _ptr(b), _ptr(stats),
                                   _stream(stream)))
+
+
+def moe_calib_mfma_loop(workgroups: int, iters: int, operands, out, stream=None) -> float:
+    """Launch the pure matrix-core loop (a measurement aid) on `stream`
+    (default: torch's current stream); returns the FLOPs it performs."""
+    fl = ctypes.c_double(0.0)
+    _check(load().moe_calib_mfma_loop(workgroups, iters, _ptr(operands), _ptr(out),
+                                      ctypes.byref(fl), _stream(stream)))
+    return fl.value
+
+
+def moe_calib_stream_read(workgroups: int, src, out, stream=None):
+    """Launch the streaming-read kernel (a measurement aid) over all of `src`."""
+    _check(load().moe_calib_stream_read(workgroups, _ptr(src), src.numel() * src.element_size(),
+                                        _ptr(out), _stream(stream)))
 
 
 def moe_profile_enable(on: bool = True):

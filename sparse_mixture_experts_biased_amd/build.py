@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "swiglu_f32.hip", "swiglu_bf16.hip",
-           "combine.hip", "bias.hip", "backward.hip"]
+           "combine.hip", "bias.hip", "backward.hip", "calib.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

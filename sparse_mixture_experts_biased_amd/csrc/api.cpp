@@ -296,6 +296,35 @@ moe_status moe_bias_update(int T, int E_r, int K, float gamma, const int32_t* lo
                     "moe_bias_update");
 }
 
+moe_status moe_calib_mfma_loop(int workgroups, int iters, const void* operands, float* out,
+                               double* flops, void* stream) {
+  if (workgroups < 1 || iters < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_calib_mfma_loop: workgroups=%d iters=%d must be >= 1",
+                workgroups, iters);
+  if (workgroups > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "moe_calib_mfma_loop: workgroups=%d > %d", workgroups, 1 << 20);
+  if (!operands || !out) return fail(MOE_ERR_INVALID_ARG, "moe_calib_mfma_loop: null pointer");
+  if (flops) *flops = moe::mfma_loop_flops(workgroups, iters);
+  return hip_status(moe::launch_mfma_loop(workgroups, iters,
+                                          static_cast<const uint16_t*>(operands), out,
+                                          as_stream(stream)),
+                    "moe_calib_mfma_loop");
+}
+
+moe_status moe_calib_stream_read(int workgroups, const void* src, size_t bytes, uint32_t* out,
+                                 void* stream) {
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "moe_calib_stream_read: workgroups=%d outside 1..%d",
+                workgroups, 1 << 20);
+  if (!src || !out) return fail(MOE_ERR_INVALID_ARG, "moe_calib_stream_read: null pointer");
+  if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_calib_stream_read: bytes (%zu) and src must be non-zero multiples of 16",
+                bytes);
+  return hip_status(moe::launch_stream_read(workgroups, src, bytes, out, as_stream(stream)),
+                    "moe_calib_stream_read");
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- profiling

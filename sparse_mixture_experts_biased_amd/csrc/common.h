@@ -88,6 +88,13 @@ struct BiasStats {
 hipError_t launch_bias_update(int T, int E, int K, float gamma, const int32_t* loads, float* b,
                               BiasStats* stats, hipStream_t s);
 
+// measurement aid: independent MFMA chains on register operands
+double mfma_loop_flops(int workgroups, int iters);
+hipError_t launch_mfma_loop(int workgroups, int iters, const uint16_t* ops, float* out,
+                            hipStream_t s);
+hipError_t launch_stream_read(int workgroups, const void* src, size_t bytes, uint32_t* out,
+                              hipStream_t s);
+
 // small utilities
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 

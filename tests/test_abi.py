@@ -181,6 +181,23 @@ def test_combine_and_bias_update_reject_bad_arguments():
     assert lib.moe_bias_update(10, 4096, 2, 0.1, P, P, None, None) == L.MOE_ERR_UNSUPPORTED
 
 
+def test_calibration_aids_reject_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    fl = ctypes.c_double(-1.0)
+    assert lib.moe_calib_mfma_loop(0, 10, P, P, ctypes.byref(fl), None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_loop(4, 0, P, P, ctypes.byref(fl), None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_loop(4, 10, None, P, ctypes.byref(fl), None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_loop(4, 10, P, None, ctypes.byref(fl), None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_mfma_loop((1 << 20) + 1, 10, P, P, None, None) == L.MOE_ERR_INVALID_ARG
+    assert fl.value == -1.0  # nothing written on a rejected call
+    assert lib.moe_calib_stream_read(0, P, 1024, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_stream_read(8, None, 1024, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_stream_read(8, P, 1000, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_stream_read(8, ctypes.c_void_p(24), 1024, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_calib_stream_read(8, P, 0, P, None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_python_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     t = torch.zeros(4)
