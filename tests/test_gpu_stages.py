@@ -436,17 +436,26 @@ def _combine_gpu(h, y_shared, y_perm, slot_row, gates, E_s):
     return y
 
 
-@pytest.mark.parametrize("T,d,K,E_s,dtype", [(64, 128, 2, 0, torch.float32),
-                                             (333, 256, 8, 1, torch.bfloat16),
-                                             (100, 7168, 8, 2, torch.bfloat16),
-                                             (31, 64, 1, 0, torch.bfloat16)])
-def test_combine_parity(T, d, K, E_s, dtype):
-    say(f"moe_combine T={T} d={d} K={K} E_s={E_s} {dtype}")
+@pytest.mark.parametrize("T,d,K,E_s,dtype,drop", [
+    (64, 128, 2, 0, torch.float32, False),
+    (333, 256, 8, 1, torch.bfloat16, False),
+    (100, 7168, 8, 2, torch.bfloat16, False),
+    (31, 64, 1, 0, torch.bfloat16, False),
+    # rows of 125 and 65 16-byte chunks: a ragged tail per wave; row strides
+    # that are not powers of two
+    (150, 1000, 4, 1, torch.bfloat16, False),
+    (77, 520, 3, 0, torch.bfloat16, True),
+    (500, 7168, 8, 1, torch.bfloat16, True),
+])
+def test_combine_parity(T, d, K, E_s, dtype, drop):
+    say(f"moe_combine T={T} d={d} K={K} E_s={E_s} {dtype} dropped slots={drop}")
     rng = np.random.default_rng(T + K)
     h = _tokens(T, d, dtype, 81)
     yp = _tokens(T * K, d, dtype, 82, 0.3)
     ys = _tokens(E_s * T, d, dtype, 83, 0.5) if E_s else None
     perm = rng.permutation(T * K).astype(np.int32)
+    if drop:   # copies dropped by a capacity limit carry slot -1 and add nothing
+        perm[rng.random(T * K) < 0.2] = -1
     g = rng.random((T, K)).astype(np.float32)
     g /= g.sum(1, keepdims=True)
     y = _combine_gpu(h, ys, yp, torch.from_numpy(perm).to(DEV), torch.from_numpy(g).to(DEV), E_s)
