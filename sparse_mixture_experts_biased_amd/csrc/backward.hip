@@ -28,7 +28,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kBM = 128, kBN = 128, kBK = 64;  // tile
 constexpr int kThreads = 256;                   // 4 waves, 2 x 2, 64 x 64 each
 constexpr int kRowBytes = kBK * 2;
-constexpr int kStage = (kBM + kBN) * kRowBytes;  // 32 KB
 constexpr int kBufferFlags = 0x00020000;
 constexpr uint32_t kOff = 0x80000000u;          // beyond every buffer (< 2 GiB)
 constexpr int kPad = 64;                         // expert rows padded to this in the
@@ -69,15 +68,43 @@ struct GemmArgs {
   int f;
 };
 
-// C = A B^T over one 128 x 128 tile; K in 64-wide slices, one register set of
-// global loads in flight while the previous slice is multiplied out of LDS.
-template <int MODE, int EPI>
-__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+// C = A B^T over one 128 x 128 tile; K in 64-wide slices.  Three register
+// sets rotate through the global loads, so up to three slices are in flight
+// while one is multiplied out of LDS: a weight-gradient tile (K = an expert's
+// padded rows, usually two or three slices) has every load in flight from the
+// start, and the long-K products keep three slices streaming.
+constexpr int kSets = 3;
+
+//
+// Tile 128 x BN with four waves in a 2 x 2 layout, each 64 rows x BN / 2
+// columns: 128 x 128 for the products over grouped rows, 128 x 256 for the
+// weight gradients, whose output rows are long (d_model or d_ffn wide): each
+// output row then leaves as a 512-byte piece (256-byte pieces scattered over
+// long rows cost about half of the HBM write rate), and the operands read per
+// byte written drop from 2 to 1.5 at 128 padded rows.
+//
+// LEAN: one LDS stage and one register set instead of two and three (the
+// weight-gradient tiles have only a few slices each, and their larger
+// accumulator tile needs the registers).
+template <int MODE, int EPI, int BM, int BN, bool LEAN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_gemm_kernel(GemmArgs p) {
+  static_assert(BM == 128, "two waves of 64 rows along M");
+  static_assert(EPI == kEpiStore || (BM == 128 && BN == 128), "SwiGLU epilogue on 128 x 128");
+  constexpr int kWN = 2;                           // waves along N (2 x 2 waves)
+  constexpr int kNB = BN / kWN / 32;               // 32-wide column blocks per wave
+  constexpr int kWNC = BN / kWN;                   // columns per wave
+  constexpr int kAP = BM / 32, kBP = BN / 32;      // load passes (32 rows each)
+  constexpr int kStageT = (BM + BN) * kRowBytes;
+  // operand stages, and the output tile staged by the epilogue (two tiles, dA
+  // and dU, for the SwiGLU-derivative epilogue)
+  constexpr int kSmem0 = (LEAN ? 1 : 2) * kStageT;
+  constexpr int kSmem1 = BM * BN * 2 * (EPI == kEpiSwigluBwd ? 2 : 1);
+  __shared__ __attribute__((aligned(16))) char smem[kSmem0 > kSmem1 ? kSmem0 : kSmem1];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int lc = tid & 7, lr = tid >> 3;  // 32 rows per load pass
 
   int g, m0, nrows, n0, kbeg, nk;
@@ -87,8 +114,8 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     const TileInfo ti = p.tiles[w / p.NT];
     g = ti.group;
     m0 = ti.m0;
-    nrows = min(ti.m1 - ti.m0, kBM);
-    n0 = (w % p.NT) * kBN;
+    nrows = min(ti.m1 - ti.m0, BM);
+    n0 = (w % p.NT) * BN;
     kbeg = 0;
     nk = p.K / kBK;
   } else {
@@ -96,20 +123,20 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     if (w >= p.n_groups * p.MT * p.NT) return;
     g = w / (p.MT * p.NT);
     const int rem = w % (p.MT * p.NT);
-    m0 = (rem / p.NT) * kBM;
-    nrows = min(p.M - m0, kBM);
-    n0 = (rem % p.NT) * kBN;
+    m0 = (rem / p.NT) * BM;
+    nrows = min(p.M - m0, BM);
+    n0 = (rem % p.NT) * BN;
     kbeg = p.kpad[g];
     nk = (p.kpad[g + 1] - kbeg) / kBK;
   }
 
   // ---- operand sources
   __amdgpu_buffer_rsrc_t rsA, rsB;
-  uint32_t a_off[4], b_off[4];
+  uint32_t a_off[kAP], b_off[kBP];
   if (MODE == kModeRows) {
     rsA = rsrc(p.A, static_cast<uint32_t>(p.a_rows) * p.lda * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAP; ++i) {
       const int r = lr + 32 * i;
       int sr = -1;
       if (r < nrows) {
@@ -121,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     rsB = rsrc(p.B + static_cast<size_t>(g) * p.b_stride,
                static_cast<uint32_t>(p.N) * p.ldb * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kBP; ++i) {
       const int n = n0 + lr + 32 * i;
       b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * p.ldb + lc * 8) * 2u : kOff;
     }
@@ -130,73 +157,108 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     rsA = rsrc(p.A + static_cast<size_t>(kbeg) * p.M, static_cast<uint32_t>(p.M) * mpad * 2u);
     rsB = rsrc(p.B + static_cast<size_t>(kbeg) * p.N, static_cast<uint32_t>(p.N) * mpad * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAP; ++i) {
       const int m = m0 + lr + 32 * i;
-      const int n = n0 + lr + 32 * i;
       a_off[i] = m < p.M ? (static_cast<uint32_t>(m) * mpad + lc * 8) * 2u : kOff;
+    }
+#pragma unroll
+    for (int i = 0; i < kBP; ++i) {
+      const int n = n0 + lr + 32 * i;
       b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * mpad + lc * 8) * 2u : kOff;
     }
   }
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][kNB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kNB; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
 
-  uint4 sa[4], sb[4];
-  auto load = [&](int kt) {
+  auto load = [&](uint4 (&sa)[kAP], uint4 (&sb)[kBP], int kt) {
     const uint32_t kb = static_cast<uint32_t>(kt) * kBK * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kAP; ++i)
       sa[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0));
-      sb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, b_off[i], kb, 0));
-    }
-  };
-  auto store = [&](int stage) {
-    char* as = smem + stage * kStage;
-    char* bs = as + kBM * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(as + swz(lr + 32 * i, lc)) = sa[i];
-      *reinterpret_cast<uint4*>(bs + swz(lr + 32 * i, lc)) = sb[i];
-    }
+    for (int i = 0; i < kBP; ++i)
+      sb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, b_off[i], kb, 0));
+  };
+  auto store = [&](const uint4 (&sa)[kAP], const uint4 (&sb)[kBP], int stage) {
+    char* as = smem + stage * kStageT;
+    char* bs = as + BM * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kAP; ++i) *reinterpret_cast<uint4*>(as + swz(lr + 32 * i, lc)) = sa[i];
+#pragma unroll
+    for (int i = 0; i < kBP; ++i) *reinterpret_cast<uint4*>(bs + swz(lr + 32 * i, lc)) = sb[i];
   };
   const int fr = lane & 31, fh = lane >> 5;
   const bool busy = wm * 64 < nrows;
   auto compute = [&](int stage) {
     if (!busy) return;
-    const char* as = smem + stage * kStage;
-    const char* bs = as + kBM * kRowBytes;
+    const char* as = smem + stage * kStageT;
+    const char* bs = as + BM * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int c = kk * 2 + fh;
-      bf16x8_t af[2], bq[2];
+      bf16x8_t af[2], bq[kNB];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
+      for (int x = 0; x < 2; ++x)
         af[x] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + x * 32 + fr, c));
-        bq[x] = *reinterpret_cast<const bf16x8_t*>(bs + swz(wn * 64 + x * 32 + fr, c));
-      }
+#pragma unroll
+      for (int x = 0; x < kNB; ++x)
+        bq[x] = *reinterpret_cast<const bf16x8_t*>(bs + swz(wn * kWNC + x * 32 + fr, c));
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kNB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bq[b], acc[a][b], 0, 0, 0);
     }
   };
 
-  if (nk > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load(kt + 1);
-      compute(kt & 1);
-      if (kt + 1 < nk) store((kt + 1) & 1);
+  // Step J multiplies slice J (LDS stage J % 2), refills the register set
+  // that held it with slice J + 3 (past the end it re-reads the last slice, an
+  // L2 hit, so every step issues the same loads and the waits stay exact) and
+  // stores slice J + 1 to the other stage.
+  if (LEAN && nk > 0) {
+    // step J: store slice J to the stage, load slice J + 1 into the freed
+    // registers, multiply slice J
+    uint4 sa0[kAP], sb0[kBP];
+    load(sa0, sb0, 0);
+    for (int kt = 0;; ++kt) {
+      store(sa0, sb0, 0);
+      __syncthreads();
+      load(sa0, sb0, min(kt + 1, nk - 1));
+      compute(0);
+      if (kt + 1 >= nk) break;
       __syncthreads();
     }
+    __syncthreads();
+  } else if (nk > 0) {
+    static_assert(kSets == 3, "the step sequence below rotates three sets");
+    uint4 sa0[kAP], sb0[kBP], sa1[kAP], sb1[kBP], sa2[kAP], sb2[kBP];
+    load(sa0, sb0, 0);
+    load(sa1, sb1, min(1, nk - 1));
+    load(sa2, sb2, min(2, nk - 1));
+    store(sa0, sb0, 0);
+    __syncthreads();
+#define MOE_BSTEP(J, LA, LB, STAGE, SA, SB) \
+  load(LA, LB, min((J) + kSets, nk - 1));   \
+  compute(STAGE);                           \
+  if ((J) + 1 >= nk) break;                 \
+  store(SA, SB, (STAGE) ^ 1);               \
+  __syncthreads();
+    for (int kt = 0;; kt += 6) {
+      MOE_BSTEP(kt + 0, sa0, sb0, 0, sa1, sb1)
+      MOE_BSTEP(kt + 1, sa1, sb1, 1, sa2, sb2)
+      MOE_BSTEP(kt + 2, sa2, sb2, 0, sa0, sb0)
+      MOE_BSTEP(kt + 3, sa0, sb0, 1, sa1, sb1)
+      MOE_BSTEP(kt + 4, sa1, sb1, 0, sa2, sb2)
+      MOE_BSTEP(kt + 5, sa2, sb2, 1, sa0, sb0)
+    }
+#undef MOE_BSTEP
+    __syncthreads();
   }
 
   // ---- epilogue through LDS (both stages are free after the last barrier):
@@ -204,19 +266,23 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
   // with row & 4, which separates the two half-waves) and written as whole
   // 16-byte row chunks.  D[row][col] of a 32x32 block is in lane
   // col + 32*((row/4)%2), register (row%4) + 4*(row/8).
-  constexpr int kORow = kBN * 2;                  // 256 B per staged row
-  char* o0 = smem;                                // [128][128] bf16
-  char* o1 = smem + kBM * kORow;                  // second tile (du) for kEpiSwigluBwd
+  constexpr int kORow = BN * 2;                   // bytes per staged row
+  constexpr int kOC = BN / 8;                     // 16-byte chunks per row
+  constexpr int kORP = kThreads / kOC;            // rows per read-out pass
+  static_assert(kORP % 8 == 0, "read-out rows keep row & 4");
+  static_assert(BM * kORow * (EPI == kEpiSwigluBwd ? 2 : 1) <= sizeof(smem), "staging fits");
+  char* o0 = smem;                                // [BM][BN] bf16
+  char* o1 = smem + BM * kORow;                   // second tile (du) for kEpiSwigluBwd
   auto opos = [&](int row, int col) {
     return row * kORow + ((((col >> 3) ^ (row & 4))) << 4) + (col & 7) * 2;
   };
-  const int rl = tid / 16, cl = tid % 16;          // read-out: 16 chunks per row, 16 rows per pass
+  const int rl = tid / kOC, cl = tid % kOC;       // read-out position
   const size_t cbase = MODE == kModeRows ? 0 : static_cast<size_t>(g) * p.c_stride;
   if (EPI == kEpiSwigluBwd) {
     // a | u of the tile's rows into the two staging tiles (16-byte loads)
 #pragma unroll
-    for (int it = 0; it < kBM / 16; ++it) {
-      const int row = it * 16 + rl;
+    for (int it = 0; it < BM / kORP; ++it) {
+      const int row = it * kORP + rl;
       uint4 av = make_uint4(0, 0, 0, 0), uv = av;
       if (row < nrows && n0 + cl * 8 < p.N) {
         const size_t r = static_cast<size_t>(m0 + row) * (2 * p.f);
@@ -234,8 +300,8 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     for (int q = 0; q < 16; ++q) {
       const int row = wm * 64 + a * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int col = wn * 64 + b * 32 + fr;
+      for (int b = 0; b < kNB; ++b) {
+        const int col = wn * kWNC + b * 32 + fr;
         const float v = acc[a][b][q];
         uint16_t* p0 = reinterpret_cast<uint16_t*>(o0 + opos(row, col));
         if (EPI == kEpiSwigluBwd) {
@@ -251,8 +317,8 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(GemmArgs p) {
     }
   __syncthreads();
 #pragma unroll
-  for (int it = 0; it < kBM / 16; ++it) {
-    const int row = it * 16 + rl;
+  for (int it = 0; it < BM / kORP; ++it) {
+    const int row = it * kORP + rl;
     if (row >= nrows || n0 + cl * 8 >= p.N) continue;
     const size_t r = static_cast<size_t>(m0 + row);
     const int sw = (cl ^ (row & 4)) << 4;
@@ -529,10 +595,15 @@ __global__ __launch_bounds__(256) void transpose_experts_kernel(int rows, int co
   }
 }
 
+// Products over grouped rows use 128 x 128 tiles, weight gradients 64 x 256.
+constexpr int kWM = 128, kWN = 256;
+
 template <int MODE, int EPI>
 hipError_t gemm(const GemmArgs& a, unsigned blocks, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, EPI>), dim3(blocks), dim3(kThreads), 0, s, a);
+  constexpr int BM = MODE == kModeKvar ? kWM : kBM, BN = MODE == kModeKvar ? kWN : kBN;
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, EPI, BM, BN, MODE == kModeKvar>), dim3(blocks),
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -639,7 +710,7 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   k.n_groups = n_groups;
   k.kpad = w.kpad;
   //    dW_gate [f, d] = da^T x ; dW_up = du^T x
-  k.M = f; k.N = d; k.MT = (f + kBM - 1) / kBM; k.NT = (d + kBN - 1) / kBN;
+  k.M = f; k.N = d; k.MT = (f + kWM - 1) / kWM; k.NT = (d + kWN - 1) / kWN;
   k.B = w.xT; k.ldc = d; k.c_stride = static_cast<size_t>(f) * d;
   const unsigned gb = static_cast<unsigned>(n_groups) * k.MT * k.NT;
   k.A = w.daT; k.C = dwg;
@@ -647,7 +718,7 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   k.A = w.duT; k.C = dwu;
   if ((err = gemm<kModeKvar, kEpiStore>(k, gb, s)) != hipSuccess) return err;
   //    dW_down [d, f] = dy^T act
-  k.M = d; k.N = f; k.MT = (d + kBM - 1) / kBM; k.NT = (f + kBN - 1) / kBN;
+  k.M = d; k.N = f; k.MT = (d + kWM - 1) / kWM; k.NT = (f + kWN - 1) / kWN;
   k.A = w.dyT; k.B = w.actT; k.C = dwd; k.ldc = f; k.c_stride = static_cast<size_t>(d) * f;
   return gemm<kModeKvar, kEpiStore>(k, static_cast<unsigned>(n_groups) * k.MT * k.NT, s);
 }
