@@ -369,14 +369,18 @@ enum { kTrCopy = 0, kTrAct = 1 };
 // 64 source columns into the expert's [C, mpad] block: dst column = the row's
 // position inside its expert.  The expert's last tile also writes the zero
 // padding columns.  kTrAct: the source value is SiLU(a) * u from src = [a | u]
-// (ld 2C).  Grid (tiles, C / 64), 256 threads.
+// (ld 2C).  Grid (tiles, C / 64), 256 threads.  Global traffic is in 16-byte
+// pieces both ways (8 columns of a source row in, 8 consecutive block columns
+// of a destination row out; tile starts inside an expert and the padded widths
+// are multiples of 64), transposed through LDS.
 template <int TR>
 __global__ __launch_bounds__(256) void pad_transpose_kernel(
     int C, int rows, int src_rows, const TileInfo* __restrict__ tiles,
     const int32_t* __restrict__ meta, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ kpad, const int32_t* __restrict__ row_index,
     const uint16_t* __restrict__ src, int ld_src, uint16_t* __restrict__ dst) {
-  __shared__ uint16_t t[64][kBM + 2];
+  constexpr int kTR = kBM + 8;  // LDS row: 128 tile rows + 16 bytes of skew
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][kTR];
   if (static_cast<int>(blockIdx.x) >= meta[0]) return;
   const TileInfo ti = tiles[blockIdx.x];
   const int g = ti.group;
@@ -386,33 +390,52 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(
   const int gstart = offsets[g];
   const int mpad = kpad[g + 1] - kpad[g];
   uint16_t* blk = dst + static_cast<size_t>(kpad[g]) * C;  // [C, mpad]
-  // load: rows m0..m0+nr, columns c0..c0+63
-  for (int q = threadIdx.x; q < kBM * 64; q += 256) {
-    const int r = q / 64, c = q % 64;
-    uint16_t v = 0;
-    if (r < nr && c0 + c < C) {
+  // load: rows m0..m0+nr, columns c0..c0+63, one 16-byte piece (8 columns) per step
+  for (int q = threadIdx.x; q < kBM * 8; q += 256) {
+    const int r = q / 8, c8 = (q % 8) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < nr && c0 + c8 < C) {
       const int gr = m0 + r;
-      int sr = row_index ? row_index[gr] : gr;
+      const int sr = row_index ? row_index[gr] : gr;
       if (sr >= 0 && sr < src_rows) {
+        const uint16_t* sp = src + static_cast<size_t>(sr) * ld_src + c0 + c8;
         if (TR == kTrAct) {
-          const float a = bf16_to_f32(src[static_cast<size_t>(sr) * ld_src + c0 + c]);
-          const float u = bf16_to_f32(src[static_cast<size_t>(sr) * ld_src + C + c0 + c]);
-          v = f32_to_bf16(silu(a) * u);
+          const uint4 av = *reinterpret_cast<const uint4*>(sp);
+          const uint4 uv = *reinterpret_cast<const uint4*>(sp + C);
+          const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = silu(__uint_as_float(aw[i] << 16)) * __uint_as_float(uw[i] << 16);
+            const float hi = silu(__uint_as_float(aw[i] & 0xffff0000u)) *
+                             __uint_as_float(uw[i] & 0xffff0000u);
+            o[i] = pack_bf16x2(lo, hi);
+          }
+          v = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
-          v = src[static_cast<size_t>(sr) * ld_src + c0 + c];
+          v = *reinterpret_cast<const uint4*>(sp);
         }
       }
     }
-    t[c][r] = v;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[c8 + 2 * i][r] = static_cast<uint16_t>(w[i] & 0xffffu);
+      t[c8 + 2 * i + 1][r] = static_cast<uint16_t>(w[i] >> 16);
+    }
   }
   __syncthreads();
   const int p0 = m0 - gstart;  // first column of this tile inside the expert block
   const bool last = ti.m1 - m0 <= kBM;
   const int width = last ? mpad - p0 : nr;  // the last tile also writes the padding
-  for (int q = threadIdx.x; q < 64 * width; q += 256) {
-    const int c = q / width, r = q % width;
+  // width <= 128 (the padding rounds the last tile's rows up to 64), and LDS
+  // rows past nr hold the zeros the load wrote for them
+  const int w8 = width / 8;
+  for (int q = threadIdx.x; q < 64 * w8; q += 256) {
+    const int c = q / w8, r8 = (q % w8) * 8;
     if (c0 + c >= C) continue;
-    blk[static_cast<size_t>(c0 + c) * mpad + p0 + r] = r < nr ? t[c][r] : 0;
+    *reinterpret_cast<uint4*>(blk + static_cast<size_t>(c0 + c) * mpad + p0 + r8) =
+        *reinterpret_cast<const uint4*>(&t[c][r8]);
   }
 }
 
