@@ -440,7 +440,13 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(
 }
 
 // Combine backward, one wave per token: dy_perm[slot] = g * dy_t (output
-// dtype), dgates = <dy_t, y_perm[slot]> in fp32 (0 for a dropped copy).
+// rows of dropped copies are not written) and dg[t, k] = <dy_t, y_perm[slot]>
+// (0 for a dropped copy).  16-byte pieces: per piece of dy_t all K rows are
+// loaded before any is used; a dropped slot reads zeros and writes nothing
+// through an out-of-range buffer offset.  The K dot products are reduced
+// across the wave once at the end.
+constexpr uint32_t kOffNoRow = 0x80000000u;
+
 __global__ __launch_bounds__(256) void combine_bwd_kernel(int T, int d, int K, int TK,
                                                           const uint16_t* __restrict__ dy,
                                                           const uint16_t* __restrict__ yp,
@@ -448,28 +454,65 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(int T, int d, int K, i
                                                           const float* __restrict__ gates,
                                                           uint16_t* __restrict__ dyp,
                                                           float* __restrict__ dg) {
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   if (t >= T) return;
-  const uint16_t* dyt = dy + static_cast<size_t>(t) * d;
-  for (int k = 0; k < K; ++k) {
-    const int s = slot_row[static_cast<size_t>(t) * K + k];
-    if (s < 0 || s >= TK) {
-      if (lane == 0) dg[static_cast<size_t>(t) * K + k] = 0.0f;
-      continue;
-    }
-    const float gk = gates[static_cast<size_t>(t) * K + k];
-    const uint16_t* ys = yp + static_cast<size_t>(s) * d;
-    uint16_t* out = dyp + static_cast<size_t>(s) * d;
-    float dot = 0.0f;
-    for (int c = lane; c < d; c += kWave) {
-      const float v = bf16_to_f32(dyt[c]);
-      dot += v * bf16_to_f32(ys[c]);
-      out[c] = f32_to_bf16(gk * v);
+  const int vecs = d / 8;
+  const uint32_t bytes = static_cast<uint32_t>(TK) * d * 2u;
+  const __amdgpu_buffer_rsrc_t rsY = rsrc(yp, bytes), rsO = rsrc(dyp, bytes);
+  const int sl = lane < K ? slot_row[static_cast<size_t>(t) * K + lane] : -1;
+  const float gl = lane < K ? gates[static_cast<size_t>(t) * K + lane] : 0.0f;
+  uint32_t off[MOE_MAX_TOPK_DEV];
+  float g[MOE_MAX_TOPK_DEV], dot[MOE_MAX_TOPK_DEV];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    const int sk = __builtin_amdgcn_readlane(sl, k);
+    off[k] = (k < K && sk >= 0 && sk < TK) ? static_cast<uint32_t>(sk) * d * 2u : kOffNoRow;
+    g[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), k));
+    dot[k] = 0.0f;
+  }
+  const uint4* dyr = reinterpret_cast<const uint4*>(dy + static_cast<size_t>(t) * d);
+  for (int c = lane; c < vecs; c += kWave) {
+    const uint4 dv = dyr[c];
+    const uint32_t cb = static_cast<uint32_t>(c) * 16u;
+    uint4 yv[MOE_MAX_TOPK_DEV];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (k < K)
+        yv[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsY, off[k] + cb, 0, 0));
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+    float df[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      df[2 * i] = __uint_as_float(dw[i] << 16);
+      df[2 * i + 1] = __uint_as_float(dw[i] & 0xffff0000u);
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
-    if (lane == 0) dg[static_cast<size_t>(t) * K + k] = dot;
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+      if (k < K) {
+        const uint32_t yw[4] = {yv[k].x, yv[k].y, yv[k].z, yv[k].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dot[k] = fmaf(df[2 * i], __uint_as_float(yw[i] << 16), dot[k]);
+          dot[k] = fmaf(df[2 * i + 1], __uint_as_float(yw[i] & 0xffff0000u), dot[k]);
+          o[i] = pack_bf16x2(g[k] * df[2 * i], g[k] * df[2 * i + 1]);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                               make_uint4(o[0], o[1], o[2], o[3])),
+            rsO, off[k] + cb, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    if (k < K) {
+      float v = dot[k];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+      if (lane == 0) dg[static_cast<size_t>(t) * K + k] = v;
+    }
   }
 }
 
