@@ -272,7 +272,8 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
  *   gates    [T, K] fp32
  *   y        [T, d_model] out (dtype), fp32 accumulation in a fixed order,
  *            bf16 output rounded to nearest even.  Deterministic.
- * Limits: d_model % 8 == 0.
+ * Limits: d_model % 8 == 0; bf16 y_perm under 2 GiB (it is read through one
+ * buffer descriptor), else MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h,
                        const void* y_shared, const void* y_perm, const int32_t* slot_row,
@@ -384,7 +385,8 @@ moe_status moe_transpose_experts(int n, int rows, int cols, const void* src, moe
  *   dy_perm [T*K, d_model] out: row slot_row[t,k] = g_{t,k} dy_t (rows of
  *           dropped copies are not written)
  *   dgates  [T, K] fp32 out: <dy_t, y_perm[slot_row[t,k]]> (0 when dropped)
- * The residual and the shared experts receive dy itself.  bf16 only.
+ * The residual and the shared experts receive dy itself.  bf16 only, d_model
+ * a multiple of 8, y_perm under 2 GiB (else MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_combine_backward(int T, int d_model, int K, const void* dy, const void* y_perm,
                                 const int32_t* slot_row, const float* gates, moe_dtype dtype,
@@ -430,6 +432,7 @@ moe_status moe_grouped_swiglu_backward(int n_groups, int d_model, int d_ffn, int
  *   dz        [T, K] fp32 out: dL/dz of the picks
  *   dh        [T, d_model] in/out (bf16): dh_t += sum_k dz_{t,k} e_{idx[t,k]}
  *   de        [E_r, d_model] fp32 out: sum over picks of dz h_t (fixed order)
+ * bf16 tokens, d_model a multiple of 8 (else MOE_ERR_UNSUPPORTED).
  */
 moe_status moe_route_backward(int T, int d_model, int E_r, int K, moe_score_fn fn, const void* h,
                               moe_dtype h_dtype, const float* e, const int32_t* topk_idx,

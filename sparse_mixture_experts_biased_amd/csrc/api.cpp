@@ -276,6 +276,8 @@ moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h, const 
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
   if (static_cast<long long>(T) * K > INT32_MAX)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: T*K overflows int32");
+  if (dtype == MOE_BF16 && static_cast<long long>(T) * K * d_model * 2 >= (1ll << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_combine: bf16 y_perm exceeds 2 GiB");
   return hip_status(moe::launch_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates,
                                         dtype == MOE_BF16, y, as_stream(stream)),
                     "moe_combine");
@@ -461,6 +463,11 @@ moe_status moe_combine_backward(int T, int d_model, int K, const void* dy, const
   if (static_cast<long long>(T) * K > INT32_MAX)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine_backward: T*K overflows int32");
   if (dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_combine_backward: bf16 only");
+  if (d_model % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_combine_backward: d_model=%d must be a multiple of 8",
+                d_model);
+  if (static_cast<long long>(T) * K * d_model * 2 >= (1ll << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_combine_backward: y_perm exceeds 2 GiB");
   if (!dy || !y_perm || !slot_row || !gates || !dy_perm || !dgates)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine_backward: null pointer");
   return hip_status(moe::launch_combine_backward(T, d_model, K, static_cast<const uint16_t*>(dy),
@@ -537,6 +544,8 @@ moe_status moe_route_backward(int T, int d_model, int E_r, int K, moe_score_fn f
   if (fn != MOE_SIGMOID && fn != MOE_SOFTMAX)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown score function %d", nm, (int)fn);
   if (h_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 tokens only", nm);
+  if (d_model % 8 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d_model=%d must be a multiple of 8", nm, d_model);
   if (!h || !e || !topk_idx || !dgates || !offsets || !row_token || !dz || !dh || !de)
     return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", nm);
   if (static_cast<long long>(T) * K > INT32_MAX)

@@ -517,35 +517,66 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(int T, int d, int K, i
 }
 
 // Router backward, one wave per token: logits of the K picks, dz, and
-// dh_t += sum_k dz_k e_k (dh in the tokens' dtype).
+// dh_t += sum_k dz_k e_k (dh in the tokens' dtype).  Each lane takes 8
+// consecutive columns per step (16 bytes of h or dh, 32 of each centroid row),
+// with the K centroid pieces loaded before any is used; the K logits are
+// reduced across the wave once.
 __global__ __launch_bounds__(256) void route_bwd_token_kernel(
     int T, int d, int E, int K, int fn, const uint16_t* __restrict__ h, const float* __restrict__ e,
     const int32_t* __restrict__ idx, const float* __restrict__ dg, float* __restrict__ dz_out,
     uint16_t* __restrict__ dh) {
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   if (t >= T) return;
-  const uint16_t* ht = h + static_cast<size_t>(t) * d;
-  float z[MOE_MAX_TOPK_DEV], w[MOE_MAX_TOPK_DEV], dgk[MOE_MAX_TOPK_DEV];
+  const int vecs = d / 8;
+  const int il = lane < K ? idx[static_cast<size_t>(t) * K + lane] : -1;
+  const float dgl = lane < K ? dg[static_cast<size_t>(t) * K + lane] : 0.0f;
   int id[MOE_MAX_TOPK_DEV];
+  float z[MOE_MAX_TOPK_DEV], w[MOE_MAX_TOPK_DEV], dgk[MOE_MAX_TOPK_DEV];
 #pragma unroll
   for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    const int i = __builtin_amdgcn_readlane(il, k);
+    id[k] = (k < K && i >= 0 && i < E) ? i : -1;
+    dgk[k] = id[k] >= 0 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, dgl), k))
+                        : 0.0f;
     z[k] = 0.0f;
-    id[k] = -1;
-    dgk[k] = 0.0f;
-    if (k < K) {
-      int i = idx[static_cast<size_t>(t) * K + k];
-      if (i < 0 || i >= E) continue;
-      id[k] = i;
-      dgk[k] = dg[static_cast<size_t>(t) * K + k];
-      const float* ei = e + static_cast<size_t>(i) * d;
-      float acc = 0.0f;
-      for (int c = lane; c < d; c += kWave) acc += bf16_to_f32(ht[c]) * ei[c];
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
-      z[k] = acc;
-    }
   }
+  const uint4* hr = reinterpret_cast<const uint4*>(h + static_cast<size_t>(t) * d);
+  auto h8 = [](const uint4& v, float (&f)[8]) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(u[i] << 16);
+      f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  };
+  for (int c = lane; c < vecs; c += kWave) {
+    float hf[8];
+    h8(hr[c], hf);
+    float4 ev[MOE_MAX_TOPK_DEV][2];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (id[k] >= 0) {
+        const float4* er = reinterpret_cast<const float4*>(e + static_cast<size_t>(id[k]) * d) + 2 * c;
+        ev[k][0] = er[0];
+        ev[k][1] = er[1];
+      }
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (id[k] >= 0) {
+        const float ef[8] = {ev[k][0].x, ev[k][0].y, ev[k][0].z, ev[k][0].w,
+                             ev[k][1].x, ev[k][1].y, ev[k][1].z, ev[k][1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[k] = fmaf(hf[j], ef[j], z[k]);
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (id[k] >= 0) {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) z[k] += __shfl_xor(z[k], m, kWave);
+    }
   // g over the picks and dz (wave-uniform scalars)
   float gsum = 0.0f, zmax = -INFINITY;
 #pragma unroll
@@ -576,13 +607,28 @@ __global__ __launch_bounds__(256) void route_bwd_token_kernel(
       if (k == lane) v = dz[k];
     dz_out[static_cast<size_t>(t) * K + lane] = v;
   }
-  uint16_t* dht = dh + static_cast<size_t>(t) * d;
-  for (int c = lane; c < d; c += kWave) {
-    float acc = bf16_to_f32(dht[c]);
+  uint4* dhr = reinterpret_cast<uint4*>(dh + static_cast<size_t>(t) * d);
+  for (int c = lane; c < vecs; c += kWave) {
+    float acc[8];
+    h8(dhr[c], acc);
+    float4 ev[MOE_MAX_TOPK_DEV][2];
 #pragma unroll
     for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
-      if (id[k] >= 0) acc += dz[k] * e[static_cast<size_t>(id[k]) * d + c];
-    dht[c] = f32_to_bf16(acc);
+      if (id[k] >= 0) {
+        const float4* er = reinterpret_cast<const float4*>(e + static_cast<size_t>(id[k]) * d) + 2 * c;
+        ev[k][0] = er[0];
+        ev[k][1] = er[1];
+      }
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (id[k] >= 0) {
+        const float ef[8] = {ev[k][0].x, ev[k][0].y, ev[k][0].z, ev[k][0].w,
+                             ev[k][1].x, ev[k][1].y, ev[k][1].z, ev[k][1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(dz[k], ef[j], acc[j]);
+      }
+    dhr[c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }
 }
 

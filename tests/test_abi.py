@@ -135,10 +135,15 @@ def test_backward_entry_points_reject_bad_arguments():
     assert lib.moe_grouped_swiglu_backward(*bad, need, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine_backward(10, 64, 2, P, P, P, P, 0, P, P, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine_backward(10, 64, 2, P, P, P, P, 1, None, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_backward(10, 60, 2, P, P, P, P, 1, P, P, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_backward(1 << 17, 8192, 8, P, P, P, P, 1, P, P, None) == \
+        L.MOE_ERR_UNSUPPORTED   # y_perm of 2^17 * 8 rows x 8192 bf16 = 16 GiB
     assert lib.moe_route_backward(10, 64, 8, 9, 0, P, 1, P, P, P, P, P, P, P, P, None) == \
         L.MOE_ERR_INVALID_ARG
     assert lib.moe_route_backward(10, 64, 8, 2, 0, P, 0, P, P, P, P, P, P, P, P, None) == \
         L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_backward(10, 60, 8, 2, 0, P, 1, P, P, P, P, P, P, P, P, None) == \
+        L.MOE_ERR_UNSUPPORTED   # d_model not a multiple of 8
     assert lib.moe_transpose_experts(2, 10, 20, P, 1, P, 9, 0, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_transpose_experts(2, 10, 20, P, 0, P, 10, 0, None) == L.MOE_ERR_UNSUPPORTED
 
@@ -175,6 +180,8 @@ def test_combine_and_bias_update_reject_bad_arguments():
     assert lib.moe_combine(10, 64, 2, 1, P, None, P, P, P, 1, P, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(10, 60, 2, 0, P, None, P, P, P, 1, P, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(10, 64, 17, 0, P, None, P, P, P, 1, P, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(1 << 17, 8192, 8, 0, P, None, P, P, P, 1, P, None) == \
+        L.MOE_ERR_UNSUPPORTED   # bf16 y_perm of 16 GiB
     assert lib.moe_bias_update(10, 8, 2, -0.1, P, P, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(10, 8, 2, float("nan"), P, P, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(10, 8, 2, 0.1, None, P, None, None) == L.MOE_ERR_INVALID_ARG
