@@ -14,10 +14,14 @@
 // Every product is an "NT" grouped GEMM (both operands K-contiguous) on
 // v_mfma_f32_32x32x16_bf16: transposed weight copies W_down^T [f, d] and
 // [W_gate^T | W_up^T] [d, 2f] (built once per weight update) serve the
-// activation gradients, and per-expert transposed activations (each expert's
-// rows padded to a multiple of 64 and laid out as its own [C, rows] block)
-// serve the weight gradients, whose K is the expert's row count.
+// activation gradients, which run on the forward pass's down-direction
+// streaming kernels (with the SwiGLU derivative as a separate elementwise
+// pass), and per-expert transposed activations (each expert's rows padded to
+// a multiple of 64 and laid out as its own [C, rows] block) serve the weight
+// gradients, whose K is the expert's row count (kernels below).
 #include "swiglu_tiles.h"
+
+#include <algorithm>
 
 namespace moe {
 namespace {
@@ -45,7 +49,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 enum { kModeRows = 0, kModeKvar = 1 };
-enum { kEpiStore = 0, kEpiSwigluBwd = 1 };
 
 struct GemmArgs {
   int M, N, K;             // Rows: N, K used (rows from the tile list); Kvar: M, N
@@ -64,8 +67,6 @@ struct GemmArgs {
   uint16_t* C;             // Rows: [rows, ldc]; Kvar: per group [M, ldc] at C + g * c_stride
   int ldc;
   size_t c_stride;
-  const uint16_t* aux;     // SwigluBwd: [rows, 2f] holding a | u
-  int f;
 };
 
 // C = A B^T over one 128 x 128 tile; K in 64-wide slices.  Three register
@@ -86,20 +87,18 @@ constexpr int kSets = 3;
 // LEAN: one LDS stage and one register set instead of two and three (the
 // weight-gradient tiles have only a few slices each, and their larger
 // accumulator tile needs the registers).
-template <int MODE, int EPI, int BM, int BN, bool LEAN>
+template <int MODE, int BM, int BN, bool LEAN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_gemm_kernel(GemmArgs p) {
   static_assert(BM == 128, "two waves of 64 rows along M");
-  static_assert(EPI == kEpiStore || (BM == 128 && BN == 128), "SwiGLU epilogue on 128 x 128");
   constexpr int kWN = 2;                           // waves along N (2 x 2 waves)
   constexpr int kNB = BN / kWN / 32;               // 32-wide column blocks per wave
   constexpr int kWNC = BN / kWN;                   // columns per wave
   constexpr int kAP = BM / 32, kBP = BN / 32;      // load passes (32 rows each)
   constexpr int kStageT = (BM + BN) * kRowBytes;
-  // operand stages, and the output tile staged by the epilogue (two tiles, dA
-  // and dU, for the SwiGLU-derivative epilogue)
+  // operand stages, and the output tile staged by the epilogue
   constexpr int kSmem0 = (LEAN ? 1 : 2) * kStageT;
-  constexpr int kSmem1 = BM * BN * 2 * (EPI == kEpiSwigluBwd ? 2 : 1);
+  constexpr int kSmem1 = BM * BN * 2;
   __shared__ __attribute__((aligned(16))) char smem[kSmem0 > kSmem1 ? kSmem0 : kSmem1];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -270,30 +269,13 @@ void bwd_gemm_kernel(GemmArgs p) {
   constexpr int kOC = BN / 8;                     // 16-byte chunks per row
   constexpr int kORP = kThreads / kOC;            // rows per read-out pass
   static_assert(kORP % 8 == 0, "read-out rows keep row & 4");
-  static_assert(BM * kORow * (EPI == kEpiSwigluBwd ? 2 : 1) <= sizeof(smem), "staging fits");
+  static_assert(BM * kORow <= sizeof(smem), "staging fits");
   char* o0 = smem;                                // [BM][BN] bf16
-  char* o1 = smem + BM * kORow;                   // second tile (du) for kEpiSwigluBwd
   auto opos = [&](int row, int col) {
     return row * kORow + ((((col >> 3) ^ (row & 4))) << 4) + (col & 7) * 2;
   };
   const int rl = tid / kOC, cl = tid % kOC;       // read-out position
   const size_t cbase = MODE == kModeRows ? 0 : static_cast<size_t>(g) * p.c_stride;
-  if (EPI == kEpiSwigluBwd) {
-    // a | u of the tile's rows into the two staging tiles (16-byte loads)
-#pragma unroll
-    for (int it = 0; it < BM / kORP; ++it) {
-      const int row = it * kORP + rl;
-      uint4 av = make_uint4(0, 0, 0, 0), uv = av;
-      if (row < nrows && n0 + cl * 8 < p.N) {
-        const size_t r = static_cast<size_t>(m0 + row) * (2 * p.f);
-        av = *reinterpret_cast<const uint4*>(p.aux + r + n0 + cl * 8);
-        uv = *reinterpret_cast<const uint4*>(p.aux + r + p.f + n0 + cl * 8);
-      }
-      *reinterpret_cast<uint4*>(o0 + row * kORow + ((cl ^ (row & 4)) << 4)) = av;
-      *reinterpret_cast<uint4*>(o1 + row * kORow + ((cl ^ (row & 4)) << 4)) = uv;
-    }
-    __syncthreads();
-  }
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -302,17 +284,7 @@ void bwd_gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int b = 0; b < kNB; ++b) {
         const int col = wn * kWNC + b * 32 + fr;
-        const float v = acc[a][b][q];
-        uint16_t* p0 = reinterpret_cast<uint16_t*>(o0 + opos(row, col));
-        if (EPI == kEpiSwigluBwd) {
-          uint16_t* p1 = reinterpret_cast<uint16_t*>(o1 + opos(row, col));
-          const float av = bf16_to_f32(*p0), uv = bf16_to_f32(*p1);
-          const float sg = sigm(av);
-          *p0 = f32_to_bf16(v * uv * sg * (1.0f + av * (1.0f - sg)));
-          *p1 = f32_to_bf16(v * av * sg);
-        } else {
-          *p0 = f32_to_bf16(v);
-        }
+        *reinterpret_cast<uint16_t*>(o0 + opos(row, col)) = f32_to_bf16(acc[a][b][q]);
       }
     }
   __syncthreads();
@@ -324,9 +296,45 @@ void bwd_gemm_kernel(GemmArgs p) {
     const int sw = (cl ^ (row & 4)) << 4;
     *reinterpret_cast<uint4*>(p.C + cbase + r * p.ldc + n0 + cl * 8) =
         *reinterpret_cast<const uint4*>(o0 + row * kORow + sw);
-    if (EPI == kEpiSwigluBwd)
-      *reinterpret_cast<uint4*>(p.C + cbase + r * p.ldc + p.f + n0 + cl * 8) =
-          *reinterpret_cast<const uint4*>(o1 + row * kORow + sw);
+  }
+}
+
+// SwiGLU derivative, elementwise over [rows, f] in 8-column pieces: with
+// a | u = au[r], s = sigma(a): da = d act * u * s (1 + a (1 - s)),
+// du = d act * a * s, written as dadu[r] = da | du.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(int rows, int f,
+                                                         const uint16_t* __restrict__ dact,
+                                                         const uint16_t* __restrict__ au,
+                                                         uint16_t* __restrict__ dadu) {
+  const int f8 = f / 8;
+  const long n8 = static_cast<long>(rows) * f8;
+  for (long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+       i += static_cast<long>(gridDim.x) * 256) {
+    const long r = i / f8;
+    const int c = static_cast<int>(i - r * f8) * 8;
+    const uint4 gv = *reinterpret_cast<const uint4*>(dact + r * f + c);
+    const uint4 av = *reinterpret_cast<const uint4*>(au + r * 2 * f + c);
+    const uint4 uv = *reinterpret_cast<const uint4*>(au + r * 2 * f + f + c);
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, aw[4] = {av.x, av.y, av.z, av.w},
+                   uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    uint32_t da[4], du[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float dv[2], dd[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float g = __uint_as_float(h ? (gw[j] & 0xffff0000u) : (gw[j] << 16));
+        const float a = __uint_as_float(h ? (aw[j] & 0xffff0000u) : (aw[j] << 16));
+        const float u = __uint_as_float(h ? (uw[j] & 0xffff0000u) : (uw[j] << 16));
+        const float sg = sigm(a);
+        dv[h] = g * u * sg * (1.0f + a * (1.0f - sg));
+        dd[h] = g * a * sg;
+      }
+      da[j] = pack_bf16x2(dv[0], dv[1]);
+      du[j] = pack_bf16x2(dd[0], dd[1]);
+    }
+    *reinterpret_cast<uint4*>(dadu + r * 2 * f + c) = make_uint4(da[0], da[1], da[2], da[3]);
+    *reinterpret_cast<uint4*>(dadu + r * 2 * f + f + c) = make_uint4(du[0], du[1], du[2], du[3]);
   }
 }
 
@@ -710,11 +718,11 @@ __global__ __launch_bounds__(256) void transpose_experts_kernel(int rows, int co
 // Products over grouped rows use 128 x 128 tiles, weight gradients 64 x 256.
 constexpr int kWM = 128, kWN = 256;
 
-template <int MODE, int EPI>
+template <int MODE>
 hipError_t gemm(const GemmArgs& a, unsigned blocks, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   constexpr int BM = MODE == kModeKvar ? kWM : kBM, BN = MODE == kModeKvar ? kWN : kBN;
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, EPI, BM, BN, MODE == kModeKvar>), dim3(blocks),
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, BM, BN, MODE == kModeKvar>), dim3(blocks),
                      dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -736,6 +744,11 @@ BwdWorkspace bwd_layout(void* base, int n_groups, int d, int f, int rows) {
       take(static_cast<size_t>(max_tiles_for(rows, n_groups, kBM)) * sizeof(TileInfo)));
   w.tiles.group_tile_start = reinterpret_cast<int32_t*>(take((n_groups + 1) * sizeof(int32_t)));
   w.tiles.meta = reinterpret_cast<int32_t*>(take(4 * sizeof(int32_t)));
+  w.tiles256.tiles = reinterpret_cast<TileInfo*>(
+      take(static_cast<size_t>(max_tiles_for(rows, n_groups, 256)) * sizeof(TileInfo)));
+  w.tiles256.group_tile_start =
+      reinterpret_cast<int32_t*>(take((n_groups + 1) * sizeof(int32_t)));
+  w.tiles256.meta = reinterpret_cast<int32_t*>(take(4 * sizeof(int32_t)));
   w.kpad = reinterpret_cast<int32_t*>(take((n_groups + 1) * sizeof(int32_t)));
   w.au = reinterpret_cast<uint16_t*>(take(static_cast<size_t>(rows) * 2 * f * 2));
   w.dadu = reinterpret_cast<uint16_t*>(take(static_cast<size_t>(rows) * 2 * f * 2));
@@ -787,21 +800,32 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
   a.ldc = 2 * f;
   a.B = wg; a.C = w.au;
-  if ((err = gemm<kModeRows, kEpiStore>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
   a.B = wu; a.C = w.au + f;
-  if ((err = gemm<kModeRows, kEpiStore>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
-  // 2. d act = dy W_down (B = W_down^T [f, d]) -> da, du into dadu [rows, 2f]
-  a.row_index = nullptr; a.a_rows = rows;
-  a.A = dy; a.lda = d;
-  a.B = wd_t; a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
-  a.C = w.dadu; a.ldc = 2 * f; a.aux = w.au; a.f = f;
-  if ((err = gemm<kModeRows, kEpiSwigluBwd>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  // 2. d act = dy W_down (B = W_down^T [f, d]) -> [rows, f], held in the daT
+  //    region (rpad >= rows; daT is written only in step 4), with the forward
+  //    pass's down-direction kernels over 256-row tiles; then da, du -> dadu
+  SwigluWorkspace t256{};
+  t256.tiles = w.tiles256.tiles;
+  t256.group_tile_start = w.tiles256.group_tile_start;
+  t256.meta = w.tiles256.meta;
+  uint16_t* dact = w.daT;
+  if ((err = launch_grouped_nt_bf16(n_groups, d, f, rows, offsets, t256, dy, wd_t, dact,
+                                    "bwd_dact_bf16", s)) != hipSuccess)
+    return err;
+  {
+    const long n8 = static_cast<long>(rows) * (f / 8);
+    const unsigned blocks = static_cast<unsigned>(std::min<long>((n8 + 255) / 256, 65536));
+    if (blocks > 0)
+      hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(blocks), dim3(256), 0, s, rows, f, dact, w.au,
+                         w.dadu);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // 3. dx = [da | du] [W_gate^T | W_up^T]^T  (K = 2f, B = [d, 2f]) -> dx [rows, d]
-  a.N = d; a.K = 2 * f; a.NT = (d + kBN - 1) / kBN;
-  a.A = w.dadu; a.lda = 2 * f;
-  a.B = wgu_t; a.ldb = 2 * f; a.b_stride = static_cast<size_t>(d) * 2 * f;
-  a.C = dx; a.ldc = d;
-  if ((err = gemm<kModeRows, kEpiStore>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  if ((err = launch_grouped_nt_bf16(n_groups, 2 * f, d, rows, offsets, t256, w.dadu, wgu_t, dx,
+                                    "bwd_dx_bf16", s)) != hipSuccess)
+    return err;
   // 4. per-expert transposed activations (rows padded to 64 per expert)
   {
     dim3 gd(max_tiles, (d + 63) / 64), gf(max_tiles, (f + 63) / 64);
@@ -826,13 +850,13 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   k.B = w.xT; k.ldc = d; k.c_stride = static_cast<size_t>(f) * d;
   const unsigned gb = static_cast<unsigned>(n_groups) * k.MT * k.NT;
   k.A = w.daT; k.C = dwg;
-  if ((err = gemm<kModeKvar, kEpiStore>(k, gb, s)) != hipSuccess) return err;
+  if ((err = gemm<kModeKvar>(k, gb, s)) != hipSuccess) return err;
   k.A = w.duT; k.C = dwu;
-  if ((err = gemm<kModeKvar, kEpiStore>(k, gb, s)) != hipSuccess) return err;
+  if ((err = gemm<kModeKvar>(k, gb, s)) != hipSuccess) return err;
   //    dW_down [d, f] = dy^T act
   k.M = d; k.N = f; k.MT = (d + kWM - 1) / kWM; k.NT = (f + kWN - 1) / kWN;
   k.A = w.dyT; k.B = w.actT; k.C = dwd; k.ldc = f; k.c_stride = static_cast<size_t>(d) * f;
-  return gemm<kModeKvar, kEpiStore>(k, static_cast<unsigned>(n_groups) * k.MT * k.NT, s);
+  return gemm<kModeKvar>(k, static_cast<unsigned>(n_groups) * k.MT * k.NT, s);
 }
 
 hipError_t launch_combine_backward(int T, int d, int K, const uint16_t* dy, const uint16_t* yp,

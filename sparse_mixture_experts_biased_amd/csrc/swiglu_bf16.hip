@@ -1179,6 +1179,37 @@ int stream_grid() {
   return cached[dev];
 }
 
+// The down-direction product over the tile list in w (built for BM rows):
+// C[r, n] = (A_r . W[g][n]) * (row_scale ? row_scale[r] : 1), K-contiguous A
+// [rows, K] and W [n_groups, N, K], C [rows, N].  The streaming kernels when
+// the shape allows (LDS-fed for groups of at least a row tile on average),
+// else the one-tile-per-workgroup kernel.
+template <int BM, int BNW, int NTHR, int NSETS>
+hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
+                       const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
+                       const float* row_scale, uint16_t* C, const char* name, hipStream_t s) {
+  const int max_tiles = max_tiles_for(rows, n_groups, BM);
+  const int nt = (N + BNW - 1) / BNW;
+  ProfScope prof_(s, name);
+  if (stream_shape(K, N, 256) && mfma_bound) {
+    hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
+                       s, K, N, rows, rows, nt, w.tiles, w.meta, nullptr, A, W, nullptr,
+                       row_scale, C);
+  } else if (stream_shape(K, N, BNW)) {
+    hipLaunchKernelGGL((bf16_regs_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
+                       dim3(NTHR), 0, s, K, N, rows, rows, max_tiles, nt, w.tiles, w.meta,
+                       nullptr, A, W, nullptr, row_scale, C);
+  } else {
+    long blocks = static_cast<long>(max_tiles) * nt;
+    blocks = (blocks + kNumXcd - 1) / kNumXcd * kNumXcd;
+    hipLaunchKernelGGL((bf16_tile_kernel<false, BM, BNW, NTHR, NSETS>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(NTHR), 0, s, K, N, rows,
+                       n_groups, nt, w.tiles, w.group_tile_start, w.meta, nullptr, A, W, nullptr,
+                       row_scale, C);
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BNW, int NTHR, int NSETS>
 hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                         const int32_t* offsets, const int32_t* row_index, const uint16_t* x,
@@ -1217,30 +1248,21 @@ hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_ro
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  const int nt2 = (d_model + BNW - 1) / BNW;
-  if (stream_shape(d_ffn, d_model, 256) && mfma_bound) {
-    ProfScope prof_(s, "down_bf16");
-    hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
-                       s, d_ffn, d_model, rows, rows, nt2, w.tiles, w.meta, nullptr, act, wd,
-                       nullptr, row_scale, y);
-  } else if (stream_shape(d_ffn, d_model, BNW)) {
-    ProfScope prof_(s, "down_bf16");
-    hipLaunchKernelGGL((bf16_regs_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
-                       dim3(NTHR), 0, s, d_ffn, d_model, rows, rows, max_tiles, nt2, w.tiles,
-                       w.meta, nullptr, act, wd, nullptr, row_scale, y);
-  } else {
-    long blocks2 = static_cast<long>(max_tiles) * nt2;
-    blocks2 = (blocks2 + kNumXcd - 1) / kNumXcd * kNumXcd;
-    ProfScope prof_(s, "down_bf16");
-    hipLaunchKernelGGL((bf16_tile_kernel<false, BM, BNW, NTHR, NSETS>),
-                       dim3(static_cast<unsigned>(blocks2)), dim3(NTHR), 0, s, d_ffn, d_model,
-                       rows, n_groups, nt2, w.tiles, w.group_tile_start, w.meta, nullptr, act,
-                       wd, nullptr, row_scale, y);
-  }
-  return hipGetLastError();
+  return launch_down<BM, BNW, NTHR, NSETS>(n_groups, d_ffn, d_model, rows, mfma_bound, w, act, wd,
+                                           row_scale, y, "down_bf16", s);
 }
 
 }  // namespace
+
+hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
+                                  const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
+                                  uint16_t* C, const char* name, hipStream_t s) {
+  hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, w, s);
+  if (err != hipSuccess) return err;
+  const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
+  return launch_down<256, 256, 512, 2>(n_groups, K, N, rows, mfma_bound, w, A, W, nullptr, C,
+                                       name, s);
+}
 
 hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                               const int32_t* offsets, const int32_t* row_index,

@@ -55,7 +55,7 @@ struct BwdWorkspace {
     TileInfo* tiles;
     int32_t* group_tile_start;
     int32_t* meta;
-  } tiles;                  // 128-row tiles of the grouped rows
+  } tiles, tiles256;        // 128- and 256-row tiles of the grouped rows
   int32_t* kpad;            // [n_groups + 1] expert rows padded to 64, prefix sums
   uint16_t* au;             // [rows, 2f]  a | u recomputed
   uint16_t* dadu;           // [rows, 2f]  da | du
@@ -84,5 +84,14 @@ hipError_t launch_transpose_experts(int n, int rows, int cols, const uint16_t* s
 
 hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* offsets,
                               const SwigluWorkspace& w, hipStream_t s);
+
+// Grouped C = A W[g]^T over the rows of each group (bf16, fp32 accumulation):
+// A [rows, K], W [n_groups, N, K], C [rows, N]; K a multiple of 64.  Builds a
+// 256-row tile list into w's tile arrays (sized by swiglu_layout with min_bm
+// <= 256) and runs the grouped SwiGLU's down-direction kernels.  `name` tags
+// the launch in the profile records.
+hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
+                                  const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
+                                  uint16_t* C, const char* name, hipStream_t s);
 
 }  // namespace moe
