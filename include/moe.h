@@ -259,6 +259,27 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
                               void* stream);
 
 /*
+ * moe_grouped_swiglu_train -- moe_grouped_swiglu for a training forward pass:
+ * the same outputs, and the gate and up projections of every grouped row
+ * (SwiGLU expert, routing-math page section 0) kept for the backward pass.
+ *
+ *   au   [rows, 2 d_ffn] bf16 out: row r holds a_r = x_r W_gate^T in
+ *        columns 0 .. d_ffn-1 and u_r = x_r W_up^T in d_ffn .. 2 d_ffn-1,
+ *        each rounded to bf16 from the fp32 accumulator; rows past
+ *        offsets[n_groups] are not written.  Caller-owned; pass it to
+ *        moe_grouped_swiglu_backward, which then skips recomputing them.
+ * Every other argument, the workspace size and the limits are those of
+ * moe_grouped_swiglu; bf16 only (else MOE_ERR_UNSUPPORTED); au NULL gives
+ * MOE_ERR_INVALID_ARG.  Costs the writes of au (4 rows d_ffn bytes).
+ */
+moe_status moe_grouped_swiglu_train(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                                    const int32_t* offsets, const int32_t* row_index,
+                                    const void* x, moe_dtype dtype, const void* w_gate,
+                                    const void* w_up, const void* w_down, const float* row_scale,
+                                    void* y, void* au, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * moe_combine -- gate-weighted sum of the expert outputs plus the residual and
  * the shared experts:
  *     y_t = h_t + sum_{j<E_s} y_shared[j, t] + sum_k gates[t,k] * y_perm[slot_row[t*K+k]]
@@ -364,6 +385,8 @@ const char* moe_version(void);
  *   moe_combine_backward          dy -> dy_perm (g * dy per copy), dgates
  *   moe_grouped_swiglu_backward   routed experts: dy_perm -> dx_perm, dW
  *   moe_grouped_swiglu_backward   shared experts: dy -> dx_shared, dW_shared
+ * (the forward's expert calls may be moe_grouped_swiglu_train, whose a|u
+ * output the backward then reads instead of recomputing)
  *   moe_combine (gates = 1)       dh = dy + sum dx_shared + sum_k dx_perm
  *   moe_route_backward            dh += router term; de
  */
@@ -403,6 +426,10 @@ moe_status moe_combine_backward(int T, int d_model, int K, const void* dy, const
  *   w_gu_t    [n_groups, d_model, 2 d_ffn] [W_gate^T | W_up^T]
  *   w_down_t  [n_groups, d_ffn, d_model] W_down^T
  *   dy        [rows, d_model] gradient of the grouped outputs
+ *   au        [rows, 2 d_ffn] bf16 [a | u] as written by
+ *             moe_grouped_swiglu_train with the same x, weights and
+ *             offsets, or NULL: the backward recomputes them (two more
+ *             grouped products) into its workspace
  *   dx        [rows, d_model] out: gradient of each grouped row's input
  *   dw_gate, dw_up [n_groups, d_ffn, d_model] out; dw_down [n_groups,
  *             d_model, d_ffn] out; groups without rows get zeros
@@ -416,8 +443,8 @@ moe_status moe_grouped_swiglu_backward(int n_groups, int d_model, int d_ffn, int
                                        int x_rows, const int32_t* offsets,
                                        const int32_t* row_index, const void* x, moe_dtype dtype,
                                        const void* w_gate, const void* w_up, const void* w_gu_t,
-                                       const void* w_down_t, const void* dy, void* dx,
-                                       void* dw_gate, void* dw_up, void* dw_down,
+                                       const void* w_down_t, const void* dy, const void* au,
+                                       void* dx, void* dw_gate, void* dw_up, void* dw_down,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -254,6 +254,28 @@ def grouped_swiglu(x: np.ndarray, offsets: np.ndarray, row_index: Optional[np.nd
     return out
 
 
+def grouped_gate_up(x: np.ndarray, offsets: np.ndarray, row_index: Optional[np.ndarray],
+                    weights: ExpertSource) -> np.ndarray:
+    """The two input projections of each grouped row's expert (the SwiGLU
+    expert of the routing-math page, section 0): fp64 [rows, 2 d_ffn] holding
+    a = x W_gate^T in the first d_ffn columns and u = x W_up^T in the rest.
+    Rows are gathered as in grouped_swiglu."""
+    rows = int(offsets[-1])
+    x64 = to_f64(x)
+    src = np.arange(rows) if row_index is None else row_index.astype(np.int64)
+    f = _expert(weights, 0)[0].shape[0]
+    out = np.zeros((rows, 2 * f), dtype=np.float64)
+    for gi in range(len(offsets) - 1):
+        lo, hi = int(offsets[gi]), int(offsets[gi + 1])
+        if hi == lo:
+            continue
+        wg, wu, _ = _expert(weights, gi)
+        xs = x64[src[lo:hi]]
+        out[lo:hi, :f] = xs @ to_f64(wg).T
+        out[lo:hi, f:] = xs @ to_f64(wu).T
+    return out
+
+
 def shared_experts(h: np.ndarray, weights: Optional[ExpertSource], E_s: int) -> np.ndarray:
     """Sum over the always-active experts (gate 1) on every token, fp64 [T, d]."""
     h64 = to_f64(h)

@@ -20,7 +20,8 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size
             "moe_route_stats", "moe_router_diag", "moe_transpose_experts",
             "moe_combine_backward", "moe_grouped_swiglu_backward_workspace_size",
             "moe_grouped_swiglu_backward", "moe_route_backward",
-            "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu", "moe_combine",
+            "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
+            "moe_grouped_swiglu_train", "moe_combine",
             "moe_bias_update", "moe_calib_mfma_loop", "moe_calib_stream_read",
             "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -71,7 +72,7 @@ def load() -> ctypes.CDLL:
         "moe_combine_backward": ([_i, _i, _i, _p, _p, _p, _p, _i, _p, _p, _p], _i),
         "moe_grouped_swiglu_backward_workspace_size": ([_i, _i, _i, _i], _sz),
         "moe_grouped_swiglu_backward": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p,
-                                         _p, _p, _p, _p, _p, _sz, _p], _i),
+                                         _p, _p, _p, _p, _p, _p, _sz, _p], _i),
         "moe_route_backward": ([_i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p],
                                _i),
         "moe_permute_capacity": ([_i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p, _sz, _p],
@@ -79,6 +80,8 @@ def load() -> ctypes.CDLL:
         "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
         "moe_grouped_swiglu": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
                                 _sz, _p], _i),
+        "moe_grouped_swiglu_train": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p,
+                                      _p, _p, _sz, _p], _i),
         "moe_combine": ([_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p], _i),
         "moe_bias_update": ([_i, _i, _i, _f, _p, _p, _p, _p], _i),
         "moe_calib_mfma_loop": ([_i, _i, _p, _p, ctypes.POINTER(ctypes.c_double), _p], _i),
@@ -201,6 +204,16 @@ def moe_grouped_swiglu(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_inde
                                      workspace_bytes, _stream(stream)))
 
 
+def moe_grouped_swiglu_train(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x,
+                             dtype, w_gate, w_up, w_down, row_scale, y, au, workspace,
+                             workspace_bytes, stream=None):
+    _check(load().moe_grouped_swiglu_train(n_groups, d_model, d_ffn, rows, x_rows, _ptr(offsets),
+                                           _ptr(row_index), _ptr(x), dtype, _ptr(w_gate),
+                                           _ptr(w_up), _ptr(w_down), _ptr(row_scale), _ptr(y),
+                                           _ptr(au), _ptr(workspace), workspace_bytes,
+                                           _stream(stream)))
+
+
 def moe_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates, dtype, y,
                 stream=None):
     _check(load().moe_combine(T, d_model, K, E_s, _ptr(h), _ptr(y_shared), _ptr(y_perm),
@@ -263,11 +276,11 @@ def moe_grouped_swiglu_backward_workspace_size(n_groups, d_model, d_ffn, rows) -
 
 
 def moe_grouped_swiglu_backward(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x,
-                                dtype, w_gate, w_up, w_gu_t, w_down_t, dy, dx, dw_gate, dw_up,
-                                dw_down, workspace, workspace_bytes, stream=None):
+                                dtype, w_gate, w_up, w_gu_t, w_down_t, dy, au, dx, dw_gate,
+                                dw_up, dw_down, workspace, workspace_bytes, stream=None):
     _check(load().moe_grouped_swiglu_backward(
         n_groups, d_model, d_ffn, rows, x_rows, _ptr(offsets), _ptr(row_index), _ptr(x), dtype,
-        _ptr(w_gate), _ptr(w_up), _ptr(w_gu_t), _ptr(w_down_t), _ptr(dy), _ptr(dx),
+        _ptr(w_gate), _ptr(w_up), _ptr(w_gu_t), _ptr(w_down_t), _ptr(dy), _ptr(au), _ptr(dx),
         _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(workspace), workspace_bytes,
         _stream(stream)))
 

@@ -205,45 +205,45 @@ size_t moe_grouped_swiglu_workspace_size(int n_groups, int d_model, int d_ffn, i
   return moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
 }
 
-moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
-                              const int32_t* offsets, const int32_t* row_index, const void* x,
-                              moe_dtype dtype, const void* w_gate, const void* w_up,
-                              const void* w_down, const float* row_scale, void* y,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared by the inference and training forms; au (bf16 only) also receives the
+// gate and up projections.
+moe_status grouped_swiglu(const char* fn, int n_groups, int d_model, int d_ffn, int rows,
+                          int x_rows, const int32_t* offsets, const int32_t* row_index,
+                          const void* x, moe_dtype dtype, const void* w_gate, const void* w_up,
+                          const void* w_down, const float* row_scale, void* y, void* au,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   if (n_groups < 1 || d_model < 1 || d_ffn < 1 || rows < 0 || x_rows < 0)
-    return fail(MOE_ERR_INVALID_ARG,
-                "moe_grouped_swiglu: n_groups=%d d_model=%d d_ffn=%d rows=%d x_rows=%d", n_groups,
-                d_model, d_ffn, rows, x_rows);
+    return fail(MOE_ERR_INVALID_ARG, "%s: n_groups=%d d_model=%d d_ffn=%d rows=%d x_rows=%d", fn,
+                n_groups, d_model, d_ffn, rows, x_rows);
   if (n_groups > MOE_MAX_EXPERTS)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_swiglu: n_groups=%d > %d", n_groups,
-                MOE_MAX_EXPERTS);
-  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: bad dtype");
+    return fail(MOE_ERR_UNSUPPORTED, "%s: n_groups=%d > %d", fn, n_groups, MOE_MAX_EXPERTS);
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: bad dtype", fn);
   if (!offsets || !x || !w_gate || !w_up || !w_down || !y || !workspace)
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: null pointer");
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (row_index == nullptr && x_rows < rows)
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: x_rows=%d < rows=%d without row_index",
-                x_rows, rows);
+    return fail(MOE_ERR_INVALID_ARG, "%s: x_rows=%d < rows=%d without row_index", fn, x_rows,
+                rows);
   const int align = dtype == MOE_BF16 ? 64 : 16;
   if (d_model % align || d_ffn % align)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "moe_grouped_swiglu: d_model=%d and d_ffn=%d must be multiples of %d", d_model,
-                d_ffn, align);
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d_model=%d and d_ffn=%d must be multiples of %d", fn,
+                d_model, d_ffn, align);
   if (static_cast<long long>(rows) * d_ffn > (1LL << 40) ||
       static_cast<long long>(d_model) * d_ffn > INT32_MAX)
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: sizes overflow");
+    return fail(MOE_ERR_INVALID_ARG, "%s: sizes overflow", fn);
   if (dtype == MOE_BF16) {
     // the matrix-core path addresses each operand with 32-bit buffer offsets
     const long long lim = (1LL << 31) - 1;
     if (2LL * x_rows * d_model > lim || 2LL * rows * d_ffn > lim || 2LL * d_model * d_ffn > lim)
       return fail(MOE_ERR_UNSUPPORTED,
-                  "moe_grouped_swiglu: bf16 operands must each be under 2 GiB "
+                  "%s: bf16 operands must each be under 2 GiB "
                   "(x %lld, activations %lld, one weight matrix %lld bytes)",
-                  2LL * x_rows * d_model, 2LL * rows * d_ffn, 2LL * d_model * d_ffn);
+                  fn, 2LL * x_rows * d_model, 2LL * rows * d_ffn, 2LL * d_model * d_ffn);
   }
   const size_t need = moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
   if (workspace_bytes < need)
-    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_swiglu: workspace %zu < %zu bytes",
-                workspace_bytes, need);
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
   if (rows == 0) return MOE_OK;
   hipError_t err;
   if (dtype == MOE_BF16)
@@ -252,14 +252,41 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
                                   static_cast<const uint16_t*>(w_gate),
                                   static_cast<const uint16_t*>(w_up),
                                   static_cast<const uint16_t*>(w_down), row_scale,
-                                  static_cast<uint16_t*>(y), workspace, as_stream(stream));
+                                  static_cast<uint16_t*>(y), static_cast<uint16_t*>(au), workspace,
+                                  as_stream(stream));
   else
     err = moe::launch_swiglu_f32(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index,
                                  static_cast<const float*>(x), static_cast<const float*>(w_gate),
                                  static_cast<const float*>(w_up),
                                  static_cast<const float*>(w_down), row_scale,
                                  static_cast<float*>(y), workspace, as_stream(stream));
-  return hip_status(err, "moe_grouped_swiglu");
+  return hip_status(err, fn);
+}
+
+}  // namespace
+
+moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                              const int32_t* offsets, const int32_t* row_index, const void* x,
+                              moe_dtype dtype, const void* w_gate, const void* w_up,
+                              const void* w_down, const float* row_scale, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_swiglu("moe_grouped_swiglu", n_groups, d_model, d_ffn, rows, x_rows, offsets,
+                        row_index, x, dtype, w_gate, w_up, w_down, row_scale, y, nullptr,
+                        workspace, workspace_bytes, stream);
+}
+
+moe_status moe_grouped_swiglu_train(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                                    const int32_t* offsets, const int32_t* row_index,
+                                    const void* x, moe_dtype dtype, const void* w_gate,
+                                    const void* w_up, const void* w_down, const float* row_scale,
+                                    void* y, void* au, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const char* fn = "moe_grouped_swiglu_train";
+  if (dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 only", fn);
+  if (!au) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  return grouped_swiglu(fn, n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, dtype,
+                        w_gate, w_up, w_down, row_scale, y, au, workspace, workspace_bytes,
+                        stream);
 }
 
 moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h, const void* y_shared,
@@ -487,8 +514,8 @@ moe_status moe_grouped_swiglu_backward(int n_groups, int d_model, int d_ffn, int
                                        int x_rows, const int32_t* offsets,
                                        const int32_t* row_index, const void* x, moe_dtype dtype,
                                        const void* w_gate, const void* w_up, const void* w_gu_t,
-                                       const void* w_down_t, const void* dy, void* dx,
-                                       void* dw_gate, void* dw_up, void* dw_down,
+                                       const void* w_down_t, const void* dy, const void* au,
+                                       void* dx, void* dw_gate, void* dw_up, void* dw_down,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "moe_grouped_swiglu_backward";
   if (n_groups < 1 || d_model < 1 || d_ffn < 1 || rows < 0 || x_rows < 0)
@@ -526,7 +553,8 @@ moe_status moe_grouped_swiglu_backward(int n_groups, int d_model, int d_ffn, int
                                   static_cast<const uint16_t*>(w_up),
                                   static_cast<const uint16_t*>(w_gu_t),
                                   static_cast<const uint16_t*>(w_down_t),
-                                  static_cast<const uint16_t*>(dy), static_cast<uint16_t*>(dx),
+                                  static_cast<const uint16_t*>(dy),
+                                  static_cast<const uint16_t*>(au), static_cast<uint16_t*>(dx),
                                   static_cast<uint16_t*>(dw_gate), static_cast<uint16_t*>(dw_up),
                                   static_cast<uint16_t*>(dw_down), workspace, as_stream(stream)),
       fn);

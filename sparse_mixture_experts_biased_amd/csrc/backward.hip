@@ -773,8 +773,9 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
                                   const int32_t* offsets, const int32_t* row_index,
                                   const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                                   const uint16_t* wgu_t, const uint16_t* wd_t,
-                                  const uint16_t* dy, uint16_t* dx, uint16_t* dwg,
-                                  uint16_t* dwu, uint16_t* dwd, void* ws, hipStream_t s) {
+                                  const uint16_t* dy, const uint16_t* au, uint16_t* dx,
+                                  uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, void* ws,
+                                  hipStream_t s) {
   BwdWorkspace w = bwd_layout(ws, n_groups, d, f, rows);
   SwigluWorkspace tl{};
   tl.tiles = w.tiles.tiles;
@@ -794,15 +795,19 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   a.n_groups = n_groups;
   a.row_index = row_index;
   a.a_rows = x_rows;
-  // 1. a = x W_gate^T, u = x W_up^T  -> au [rows, 2f]
-  a.N = f; a.K = d; a.NT = (f + kBN - 1) / kBN;
-  a.A = x; a.lda = d;
-  a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
-  a.ldc = 2 * f;
-  a.B = wg; a.C = w.au;
-  if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
-  a.B = wu; a.C = w.au + f;
-  if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+  // 1. a = x W_gate^T, u = x W_up^T  -> au [rows, 2f], unless the forward
+  //    pass stored them
+  if (au == nullptr) {
+    a.N = f; a.K = d; a.NT = (f + kBN - 1) / kBN;
+    a.A = x; a.lda = d;
+    a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
+    a.ldc = 2 * f;
+    a.B = wg; a.C = w.au;
+    if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+    a.B = wu; a.C = w.au + f;
+    if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+    au = w.au;
+  }
   // 2. d act = dy W_down (B = W_down^T [f, d]) -> [rows, f], held in the daT
   //    region (rpad >= rows; daT is written only in step 4), with the forward
   //    pass's down-direction kernels over 256-row tiles; then da, du -> dadu
@@ -818,7 +823,7 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
     const long n8 = static_cast<long>(rows) * (f / 8);
     const unsigned blocks = static_cast<unsigned>(std::min<long>((n8 + 255) / 256, 65536));
     if (blocks > 0)
-      hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(blocks), dim3(256), 0, s, rows, f, dact, w.au,
+      hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(blocks), dim3(256), 0, s, rows, f, dact, au,
                          w.dadu);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -834,7 +839,7 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gd, dim3(256), 0, s, d, rows, rows,
                        tl.tiles, tl.meta, offsets, w.kpad, nullptr, dy, d, w.dyT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrAct>, gf, dim3(256), 0, s, f, rows, rows,
-                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.au, 2 * f, w.actT);
+                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, au, 2 * f, w.actT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gf, dim3(256), 0, s, f, rows, rows,
                        tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.dadu, 2 * f, w.daT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gf, dim3(256), 0, s, f, rows, rows,

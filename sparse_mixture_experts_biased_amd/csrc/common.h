@@ -72,7 +72,7 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
                               const int32_t* offsets, const int32_t* row_index,
                               const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                               const uint16_t* wd, const float* row_scale, uint16_t* y,
-                              void* ws, hipStream_t s);
+                              uint16_t* au, void* ws, hipStream_t s);
 
 // combine
 hipError_t launch_combine(int T, int d, int K, int E_s, const void* h, const void* y_shared,

@@ -75,7 +75,7 @@ struct Tile {
 
 // GATEUP: 64 act columns per tile, W0 = W_gate, W1 = W_up
 // DOWN:   128 y columns per tile,  W0 = W_down
-template <bool GATEUP, int BM, int BNW, int NTHR, int NSETS>
+template <bool GATEUP, int BM, int BNW, int NTHR, int NSETS, bool AU = false>
 __global__ __launch_bounds__(NTHR)
 __attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
                                    Tile<BM, BNW, NTHR>::kWavesPerEU)))
@@ -84,7 +84,7 @@ void bf16_tile_kernel(
     const int32_t* __restrict__ gts, const int32_t* __restrict__ meta,
     const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    const float* __restrict__ row_scale, uint16_t* __restrict__ out) {
+    const float* __restrict__ row_scale, uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using TL = Tile<BM, BNW, NTHR>;
   constexpr int kALoads = TL::kALoads;
   constexpr int kBLoads = TL::kBLoads;
@@ -286,6 +286,14 @@ void bf16_tile_kernel(
   static_assert(BM * kCols * 2 <= 2 * TL::kStageBytes, "output tile exceeds LDS");
   constexpr int kOutRowBytes = kCols * 2;
   constexpr int kOutChunks = kCols / 8;
+  // Gate/up with AU: pass 0 also stages a in the second half of the LDS (the
+  // gate accumulators are then dead for the read-outs), pass 1 stages u; both
+  // go to au [rows, 2N].
+  static_assert(!AU || 2 * BM * kCols * 2 <= 2 * TL::kStageBytes, "a|u tiles exceed LDS");
+  constexpr int npass = (GATEUP && AU) ? 2 : 1;
+  constexpr int kHalf = BM * kOutRowBytes;
+#pragma unroll
+  for (int pass = 0; pass < npass; ++pass) {
   __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -299,9 +307,14 @@ void bf16_tile_kernel(
 #pragma unroll
         for (int nb = 0; nb < kNB / 2; ++nb) {
           const int c = brow[nb] + fr;
-          const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
-          *reinterpret_cast<uint16_t*>(orow + (((c >> 3) ^ sw) << 4) + (c & 7) * 2) =
-              f32_to_bf16(v);
+          const int co = (((c >> 3) ^ sw) << 4) + (c & 7) * 2;
+          const float gv = acc[mb][nb][q], uv = acc[mb][nb + kNB / 2][q];
+          if (pass == 0) {
+            *reinterpret_cast<uint16_t*>(orow + co) = f32_to_bf16(silu(gv) * uv);
+            if (AU) *reinterpret_cast<uint16_t*>(orow + kHalf + co) = f32_to_bf16(gv);
+          } else {
+            *reinterpret_cast<uint16_t*>(orow + co) = f32_to_bf16(uv);
+          }
         }
       } else {
         const float sc = row_scale ? row_scale[ti.m0 + row] : 1.0f;
@@ -315,16 +328,25 @@ void bf16_tile_kernel(
     }
   }
   __syncthreads();
+  // pass 0: half 0 -> out (and, with AU, half 1 -> a); pass 1: half 0 -> u
+  constexpr int kHalves = AU ? 2 : 1;
 #pragma unroll
-  for (int it = 0; it < BM * kOutChunks / NTHR; ++it) {
-    const int idx = it * NTHR + tid;
-    const int r = idx / kOutChunks;
-    const int c = idx % kOutChunks;
-    if (r < nrows && n0 + c * 8 < N) {
-      const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kOutRowBytes +
-                                                     ((c ^ (r & 4)) << 4));
-      *reinterpret_cast<uint4*>(out + static_cast<size_t>(ti.m0 + r) * N + n0 + c * 8) = v;
+  for (int hf = 0; hf < kHalves; ++hf) {
+    if (pass == 1 && hf == 1) break;
+    const size_t ldo = (pass == 0 && hf == 0) ? static_cast<size_t>(N) : 2 * static_cast<size_t>(N);
+    uint16_t* const ob = (pass == 0 && hf == 0) ? out : au + (pass == 1 ? N : 0);
+#pragma unroll
+    for (int it = 0; it < BM * kOutChunks / NTHR; ++it) {
+      const int idx = it * NTHR + tid;
+      const int r = idx / kOutChunks;
+      const int c = idx % kOutChunks;
+      if (r < nrows && n0 + c * 8 < N) {
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + hf * kHalf + r * kOutRowBytes +
+                                                       ((c ^ (r & 4)) << 4));
+        *reinterpret_cast<uint4*>(ob + static_cast<size_t>(ti.m0 + r) * ldo + n0 + c * 8) = v;
+      }
     }
+  }
   }
 }
 
@@ -407,14 +429,14 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, void* lds, uint32
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
 
-template <bool GATEUP, int BK>
+template <bool GATEUP, int BK, bool AU = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bf16_stream_kernel(
     int Kdim, int N, int x_rows, int rows, int NT, const TileInfo* __restrict__ tiles,
     const int32_t* __restrict__ meta, const int32_t* __restrict__ row_index,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
     const uint16_t* __restrict__ W1, const float* __restrict__ row_scale,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using G = StreamGeom<BK>;
   constexpr int BM = 256, BNW = 256, NTHR = 512;
   constexpr int kWavesN = 2;                  // waves: 4 along rows x 2 along weight rows
@@ -654,6 +676,9 @@ void bf16_stream_kernel(
     char* const ot = st_last;
     // every wave has multiplied the last stage
     asm volatile("s_barrier" ::: "memory");
+    // gate/up with AU: two more passes write a and u to au [rows, 2N]
+    constexpr int npass = (GATEUP && AU) ? 3 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
 #pragma unroll
     for (int r0 = 0; r0 < BM; r0 += kRoundRows) {
       if (r0 >= c_nrows) break;
@@ -688,7 +713,8 @@ void bf16_stream_kernel(
               if (GATEUP) {
 #pragma unroll
                 for (int nb = 0; nb < kNB / 2; ++nb) {
-                  const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
+                  const float gv = acc[mb][nb][q], uv = acc[mb][nb + kNB / 2][q];
+                  const float v = pass == 0 ? silu(gv) * uv : (pass == 1 ? gv : uv);
                   *reinterpret_cast<uint16_t*>(orow + cofs[nb]) = f32_to_bf16(v);
                 }
               } else {
@@ -704,14 +730,17 @@ void bf16_stream_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       const int rl = etid / kOutChunks, cl = etid % kOutChunks;
       const char* src = ot + rl * kOutRowBytes + ((cl ^ (rl & 4)) << 4);
-      uint16_t* dst = out + static_cast<size_t>(c_m0 + r0 + rl) * N + c_n0 + cl * 8;
+      const size_t ldo = pass == 0 ? static_cast<size_t>(N) : 2 * static_cast<size_t>(N);
+      uint16_t* dst = (pass == 0 ? out : au + (pass == 2 ? N : 0)) +
+                      static_cast<size_t>(c_m0 + r0 + rl) * ldo + c_n0 + cl * 8;
 #pragma unroll
       for (int it = 0; it < kRoundRows / kReadRows; ++it) {
         if (rl < c_nrows - r0 - it * kReadRows)
-          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(it) * kReadRows * N) =
+          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(it) * kReadRows * ldo) =
               *reinterpret_cast<const uint4*>(src + it * kReadRows * kOutRowBytes);
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     }
   };
 
@@ -785,7 +814,7 @@ bool stream_shape(int K, int N, int cols) {
 // wait counts stay exact).  Used when K is an even number of at least
 // kMinStreamSlices slices and N is a multiple of the column tile.
 
-template <bool GATEUP, int BM, int BNW, int NTHR>
+template <bool GATEUP, int BM, int BNW, int NTHR, bool AU = false>
 __global__ __launch_bounds__(NTHR)
 __attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
                                    Tile<BM, BNW, NTHR>::kWavesPerEU)))
@@ -794,7 +823,7 @@ void bf16_regs_stream_kernel(
     const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
     const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
     const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    const float* __restrict__ row_scale, uint16_t* __restrict__ out) {
+    const float* __restrict__ row_scale, uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using TL = Tile<BM, BNW, NTHR>;
   constexpr int kALoads = TL::kALoads;
   constexpr int kBLoads = TL::kBLoads;
@@ -1061,6 +1090,9 @@ void bf16_regs_stream_kernel(
     constexpr int kReadRows = NTHR / kOutChunks;
     static_assert(NTHR % kOutChunks == 0 && kReadRows % 8 == 0, "read-out rows keep row & 4");
     static_assert(kRoundRows % 64 == 0 && BM % kRoundRows == 0, "rounds hold whole waves' rows");
+    // gate/up with AU: two more passes write a and u to au [rows, 2N]
+    constexpr int npass = (GATEUP && AU) ? 3 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
 #pragma unroll
     for (int r0 = 0; r0 < BM; r0 += kRoundRows) {
       if (r0 >= c_nrows) break;
@@ -1089,7 +1121,8 @@ void bf16_regs_stream_kernel(
             if (GATEUP) {
 #pragma unroll
               for (int nb = 0; nb < kNB / 2; ++nb) {
-                const float v = silu(acc[mb][nb][q]) * acc[mb][nb + kNB / 2][q];
+                const float gv = acc[mb][nb][q], uv = acc[mb][nb + kNB / 2][q];
+                const float v = pass == 0 ? silu(gv) * uv : (pass == 1 ? gv : uv);
                 *reinterpret_cast<uint16_t*>(orow + cofs[nb]) = f32_to_bf16(v);
               }
             } else if (row_scale == nullptr) {
@@ -1110,14 +1143,17 @@ void bf16_regs_stream_kernel(
       __syncthreads();
       const int rl = etid / kOutChunks, cl = etid % kOutChunks;
       const char* src = ot + rl * kOutRowBytes + ((cl ^ (rl & 4)) << 4);
-      uint16_t* dst = out + static_cast<size_t>(c_m0 + r0 + rl) * N + c_n0 + cl * 8;
+      const size_t ldo = pass == 0 ? static_cast<size_t>(N) : 2 * static_cast<size_t>(N);
+      uint16_t* dst = (pass == 0 ? out : au + (pass == 2 ? N : 0)) +
+                      static_cast<size_t>(c_m0 + r0 + rl) * ldo + c_n0 + cl * 8;
 #pragma unroll
       for (int it = 0; it < kRoundRows / kReadRows; ++it) {
         if (rl < c_nrows - r0 - it * kReadRows)
-          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(it) * kReadRows * N) =
+          *reinterpret_cast<uint4*>(dst + static_cast<size_t>(it) * kReadRows * ldo) =
               *reinterpret_cast<const uint4*>(src + it * kReadRows * kOutRowBytes);
       }
       __syncthreads();
+    }
     }
   };
 
@@ -1194,18 +1230,50 @@ hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
   if (stream_shape(K, N, 256) && mfma_bound) {
     hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
                        s, K, N, rows, rows, nt, w.tiles, w.meta, nullptr, A, W, nullptr,
-                       row_scale, C);
+                       row_scale, C, nullptr);
   } else if (stream_shape(K, N, BNW)) {
     hipLaunchKernelGGL((bf16_regs_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, K, N, rows, rows, max_tiles, nt, w.tiles, w.meta,
-                       nullptr, A, W, nullptr, row_scale, C);
+                       nullptr, A, W, nullptr, row_scale, C, nullptr);
   } else {
     long blocks = static_cast<long>(max_tiles) * nt;
     blocks = (blocks + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL((bf16_tile_kernel<false, BM, BNW, NTHR, NSETS>),
                        dim3(static_cast<unsigned>(blocks)), dim3(NTHR), 0, s, K, N, rows,
                        n_groups, nt, w.tiles, w.group_tile_start, w.meta, nullptr, A, W, nullptr,
-                       row_scale, C);
+                       row_scale, C, nullptr);
+  }
+  return hipGetLastError();
+}
+
+// The gate/up product act = SiLU(x W_gate^T) * (x W_up^T) over the tile list
+// in w; with AU the gate and up values also go to au [rows, 2 d_ffn].
+// Groups of at least a full row tile on average make the products matrix-core
+// bound: LDS-fed kernel.  Fewer rows make them weight-streaming bound:
+// register-staged kernel, which keeps more weight bytes in flight per CU.
+template <int BM, int BNW, int NTHR, int NSETS, bool AU>
+hipError_t launch_gateup(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                         bool mfma_bound, const int32_t* row_index, const uint16_t* x,
+                         const uint16_t* wg, const uint16_t* wu, uint16_t* act, uint16_t* au,
+                         const SwigluWorkspace& w, hipStream_t s) {
+  const int max_tiles = max_tiles_for(rows, n_groups, BM);
+  const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
+  ProfScope prof_(s, "gateup_bf16");
+  if (stream_shape(d_model, d_ffn, 128) && mfma_bound) {
+    hipLaunchKernelGGL((bf16_stream_kernel<true, kStreamBK, AU>), dim3(stream_grid()), dim3(512),
+                       0, s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, wg,
+                       wu, nullptr, act, au);
+  } else if (stream_shape(d_model, d_ffn, BNW / 2)) {
+    hipLaunchKernelGGL((bf16_regs_stream_kernel<true, BM, BNW, NTHR, AU>), dim3(stream_grid()),
+                       dim3(NTHR), 0, s, d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles,
+                       w.meta, row_index, x, wg, wu, nullptr, act, au);
+  } else {
+    long blocks1 = static_cast<long>(max_tiles) * nt1;
+    blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
+    hipLaunchKernelGGL((bf16_tile_kernel<true, BM, BNW, NTHR, NSETS, AU>),
+                       dim3(static_cast<unsigned>(blocks1)), dim3(NTHR), 0, s, d_model, d_ffn,
+                       x_rows, n_groups, nt1, w.tiles, w.group_tile_start, w.meta, row_index, x,
+                       wg, wu, nullptr, act, au);
   }
   return hipGetLastError();
 }
@@ -1214,38 +1282,19 @@ template <int BM, int BNW, int NTHR, int NSETS>
 hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                         const int32_t* offsets, const int32_t* row_index, const uint16_t* x,
                         const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
-                        const float* row_scale, uint16_t* y, const SwigluWorkspace& w,
-                        hipStream_t s) {
+                        const float* row_scale, uint16_t* y, uint16_t* au,
+                        const SwigluWorkspace& w, hipStream_t s) {
   hipError_t err = launch_build_tiles(n_groups, rows, BM, offsets, w, s);
   if (err != hipSuccess) return err;
-  const int max_tiles = max_tiles_for(rows, n_groups, BM);
   uint16_t* act = static_cast<uint16_t*>(w.act);
-
-  const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
-  // Groups of at least a full row tile on average make the products matrix-core
-  // bound: LDS-fed kernel.  Fewer rows make them weight-streaming bound:
-  // register-staged kernel, which keeps more weight bytes in flight per CU.
   const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
-  if (stream_shape(d_model, d_ffn, 128) && mfma_bound) {
-    ProfScope prof_(s, "gateup_bf16");
-    hipLaunchKernelGGL((bf16_stream_kernel<true, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
-                       s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, wg,
-                       wu, nullptr, act);
-  } else if (stream_shape(d_model, d_ffn, BNW / 2)) {
-    ProfScope prof_(s, "gateup_bf16");
-    hipLaunchKernelGGL((bf16_regs_stream_kernel<true, BM, BNW, NTHR>), dim3(stream_grid()),
-                       dim3(NTHR), 0, s, d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles,
-                       w.meta, row_index, x, wg, wu, nullptr, act);
-  } else {
-    long blocks1 = static_cast<long>(max_tiles) * nt1;
-    blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
-    ProfScope prof_(s, "gateup_bf16");
-    hipLaunchKernelGGL((bf16_tile_kernel<true, BM, BNW, NTHR, NSETS>),
-                       dim3(static_cast<unsigned>(blocks1)), dim3(NTHR), 0, s, d_model, d_ffn,
-                       x_rows, n_groups, nt1, w.tiles, w.group_tile_start, w.meta, row_index, x,
-                       wg, wu, nullptr, act);
-  }
-  err = hipGetLastError();
+  err = au != nullptr
+            ? launch_gateup<BM, BNW, NTHR, NSETS, true>(n_groups, d_model, d_ffn, rows, x_rows,
+                                                        mfma_bound, row_index, x, wg, wu, act, au,
+                                                        w, s)
+            : launch_gateup<BM, BNW, NTHR, NSETS, false>(n_groups, d_model, d_ffn, rows, x_rows,
+                                                         mfma_bound, row_index, x, wg, wu, act,
+                                                         nullptr, w, s);
   if (err != hipSuccess) return err;
 
   return launch_down<BM, BNW, NTHR, NSETS>(n_groups, d_ffn, d_model, rows, mfma_bound, w, act, wd,
@@ -1268,10 +1317,10 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
                               const int32_t* offsets, const int32_t* row_index,
                               const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                               const uint16_t* wd, const float* row_scale, uint16_t* y,
-                              void* ws, hipStream_t s) {
+                              uint16_t* au, void* ws, hipStream_t s) {
   SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
   return launch_tiles<256, 256, 512, 2>(n_groups, d_model, d_ffn, rows, x_rows, offsets,
-                                        row_index, x, wg, wu, wd, row_scale, y, w, s);
+                                        row_index, x, wg, wu, wd, row_scale, y, au, w, s);
 }
 
 }  // namespace moe

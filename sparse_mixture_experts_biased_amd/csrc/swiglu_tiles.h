@@ -70,8 +70,9 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
                                   const int32_t* offsets, const int32_t* row_index,
                                   const uint16_t* x, const uint16_t* wg, const uint16_t* wu,
                                   const uint16_t* wgu_t, const uint16_t* wd_t,
-                                  const uint16_t* dy, uint16_t* dx, uint16_t* dwg,
-                                  uint16_t* dwu, uint16_t* dwd, void* ws, hipStream_t s);
+                                  const uint16_t* dy, const uint16_t* au, uint16_t* dx,
+                                  uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, void* ws,
+                                  hipStream_t s);
 hipError_t launch_combine_backward(int T, int d, int K, const uint16_t* dy, const uint16_t* yp,
                                    const int32_t* slot_row, const float* gates, uint16_t* dyp,
                                    float* dg, hipStream_t s);

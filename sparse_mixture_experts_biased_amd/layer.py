@@ -87,6 +87,8 @@ class MoELayer:
         self.sw_ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=device)
         self.y = torch.empty((T, d), dtype=self.tdt, device=device)
         self.stats = torch.zeros((4,), dtype=torch.int32, device=device)
+        # [a | u] of the routed and shared experts, kept by a training forward
+        self.au_perm = self.au_shared = None
 
     # individual stages -------------------------------------------------
     def route(self, h, b, stream=None):
@@ -124,9 +126,15 @@ class MoELayer:
         s = self.shape
         if self.profile_tags:
             L.moe_profile_tag("routed.")
-        L.moe_grouped_swiglu(s.E_r, s.d_model, s.d_ffn, s.T * s.K, s.T, self.offsets,
-                             self.row_token, h, self.dt, self.w_gate, self.w_up, self.w_down,
-                             None, self.y_perm, self.sw_ws, self.sw_ws_bytes, stream)
+        if self.au_perm is None:
+            L.moe_grouped_swiglu(s.E_r, s.d_model, s.d_ffn, s.T * s.K, s.T, self.offsets,
+                                 self.row_token, h, self.dt, self.w_gate, self.w_up, self.w_down,
+                                 None, self.y_perm, self.sw_ws, self.sw_ws_bytes, stream)
+        else:
+            L.moe_grouped_swiglu_train(s.E_r, s.d_model, s.d_ffn, s.T * s.K, s.T, self.offsets,
+                                       self.row_token, h, self.dt, self.w_gate, self.w_up,
+                                       self.w_down, None, self.y_perm, self.au_perm, self.sw_ws,
+                                       self.sw_ws_bytes, stream)
         if self.profile_tags:
             L.moe_profile_tag("")
 
@@ -136,9 +144,16 @@ class MoELayer:
             return
         if self.profile_tags:
             L.moe_profile_tag("shared.")
-        L.moe_grouped_swiglu(s.E_s, s.d_model, s.d_ffn, s.E_s * s.T, s.T, self.sh_offsets,
-                             self.sh_rows, h, self.dt, self.ws_gate, self.ws_up, self.ws_down,
-                             None, self.y_shared, self.sw_ws, self.sw_ws_bytes, stream)
+        if self.au_shared is None:
+            L.moe_grouped_swiglu(s.E_s, s.d_model, s.d_ffn, s.E_s * s.T, s.T, self.sh_offsets,
+                                 self.sh_rows, h, self.dt, self.ws_gate, self.ws_up,
+                                 self.ws_down, None, self.y_shared, self.sw_ws, self.sw_ws_bytes,
+                                 stream)
+        else:
+            L.moe_grouped_swiglu_train(s.E_s, s.d_model, s.d_ffn, s.E_s * s.T, s.T,
+                                       self.sh_offsets, self.sh_rows, h, self.dt, self.ws_gate,
+                                       self.ws_up, self.ws_down, None, self.y_shared,
+                                       self.au_shared, self.sw_ws, self.sw_ws_bytes, stream)
         if self.profile_tags:
             L.moe_profile_tag("")
 
@@ -168,9 +183,12 @@ class MoELayer:
         return self.y
 
     # backward -----------------------------------------------------------
-    def prepare_backward(self, stream=None):
+    def prepare_backward(self, stream=None, keep_au: bool = True):
         """Allocate the backward buffers and build the transposed weight copies
-        ([W_gate^T | W_up^T] and W_down^T); call again after the weights change."""
+        ([W_gate^T | W_up^T] and W_down^T); call again after the weights change.
+        With keep_au, later forwards also store the experts' gate and up
+        projections ([rows, 2 d_ffn] bf16 each for the routed and shared
+        experts), which the backward reads instead of recomputing."""
         s = self.shape
         if s.dtype != "bf16":
             raise NotImplementedError("the backward pass runs on bf16 layers")
@@ -214,6 +232,11 @@ class MoELayer:
             self.dx_shared = None
         self.bw_ws_bytes = bw
         self.bw_ws = torch.empty((bw,), dtype=torch.uint8, device=dev)
+        if keep_au:
+            self.au_perm = torch.empty((T * K, 2 * f), **bf)
+            self.au_shared = torch.empty((T, 2 * f), **bf) if s.E_s else None
+        else:
+            self.au_perm = self.au_shared = None
         if self.capacity is not None:   # the router's gradient covers every pick
             self.all_offsets = torch.empty((E + 1,), **i32)
             self.all_row_token = torch.empty((T * K,), **i32)
@@ -222,19 +245,22 @@ class MoELayer:
     def backward(self, h, dy, stream=None):
         """Gradients of sum_t <dy_t, y_t> after forward(h): dh, de and the
         expert weight gradients (routed: dw_*, shared: dws_*), with the
-        forward's routing decisions fixed.  Requires prepare_backward()."""
+        forward's routing decisions fixed.  Requires prepare_backward() before
+        that forward."""
         s = self.shape
         T, K, E, d, f = s.T, s.K, s.E_r, s.d_model, s.d_ffn
         L.moe_combine_backward(T, d, K, dy, self.y_perm, self.slot_row, self.gates, self.dt,
                                self.dy_perm, self.dgates, stream)
         L.moe_grouped_swiglu_backward(E, d, f, T * K, T, self.offsets, self.row_token, h, self.dt,
                                       self.w_gate, self.w_up, self.w_gu_t, self.w_down_t,
-                                      self.dy_perm, self.dx_perm, self.dw_gate, self.dw_up,
-                                      self.dw_down, self.bw_ws, self.bw_ws_bytes, stream)
+                                      self.dy_perm, self.au_perm, self.dx_perm, self.dw_gate,
+                                      self.dw_up, self.dw_down, self.bw_ws, self.bw_ws_bytes,
+                                      stream)
         if s.E_s:
             L.moe_grouped_swiglu_backward(s.E_s, d, f, T, T, self.sh_offsets, self.sh_rows, h,
                                           self.dt, self.ws_gate, self.ws_up, self.ws_gu_t,
-                                          self.ws_down_t, dy, self.dx_shared, self.dws_gate,
+                                          self.ws_down_t, dy, self.au_shared, self.dx_shared,
+                                          self.dws_gate,
                                           self.dws_up, self.dws_down, self.bw_ws,
                                           self.bw_ws_bytes, stream)
         # dh = dy + dx_shared + sum_k dx_perm[slot] (the combine with unit gates)

@@ -124,7 +124,7 @@ def test_backward_entry_points_reject_bad_arguments():
     P = ctypes.c_void_p(16)
     need = L.moe_grouped_swiglu_backward_workspace_size(8, 256, 512, 1000)
     assert need >= 1000 * 4 * 512 * 2            # a|u and da|du at least
-    args = [8, 256, 512, 1000, 500, P, P, P, 1, P, P, P, P, P, P, P, P, P, P]
+    args = [8, 256, 512, 1000, 500, P, P, P, 1, P, P, P, P, P, None, P, P, P, P, P]
     rc, msg = _st(lib.moe_grouped_swiglu_backward(*args, need - 1, None))
     assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
     bad = list(args); bad[8] = 0                   # fp32
@@ -172,6 +172,18 @@ def test_grouped_swiglu_rejects_bad_arguments():
     # zero rows is a valid no-op
     assert lib.moe_grouped_swiglu(8, 256, 512, 0, 500, P, P, P, 1, P, P, P, None, P, P,
                                   need, None) == L.MOE_OK
+    # the training form: bf16 only, a|u required, otherwise the same checks
+    rc, msg = _st(lib.moe_grouped_swiglu_train(8, 256, 512, 1000, 500, P, P, P, 0, P, P, P,
+                                               None, P, P, P, need, None))
+    assert rc == L.MOE_ERR_UNSUPPORTED and "bf16" in msg
+    rc, msg = _st(lib.moe_grouped_swiglu_train(8, 256, 512, 1000, 500, P, P, P, 1, P, P, P,
+                                               None, P, None, P, need, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "null" in msg
+    rc, msg = _st(lib.moe_grouped_swiglu_train(8, 256, 512, 1000, 500, P, P, P, 1, P, P, P,
+                                               None, P, P, P, need - 1, None))
+    assert rc == L.MOE_ERR_INVALID_ARG and "moe_grouped_swiglu_train: workspace" in msg
+    assert lib.moe_grouped_swiglu_train(8, 256, 512, 0, 500, P, P, P, 1, P, P, P, None, P, P, P,
+                                        need, None) == L.MOE_OK
 
 
 def test_combine_and_bias_update_reject_bad_arguments():

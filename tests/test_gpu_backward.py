@@ -49,14 +49,17 @@ def test_transpose_experts():
     assert torch.all(out[:, :, :50] == 0) and torch.all(out[:, :, 120:] == 0)
 
 
+@pytest.mark.parametrize("stored", [False, True], ids=["recompute", "stored_au"])
 @pytest.mark.parametrize("T,d,f,E,K,identity", [
     (200, 128, 128, 6, 2, False),
     (700, 256, 192, 5, 3, False),     # 192 = one and a half column tiles
     (3, 128, 64, 16, 2, False),       # nearly all groups empty
     (1100, 64, 128, 3, 1, False),     # groups of ~370 rows: several 128-row tiles
-    (300, 128, 128, 1, 1, True)])     # one group, identity rows (shared-expert form)
-def test_grouped_swiglu_backward_parity(T, d, f, E, K, identity):
-    say(f"moe_grouped_swiglu_backward T={T} d={d} f={f} E={E} K={K} identity={identity}")
+    (300, 128, 128, 1, 1, True),      # one group, identity rows (shared-expert form)
+    (1300, 512, 512, 4, 1, False)])   # streaming-kernel shapes in the a|u forward
+def test_grouped_swiglu_backward_parity(T, d, f, E, K, identity, stored):
+    say(f"moe_grouped_swiglu_backward T={T} d={d} f={f} E={E} K={K} identity={identity} "
+        f"stored={stored}")
     rng = np.random.default_rng(T + E)
     x = _bf16((T, d), 1.0, 3 + T)
     wg = _bf16((E, f, d), 1 / math.sqrt(d), 4)
@@ -73,11 +76,20 @@ def test_grouped_swiglu_backward_parity(T, d, f, E, K, identity):
     gu_t, d_t = _prep_t(wg, wu, wd)
     dx = torch.zeros((rows, d), dtype=torch.bfloat16, device=DEV)
     dwg, dwu, dwd = torch.full_like(wg, 7.0), torch.full_like(wu, 7.0), torch.full_like(wd, 7.0)
+    offs = torch.from_numpy(off).to(DEV)
+    ri = None if rt is None else torch.from_numpy(rt).to(DEV)
+    au = None
+    if stored:   # the training forward's a|u
+        fb = L.moe_grouped_swiglu_workspace_size(E, d, f, rows, L.MOE_BF16)
+        fws = torch.empty(fb, dtype=torch.uint8, device=DEV)
+        au = torch.empty((rows, 2 * f), dtype=torch.bfloat16, device=DEV)
+        y = torch.empty((rows, d), dtype=torch.bfloat16, device=DEV)
+        L.moe_grouped_swiglu_train(E, d, f, rows, T, offs, ri, x, L.MOE_BF16, wg, wu, wd, None,
+                                   y, au, fws, fb)
     wsb = L.moe_grouped_swiglu_backward_workspace_size(E, d, f, rows)
     ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
-    L.moe_grouped_swiglu_backward(E, d, f, rows, T, torch.from_numpy(off).to(DEV),
-                                  None if rt is None else torch.from_numpy(rt).to(DEV), x,
-                                  L.MOE_BF16, wg, wu, gu_t, d_t, dy, dx, dwg, dwu, dwd, ws, wsb)
+    L.moe_grouped_swiglu_backward(E, d, f, rows, T, offs, ri, x, L.MOE_BF16, wg, wu, gu_t, d_t,
+                                  dy, au, dx, dwg, dwu, dwd, ws, wsb)
     torch.cuda.synchronize()
     w_host = (host_array(wg), host_array(wu), host_array(wd))
     rdx, rdw = O.grouped_swiglu_backward(host_array(x), off, rt, w_host, to_host_f64(dy))
@@ -154,14 +166,16 @@ def _small_bf16_layer(T, d, f, E, K, E_s, fn, seed):
     return h, e, w, ws, b
 
 
-@pytest.mark.parametrize("fn,cf,E_s", [("sigmoid", None, 1), ("softmax", None, 0),
-                                       ("sigmoid", 1.0, 1)])
-def test_layer_backward_small(fn, cf, E_s):
+@pytest.mark.parametrize("fn,cf,E_s,keep_au", [("sigmoid", None, 1, True),
+                                               ("softmax", None, 0, True),
+                                               ("sigmoid", 1.0, 1, True),
+                                               ("sigmoid", None, 1, False)])
+def test_layer_backward_small(fn, cf, E_s, keep_au):
     T, d, f, E, K = 256, 256, 128, 16, 4
     h, e, w, ws, b = _small_bf16_layer(T, d, f, E, K, E_s, fn, 20)
     shape = LayerShape(T, d, E, K, E_s, f, "bf16", fn)
     run = MoELayer(shape, e, *w, *ws, capacity_factor=cf)
-    run.prepare_backward()
+    run.prepare_backward(keep_au=keep_au)
     run.forward(h, b)
     dy = _bf16((T, d), 1.0, 30)
     run.backward(h, dy)

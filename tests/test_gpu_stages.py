@@ -367,6 +367,44 @@ def test_grouped_swiglu_parity(T, d, f, E, K, dtype):
                 "bf16" if dtype == torch.bfloat16 else "f32")
 
 
+@pytest.mark.parametrize("T,d,f,E,K", [
+    (333, 256, 192, 5, 2),     # one-tile-per-workgroup kernel, partial column tile
+    (3, 128, 128, 64, 2),      # mostly empty experts
+    (300, 512, 256, 16, 4),    # register-staged streaming kernel
+    (1500, 512, 512, 6, 2),    # LDS-fed streaming kernel
+])
+def test_grouped_swiglu_train_outputs(T, d, f, E, K):
+    """The training form: the same y as the inference form (bit for bit: the
+    same kernels, with extra output passes), and a|u against the oracle's
+    projections; rows past the last group are left alone."""
+    say(f"moe_grouped_swiglu_train T={T} d={d} f={f} E={E} K={K}")
+    rng = np.random.default_rng(T + d + f + 1)
+    idx = O.biased_topk(rng.random((T, E)).astype(np.float32), None, K)
+    off, rt, _ = O.permute(idx, E)
+    rows = T * K + 3                                   # three rows outside every group
+    rt_pad = np.concatenate([rt, np.full(3, -1, np.int32)])
+    x = _tokens(T, d, torch.bfloat16, 90 + T)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, 91 + E)
+    offs, ri = torch.from_numpy(off).to(DEV), torch.from_numpy(rt_pad).to(DEV)
+    y_inf = _swiglu_gpu(x, offs, ri, wg, wu, wd, rows)
+    wsb = L.moe_grouped_swiglu_workspace_size(E, d, f, rows, L.MOE_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    y = torch.zeros((rows, d), dtype=torch.bfloat16, device=DEV)
+    au = torch.full((rows, 2 * f), 7.0, dtype=torch.bfloat16, device=DEV)
+    L.moe_grouped_swiglu_train(E, d, f, rows, T, offs, ri, x, L.MOE_BF16, wg, wu, wd, None, y,
+                               au, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_inf)
+    auh = to_host_f64(au)
+    assert np.all(auh[T * K:] == 7.0)
+    w_host = (host_array(wg), host_array(wu), host_array(wd))
+    ref = O.grouped_gate_up(host_array(x), off, rt, w_host)
+    for half in (slice(0, f), slice(f, 2 * f)):       # a and u separately
+        err = rel_err(auh[:T * K, half], ref[:, half])
+        say(f"a|u half {half.start}: max|d|/max|ref| = {err:.3e}")
+        assert err <= out_tol("bf16")
+
+
 def test_grouped_swiglu_row_scale_and_direct_rows():
     T, d, f, E = 257, 128, 128, 3
     x = _tokens(T, d, torch.bfloat16, 61)

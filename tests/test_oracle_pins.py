@@ -425,6 +425,42 @@ def test_grouped_swiglu_is_per_expert_dense():
         assert np.allclose(y[off[i]:off[i + 1]], ref, rtol=0, atol=1e-13)
 
 
+def test_grouped_gate_up_scaled_identity_closed_form():
+    # W_gate[g] = (g + 1) I and W_up[g] = -(g + 2) I give a = (g + 1) x and
+    # u = -(g + 2) x on each gathered row: fixes the group of each row, the
+    # gather, and which half holds which projection.
+    rng = np.random.default_rng(17)
+    T, d, E = 9, 6, 3
+    x = rng.standard_normal((T, d))
+    off = np.array([0, 4, 4, 11], np.int64)          # expert 1 has no rows
+    ri = np.array([8, 0, 3, 3, 1, 2, 5, 7, 6, 4, 0], np.int32)
+    eye = np.eye(d)
+    wg = np.stack([(g + 1) * eye for g in range(E)])
+    wu = np.stack([-(g + 2) * eye for g in range(E)])
+    wd = np.zeros((E, d, d))
+    au = O.grouped_gate_up(x, off, ri, (wg, wu, wd))
+    for g in range(E):
+        for r in range(off[g], off[g + 1]):
+            assert np.array_equal(au[r, :d], (g + 1) * x[ri[r]])
+            assert np.array_equal(au[r, d:], -(g + 2) * x[ri[r]])
+
+
+def test_grouped_gate_up_feeds_grouped_swiglu():
+    # SiLU(a) * u through W_down reproduces the grouped SwiGLU, for random
+    # weights and a routed gather
+    rng = np.random.default_rng(18)
+    T, d, f, E, K = 20, 8, 12, 4, 2
+    h, e, w, _ = _small_layer(rng, T, d, f, E, 0)
+    r = O.route(h, e, None, K, "sigmoid")
+    off, row_token, _ = O.permute(r["idx"], E)
+    au = O.grouped_gate_up(h, off, row_token, w)
+    y = O.grouped_swiglu(h, off, row_token, w)
+    for i in range(E):
+        lo, hi = off[i], off[i + 1]
+        act = au[lo:hi, :f] / (1 + np.exp(-au[lo:hi, :f])) * au[lo:hi, f:]
+        assert np.allclose(act @ w[2][i].astype(np.float64).T, y[lo:hi], rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------------------------ capacity dispatch
 # Routing-math page, section 3: C = ceil(CF * T * K / E_r); a copy routed to a
 # full expert is dropped.  Routing-and-load-balancing page, section 5: tokens
