@@ -296,7 +296,9 @@ def main(argv=None):
         with open(os.path.join(ROOT, "tests", "golden", "skew_beta.json")) as f:
             beta = json.load(f)["beta"]
     lay = make_layer(cfg, device="cuda", beta=beta)
-    hs = [lay.h] + [make_tokens(cfg, step=i, device="cuda") for i in range(1, args.rotate)]
+    # a multi-step training run takes a fresh batch every step
+    n_batches = max(args.rotate, cfg.steps)
+    hs = [lay.h] + [make_tokens(cfg, step=i, device="cuda") for i in range(1, n_batches)]
     torch.cuda.synchronize()
     log(f"inputs drawn in {time.perf_counter() - t0:.1f}s "
         f"({cfg.weight_bytes() / 1e9:.2f} GB of expert weights)")
@@ -315,28 +317,39 @@ def main(argv=None):
         run.prepare_backward(stream)     # transposed weight copies: outside the timed steps
         dy = make_tokens(cfg, step=10_000, device="cuda")
 
+    # per-step load statistics of a multi-step training run (the skewed workload):
+    # a 16-byte device copy after each step's bias update
+    stats_hist = None
+
     def step(i):
         run.forward(hs[i % len(hs)], b, gamma, stream)
         if dy is not None:
             run.backward(hs[i % len(hs)], dy, stream)
+        if stats_hist is not None:
+            stats_hist[i].copy_(run.stats, non_blocking=True)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     moe_profile_report()  # drop warm-up records
     moe_profile_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if cfg.steps > 1 and gamma is not None:
+        stats_hist = torch.zeros((args.steps, 4), dtype=torch.int32, device="cuda")
+        b.copy_(lay.b)   # the timed steps are steps 0, 1, ... of the run, from b0
+    # one event per step boundary (recording does not synchronise): per-step times
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         step(i)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     moe_profile_enable(False)
     prof = moe_profile_report()
-    ev_ms = ev0.elapsed_time(ev1)
+    ev_ms = evs[0].elapsed_time(evs[-1])
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
 
     ms_per_step = wall * 1000.0 / args.steps
     tokens_per_s = cfg.T / (ms_per_step / 1000.0)
@@ -372,6 +385,8 @@ def main(argv=None):
                  mfma_tflops=round(layer_flops / (ms_per_step / 1000.0) / 1e12, 1),
                  mfma_frac=round(layer_flops / (ms_per_step / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  experts_touched=n_touched, stats=run.stats_host())
+    # the roofline fraction the layer attains: the larger of its MFMA and HBM fractions
+    layer["attainable_frac"] = max(layer["hbm_frac"], layer["mfma_frac"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -391,15 +406,22 @@ def main(argv=None):
                                 f"{cfg.T * cfg.K} copies dropped)"),
                    "tokens_per_step": cfg.T, "parallelism": "single GPU"},
         "roofline": roofline, "layer": layer, "stages_ms": stages, "cpu_baseline": cpu,
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
+                    "max": round(step_ms[-1], 4)},
     }
+    if stats_hist is not None:
+        h = stats_hist.cpu()
+        out["load_stats_per_step"] = [
+            {"max_load": int(r[0]), "min_load": int(r[1]),
+             "max_vio": round(float(r[2:3].view(torch.float32)[0]), 4)} for r in h]
     if args.diagnostics:
         out["router_diag"] = {k: round(v, 6) for k, v in run.diag_host().items()}
     if args.backward:
-        # per touched expert: W_gate, W_up (recomputed a, u), W_down^T, [W_gate^T | W_up^T]
-        # read, three gradients written: 8 d f words; per assignment row dy_perm, dx
-        # (2 d words) and the staged a|u, da|du (4 f words) are overhead
+        # per touched expert: W_down^T and [W_gate^T | W_up^T] read, three gradients
+        # written: 6 d f words; per assignment row dy_perm, dx (2 d words) and the
+        # a|u kept by the forward, da|du (4 f words) are overhead
         d, f = cfg.d_model, cfg.d_ffn
-        bw_bytes = (n_touched + cfg.E_s) * 8 * d * f * 2
+        bw_bytes = (n_touched + cfg.E_s) * 6 * d * f * 2
         bw_ms = sum(v[1] for k, v in prof.items() if "backward" in k) / args.steps
         out["mode"] = "forward+backward"
         out["backward"] = dict(ms_per_step=round(bw_ms, 4), algorithmic_bytes=bw_bytes,
