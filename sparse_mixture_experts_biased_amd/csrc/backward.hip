@@ -28,6 +28,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;  // tile
 constexpr int kThreads = 256;                   // 4 waves, 2 x 2, 64 x 64 each
@@ -294,8 +295,15 @@ void bwd_gemm_kernel(GemmArgs p) {
     if (row >= nrows || n0 + cl * 8 >= p.N) continue;
     const size_t r = static_cast<size_t>(m0 + row);
     const int sw = (cl ^ (row & 4)) << 4;
-    *reinterpret_cast<uint4*>(p.C + cbase + r * p.ldc + n0 + cl * 8) =
-        *reinterpret_cast<const uint4*>(o0 + row * kORow + sw);
+    uint16_t* dst = p.C + cbase + r * p.ldc + n0 + cl * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(o0 + row * kORow + sw);
+    if (MODE == kModeKvar) {
+      // weight gradients are not read again here: streaming stores keep them
+      // from displacing the operand blocks that later tiles re-read from L2
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(dst));
+    } else {
+      *reinterpret_cast<uint4*>(dst) = v;
+    }
   }
 }
 
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(256) void transpose_experts_kernel(int rows, int co
   }
 }
 
-// Products over grouped rows use 128 x 128 tiles, weight gradients 64 x 256.
+// Products over grouped rows use 128 x 128 tiles, weight gradients 128 x 256.
 constexpr int kWM = 128, kWN = 256;
 
 template <int MODE>
