@@ -10,6 +10,9 @@
 //            the B tile stacks 128 W_gate rows over the same 128 W_up rows,
 //            so each lane holds matching gate and up accumulators.
 //   down:    y[r, n] = (act_r . Wd[n]) * row_scale[r]          K = d_ffn
+// The training form of gate/up (a compile-time variant) also writes a = x.Wg
+// and u = x.Wu to au [rows, 2 d_ffn] from the same accumulators, in extra
+// passes of its epilogue, for the backward pass.
 //
 // Tile: 256 grouped rows x 256 weight rows x 64 k, eight waves (two per
 // SIMD) in a 4 x 2 layout, each wave 64 rows x 128 weight rows as 2 x 4

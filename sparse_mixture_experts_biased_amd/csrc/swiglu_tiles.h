@@ -57,7 +57,7 @@ struct BwdWorkspace {
     int32_t* meta;
   } tiles, tiles256;        // 128- and 256-row tiles of the grouped rows
   int32_t* kpad;            // [n_groups + 1] expert rows padded to 64, prefix sums
-  uint16_t* au;             // [rows, 2f]  a | u recomputed
+  uint16_t* au;             // [rows, 2f]  a | u, when the backward recomputes them
   uint16_t* dadu;           // [rows, 2f]  da | du
   uint16_t *xT, *dyT;       // per-expert [d, mpad] blocks
   uint16_t *actT, *daT, *duT;  // per-expert [f, mpad] blocks
