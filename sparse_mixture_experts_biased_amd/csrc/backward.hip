@@ -37,6 +37,7 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr uint32_t kOff = 0x80000000u;          // beyond every buffer (< 2 GiB)
 constexpr int kPad = 64;                         // expert rows padded to this in the
                                                  // transposed layouts
+constexpr int kNumXcdB = 8;                      // XCDs (L2 domains) of the chip
 
 __device__ __forceinline__ int swz(int r, int c) {
   return r * kRowBytes + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
@@ -49,8 +50,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
-enum { kModeRows = 0, kModeKvar = 1 };
-
+// Arguments of the two backward GEMMs: "Rows" = bwd_gemm_kernel (products
+// over the grouped rows), "Kvar" = kvar_stream_kernel (weight gradients).
 struct GemmArgs {
   int M, N, K;             // Rows: N, K used (rows from the tile list); Kvar: M, N
   int NT, MT;              // column / row tiles per group
@@ -70,35 +71,22 @@ struct GemmArgs {
   size_t c_stride;
 };
 
-// C = A B^T over one 128 x 128 tile; K in 64-wide slices.  Three register
-// sets rotate through the global loads, so up to three slices are in flight
-// while one is multiplied out of LDS: a weight-gradient tile (K = an expert's
-// padded rows, usually two or three slices) has every load in flight from the
-// start, and the long-K products keep three slices streaming.
+// C = A B^T over one 128 x 128 tile of the grouped rows (the a, u recompute);
+// K in 64-wide slices.  Three register sets rotate through the global loads,
+// so up to three slices are in flight while one is multiplied out of LDS.
+// Four waves in a 2 x 2 layout, each 64 x 64.
 constexpr int kSets = 3;
 
-//
-// Tile 128 x BN with four waves in a 2 x 2 layout, each 64 rows x BN / 2
-// columns: 128 x 128 for the products over grouped rows, 128 x 256 for the
-// weight gradients, whose output rows are long (d_model or d_ffn wide): each
-// output row then leaves as a 512-byte piece (256-byte pieces scattered over
-// long rows cost about half of the HBM write rate), and the operands read per
-// byte written drop from 2 to 1.5 at 128 padded rows.
-//
-// LEAN: one LDS stage and one register set instead of two and three (the
-// weight-gradient tiles have only a few slices each, and their larger
-// accumulator tile needs the registers).
-template <int MODE, int BM, int BN, bool LEAN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_gemm_kernel(GemmArgs p) {
-  static_assert(BM == 128, "two waves of 64 rows along M");
+  constexpr int BM = kBM, BN = kBN;
   constexpr int kWN = 2;                           // waves along N (2 x 2 waves)
   constexpr int kNB = BN / kWN / 32;               // 32-wide column blocks per wave
   constexpr int kWNC = BN / kWN;                   // columns per wave
   constexpr int kAP = BM / 32, kBP = BN / 32;      // load passes (32 rows each)
   constexpr int kStageT = (BM + BN) * kRowBytes;
   // operand stages, and the output tile staged by the epilogue
-  constexpr int kSmem0 = (LEAN ? 1 : 2) * kStageT;
+  constexpr int kSmem0 = 2 * kStageT;
   constexpr int kSmem1 = BM * BN * 2;
   __shared__ __attribute__((aligned(16))) char smem[kSmem0 > kSmem1 ? kSmem0 : kSmem1];
   const int tid = threadIdx.x;
@@ -107,65 +95,34 @@ void bwd_gemm_kernel(GemmArgs p) {
   const int wm = wave / kWN, wn = wave % kWN;
   const int lc = tid & 7, lr = tid >> 3;  // 32 rows per load pass
 
-  int g, m0, nrows, n0, kbeg, nk;
-  if (MODE == kModeRows) {
-    const int w = blockIdx.x;
-    if (w >= p.meta[0] * p.NT) return;
-    const TileInfo ti = p.tiles[w / p.NT];
-    g = ti.group;
-    m0 = ti.m0;
-    nrows = min(ti.m1 - ti.m0, BM);
-    n0 = (w % p.NT) * BN;
-    kbeg = 0;
-    nk = p.K / kBK;
-  } else {
-    const int w = blockIdx.x;
-    if (w >= p.n_groups * p.MT * p.NT) return;
-    g = w / (p.MT * p.NT);
-    const int rem = w % (p.MT * p.NT);
-    m0 = (rem / p.NT) * BM;
-    nrows = min(p.M - m0, BM);
-    n0 = (rem % p.NT) * BN;
-    kbeg = p.kpad[g];
-    nk = (p.kpad[g + 1] - kbeg) / kBK;
-  }
+  const int w = blockIdx.x;
+  if (w >= p.meta[0] * p.NT) return;
+  const TileInfo ti = p.tiles[w / p.NT];
+  const int g = ti.group;
+  const int m0 = ti.m0;
+  const int nrows = min(ti.m1 - ti.m0, BM);
+  const int n0 = (w % p.NT) * BN;
+  const int nk = p.K / kBK;
 
   // ---- operand sources
   __amdgpu_buffer_rsrc_t rsA, rsB;
   uint32_t a_off[kAP], b_off[kBP];
-  if (MODE == kModeRows) {
-    rsA = rsrc(p.A, static_cast<uint32_t>(p.a_rows) * p.lda * 2u);
+  rsA = rsrc(p.A, static_cast<uint32_t>(p.a_rows) * p.lda * 2u);
 #pragma unroll
-    for (int i = 0; i < kAP; ++i) {
-      const int r = lr + 32 * i;
-      int sr = -1;
-      if (r < nrows) {
-        sr = p.row_index ? p.row_index[m0 + r] : m0 + r;
-        if (sr < 0 || sr >= p.a_rows) sr = -1;
-      }
-      a_off[i] = sr >= 0 ? (static_cast<uint32_t>(sr) * p.lda + lc * 8) * 2u : kOff;
+  for (int i = 0; i < kAP; ++i) {
+    const int r = lr + 32 * i;
+    int sr = -1;
+    if (r < nrows) {
+      sr = p.row_index ? p.row_index[m0 + r] : m0 + r;
+      if (sr < 0 || sr >= p.a_rows) sr = -1;
     }
-    rsB = rsrc(p.B + static_cast<size_t>(g) * p.b_stride,
-               static_cast<uint32_t>(p.N) * p.ldb * 2u);
+    a_off[i] = sr >= 0 ? (static_cast<uint32_t>(sr) * p.lda + lc * 8) * 2u : kOff;
+  }
+  rsB = rsrc(p.B + static_cast<size_t>(g) * p.b_stride, static_cast<uint32_t>(p.N) * p.ldb * 2u);
 #pragma unroll
-    for (int i = 0; i < kBP; ++i) {
-      const int n = n0 + lr + 32 * i;
-      b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * p.ldb + lc * 8) * 2u : kOff;
-    }
-  } else {
-    const int mpad = p.kpad[g + 1] - kbeg;
-    rsA = rsrc(p.A + static_cast<size_t>(kbeg) * p.M, static_cast<uint32_t>(p.M) * mpad * 2u);
-    rsB = rsrc(p.B + static_cast<size_t>(kbeg) * p.N, static_cast<uint32_t>(p.N) * mpad * 2u);
-#pragma unroll
-    for (int i = 0; i < kAP; ++i) {
-      const int m = m0 + lr + 32 * i;
-      a_off[i] = m < p.M ? (static_cast<uint32_t>(m) * mpad + lc * 8) * 2u : kOff;
-    }
-#pragma unroll
-    for (int i = 0; i < kBP; ++i) {
-      const int n = n0 + lr + 32 * i;
-      b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * mpad + lc * 8) * 2u : kOff;
-    }
+  for (int i = 0; i < kBP; ++i) {
+    const int n = n0 + lr + 32 * i;
+    b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * p.ldb + lc * 8) * 2u : kOff;
   }
 
   f32x16_t acc[2][kNB];
@@ -221,21 +178,7 @@ void bwd_gemm_kernel(GemmArgs p) {
   // that held it with slice J + 3 (past the end it re-reads the last slice, an
   // L2 hit, so every step issues the same loads and the waits stay exact) and
   // stores slice J + 1 to the other stage.
-  if (LEAN && nk > 0) {
-    // step J: store slice J to the stage, load slice J + 1 into the freed
-    // registers, multiply slice J
-    uint4 sa0[kAP], sb0[kBP];
-    load(sa0, sb0, 0);
-    for (int kt = 0;; ++kt) {
-      store(sa0, sb0, 0);
-      __syncthreads();
-      load(sa0, sb0, min(kt + 1, nk - 1));
-      compute(0);
-      if (kt + 1 >= nk) break;
-      __syncthreads();
-    }
-    __syncthreads();
-  } else if (nk > 0) {
+  if (nk > 0) {
     static_assert(kSets == 3, "the step sequence below rotates three sets");
     uint4 sa0[kAP], sb0[kBP], sa1[kAP], sb1[kBP], sa2[kAP], sb2[kBP];
     load(sa0, sb0, 0);
@@ -276,7 +219,6 @@ void bwd_gemm_kernel(GemmArgs p) {
     return row * kORow + ((((col >> 3) ^ (row & 4))) << 4) + (col & 7) * 2;
   };
   const int rl = tid / kOC, cl = tid % kOC;       // read-out position
-  const size_t cbase = MODE == kModeRows ? 0 : static_cast<size_t>(g) * p.c_stride;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -295,15 +237,8 @@ void bwd_gemm_kernel(GemmArgs p) {
     if (row >= nrows || n0 + cl * 8 >= p.N) continue;
     const size_t r = static_cast<size_t>(m0 + row);
     const int sw = (cl ^ (row & 4)) << 4;
-    uint16_t* dst = p.C + cbase + r * p.ldc + n0 + cl * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(o0 + row * kORow + sw);
-    if (MODE == kModeKvar) {
-      // weight gradients are not read again here: streaming stores keep them
-      // from displacing the operand blocks that later tiles re-read from L2
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(dst));
-    } else {
-      *reinterpret_cast<uint4*>(dst) = v;
-    }
+    *reinterpret_cast<uint4*>(p.C + r * p.ldc + n0 + cl * 8) =
+        *reinterpret_cast<const uint4*>(o0 + row * kORow + sw);
   }
 }
 
@@ -723,15 +658,263 @@ __global__ __launch_bounds__(256) void transpose_experts_kernel(int rows, int co
   }
 }
 
-// Products over grouped rows use 128 x 128 tiles, weight gradients 128 x 256.
-constexpr int kWM = 128, kWN = 256;
 
-template <int MODE>
-hipError_t gemm(const GemmArgs& a, unsigned blocks, hipStream_t s) {
+// ---------------------------------------------------------------- weight gradients, streamed
+//
+// C[g] [M, N] = A_g [M, K_g] B_g [N, K_g]^T for every group g, K_g = the
+// group's padded row count (two or three 64-k slices at 128 rows per expert),
+// over 256 x 256 output tiles.  One tile's own work is short, so a workgroup
+// per tile waits out its first loads every time.  Here one persistent
+// workgroup per CU walks an XCD-contiguous run of tiles as one continuous
+// stream of k-slices, laid out like the forward pass's register-staged
+// streaming kernel: two register sets keep the two slices after the current
+// one in flight (also across tiles), two LDS stages alternate, and after a
+// tile's last slice its output leaves through the stage that slice used, in
+// two rounds of 128 rows.  Eight waves, 4 along M x 2 along N, each 64 x 128
+// (2 x 4 blocks of v_mfma_f32_32x32x16_bf16).  A group without rows still
+// gets one slice (every load out of range: zeros), so its tiles are written
+// as zeros.  Past the last tile the load side re-reads its last slice (an L2
+// hit), so every step issues the same loads.
+constexpr int kVM = 256, kVN = 256, kVThreads = 512;
+
+__global__ __launch_bounds__(kVThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void kvar_stream_kernel(GemmArgs p, const int32_t* __restrict__ kpad) {
+  constexpr int kWNw = 2;                          // waves along N
+  constexpr int kNB = kVN / kWNw / 32;             // 32-wide column blocks per wave
+  constexpr int kWNC = kVN / kWNw;                 // columns per wave
+  constexpr int kRP = kVThreads / 8;               // rows per load pass
+  constexpr int kAP = kVM / kRP, kBP = kVN / kRP;  // load passes per operand
+  constexpr int kStage = (kVM + kVN) * kRowBytes;  // one k-slice of both operands
+  constexpr int kORow = kVN * 2;                   // bytes per staged output row
+  constexpr int kOC = kVN / 8;                     // 16-byte chunks per output row
+  constexpr int kORP = kVThreads / kOC;            // rows per read-out pass
+  constexpr int kRound = kStage / kORow;           // output rows per round
+  static_assert(kVM % kRound == 0 && kRound % 64 == 0, "rounds hold whole waves' rows");
+  static_assert(kORP % 8 == 0 && kRound % kORP == 0, "read-out rows keep row & 4");
+  __shared__ __attribute__((aligned(16))) char st0[kStage];
+  __shared__ __attribute__((aligned(16))) char st1[kStage];
+
+  // ---- this workgroup's tiles: first, first + nslot, ... below end
+  const int total = p.n_groups * p.MT * p.NT;
+  const int nslot = gridDim.x / kNumXcdB;
+  const int xcd = blockIdx.x % kNumXcdB;
+  const int per_xcd = (total + kNumXcdB - 1) / kNumXcdB;
+  const int first = xcd * per_xcd + static_cast<int>(blockIdx.x) / kNumXcdB;
+  const int end = min(total, (xcd + 1) * per_xcd);
+  if (first >= end) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int wm = wave / kWNw, wn = wave % kWNw;
+  const int lc = tid & 7, lr = tid >> 3;
+
+  // tile w: group, first row and column, slices
+  auto tile = [&](int w, int& g, int& m0, int& n0, int& nk, int& kbeg, int& mpad) {
+    w = __builtin_amdgcn_readfirstlane(w);
+    g = w / (p.MT * p.NT);
+    const int rem = w - g * (p.MT * p.NT);
+    m0 = (rem / p.NT) * kVM;
+    n0 = (rem % p.NT) * kVN;
+    kbeg = kpad[g];
+    mpad = kpad[g + 1] - kbeg;
+    nk = max(mpad / kBK, 1);
+  };
+
+  // ---- load side: the slice after next in the stream
+  int l_w = first, l_j = 0, l_nk, l_g, l_m0, l_n0;
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  uint32_t a_off[kAP], b_off[kBP];
+  auto set_load_tile = [&]() {
+    int kbeg, mpad;
+    tile(l_w, l_g, l_m0, l_n0, l_nk, kbeg, mpad);
+    rsA = rsrc(p.A + static_cast<size_t>(kbeg) * p.M, static_cast<uint32_t>(p.M) * mpad * 2u);
+    rsB = rsrc(p.B + static_cast<size_t>(kbeg) * p.N, static_cast<uint32_t>(p.N) * mpad * 2u);
+#pragma unroll
+    for (int i = 0; i < kAP; ++i) {
+      const int m = l_m0 + lr + kRP * i;
+      a_off[i] = m < p.M ? (static_cast<uint32_t>(m) * mpad + lc * 8) * 2u : kOff;
+    }
+#pragma unroll
+    for (int i = 0; i < kBP; ++i) {
+      const int n = l_n0 + lr + kRP * i;
+      b_off[i] = n < p.N ? (static_cast<uint32_t>(n) * mpad + lc * 8) * 2u : kOff;
+    }
+  };
+  set_load_tile();
+  // loads the load side's slice into (SA, SB) and moves it on
+#define MOE_VLOAD(SA, SB)                                                                    \
+  do {                                                                                      \
+    const uint32_t kb_ = static_cast<uint32_t>(l_j) * kBK * 2u;                             \
+    _Pragma("unroll") for (int i = 0; i < kAP; ++i) SA[i] = __builtin_bit_cast(             \
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb_, 0));               \
+    _Pragma("unroll") for (int i = 0; i < kBP; ++i) SB[i] = __builtin_bit_cast(             \
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, b_off[i], kb_, 0));               \
+    if (l_j + 1 < l_nk) {                                                                   \
+      ++l_j;                                                                                \
+    } else if (l_w + nslot < end) {                                                         \
+      l_w += nslot;                                                                         \
+      l_j = 0;                                                                              \
+      set_load_tile();                                                                      \
+    }                                                                                       \
+  } while (0)
+#define MOE_VSTORE(SA, SB, ST)                                                               \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < kAP; ++i)                                         \
+        *reinterpret_cast<uint4*>((ST) + swz(lr + kRP * i, lc)) = SA[i];                    \
+    _Pragma("unroll") for (int i = 0; i < kBP; ++i)                                         \
+        *reinterpret_cast<uint4*>((ST) + kVM * kRowBytes + swz(lr + kRP * i, lc)) = SB[i];  \
+  } while (0)
+
+  // ---- compute side
+  int c_w = first, c_j = 0, c_nk, c_g, c_m0, c_n0;
+  {
+    int kbeg, mpad;
+    tile(c_w, c_g, c_m0, c_n0, c_nk, kbeg, mpad);
+  }
+  f32x16_t acc[2][kNB];
+  auto zero = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
+  };
+  zero();
+  const int fr = lane & 31, fh = lane >> 5;
+  auto compute = [&](const char* st) {
+    const bool busy = c_m0 + wm * 64 < p.M;
+    if (!busy) return;
+    const char* bs = st + kVM * kRowBytes;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int c = kk * 2 + fh;
+      bf16x8_t af[2], bq[kNB];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        af[x] = *reinterpret_cast<const bf16x8_t*>(st + swz(wm * 64 + x * 32 + fr, c));
+#pragma unroll
+      for (int x = 0; x < kNB; ++x)
+        bq[x] = *reinterpret_cast<const bf16x8_t*>(bs + swz(wn * kWNC + x * 32 + fr, c));
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bq[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // Output tile through the free stage ot, in rounds of kRound rows: round r
+  // holds the rows of the waves with wm * 64 in it, staged as bf16 rows of
+  // 256 columns (16-byte chunk index XORed with row & 4) and written as whole
+  // 16-byte row chunks by buffer stores (an out-of-range offset drops one, so
+  // every lane issues the same stores).  D[row][col] of a 32x32 block is in
+  // lane col + 32*((row/4)%2), register (row%4) + 4*(row/8).
+  auto epilogue = [&](char* ot) {
+    // lane constants rederived from the hardware lane id (an opaque zero keeps
+    // them from being hoisted and held through the slice loop)
+    int ez = 0;
+    asm volatile("" : "+v"(ez));
+    const int e_lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, ez));
+    const int e_tid = wave * kWave + e_lane;
+    const int e_fr = e_lane & 31, e_fh = e_lane >> 5;
+    const __amdgpu_buffer_rsrc_t rsC = rsrc(p.C + static_cast<size_t>(c_g) * p.c_stride,
+                                            static_cast<uint32_t>(p.M) * p.ldc * 2u);
+    const int rl = e_tid / kOC, cl = e_tid % kOC;
+#pragma unroll
+    for (int r = 0; r < kVM / kRound; ++r) {
+      if (wm * 64 >= r * kRound && wm * 64 < (r + 1) * kRound) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int row = wm * 64 - r * kRound + a * 32 + 8 * (q >> 2) + 4 * e_fh + (q & 3);
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) {
+              const int col = wn * kWNC + b * 32 + e_fr;
+              *reinterpret_cast<uint16_t*>(ot + row * kORow + (((col >> 3) ^ (row & 4)) << 4) +
+                                           (col & 7) * 2) = f32_to_bf16(acc[a][b][q]);
+            }
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < kRound / kORP; ++it) {
+        const int row = it * kORP + rl;
+        const int m = c_m0 + r * kRound + row;
+        const uint32_t off = (m < p.M && c_n0 + cl * 8 < p.N)
+                                 ? (static_cast<uint32_t>(m) * p.ldc + c_n0 + cl * 8) * 2u
+                                 : kOff;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, *reinterpret_cast<const uint4*>(
+                                            ot + row * kORow + ((cl ^ (row & 4)) << 4))),
+            rsC, off, 0, 2 /* streaming: not read again here */);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+
+  // ---- the stream.  Slice s sits in register set s % 2 and LDS stage s % 2.
+  // Step j: load slice j + 2 into the set that held slice j (stored to LDS in
+  // step j - 1), multiply slice j, store slice j + 1 to the other stage,
+  // barrier; after a tile's last slice, write its output through stage j % 2.
+  uint4 sa0[kAP], sb0[kBP], sa1[kAP], sb1[kBP];
+  MOE_VLOAD(sa0, sb0);
+  MOE_VLOAD(sa1, sb1);
+  MOE_VSTORE(sa0, sb0, st0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#define MOE_VSTEP(LA, LB, CS, SA, SB, SS)                                                    \
+  MOE_VLOAD(LA, LB);                                                                        \
+  compute(CS);                                                                              \
+  MOE_VSTORE(SA, SB, SS);                                                                   \
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                           \
+  if (++c_j >= c_nk) {                                                                      \
+    epilogue(CS);                                                                           \
+    if (c_w + nslot >= end) break;                                                          \
+    c_w += nslot;                                                                           \
+    c_j = 0;                                                                                \
+    int kbeg_, mpad_;                                                                       \
+    tile(c_w, c_g, c_m0, c_n0, c_nk, kbeg_, mpad_);                                         \
+    zero();                                                                                 \
+  }
+  for (;;) {
+    MOE_VSTEP(sa0, sb0, st0, sa1, sb1, st1)
+    MOE_VSTEP(sa1, sb1, st1, sa0, sb0, st0)
+  }
+#undef MOE_VSTEP
+#undef MOE_VLOAD
+#undef MOE_VSTORE
+  // the last loads and the output stores complete before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Workgroups of the streamed weight-gradient kernel: one per CU, a multiple of
+// the XCD count.
+int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < kNumXcdB)
+      cus = 256;
+    cached[dev] = cus / kNumXcdB * kNumXcdB;
+  }
+  return cached[dev];
+}
+
+hipError_t kvar_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.n_groups * a.MT * a.NT == 0) return hipSuccess;
+  hipLaunchKernelGGL(kvar_stream_kernel, dim3(persistent_grid()), dim3(kVThreads), 0, s, a,
+                     a.kpad);
+  return hipGetLastError();
+}
+
+hipError_t rows_gemm(const GemmArgs& a, unsigned blocks, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
-  constexpr int BM = MODE == kModeKvar ? kWM : kBM, BN = MODE == kModeKvar ? kWN : kBN;
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, BM, BN, MODE == kModeKvar>), dim3(blocks),
-                     dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(bwd_gemm_kernel, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -811,9 +994,9 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
     a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
     a.ldc = 2 * f;
     a.B = wg; a.C = w.au;
-    if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+    if ((err = rows_gemm(a, max_tiles * a.NT, s)) != hipSuccess) return err;
     a.B = wu; a.C = w.au + f;
-    if ((err = gemm<kModeRows>(a, max_tiles * a.NT, s)) != hipSuccess) return err;
+    if ((err = rows_gemm(a, max_tiles * a.NT, s)) != hipSuccess) return err;
     au = w.au;
   }
   // 2. d act = dy W_down (B = W_down^T [f, d]) -> [rows, f], held in the daT
@@ -859,17 +1042,16 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   k.n_groups = n_groups;
   k.kpad = w.kpad;
   //    dW_gate [f, d] = da^T x ; dW_up = du^T x
-  k.M = f; k.N = d; k.MT = (f + kWM - 1) / kWM; k.NT = (d + kWN - 1) / kWN;
+  k.M = f; k.N = d; k.MT = (f + kVM - 1) / kVM; k.NT = (d + kVN - 1) / kVN;
   k.B = w.xT; k.ldc = d; k.c_stride = static_cast<size_t>(f) * d;
-  const unsigned gb = static_cast<unsigned>(n_groups) * k.MT * k.NT;
   k.A = w.daT; k.C = dwg;
-  if ((err = gemm<kModeKvar>(k, gb, s)) != hipSuccess) return err;
+  if ((err = kvar_gemm(k, s)) != hipSuccess) return err;
   k.A = w.duT; k.C = dwu;
-  if ((err = gemm<kModeKvar>(k, gb, s)) != hipSuccess) return err;
+  if ((err = kvar_gemm(k, s)) != hipSuccess) return err;
   //    dW_down [d, f] = dy^T act
-  k.M = d; k.N = f; k.MT = (d + kWM - 1) / kWM; k.NT = (f + kWN - 1) / kWN;
+  k.M = d; k.N = f; k.MT = (d + kVM - 1) / kVM; k.NT = (f + kVN - 1) / kVN;
   k.A = w.dyT; k.B = w.actT; k.C = dwd; k.ldc = f; k.c_stride = static_cast<size_t>(d) * f;
-  return gemm<kModeKvar>(k, static_cast<unsigned>(n_groups) * k.MT * k.NT, s);
+  return kvar_gemm(k, s);
 }
 
 hipError_t launch_combine_backward(int T, int d, int K, const uint16_t* dy, const uint16_t* yp,
