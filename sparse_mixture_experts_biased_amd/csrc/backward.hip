@@ -690,7 +690,7 @@ void kvar_stream_kernel(GemmArgs p, const int32_t* __restrict__ kpad) {
   constexpr int kORP = kVThreads / kOC;            // rows per read-out pass
   constexpr int kRound = kStage / kORow;           // output rows per round
   static_assert(kVM % kRound == 0 && kRound % 64 == 0, "rounds hold whole waves' rows");
-  static_assert(kORP % 8 == 0 && kRound % kORP == 0, "read-out rows keep row & 4");
+  static_assert(kRound % kORP == 0 && kOC == 32, "read-out rows; 32 chunks per staged row");
   __shared__ __attribute__((aligned(16))) char st0[kStage];
   __shared__ __attribute__((aligned(16))) char st1[kStage];
 
@@ -797,20 +797,26 @@ void kvar_stream_kernel(GemmArgs p, const int32_t* __restrict__ kpad) {
 #pragma unroll
       for (int x = 0; x < kNB; ++x)
         bq[x] = *reinterpret_cast<const bf16x8_t*>(bs + swz(wn * kWNC + x * 32 + fr, c));
+      // B A^T: acc[a][b] holds the block transposed, so a lane's registers
+      // run along an output row (see the epilogue)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < kNB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bq[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[b], af[a], acc[a][b], 0, 0, 0);
     }
   };
 
   // Output tile through the free stage ot, in rounds of kRound rows: round r
   // holds the rows of the waves with wm * 64 in it, staged as bf16 rows of
-  // 256 columns (16-byte chunk index XORed with row & 4) and written as whole
-  // 16-byte row chunks by buffer stores (an out-of-range offset drops one, so
-  // every lane issues the same stores).  D[row][col] of a 32x32 block is in
-  // lane col + 32*((row/4)%2), register (row%4) + 4*(row/8).
+  // 256 columns and written as whole 16-byte row chunks by buffer stores (an
+  // out-of-range offset drops one, so every lane issues the same stores).
+  // The blocks were multiplied as B A^T, so output [row][col] of a 32x32
+  // block is in lane row + 32*((col/4)%2), register (col%4) + 4*(col/8): a
+  // lane holds four consecutive columns per register quad and stages them
+  // with one 8-byte write.  The 16-byte chunk index of a staged row is XORed
+  // with row % 32, so the 32 rows of one write instruction fall on distinct
+  // chunks.
   auto epilogue = [&](char* ot) {
     // lane constants rederived from the hardware lane id (an opaque zero keeps
     // them from being hoisted and held through the slice loop)
@@ -826,17 +832,20 @@ void kvar_stream_kernel(GemmArgs p, const int32_t* __restrict__ kpad) {
     for (int r = 0; r < kVM / kRound; ++r) {
       if (wm * 64 >= r * kRound && wm * 64 < (r + 1) * kRound) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a) {
+          const int row = wm * 64 - r * kRound + a * 32 + e_fr;
+          char* orow = ot + row * kORow;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int row = wm * 64 - r * kRound + a * 32 + 8 * (q >> 2) + 4 * e_fh + (q & 3);
+          for (int b = 0; b < kNB; ++b)
 #pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-              const int col = wn * kWNC + b * 32 + e_fr;
-              *reinterpret_cast<uint16_t*>(ot + row * kORow + (((col >> 3) ^ (row & 4)) << 4) +
-                                           (col & 7) * 2) = f32_to_bf16(acc[a][b][q]);
+            for (int qq = 0; qq < 4; ++qq) {
+              const int col = wn * kWNC + b * 32 + 8 * qq + 4 * e_fh;
+              const uint2 v = make_uint2(
+                  pack_bf16x2(acc[a][b][4 * qq], acc[a][b][4 * qq + 1]),
+                  pack_bf16x2(acc[a][b][4 * qq + 2], acc[a][b][4 * qq + 3]));
+              *reinterpret_cast<uint2*>(orow + (((col >> 3) ^ (row & 31)) << 4) + (col & 4) * 2) = v;
             }
-          }
+        }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
@@ -848,7 +857,7 @@ void kvar_stream_kernel(GemmArgs p, const int32_t* __restrict__ kpad) {
                                  : kOff;
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4_t, *reinterpret_cast<const uint4*>(
-                                            ot + row * kORow + ((cl ^ (row & 4)) << 4))),
+                                            ot + row * kORow + ((cl ^ (row & 31)) << 4))),
             rsC, off, 0, 2 /* streaming: not read again here */);
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
