@@ -621,36 +621,53 @@ void bf16_stream_kernel(
 
   // Wave (wm, wn) multiplies the 32-row blocks 2 wm and 2 wm + 1 (a block
   // with no row of the item is skipped) against its kNB weight blocks.
+  //
+  // Both 32-row blocks of a busy wave are multiplied (rows past the group hold
+  // zeros in LDS and are never written out), so a step is one basic block:
+  // the fragment reads of its second 32-k half are issued between the MFMAs
+  // of the first half (one read after each MFMA), where their LDS latency is
+  // covered, instead of after them.
   auto compute = [&](const char* st) {
-    const bool mb0 = wm * 64 < c_nrows;
-    const bool mb1 = wm * 64 + 32 < c_nrows;
-    if (!mb0) return;
+    if (wm * 64 >= c_nrows) return;
     const char* bs = st + G::kTileBytes;
+    bf16x8_t bq[BK / 32][2][kNB], aq[BK / 32][2][2];
 #pragma unroll
-    for (int kh = 0; kh < BK / 32; ++kh) {
-      bf16x8_t bq[2][kNB], aq[2][2];
+    for (int kh = 0; kh < BK / 32; ++kh)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int c = kh * 4 + kk * 2 + fh;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb)
-          bq[kk][nb] = *reinterpret_cast<const bf16x8_t*>(bs + G::swz(brow[nb] + fr, c));
-        aq[kk][0] = *reinterpret_cast<const bf16x8_t*>(st + G::swz(wm * 64 + fr, c));
-        if (mb1) aq[kk][1] = *reinterpret_cast<const bf16x8_t*>(st + G::swz(wm * 64 + 32 + fr, c));
+          bq[kh][kk][nb] = *reinterpret_cast<const bf16x8_t*>(bs + G::swz(brow[nb] + fr, c));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          aq[kh][kk][mb] = *reinterpret_cast<const bf16x8_t*>(st + G::swz(wm * 64 + mb * 32 + fr, c));
       }
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+    for (int kh = 0; kh < BK / 32; ++kh)
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
-          acc[0][nb] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk][0], bq[kk][nb], acc[0][nb], 0, 0, 0);
-        if (mb1) {
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb)
-            acc[1][nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk][1], bq[kk][nb], acc[1][nb], 0, 0, 0);
-        }
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kh][kk][mb], bq[kh][kk][nb],
+                                                                  acc[mb][nb], 0, 0, 0);
+    // order: the first half's reads, then each of the first half's MFMAs
+    // followed by one read of the second half, then the remaining MFMAs
+    constexpr int kReadsHalf = 2 * (kNB + 2);
+    constexpr int kMfmaHalf = 2 * 2 * kNB;
+    static_assert(kReadsHalf <= kMfmaHalf, "one read after each MFMA of the first half");
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadsHalf, 0);
+    if constexpr (BK == 64) {
+#pragma unroll
+      for (int i = 0; i < kReadsHalf; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaHalf - kReadsHalf, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaHalf, 0);
     }
   };
 
