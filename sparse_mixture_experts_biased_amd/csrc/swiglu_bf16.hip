@@ -35,10 +35,11 @@
 // and a register-staged one for smaller groups, where streaming the weights
 // from HBM bounds them and more bytes in flight per CU pay.
 //
-// Work order: (group, column tile, row tile); block ids are remapped so each
-// XCD walks a contiguous run of it: row tiles of one (expert, column tile) run
-// side by side on one XCD and share the weight slice through its L2, and the
-// column tiles of one expert reuse its gathered x rows from that L2.
+// Work order: by group, then blocks of up to four row tiles by all column
+// tiles, row tile fastest (item_tile); block ids are remapped so each XCD
+// walks a contiguous run of it: the row tiles of one (expert, column tile)
+// run side by side on one XCD and share the weight slice through its L2, and
+// the column tiles of the same row tiles reuse their gathered x rows from it.
 #include "swiglu_tiles.h"
 
 namespace moe {
@@ -50,6 +51,32 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kBK = 64;         // k per LDS stage (8 chunks of 16 B per row)
 constexpr int kRowBytes = kBK * 2;                     // 128 B
 constexpr int kNumXcd = 8;
+
+// Row and column tile of item `local` of a group with nmt row tiles and NT
+// column tiles.  Items run in blocks of kItemRows row tiles by all column
+// tiles, row tile fastest inside a block, so the items an XCD's workgroups
+// take side by side (consecutive items) cover a few row tiles by several
+// column tiles and share both operands' slices through its L2; groups of at
+// most kItemRows row tiles keep plain row-tile-fastest order.
+constexpr int kItemRows = 4;
+__device__ __forceinline__ void item_tile(int local, int nmt, int NT, int& mt, int& nt) {
+  if (nmt <= kItemRows) {  // one block: a single division
+    nt = local / nmt;
+    mt = local - nt * nmt;
+    return;
+  }
+  const int full = nmt / kItemRows;
+  const int span = kItemRows * NT;
+  if (local < full * span) {
+    const int sr = local / span, j = local - sr * span;
+    mt = sr * kItemRows + j % kItemRows;
+    nt = j / kItemRows;
+  } else {
+    const int j = local - full * span, rl = nmt - full * kItemRows;
+    mt = full * kItemRows + j % rl;
+    nt = j / rl;
+  }
+}
 constexpr int kBufferFlags = 0x00020000;               // raw buffer, 32-bit data format
 
 // LDS byte offset of 16-byte chunk c of tile row r.  The chunk index is XORed
@@ -106,9 +133,9 @@ void bf16_tile_kernel(
   const int g = tiles[w / NT].group;
   const int gstart = gts[g];
   const int nmt = gts[g + 1] - gstart;
-  const int local = w - gstart * NT;
-  const int ntile = local / nmt;
-  const TileInfo ti = tiles[gstart + local % nmt];
+  int mtile, ntile;
+  item_tile(w - gstart * NT, nmt, NT, mtile, ntile);
+  const TileInfo ti = tiles[gstart + mtile];
   const int nrows = min(ti.m1 - ti.m0, BM);
 
   constexpr int kCols = GATEUP ? BNW / 2 : BNW;
@@ -499,10 +526,10 @@ void bf16_stream_kernel(
   int l_item = 0, l_g, l_ntile, l_m0, l_nrows;
   {
     const TileInfo t0 = tiles[first / NT];
-    const int local = first - t0.gstart * NT;
-    const TileInfo ti = tiles[t0.gstart + local % t0.ntiles];
+    int mt;
+    item_tile(first - t0.gstart * NT, max(t0.ntiles, 1), NT, mt, l_ntile);
+    const TileInfo ti = tiles[t0.gstart + mt];
     l_g = t0.group;
-    l_ntile = local / t0.ntiles;
     l_m0 = ti.m0;
     l_nrows = min(ti.m1 - ti.m0, BM);
   }
@@ -558,10 +585,10 @@ void bf16_stream_kernel(
       f_gstart = t.gstart;
       f_ntiles = max(t.ntiles, 1);
     } else if (lk == 2) {
-      const int local = nw - f_gstart * NT;
-      n_ntile = local / f_ntiles;
+      int mt;
+      item_tile(nw - f_gstart * NT, f_ntiles, NT, mt, n_ntile);
       n_g = f_group;
-      const TileInfo u = tiles[f_gstart + local - n_ntile * f_ntiles];
+      const TileInfo u = tiles[f_gstart + mt];
       f_m0 = u.m0;
       f_m1 = u.m1;
     } else if (lk == 4) {
@@ -896,10 +923,10 @@ void bf16_regs_stream_kernel(
   {
     const int w = first;
     const TileInfo t0 = tiles[w / NT];
-    const int local = w - t0.gstart * NT;
-    const TileInfo ti = tiles[t0.gstart + local % t0.ntiles];
+    int mt;
+    item_tile(w - t0.gstart * NT, max(t0.ntiles, 1), NT, mt, l_ntile);
+    const TileInfo ti = tiles[t0.gstart + mt];
     l_g = t0.group;
-    l_ntile = local / t0.ntiles;
     l_m0 = ti.m0;
     l_nrows = min(ti.m1 - ti.m0, BM);
   }
@@ -975,10 +1002,10 @@ void bf16_regs_stream_kernel(
     if (fa == 1) { /* the group record just arrived: locate the row tile */                 \
       const int gstart_ = __builtin_amdgcn_readlane(p, 3);                                  \
       const int gnt_ = max(__builtin_amdgcn_readlane(p, 4), 1);                             \
-      const int local_ = nw - gstart_ * NT;                                                 \
+      int mt_;                                                                              \
+      item_tile(nw - gstart_ * NT, gnt_, NT, mt_, n_ntile);                                 \
       n_g = __builtin_amdgcn_readlane(p, 0);                                                \
-      n_ntile = local_ / gnt_;                                                              \
-      rec = gstart_ + local_ - n_ntile * gnt_;                                              \
+      rec = gstart_ + mt_;                                                                  \
     }                                                                                       \
     n_m0 = __builtin_amdgcn_readlane(p, 9);                                                 \
     n_nrows = min(__builtin_amdgcn_readlane(p, 10) - n_m0, BM);                             \
