@@ -405,6 +405,30 @@ def test_grouped_swiglu_train_outputs(T, d, f, E, K):
         assert err <= out_tol("bf16")
 
 
+@pytest.mark.parametrize("d,f,extra_empty", [(512, 512, 0), (512, 512, 16), (256, 192, 0)])
+def test_grouped_swiglu_many_row_tiles_per_group(d, f, extra_empty):
+    """Groups of 5, 6 and 9 row tiles (256 rows each), walked in blocks of
+    four row tiles by all column tiles with a partial last block; an empty
+    group between them.  (512, 512): the LDS-fed streaming kernel, or with 16
+    more empty groups (under 256 rows per group on average) the
+    register-staged one; (256, 192): the one-tile-per-workgroup kernel."""
+    sizes = [1100, 0, 1500, 2200] + [0] * extra_empty
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = int(off[-1])
+    say(f"many row tiles per group: d={d} f={f} groups {sizes}")
+    x = _tokens(T, d, torch.bfloat16, 95)
+    wg, wu, wd = _weights(len(sizes), d, f, torch.bfloat16, 96)
+    ri = np.random.default_rng(97).permutation(T).astype(np.int32)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(ri).to(DEV), wg, wu, wd, T)
+    w_host = (host_array(wg), host_array(wu), host_array(wd))
+    ref = O.grouped_swiglu(host_array(x), off, ri, w_host)
+    yh = to_host_f64(y)
+    for i in range(len(sizes)):
+        lo, hi = off[i], off[i + 1]
+        if hi > lo:
+            assert rel_err(yh[lo:hi], ref[lo:hi]) <= out_tol("bf16"), i
+
+
 def test_grouped_swiglu_row_scale_and_direct_rows():
     T, d, f, E = 257, 128, 128, 3
     x = _tokens(T, d, torch.bfloat16, 61)
