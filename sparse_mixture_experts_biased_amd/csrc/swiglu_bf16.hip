@@ -680,22 +680,23 @@ void bf16_stream_kernel(
           for (int nb = 0; nb < kNB; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kh][kk][mb], bq[kh][kk][nb],
                                                                   acc[mb][nb], 0, 0, 0);
-    // order: the first half's reads, then each of the first half's MFMAs
-    // followed by one read of the second half, then the remaining MFMAs
-    constexpr int kReadsHalf = 2 * (kNB + 2);
-    constexpr int kMfmaHalf = 2 * 2 * kNB;
-    static_assert(kReadsHalf <= kMfmaHalf, "one read after each MFMA of the first half");
-    __builtin_amdgcn_sched_group_barrier(0x100, kReadsHalf, 0);
-    if constexpr (BK == 64) {
+    // order: the first 16-k step's reads, then each 16-k step's MFMAs with
+    // the next step's reads one after each MFMA, then the last step's MFMAs
+    constexpr int kReadsKK = kNB + 2;       // fragment reads of one 16-k step
+    constexpr int kMfmaKK = 2 * kNB;        // its MFMAs
+    constexpr int kSteps = BK / 16;
+    static_assert(kReadsKK <= kMfmaKK, "one read after each MFMA of the step before");
+    __builtin_amdgcn_sched_group_barrier(0x100, kReadsKK, 0);
 #pragma unroll
-      for (int i = 0; i < kReadsHalf; ++i) {
+    for (int st = 0; st + 1 < kSteps; ++st) {
+#pragma unroll
+      for (int i = 0; i < kReadsKK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMfmaHalf - kReadsHalf, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaHalf, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaKK - kReadsKK, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaKK, 0);
   };
 
   // Output tile of the compute-side item, staged through the last stage (free
