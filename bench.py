@@ -85,13 +85,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256, capacity=None):
+def cpu_baseline(cfg, lay, b_host, budget_s=12.0, chunk=8, sample_shared=1024, capacity=None):
     """Time the oracle on a bounded sample of the same workload on host cores.
 
-    Sample: routing of all T tokens; the routed experts 0..sample_experts-1 on
-    all their rows; the shared expert on sample_shared tokens; the full combine
-    and bias update.  Expert time is scaled by E_r / sample_experts and the
-    shared-expert time by T / sample_shared to a whole-layer estimate.
+    Sample: routing of all T tokens; the routed experts in ascending order, in
+    chunks of `chunk`, on all their rows, until their oracle time reaches
+    budget_s or every expert is done; the shared expert on the first
+    sample_shared tokens; the full combine and bias update.  Expert time is
+    scaled by E_r / experts run and the shared-expert time by T / tokens run
+    to a whole-layer estimate (no scaling where the sample is the whole).
     """
     import numpy as np
 
@@ -106,8 +108,6 @@ def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256, capacity
         blas, threads = [], len(os.sched_getaffinity(0))
     h = host_array(lay.h)
     e = host_array(lay.e)
-    w = {i: (host_array(lay.w_gate[i]), host_array(lay.w_up[i]), host_array(lay.w_down[i]))
-         for i in range(sample_experts)}
     ws = (host_array(lay.ws_gate[0]), host_array(lay.ws_up[0]), host_array(lay.ws_down[0])) \
         if cfg.E_s else None
 
@@ -119,15 +119,26 @@ def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256, capacity
         off, rt, sr, _ = O.permute_capacity(r["idx"], cfg.E_r, capacity)
     t_route = time.perf_counter() - t0
 
-    t0 = time.perf_counter()
-    y_perm = O.grouped_swiglu(h, off, rt, lambda i: w[i], groups=range(sample_experts))
-    t_exp = time.perf_counter() - t0
-    rows = int(off[sample_experts])
+    # Expert weights come to the host one chunk at a time (outside the timed
+    # calls), so host memory stays at one chunk's weights.
+    y_perm = None
+    t_exp, n_exp = 0.0, 0
+    while n_exp < cfg.E_r and (n_exp == 0 or t_exp < budget_s):
+        grp = range(n_exp, min(cfg.E_r, n_exp + chunk))
+        w = {i: (host_array(lay.w_gate[i]), host_array(lay.w_up[i]), host_array(lay.w_down[i]))
+             for i in grp}
+        t0 = time.perf_counter()
+        part = O.grouped_swiglu(h, off, rt, lambda i: w[i], groups=grp)
+        t_exp += time.perf_counter() - t0
+        y_perm = part if y_perm is None else y_perm + part   # disjoint rows; the rest stay 0
+        n_exp = grp.stop
+        del w
+    rows = int(off[n_exp])
 
-    t_sh = 0.0
+    t_sh, n_sh = 0.0, min(cfg.T, sample_shared)
     if ws is not None:
         t0 = time.perf_counter()
-        O.swiglu(h[:sample_shared], *ws)
+        O.swiglu(h[:n_sh], *ws)
         t_sh = time.perf_counter() - t0
 
     t0 = time.perf_counter()
@@ -136,20 +147,20 @@ def cpu_baseline(cfg, lay, b_host, sample_experts=8, sample_shared=256, capacity
                   cfg.T, cfg.K, 0.001)
     t_comb = time.perf_counter() - t0
 
-    est = t_route + t_exp * cfg.E_r / sample_experts + t_comb
+    est = t_route + t_exp * cfg.E_r / n_exp + t_comb
     if ws is not None:
-        est += t_sh * cfg.T / sample_shared
+        est += t_sh * cfg.T / n_sh
     measured = t_route + t_exp + t_sh + t_comb
-    log(f"cpu oracle: route {t_route:.2f}s, {sample_experts} experts ({rows} rows) {t_exp:.2f}s,"
-        f" shared on {sample_shared} tokens {t_sh:.2f}s, combine {t_comb:.2f}s -> layer est "
+    log(f"cpu oracle: route {t_route:.2f}s, {n_exp} experts ({rows} rows) {t_exp:.2f}s,"
+        f" shared on {n_sh} tokens {t_sh:.2f}s, combine {t_comb:.2f}s -> layer est "
         f"{est:.1f}s")
     return dict(
         value=cfg.T / est, unit="tokens/s", cores=int(threads), kind="oracle",
         sample=(f"oracle (NumPy fp64, BLAS {blas}) on: routing of all {cfg.T} tokens, routed "
-                f"experts 0-{sample_experts - 1} of {cfg.E_r} on their {rows} rows, shared "
-                f"expert on {sample_shared} of {cfg.T} tokens, full combine + bias update; "
-                f"expert time x{cfg.E_r / sample_experts:g}, shared time "
-                f"x{cfg.T / sample_shared:g} -> whole-layer estimate {est:.2f} s "
+                f"experts 0-{n_exp - 1} of {cfg.E_r} on their {rows} rows, shared "
+                f"expert on {n_sh if ws is not None else 0} of {cfg.T} tokens, full combine + bias "
+                f"update; expert time x{cfg.E_r / n_exp:g}, shared time "
+                f"x{(cfg.T / n_sh) if ws is not None else 0:g} -> whole-layer estimate {est:.2f} s "
                 f"({measured:.2f} s measured)"),
     )
 
