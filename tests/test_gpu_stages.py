@@ -341,6 +341,10 @@ SWIGLU_CASES = [
     (4000, 1024, 1024, 48, 4, torch.bfloat16),  # several work items per workgroup
     # >= 256 rows per expert on average: the LDS-fed streaming kernel
     (1500, 512, 512, 6, 2, torch.bfloat16),    # ragged groups of ~500 rows
+    # longer K (gate/up 1024, down 2048), < 256 rows per expert on average:
+    # the register-staged streaming kernel over many slices and items
+    (2000, 1024, 2048, 96, 4, torch.bfloat16),  # ~83-row groups, several items per workgroup
+    (40, 1024, 1024, 64, 2, torch.bfloat16),    # decode-like: 0-4 rows per group
 ]
 
 
@@ -372,6 +376,7 @@ def test_grouped_swiglu_parity(T, d, f, E, K, dtype):
     (3, 128, 128, 64, 2),      # mostly empty experts
     (300, 512, 256, 16, 4),    # register-staged streaming kernel
     (1500, 512, 512, 6, 2),    # LDS-fed streaming kernel
+    (2000, 1024, 1024, 40, 2),  # register-staged streaming kernel, K = 1024
 ])
 def test_grouped_swiglu_train_outputs(T, d, f, E, K):
     """The training form: the same y as the inference form (bit for bit: the
@@ -405,13 +410,15 @@ def test_grouped_swiglu_train_outputs(T, d, f, E, K):
         assert err <= out_tol("bf16")
 
 
-@pytest.mark.parametrize("d,f,extra_empty", [(512, 512, 0), (512, 512, 16), (256, 192, 0)])
+@pytest.mark.parametrize("d,f,extra_empty", [(512, 512, 0), (512, 512, 16), (256, 192, 0),
+                                              (1024, 1024, 16)])
 def test_grouped_swiglu_many_row_tiles_per_group(d, f, extra_empty):
     """Groups of 5, 6 and 9 row tiles (256 rows each), walked in blocks of
     four row tiles by all column tiles with a partial last block; an empty
     group between them.  (512, 512): the LDS-fed streaming kernel, or with 16
     more empty groups (under 256 rows per group on average) the
-    register-staged one; (256, 192): the one-tile-per-workgroup kernel."""
+    register-staged one; (256, 192): the one-tile-per-workgroup kernel;
+    (1024, 1024) with 16 empty groups: the register-staged one at K = 1024."""
     sizes = [1100, 0, 1500, 2200] + [0] * extra_empty
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     T = int(off[-1])
@@ -442,18 +449,20 @@ def test_grouped_swiglu_row_scale_and_direct_rows():
     assert rel_err(to_host_f64(y), ref) <= out_tol("bf16")
 
 
-@pytest.mark.parametrize("T,off", [
+@pytest.mark.parametrize("T,off,d", [
     # < 256 rows per group on average: the register-staged streaming kernel
-    (700, [0, 300, 300, 301, 590, 700]),
+    (700, [0, 300, 300, 301, 590, 700], 512),
     # >= 256 rows per group on average: the LDS-fed one (a 589-row group spans three row tiles)
-    (1300, [0, 600, 600, 601, 1190, 1300]),
+    (1300, [0, 600, 600, 601, 1190, 1300], 512),
+    # the register-staged kernel at K = 1024
+    (700, [0, 300, 300, 301, 590, 700], 1024),
 ])
-def test_grouped_swiglu_streaming_row_scale_direct_rows_and_bad_rows(T, off):
+def test_grouped_swiglu_streaming_row_scale_direct_rows_and_bad_rows(T, off, d):
     """The streaming kernels (d, f >= 512) with a per-row scale, identity rows
     (row_index NULL) and gathered rows with out-of-range entries; empty and
     1-row groups."""
-    say(f"streaming swiglu T={T} groups={off}")
-    d, f, E = 512, 512, 5
+    say(f"streaming swiglu T={T} groups={off} d=f={d}")
+    f, E = d, 5
     x = _tokens(T, d, torch.bfloat16, 81)
     wg, wu, wd = _weights(E, d, f, torch.bfloat16, 82)
     w_host = (host_array(wg), host_array(wu), host_array(wd))
