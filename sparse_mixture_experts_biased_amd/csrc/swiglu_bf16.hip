@@ -28,12 +28,15 @@
 // writes are bank-conflict free).  This shape measured fastest for both the
 // weight-streaming (few rows per expert) and the matrix-core-bound shapes.
 //
-// Three kernels share the tile: a one-tile-per-workgroup kernel (any shape),
-// and two persistent streaming kernels for K and N that fit whole slices and
-// column tiles: an LDS-fed one (operands loaded straight into LDS) for groups
-// of at least 256 rows on average, where the matrix cores bound the products,
-// and a register-staged one for smaller groups, where streaming the weights
-// from HBM bounds them and more bytes in flight per CU pay.
+// Four kernels share the tile: a one-tile-per-workgroup kernel (any shape),
+// and three persistent streaming kernels for K and N that fit whole slices
+// and column tiles: an LDS-fed one (operands loaded straight into LDS) for
+// groups of at least 256 rows on average, where the matrix cores bound the
+// products; for smaller groups, where streaming the weights from HBM bounds
+// them, one that sends the weights straight into a three-stage LDS ring and
+// keeps the x rows on the register path (inference forms), and the
+// register-staged one (both operands through registers; the training form
+// and the down product with a row scale).
 //
 // Work order: by group, then blocks of up to four row tiles by all column
 // tiles, row tile fastest (item_tile); block ids are remapped so each XCD
@@ -1248,6 +1251,419 @@ void bf16_regs_stream_kernel(
 #undef MOE_STORE_SLICE
 }
 
+// ---------------------------------------------------------------- streaming, weights by LDS DMA
+//
+// The register-staged kernel with its weight side moved out of registers:
+// each weight slice (256 rows x 64 k, 32 KB) goes from memory straight into
+// one of three LDS stages by buffer loads with an LDS destination, two slices
+// ahead of the multiply, while the x rows keep the register path (coalesced
+// 16-byte loads, one register set, two LDS stages).  A step stores the x rows
+// of the next slice (loaded one step earlier) to LDS, loads the rows of the
+// slice after it, sends that slice's weights, multiplies, then waits for the
+// weights of the next slice and meets the barrier.  Loads complete in order
+// and each step issues its row loads before its weight loads, so neither
+// wait covers the newest weight slice: every weight slice has about two steps
+// to arrive (the register-staged kernel gives it one).  The slice count is
+// padded to a multiple of the three weight stages with slices that read
+// zeros (out-of-range offsets move no data), so every item starts on the
+// first stage and the stage of each step is known when compiling; the row
+// stages alternate at run time.  The MFMAs take the weight fragment first,
+// so the epilogue packs four consecutive output columns per 8-byte LDS write.
+// Every LDS access keeps its alias scope: an LDS access the compiler cannot
+// tell apart from the weight stages would wait for every weight slice in
+// flight.  Used for groups of fewer rows than a tile on average (weight
+// streaming) when K has at least kMinStreamSlices slices.
+constexpr int kWdmaStages = 3;
+
+template <bool GATEUP, bool AU = false>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bf16_wdma_kernel(
+    int Kdim, int N, int x_rows, int rows, int max_tiles, int NT,
+    const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
+    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, uint16_t* __restrict__ out,
+    uint16_t* __restrict__ au) {
+  using G = StreamGeom<64>;
+  using TL = Tile<256, 256, 512>;
+  constexpr int BM = 256, BNW = 256, NTHR = 512;
+  constexpr int kALoads = TL::kALoads;
+  constexpr int kNB = TL::kNB;
+  constexpr int kRP = TL::kRowsPerPass;
+  constexpr int kWavesN = TL::kWavesN;
+  constexpr int kCols = GATEUP ? BNW / 2 : BNW;
+  constexpr int kNI = G::kNI, kRPI = G::kRPI;  // weight loads per wave and slice, rows per load
+  constexpr uint32_t kOff = 0x80000000u;       // beyond every buffer (sizes < 2 GiB)
+  constexpr int kTile = G::kTileBytes;         // one 256-row operand tile of a slice
+  static_assert(kWdmaStages == 3, "the step loop is unrolled over three weight stages");
+  __shared__ __attribute__((aligned(16))) char a_st[2 * kTile];  // x-row stages (LDS writes)
+  __shared__ __attribute__((aligned(16))) char b0[kTile];        // weight stages (LDS DMA)
+  __shared__ __attribute__((aligned(16))) char b1[kTile];
+  __shared__ __attribute__((aligned(16))) char b2[kTile];
+
+  // ---- this workgroup's items: first, first + nslot, ... below end
+  const int total = meta[0] * NT;
+  const int nslot = gridDim.x / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int first = xcd * per_xcd + static_cast<int>(blockIdx.x) / kNumXcd;
+  const int end = min(total, (xcd + 1) * per_xcd);
+  if (first >= end) return;
+  const int n_items = (end - first + nslot - 1) / nslot;
+  const int nk = Kdim / kBK;
+  const int nkp = (nk + kWdmaStages - 1) / kWdmaStages * kWdmaStages;  // with zero slices
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar
+  const int lane = tid % kWave;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int lc = tid & 7;
+  const int lr = tid >> 3;  // 0 .. kRP-1
+  const uint32_t rowbytes = static_cast<uint32_t>(Kdim) * 2u;
+  const uint32_t wbytes = static_cast<uint32_t>(N) * rowbytes;
+  const uint32_t kb_end = static_cast<uint32_t>(nk) * kBK * 2u;    // past the last real slice
+  const uint32_t kbp_end = static_cast<uint32_t>(nkp) * kBK * 2u;  // past the last padded one
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(A, static_cast<uint32_t>(x_rows) * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsT =
+      buffer_rsrc(tiles, static_cast<uint32_t>(max_tiles) * sizeof(TileInfo));
+  const bool gather = GATEUP && row_index != nullptr;
+  const __amdgpu_buffer_rsrc_t rsR =
+      buffer_rsrc(row_index, gather ? static_cast<uint32_t>(rows) * 4u : 0u);
+
+  // x-row offset of load slot i (tile row lr + kRP * i, source row sr)
+  auto a_offset = [&](int i, int nrows, int sr) -> uint32_t {
+    return (lr < nrows - kRP * i && sr >= 0 && sr < x_rows)
+               ? static_cast<uint32_t>(sr) * rowbytes + static_cast<uint32_t>(lc) * 16u
+               : kOff;
+  };
+
+  // ---- load-side item
+  int l_item = 0, l_g, l_ntile, l_m0, l_nrows;
+  {
+    const TileInfo t0 = tiles[first / NT];
+    int mt;
+    item_tile(first - t0.gstart * NT, max(t0.ntiles, 1), NT, mt, l_ntile);
+    const TileInfo ti = tiles[t0.gstart + mt];
+    l_g = t0.group;
+    l_m0 = ti.m0;
+    l_nrows = min(ti.m1 - ti.m0, BM);
+  }
+  uint32_t a_off[kALoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) {
+    const int r = lr + kRP * i;
+    int sr = l_m0 + r;
+    if (gather) sr = (r < l_nrows) ? row_index[l_m0 + r] : -1;
+    a_off[i] = a_offset(i, l_nrows, sr);
+  }
+  // Weight-slice load i of a wave sends tile rows kRPI (wave + 8 i) + drow;
+  // lane l lands at LDS chunk l % 8 of its row, so it loads the k chunk that
+  // the swizzle stores there.
+  const int drow = lane / G::kChunks;
+  const int dchunk = (lane % G::kChunks) ^ drow ^ (wave & 1);
+  const uint32_t b_off = static_cast<uint32_t>(kRPI * wave + drow) * rowbytes +
+                         static_cast<uint32_t>(dchunk) * 16u;
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  uint32_t bcol;
+  auto set_weights = [&]() {
+    rb0 = buffer_rsrc(W0 + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    rb1 = buffer_rsrc((GATEUP ? W1 : W0) + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
+  };
+  set_weights();
+  uint32_t kb = 0;  // byte offset of the load side's next k-slice
+
+  // Loads the x rows of the load side's slice into sa, then sends its weight
+  // slice into stage ST; zero slices (past K) read nothing.
+  uint4 sa[kALoads];
+#define MOE_WLOAD(ST)                                                                        \
+  do {                                                                                      \
+    const uint32_t zmask_ = kb < kb_end ? 0u : kOff;                                        \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) sa[i] = __builtin_bit_cast(           \
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i] | zmask_, kb, 0));        \
+    __builtin_amdgcn_sched_barrier(0); /* rows before weights: see the step's waits */      \
+    _Pragma("unroll") for (int i = 0; i < kNI; ++i) {                                       \
+      const int add_ = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;                  \
+      dma<16>((GATEUP && i >= kNI / 2) ? rb1 : rb0, (ST) + kRPI * (wave + 8 * i) * G::kRow,   \
+              b_off | zmask_, bcol + static_cast<uint32_t>(add_) * rowbytes + kb);          \
+    }                                                                                       \
+    kb += kBK * 2;                                                                          \
+  } while (0)
+#define MOE_WSTORE(AST)                                                                      \
+  do {                                                                                      \
+    char* as_ = a_st + (AST) * kTile;                                                       \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i)                                     \
+        *reinterpret_cast<uint4*>(as_ + swz(lr + kRP * i, lc)) = sa[i];                     \
+  } while (0)
+
+  // ---- next item, fetched ahead (as in the register-staged kernel): p holds,
+  // in lane l, dword (l & 7) of the tile record of the next item's group
+  // start (l & 8 == 0) or of its row tile (l & 8 != 0); ri holds, in lane
+  // j + 8 i, the source row of tile row 8 * wave + j + kRP * i.  Refetched on
+  // every third step, after that step's loads, and read three steps later.
+  static_assert(kALoads * 8 <= kWave, "one lane per gathered row of the wave");
+  int p = 0, ri = -1;
+  int n_g = 0, n_ntile = 0, n_m0 = 0, n_nrows = 0;
+  int nw = first + min(1, n_items - 1) * nslot;  // next item
+  int t0rec = nw / NT;                           // a tile of its group
+  int rec = 0;                                   // its row tile
+  int fa = 0;                                    // fetches since nw changed
+
+#define MOE_WADVANCE()                                                                       \
+  do {                                                                                      \
+    if (fa == 1) { /* the group record just arrived: locate the row tile */                 \
+      const int gstart_ = __builtin_amdgcn_readlane(p, 3);                                  \
+      const int gnt_ = max(__builtin_amdgcn_readlane(p, 4), 1);                             \
+      int mt_;                                                                              \
+      item_tile(nw - gstart_ * NT, gnt_, NT, mt_, n_ntile);                                 \
+      n_g = __builtin_amdgcn_readlane(p, 0);                                                \
+      rec = gstart_ + mt_;                                                                  \
+    }                                                                                       \
+    n_m0 = __builtin_amdgcn_readlane(p, 9);                                                 \
+    n_nrows = min(__builtin_amdgcn_readlane(p, 10) - n_m0, BM);                             \
+    if (kb == kbp_end) {                                                                    \
+      if (l_item + 1 < n_items) {                                                           \
+        ++l_item;                                                                           \
+        kb = 0;                                                                             \
+        l_g = n_g; l_ntile = n_ntile; l_m0 = n_m0; l_nrows = n_nrows;                       \
+        set_weights();                                                                      \
+        _Pragma("unroll") for (int i = 0; i < kALoads; ++i) {                               \
+          const int sr_ = gather ? __builtin_amdgcn_ds_bpermute(((lane >> 3) + 8 * i) * 4, ri) \
+                                 : l_m0 + kRP * i + lr;                                     \
+          a_off[i] = a_offset(i, l_nrows, sr_);                                             \
+        }                                                                                   \
+        nw = first + min(l_item + 1, n_items - 1) * nslot;                                  \
+        t0rec = nw / NT;                                                                    \
+        fa = 0;                                                                             \
+      } else {                                                                              \
+        kb = kbp_end - kBK * 2; /* past the last item: its last slice again */              \
+      }                                                                                     \
+    }                                                                                       \
+  } while (0)
+#define MOE_WFETCH()                                                                         \
+  do {                                                                                      \
+    int z_ = 0;                                                                             \
+    asm volatile("" : "+v"(z_));                                                            \
+    const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z_));     \
+    if (GATEUP) { /* without row_index every load is out of range: no branch */             \
+      const int r_ = wave * 8 + (ln_ & 7) + kRP * ((ln_ >> 3) & (kALoads - 1));             \
+      ri = __builtin_amdgcn_raw_buffer_load_b32(                                            \
+          rsR, r_ < n_nrows ? static_cast<uint32_t>(n_m0 + r_) * 4u : kOff, 0, 0);          \
+    }                                                                                       \
+    p = __builtin_amdgcn_raw_buffer_load_b32(                                               \
+        rsT, static_cast<uint32_t>((ln_ & 8) ? rec : t0rec) * 32u + (ln_ & 7) * 4u, 0, 0);  \
+    fa = min(fa + 1, 3);                                                                    \
+  } while (0)
+
+  // ---- compute side (trails the load side by two slices)
+  int c_m0 = l_m0, c_nrows = l_nrows, c_n0 = l_ntile * kCols;
+  int gk = 0;  // steps so far: the x-row stage of step gk is gk & 1
+
+  int brow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (GATEUP) {
+      const int half = kNB / 2;
+      const int base = wn * (BNW / 2 / kWavesN);
+      brow[nb] = (nb < half) ? base + nb * 32 : BNW / 2 + base + (nb - half) * 32;
+    } else {
+      brow[nb] = wn * (BNW / kWavesN) + nb * 32;
+    }
+  }
+
+  f32x16_t acc[2][kNB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
+
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  constexpr int kSteps = kBK / 16;
+
+  // Wave (wm, wn) multiplies its two 32-row blocks (rows past the item hold
+  // zeros or stale rows, never written out) by its kNB weight blocks; a wave
+  // with no row of the item skips.  MFMAs weight block by weight block, both
+  // row blocks each, the weight fragment first; the fragments of 16-k step
+  // kk + 1 are read between the MFMAs of step kk.
+  auto compute = [&](const char* as, const char* bs) {
+    if (wm * 64 >= c_nrows) return;
+    bf16x8_t bq[kSteps][kNB], aq[kSteps][2];
+#pragma unroll
+    for (int kk = 0; kk < kSteps; ++kk) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        bq[kk][nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(brow[nb] + fr, kk * 2 + fh));
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        aq[kk][mb] = *reinterpret_cast<const bf16x8_t*>(as + swz(wm * 64 + mb * 32 + fr, kk * 2 + fh));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kSteps; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk][nb], aq[kk][mb],
+                                                                acc[mb][nb], 0, 0, 0);
+    // the first step's reads, then per step: (2 MFMAs, 1 read) x kNB for the
+    // next step's weight fragments, its two row fragments after them
+    __builtin_amdgcn_sched_group_barrier(0x100, kNB + 2, 0);
+#pragma unroll
+    for (int st = 0; st + 1 < kSteps; ++st) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 2; i < kNB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kNB, 0);
+  };
+
+  // Output tile of the compute-side item, staged through the x-row stage it
+  // was last multiplied from (free until the next item's second store) in
+  // rounds of kRoundRows rows.  Block (mb, nb) of a lane holds tile row
+  // wm*64 + mb*32 + (lane & 31) at the four consecutive weight columns
+  // 8*(q/4) + 4*(lane/32) + 0..3 of registers q: one 8-byte LDS write each,
+  // at 16-byte chunk (col / 8) XOR (row & 15) of a bf16 row of kCols, read
+  // back as whole 16-byte chunks.
+  constexpr int kOutRowBytes = kCols * 2;
+  constexpr int kRoundRows = kTile / kOutRowBytes < BM ? kTile / kOutRowBytes : BM;
+  constexpr int kOutChunks = kCols / 8;
+  constexpr int kReadRows = NTHR / kOutChunks;
+  static_assert(kRoundRows % 64 == 0 && BM % kRoundRows == 0, "rounds hold whole waves' rows");
+  static_assert(NTHR % kOutChunks == 0 && kReadRows % 16 == 0, "read-out rows keep row & 15");
+  auto epilogue = [&](int obase) {  // obase: byte offset of the staging stage in a_st
+    int ez = 0;  // opaque zero: keeps the lane-id computation inside the loop
+    asm volatile("" : "+v"(ez));
+    const int e_lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, ez));
+    const int etid = wave * kWave + e_lane;
+    const int e_fr = e_lane & 31, e_fh = e_lane >> 5;
+    constexpr int npass = (GATEUP && AU) ? 3 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+#pragma unroll
+    for (int r0 = 0; r0 < BM; r0 += kRoundRows) {
+      if (r0 >= c_nrows) break;
+      if (wm * 64 >= r0 && wm * 64 < r0 + kRoundRows) {  // a wave's 64 rows lie in one round
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          // rows past the item are staged too (never written out)
+          const int R = wm * 64 + mb * 32 + e_fr - r0;
+          int roff = obase + R * kOutRowBytes;
+          asm("" : "+v"(roff));  // one opaque offset: keeps each store's pointer chain short
+#pragma unroll
+          for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = (GATEUP ? wn * (BNW / 2 / kWavesN) : wn * (BNW / kWavesN)) + nb * 32 +
+                              8 * g + 4 * e_fh;
+              float v[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float gv = acc[mb][nb][4 * g + j];
+                if (GATEUP) {
+                  const float uv = acc[mb][nb + kNB / 2][4 * g + j];
+                  v[j] = pass == 0 ? silu(gv) * uv : (pass == 1 ? gv : uv);
+                } else {
+                  v[j] = gv;
+                }
+              }
+              // one 64-bit store (two 32-bit ones get merged without their alias
+              // scope), a few pointer steps from a_st (a longer chain of them
+              // loses it too)
+              *reinterpret_cast<uint64_t*>(
+                  a_st + (roff + ((((col >> 3) ^ (R & 15)) << 4) + (col & 4) * 2))) =
+                  static_cast<uint64_t>(pack_bf16x2(v[0], v[1])) |
+                  (static_cast<uint64_t>(pack_bf16x2(v[2], v[3])) << 32);
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const int rl = etid / kOutChunks, cl = etid % kOutChunks;
+      int soff = obase + rl * kOutRowBytes + ((cl ^ (rl & 15)) << 4);
+      asm("" : "+v"(soff));
+      const size_t ldo = pass == 0 ? static_cast<size_t>(N) : 2 * static_cast<size_t>(N);
+      uint16_t* dst = (pass == 0 ? out : au + (pass == 2 ? N : 0)) +
+                      static_cast<size_t>(c_m0 + r0 + rl) * ldo + c_n0 + cl * 8;
+#pragma unroll
+      for (int it = 0; it < kRoundRows / kReadRows; ++it) {
+        if (rl < c_nrows - r0 - it * kReadRows)
+          // vector copies: a uint4 assignment is a memcpy, whose LDS load
+          // carries no alias scope
+          *reinterpret_cast<bf16x8_t*>(dst + static_cast<size_t>(it) * kReadRows * ldo) =
+              *reinterpret_cast<const bf16x8_t*>(a_st + (soff + it * kReadRows * kOutRowBytes));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    }
+  };
+
+  // ---- stream.  Prologue: rows and weights of slice 0 in LDS, those of
+  // slice 1 in flight.  Step gk (compute slice k, weight stage k % 3): store
+  // the rows of slice k + 1, load the rows of slice k + 2 and send its
+  // weights, multiply slice k, wait for slice k + 1's weights, barrier.  The
+  // wait leaves in flight what was issued after those weights: this step's
+  // row and weight loads (kALoads + kNI) and the fetch loads of the steps
+  // between (position 1 of each three issues them).
+  constexpr int kNF = GATEUP ? 2 : 1;  // fetch loads
+  // (slice 1's loads go last, as in a step, so that the loop sees the same
+  // loads in flight from the prologue as from its own last step)
+  MOE_WLOAD(b0);
+  MOE_WSTORE(0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  MOE_WLOAD(b1);
+  // the compiler may sink slice 1's row loads below its weight loads (they
+  // read memory nothing here writes); using them here keeps them first
+  asm volatile("" ::"v"(sa[0].x), "v"(sa[1].x), "v"(sa[2].x), "v"(sa[3].x) : "memory");
+#define MOE_WSTEP(U, BCUR, BNEXT, WAITN)                                                     \
+  if ((U) == 1) MOE_WADVANCE();                                                             \
+  MOE_WSTORE((gk + 1) & 1);                                                                 \
+  __builtin_amdgcn_sched_barrier(0); /* the stores' waits must not cover the new loads */   \
+  MOE_WLOAD(BNEXT);                                                                         \
+  if ((U) == 1) MOE_WFETCH();                                                               \
+  compute(a_st + (gk & 1) * kTile, BCUR);                                                   \
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(WAITN)      \
+               : "memory");                                                                 \
+  ++gk;
+  for (int j = 0; j < n_items; ++j) {
+    for (int kt = 0; kt < nkp; kt += kWdmaStages) {
+      MOE_WSTEP(0, b0, b2, kALoads + kNI)
+      MOE_WSTEP(1, b1, b0, kALoads + kNI + kNF)
+      MOE_WSTEP(2, b2, b1, kALoads + kNI + kNF)
+    }
+    epilogue(((gk + 1) & 1) * kTile);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;
+    c_m0 = l_m0;
+    c_nrows = l_nrows;
+    c_n0 = l_ntile * kCols;
+  }
+#undef MOE_WSTEP
+#undef MOE_WADVANCE
+#undef MOE_WFETCH
+#undef MOE_WLOAD
+#undef MOE_WSTORE
+  // the trailing weight slices still write LDS: drain them before exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Shapes the weight-DMA streaming kernel takes (K of whole slices, at least
+// kMinStreamSlices of them; N of whole column tiles).
+bool wdma_shape(int K, int N, int cols) {
+  return K % kBK == 0 && K / kBK >= kMinStreamSlices && N % cols == 0;
+}
+
 // Workgroups of the streaming kernels: one per CU, a multiple of the XCD count.
 int stream_grid() {
   static int cached[64] = {0};
@@ -1279,6 +1695,10 @@ hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
     hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
                        s, K, N, rows, rows, nt, w.tiles, w.meta, nullptr, A, W, nullptr,
                        row_scale, C, nullptr);
+  } else if (BM == 256 && BNW == 256 && row_scale == nullptr && wdma_shape(K, N, 256)) {
+    hipLaunchKernelGGL((bf16_wdma_kernel<false>), dim3(stream_grid()), dim3(512), 0, s, K, N,
+                       rows, rows, max_tiles, nt, w.tiles, w.meta, nullptr, A, W, nullptr, C,
+                       nullptr);
   } else if (stream_shape(K, N, BNW)) {
     hipLaunchKernelGGL((bf16_regs_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, K, N, rows, rows, max_tiles, nt, w.tiles, w.meta,
@@ -1297,8 +1717,8 @@ hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
 // The gate/up product act = SiLU(x W_gate^T) * (x W_up^T) over the tile list
 // in w; with AU the gate and up values also go to au [rows, 2 d_ffn].
 // Groups of at least a full row tile on average make the products matrix-core
-// bound: LDS-fed kernel.  Fewer rows make them weight-streaming bound:
-// register-staged kernel, which keeps more weight bytes in flight per CU.
+// bound: LDS-fed kernel.  Fewer rows make them weight-streaming bound: the
+// weight-DMA kernel, or for the training form the register-staged one.
 template <int BM, int BNW, int NTHR, int NSETS, bool AU>
 hipError_t launch_gateup(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                          bool mfma_bound, const int32_t* row_index, const uint16_t* x,
@@ -1311,6 +1731,10 @@ hipError_t launch_gateup(int n_groups, int d_model, int d_ffn, int rows, int x_r
     hipLaunchKernelGGL((bf16_stream_kernel<true, kStreamBK, AU>), dim3(stream_grid()), dim3(512),
                        0, s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, wg,
                        wu, nullptr, act, au);
+  } else if (!AU && BM == 256 && BNW == 256 && wdma_shape(d_model, d_ffn, 128)) {
+    hipLaunchKernelGGL((bf16_wdma_kernel<true, false>), dim3(stream_grid()), dim3(512), 0, s,
+                       d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles, w.meta, row_index,
+                       x, wg, wu, act, nullptr);
   } else if (stream_shape(d_model, d_ffn, BNW / 2)) {
     hipLaunchKernelGGL((bf16_regs_stream_kernel<true, BM, BNW, NTHR, AU>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles,
