@@ -67,7 +67,7 @@ template <int EJ>
 __device__ __forceinline__ void select_token(int t, int E, int K, int fn, const float (&z)[EJ],
                                              const float (&bias)[EJ], int32_t* __restrict__ idx_out,
                                              float* __restrict__ gate_out,
-                                             int32_t* __restrict__ loads,
+                                             int32_t* __restrict__ loads, int lstride,
                                              float* __restrict__ prow,
                                              float* __restrict__ lsq) {
   const int lane = threadIdx.x % kWave;
@@ -175,7 +175,7 @@ __device__ __forceinline__ void select_token(int t, int E, int K, int fn, const 
   if (lane < K) {
     idx_out[static_cast<size_t>(t) * K + lane] = my_id;
     gate_out[static_cast<size_t>(t) * K + lane] = my_s / den;
-    if (my_id >= 0 && my_id < E) atomicAdd(&loads[my_id], 1);
+    if (my_id >= 0 && my_id < E) atomicAdd(&loads[my_id * lstride], 1);
   }
 }
 
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
       int ex = lane + kWave * j;
       z[j] = (ex < E) ? zs[r * E + ex] : 0.0f;
     }
-    select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, prow, lsq);
+    select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, 1, prow, lsq);
   }
 }
 
@@ -271,6 +271,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kZT = 128;   // tokens per workgroup tile
 constexpr int kZE = 128;   // experts per workgroup tile
+// The T*K load increments of the split path go to counters 256 bytes apart
+// (then compacted into loads): packed into one 1 KB block, the same-line
+// atomics queue on one or two L2 channels.
+constexpr int kLoadStride = 64;
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo_bits, uint32_t hi_bits) {
   return (lo_bits >> 16) | (hi_bits & 0xffff0000u);
@@ -399,7 +403,20 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int K, in
     z[j] = acc;
     bias[j] = (b != nullptr && ex < E) ? b[ex] : 0.0f;
   }
-  select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, prow, lsq);
+  select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, kLoadStride, prow, lsq);
+}
+
+// loads[e] = the strided counter of expert e.
+__global__ __launch_bounds__(256) void compact_loads_kernel(int E, const int32_t* __restrict__ lpad,
+                                                            int32_t* __restrict__ loads) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < E) loads[e] = lpad[static_cast<size_t>(e) * kLoadStride];
+}
+
+// Zeroes the strided counters.
+__global__ __launch_bounds__(256) void zero_strided_kernel(int n, int32_t* __restrict__ p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[static_cast<size_t>(i) * kLoadStride] = 0;
 }
 
 // ------------------------------------------------------------ diagnostics
@@ -484,9 +501,13 @@ int route_splits(int T, int d, int E, int h_bf16) {
   return S;
 }
 
+// Split-K logit partials [S][T][E], then one load counter per 256 bytes
+// (none without splits: the fp32 path counts into loads directly).
 size_t route_workspace_bytes(int T, int d, int E, int h_bf16) {
   const int S = route_splits(T, d, E, h_bf16);
-  return align_up(static_cast<size_t>(S) * T * E * sizeof(float), 256);
+  if (S == 0) return 0;
+  return align_up(static_cast<size_t>(S) * T * E * sizeof(float), 256) +
+         align_up(static_cast<size_t>(E) * kLoadStride * sizeof(int32_t), 256);
 }
 
 // Diagnostics scratch after the logits: p rows [T][E], logsumexp^2 [T],
@@ -525,8 +546,7 @@ hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h
                         const float* e, const float* b, int32_t* idx, float* gates,
                         int32_t* loads, void* ws, float* p_mean, float* zsq_mean,
                         hipStream_t s) {
-  hipError_t err = launch_fill_i32(loads, 0, static_cast<size_t>(E), s);
-  if (err != hipSuccess) return err;
+  hipError_t err;
   const int S = route_splits(T, d, E, h_bf16);
   float* prow = nullptr;
   float* lsq = nullptr;
@@ -540,12 +560,17 @@ hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h
   }
   if (S == 0) {
     if (h_bf16) return hipErrorInvalidValue;  // rejected on the host before this point
+    err = launch_fill_i32(loads, 0, static_cast<size_t>(E), s);
+    if (err != hipSuccess) return err;
     err = launch_route_f32(T, d, E, K, fn, static_cast<const float*>(h), e, b, idx, gates,
                            loads, prow, lsq, s);
     if (err != hipSuccess || p_mean == nullptr) return err;
     return launch_route_stats(T, E, prow, lsq, part, p_mean, zsq_mean, s);
   }
   float* zpart = static_cast<float*>(ws);
+  int32_t* lpad = reinterpret_cast<int32_t*>(
+      static_cast<char*>(ws) + align_up(static_cast<size_t>(S) * T * E * sizeof(float), 256));
+  hipLaunchKernelGGL(zero_strided_kernel, dim3((E + 255) / 256), dim3(256), 0, s, E, lpad);
   {
     ProfScope prof_(s, "route_logits");
     dim3 grid((T + kZT - 1) / kZT, (E + kZE - 1) / kZE, S);
@@ -560,14 +585,15 @@ hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h
     dim3 grid((T + 3) / 4), block(256);
     const float* zp = zpart;
     if (ej <= 1)
-      hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
+      hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, lpad, prow, lsq);
     else if (ej <= 2)
-      hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
+      hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, lpad, prow, lsq);
     else if (ej <= 4)
-      hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
+      hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, lpad, prow, lsq);
     else
-      hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, loads, prow, lsq);
+      hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, T, E, K, fn, S, zp, b, idx, gates, lpad, prow, lsq);
   }
+  hipLaunchKernelGGL(compact_loads_kernel, dim3((E + 255) / 256), dim3(256), 0, s, E, lpad, loads);
   err = hipGetLastError();
   if (err != hipSuccess || p_mean == nullptr) return err;
   return launch_route_stats(T, E, prow, lsq, part, p_mean, zsq_mean, s);
