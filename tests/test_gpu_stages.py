@@ -345,6 +345,7 @@ SWIGLU_CASES = [
     # the register-staged streaming kernel over many slices and items
     (2000, 1024, 2048, 96, 4, torch.bfloat16),  # ~83-row groups, several items per workgroup
     (40, 1024, 1024, 64, 2, torch.bfloat16),    # decode-like: 0-4 rows per group
+    (600, 768, 1536, 16, 2, torch.bfloat16),    # 12 and 24 slices: no zero slices padded in
 ]
 
 
