@@ -270,6 +270,9 @@ def main(argv=None):
     ap.add_argument("--backward", action="store_true",
                     help="time a training step: the forward pass plus the backward pass of the "
                          "layer (gradients of tokens, centroids and every expert weight)")
+    ap.add_argument("--serial-shared", action="store_true",
+                    help="run the shared experts after the routed ones on one stream "
+                         "(default: on a second stream beside the routing)")
     ap.add_argument("--diagnostics", action="store_true",
                     help="route with the router statistics and compute the balance diagnostics "
                          "(Switch f.P, z-loss, load entropy, MaxVio, dropped rate) every step")
@@ -317,6 +320,7 @@ def main(argv=None):
                        cfg.score)
     run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
                    lay.ws_down, capacity_factor=args.capacity_factor,
+                   overlap_shared=not args.serial_shared,
                    diagnostics=args.diagnostics)
     b = lay.b.clone() if lay.b is not None else None
     b_host0 = host_array(lay.b) if lay.b is not None else None

@@ -34,11 +34,14 @@ class LayerShape:
 class MoELayer:
     def __init__(self, shape: LayerShape, e, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
                  ws_down=None, device="cuda", capacity_factor: Optional[float] = None,
-                 diagnostics: bool = False):
+                 diagnostics: bool = False, overlap_shared: bool = True):
         """capacity_factor: None dispatches every copy; a factor CF caps each
         expert at C = ceil(CF*T*K/E_r) rows, admitted in token order.
         diagnostics: route with moe_route_stats and fill the router's balance
-        diagnostics (moe_router_diag) after the dispatch of every forward."""
+        diagnostics (moe_router_diag) after the dispatch of every forward.
+        overlap_shared: run the shared experts (which need no routing) on a
+        second stream, side by side with the routing and the routed experts,
+        joined before the combine; False runs them in sequence."""
         s = self.shape = shape
         self.capacity = (None if capacity_factor is None else
                          L.moe_expert_capacity(s.T, s.K, s.E_r, capacity_factor))
@@ -75,9 +78,18 @@ class MoELayer:
         self.perm_ws = torch.empty((self.perm_ws_bytes,), dtype=torch.uint8, device=device)
         self.y_perm = torch.empty((TK, d), dtype=self.tdt, device=device)
         ws_bytes = L.moe_grouped_swiglu_workspace_size(E, d, s.d_ffn, TK, self.dt)
+        self.side = None
         if s.E_s:
-            ws_bytes = max(ws_bytes, L.moe_grouped_swiglu_workspace_size(
-                s.E_s, d, s.d_ffn, s.E_s * T, self.dt))
+            sh_bytes = L.moe_grouped_swiglu_workspace_size(s.E_s, d, s.d_ffn, s.E_s * T, self.dt)
+            ws_bytes = max(ws_bytes, sh_bytes)
+            if overlap_shared:
+                # the shared experts get their own workspace, stream and events
+                # (default priority, like every stream here)
+                self.sh_ws_bytes = sh_bytes
+                self.sh_ws = torch.empty((sh_bytes,), dtype=torch.uint8, device=device)
+                self.side = torch.cuda.Stream(device=device)
+                self.ev_in = torch.cuda.Event()
+                self.ev_sh = torch.cuda.Event()
             self.sh_offsets = (torch.arange(s.E_s + 1, **i32) * T).contiguous()
             self.sh_rows = torch.arange(T, **i32).repeat(s.E_s).contiguous()
             self.y_shared = torch.empty((s.E_s * T, d), dtype=self.tdt, device=device)
@@ -85,6 +97,8 @@ class MoELayer:
             self.sh_offsets = self.sh_rows = self.y_shared = None
         self.sw_ws_bytes = ws_bytes
         self.sw_ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=device)
+        if self.side is None:
+            self.sh_ws, self.sh_ws_bytes = self.sw_ws, self.sw_ws_bytes
         self.y = torch.empty((T, d), dtype=self.tdt, device=device)
         self.stats = torch.zeros((4,), dtype=torch.int32, device=device)
         # [a | u] of the routed and shared experts, kept by a training forward
@@ -147,13 +161,13 @@ class MoELayer:
         if self.au_shared is None:
             L.moe_grouped_swiglu(s.E_s, s.d_model, s.d_ffn, s.E_s * s.T, s.T, self.sh_offsets,
                                  self.sh_rows, h, self.dt, self.ws_gate, self.ws_up,
-                                 self.ws_down, None, self.y_shared, self.sw_ws, self.sw_ws_bytes,
+                                 self.ws_down, None, self.y_shared, self.sh_ws, self.sh_ws_bytes,
                                  stream)
         else:
             L.moe_grouped_swiglu_train(s.E_s, s.d_model, s.d_ffn, s.E_s * s.T, s.T,
                                        self.sh_offsets, self.sh_rows, h, self.dt, self.ws_gate,
                                        self.ws_up, self.ws_down, None, self.y_shared,
-                                       self.au_shared, self.sw_ws, self.sw_ws_bytes, stream)
+                                       self.au_shared, self.sh_ws, self.sh_ws_bytes, stream)
         if self.profile_tags:
             L.moe_profile_tag("")
 
@@ -171,12 +185,24 @@ class MoELayer:
                 stream=None):
         """One layer forward; when gamma is given, b is updated in place after
         the loads are counted (the update affects the next call)."""
+        # the shared experts on the side stream once h is ready on this one
+        # (a raw stream handle cannot carry events: then in sequence)
+        overlap = self.side is not None and not isinstance(stream, int)
+        if overlap:
+            main = stream if stream is not None else torch.cuda.current_stream()
+            self.ev_in.record(main)
+            self.side.wait_event(self.ev_in)
+            self.shared_experts(h, self.side)
+            self.ev_sh.record(self.side)
         self.route(h, b, stream)
         self.permute(stream=stream)
         if self.diagnostics:
             self.router_diag(stream)
         self.routed_experts(h, stream)
-        self.shared_experts(h, stream)
+        if overlap:
+            main.wait_event(self.ev_sh)
+        else:
+            self.shared_experts(h, stream)
         self.combine(h, stream)
         if gamma is not None and b is not None:
             self.bias_update(b, gamma, stream)
