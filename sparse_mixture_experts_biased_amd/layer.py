@@ -258,6 +258,10 @@ class MoELayer:
             self.dx_shared = None
         self.bw_ws_bytes = bw
         self.bw_ws = torch.empty((bw,), dtype=torch.uint8, device=dev)
+        self.sh_bw_ws, self.sh_bw_ws_bytes = self.bw_ws, self.bw_ws_bytes
+        if s.E_s and self.side is not None:  # the shared experts' backward on the side stream
+            self.sh_bw_ws_bytes = L.moe_grouped_swiglu_backward_workspace_size(s.E_s, d, f, T)
+            self.sh_bw_ws = torch.empty((self.sh_bw_ws_bytes,), dtype=torch.uint8, device=dev)
         if keep_au:
             self.au_perm = torch.empty((T * K, 2 * f), **bf)
             self.au_shared = torch.empty((T, 2 * f), **bf) if s.E_s else None
@@ -275,6 +279,22 @@ class MoELayer:
         that forward."""
         s = self.shape
         T, K, E, d, f = s.T, s.K, s.E_r, s.d_model, s.d_ffn
+
+        def shared_backward(st):  # needs only dy, h and the forward's a | u
+            L.moe_grouped_swiglu_backward(s.E_s, d, f, T, T, self.sh_offsets, self.sh_rows, h,
+                                          self.dt, self.ws_gate, self.ws_up, self.ws_gu_t,
+                                          self.ws_down_t, dy, self.au_shared, self.dx_shared,
+                                          self.dws_gate, self.dws_up, self.dws_down,
+                                          self.sh_bw_ws, self.sh_bw_ws_bytes, st)
+
+        # the shared experts' backward on the side stream, beside the routed one
+        overlap = bool(s.E_s) and self.side is not None and not isinstance(stream, int)
+        if overlap:
+            main = stream if stream is not None else torch.cuda.current_stream()
+            self.ev_in.record(main)
+            self.side.wait_event(self.ev_in)
+            shared_backward(self.side)
+            self.ev_sh.record(self.side)
         L.moe_combine_backward(T, d, K, dy, self.y_perm, self.slot_row, self.gates, self.dt,
                                self.dy_perm, self.dgates, stream)
         L.moe_grouped_swiglu_backward(E, d, f, T * K, T, self.offsets, self.row_token, h, self.dt,
@@ -282,13 +302,10 @@ class MoELayer:
                                       self.dy_perm, self.au_perm, self.dx_perm, self.dw_gate,
                                       self.dw_up, self.dw_down, self.bw_ws, self.bw_ws_bytes,
                                       stream)
-        if s.E_s:
-            L.moe_grouped_swiglu_backward(s.E_s, d, f, T, T, self.sh_offsets, self.sh_rows, h,
-                                          self.dt, self.ws_gate, self.ws_up, self.ws_gu_t,
-                                          self.ws_down_t, dy, self.au_shared, self.dx_shared,
-                                          self.dws_gate,
-                                          self.dws_up, self.dws_down, self.bw_ws,
-                                          self.bw_ws_bytes, stream)
+        if overlap:
+            main.wait_event(self.ev_sh)
+        elif s.E_s:
+            shared_backward(stream)
         # dh = dy + dx_shared + sum_k dx_perm[slot] (the combine with unit gates)
         L.moe_combine(T, d, K, s.E_s, dy, self.dx_shared, self.dx_perm, self.slot_row,
                       self.ones, self.dt, self.dh, stream)
