@@ -336,10 +336,18 @@ def main(argv=None):
     # a 16-byte device copy after each step's bias update
     stats_hist = None
 
+    # backward wall time per timed step: events on the caller's stream around
+    # run.backward (which returns after joining the side stream's work)
+    bw_evs = None
+
     def step(i):
         run.forward(hs[i % len(hs)], b, gamma, stream)
         if dy is not None:
+            if bw_evs is not None:
+                bw_evs[i][0].record(stream)
             run.backward(hs[i % len(hs)], dy, stream)
+            if bw_evs is not None:
+                bw_evs[i][1].record(stream)
         if stats_hist is not None:
             stats_hist[i].copy_(run.stats, non_blocking=True)
 
@@ -353,6 +361,9 @@ def main(argv=None):
         b.copy_(lay.b)   # the timed steps are steps 0, 1, ... of the run, from b0
     # one event per step boundary (recording does not synchronise): per-step times
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    if dy is not None:
+        bw_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     evs[0].record(stream)
@@ -437,7 +448,7 @@ def main(argv=None):
         # a|u kept by the forward, da|du (4 f words) are overhead
         d, f = cfg.d_model, cfg.d_ffn
         bw_bytes = (n_touched + cfg.E_s) * 6 * d * f * 2
-        bw_ms = sum(v[1] for k, v in prof.items() if "backward" in k) / args.steps
+        bw_ms = sum(e0.elapsed_time(e1) for e0, e1 in bw_evs) / args.steps
         out["mode"] = "forward+backward"
         out["backward"] = dict(ms_per_step=round(bw_ms, 4), algorithmic_bytes=bw_bytes,
                                hbm_gbs=round(bw_bytes / (bw_ms / 1000.0) / 1e9, 1),
