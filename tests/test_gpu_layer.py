@@ -58,3 +58,32 @@ def test_mixtral_layer_ragged_tokens():
     lay = make_layer(cfg, device="cuda")
     run = runner_for(lay)
     check_layer(lay, lay.h, None, None, run, n_tok_sample=8, n_exp_sample=2, seed=2)
+
+
+def test_shared_expert_overlap_matches_sequential():
+    """The shared experts on the side stream give the same bits as run in
+    sequence, forward and backward, and again on a second call."""
+    from dataclasses import replace
+    from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
+    cfg = replace(CONFIGS["dsv3_prefill"], T=300, d_model=1024, E_r=32, K=4, d_ffn=512)
+    say(f"overlap vs sequential: T={cfg.T} d={cfg.d_model} E={cfg.E_r} K={cfg.K} E_s={cfg.E_s}")
+    lay = make_layer(cfg, device="cuda")
+    shape = LayerShape(cfg.T, cfg.d_model, cfg.E_r, cfg.K, cfg.E_s, cfg.d_ffn, cfg.dtype,
+                       cfg.score)
+    dy = torch.randn(cfg.T, cfg.d_model, generator=torch.Generator("cuda").manual_seed(5),
+                     device="cuda").to(torch.bfloat16)
+    outs = {}
+    for name, overlap in (("overlap", True), ("sequential", False)):
+        run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
+                       lay.ws_down, overlap_shared=overlap)
+        run.prepare_backward()
+        ys = []
+        for _ in range(2):
+            ys.append(run.forward(lay.h, lay.b).clone())
+            run.backward(lay.h, dy)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[0], ys[1]), name
+        outs[name] = (ys[0], run.dh.clone(), run.dws_gate.clone(), run.dws_down.clone(),
+                      run.de.clone())
+    for a, b in zip(outs["overlap"], outs["sequential"]):
+        assert torch.equal(a, b)
