@@ -85,15 +85,42 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(cfg, lay, b_host, budget_s=12.0, chunk=8, sample_shared=1024, capacity=None):
+def spread_order(n: int):
+    """0..n-1 in bit-reversed order: every prefix is spread over the range."""
+    bits = max(1, (n - 1).bit_length())
+    out = []
+    for i in range(1 << bits):
+        r = int(f"{i:0{bits}b}"[::-1], 2)
+        if r < n:
+            out.append(r)
+    return out
+
+
+def fit_expert_cost(rows, secs):
+    """Least-squares fit secs ~ a + b * rows with a, b >= 0 (one sample: b only)."""
+    import numpy as np
+    from scipy.optimize import nnls
+    rows = np.asarray(rows, dtype=np.float64)
+    secs = np.asarray(secs, dtype=np.float64)
+    if len(rows) < 2 or np.all(rows == rows[0]):
+        return 0.0, float(secs.sum() / rows.sum())
+    coef, _ = nnls(np.stack([np.ones_like(rows), rows], axis=1), secs)
+    return float(coef[0]), float(coef[1])
+
+
+def cpu_baseline(cfg, lay, b_host, budget_s=12.0, sample_shared=1024, capacity=None,
+                 idx_gpu=None):
     """Time the oracle on a bounded sample of the same workload on host cores.
 
-    Sample: routing of all T tokens; the routed experts in ascending order, in
-    chunks of `chunk`, on all their rows, until their oracle time reaches
-    budget_s or every expert is done; the shared expert on the first
-    sample_shared tokens; the full combine and bias update.  Expert time is
-    scaled by E_r / experts run and the shared-expert time by T / tokens run
-    to a whole-layer estimate (no scaling where the sample is the whole).
+    Sample: routing of all T tokens; routed experts one at a time, on all
+    their rows, in an order spread over the experts sorted by row count (so a
+    skewed load's few large experts and many small ones are both sampled early),
+    until their oracle time reaches budget_s or every expert is done; the shared
+    expert on the first sample_shared tokens; the full combine and bias update.
+    Unsampled experts are costed by a fit a + b * rows over the sampled ones
+    (weight conversion per expert, GEMM work per row); the shared-expert time
+    is scaled by T / tokens run.  With idx_gpu (the GPU's picks for the same
+    tokens and bias), also counts near-ties and tokens whose picks differ.
     """
     import numpy as np
 
@@ -119,21 +146,38 @@ def cpu_baseline(cfg, lay, b_host, budget_s=12.0, chunk=8, sample_shared=1024, c
         off, rt, sr, _ = O.permute_capacity(r["idx"], cfg.E_r, capacity)
     t_route = time.perf_counter() - t0
 
-    # Expert weights come to the host one chunk at a time (outside the timed
-    # calls), so host memory stays at one chunk's weights.
+    routing = None
+    if idx_gpu is not None:
+        near = O.topk_margin(r["s"], b_host, cfg.K) < 1e-5
+        same = np.all(idx_gpu == r["idx"], axis=1)
+        routing = dict(tokens=int(cfg.T), near_ties=int(near.sum()),
+                       flipped=int((~same).sum()), flipped_not_near=int((~same & ~near).sum()))
+
+    rows_e = np.diff(off.astype(np.int64))
+    nz = np.nonzero(rows_e > 0)[0]
+    by_rows = nz[np.argsort(rows_e[nz], kind="stable")]
+    order = [int(by_rows[j]) for j in spread_order(len(by_rows))]
+    # Expert weights come to the host one at a time (outside the timed calls),
+    # so host memory stays at one expert's weights.
     y_perm = None
-    t_exp, n_exp = 0.0, 0
-    while n_exp < cfg.E_r and (n_exp == 0 or t_exp < budget_s):
-        grp = range(n_exp, min(cfg.E_r, n_exp + chunk))
-        w = {i: (host_array(lay.w_gate[i]), host_array(lay.w_up[i]), host_array(lay.w_down[i]))
-             for i in grp}
+    done, secs = [], []
+    for i in order:
+        if done and sum(secs) >= budget_s:
+            break
+        w = (host_array(lay.w_gate[i]), host_array(lay.w_up[i]), host_array(lay.w_down[i]))
         t0 = time.perf_counter()
-        part = O.grouped_swiglu(h, off, rt, lambda i: w[i], groups=grp)
-        t_exp += time.perf_counter() - t0
+        part = O.grouped_swiglu(h, off, rt, lambda _: w, groups=[i])
+        secs.append(time.perf_counter() - t0)
+        done.append(i)
         y_perm = part if y_perm is None else y_perm + part   # disjoint rows; the rest stay 0
-        n_exp = grp.stop
         del w
-    rows = int(off[n_exp])
+    t_exp = sum(secs)
+    a, bcoef = fit_expert_cost(rows_e[done], secs)
+    if len(done) == len(nz):
+        est_exp = t_exp
+    else:
+        est_exp = t_exp + sum(a + bcoef * rows_e[i] for i in set(nz.tolist()) - set(done))
+    rows = int(rows_e[done].sum())
 
     t_sh, n_sh = 0.0, min(cfg.T, sample_shared)
     if ws is not None:
@@ -147,22 +191,24 @@ def cpu_baseline(cfg, lay, b_host, budget_s=12.0, chunk=8, sample_shared=1024, c
                   cfg.T, cfg.K, 0.001)
     t_comb = time.perf_counter() - t0
 
-    est = t_route + t_exp * cfg.E_r / n_exp + t_comb
+    est = t_route + est_exp + t_comb
     if ws is not None:
         est += t_sh * cfg.T / n_sh
     measured = t_route + t_exp + t_sh + t_comb
-    log(f"cpu oracle: route {t_route:.2f}s, {n_exp} experts ({rows} rows) {t_exp:.2f}s,"
-        f" shared on {n_sh} tokens {t_sh:.2f}s, combine {t_comb:.2f}s -> layer est "
-        f"{est:.1f}s")
-    return dict(
+    log(f"cpu oracle: route {t_route:.2f}s, {len(done)} of {len(nz)} experts ({rows} of "
+        f"{int(rows_e.sum())} rows) {t_exp:.2f}s, fit {a:.4f}s + {bcoef * 1e3:.4f}ms/row, "
+        f"shared on {n_sh} tokens {t_sh:.2f}s, combine {t_comb:.2f}s -> layer est {est:.1f}s")
+    out = dict(
         value=cfg.T / est, unit="tokens/s", cores=int(threads), kind="oracle",
-        sample=(f"oracle (NumPy fp64, BLAS {blas}) on: routing of all {cfg.T} tokens, routed "
-                f"experts 0-{n_exp - 1} of {cfg.E_r} on their {rows} rows, shared "
-                f"expert on {n_sh if ws is not None else 0} of {cfg.T} tokens, full combine + bias "
-                f"update; expert time x{cfg.E_r / n_exp:g}, shared time "
-                f"x{(cfg.T / n_sh) if ws is not None else 0:g} -> whole-layer estimate {est:.2f} s "
-                f"({measured:.2f} s measured)"),
+        sample=(f"oracle (NumPy fp64, BLAS {blas}) on: routing of all {cfg.T} tokens; "
+                f"{len(done)} of {len(nz)} touched routed experts on all their rows ({rows} of "
+                f"{int(rows_e.sum())} rows), taken spread over the experts sorted by rows; "
+                f"the others costed by the fit {a:.4f} s + {bcoef * 1e3:.4f} ms per row; "
+                f"shared expert on {n_sh if ws is not None else 0} of {cfg.T} tokens "
+                f"(time x{(cfg.T / n_sh) if ws is not None else 0:g}); full combine + bias "
+                f"update -> whole-layer estimate {est:.2f} s ({measured:.2f} s measured)"),
     )
+    return out, routing
 
 
 def copy_probe(nbytes: int) -> int:
@@ -414,9 +460,14 @@ def main(argv=None):
     # the roofline fraction the layer attains: the larger of its MFMA and HBM fractions
     layer["attainable_frac"] = max(layer["hbm_frac"], layer["mfma_frac"])
 
-    cpu = None
+    cpu = routing = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, lay, b_host0, capacity=run.capacity)
+        # the GPU's picks for the first batch from the initial bias (outside the
+        # timed steps), compared with the oracle's in the baseline leg
+        b0 = lay.b.clone() if lay.b is not None else None
+        run.route(lay.h, b0)
+        idx_gpu = run.topk_idx.cpu().numpy()
+        cpu, routing = cpu_baseline(cfg, lay, b_host0, capacity=run.capacity, idx_gpu=idx_gpu)
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -432,6 +483,7 @@ def main(argv=None):
                                 f"{cfg.T * cfg.K} copies dropped)"),
                    "tokens_per_step": cfg.T, "parallelism": "single GPU"},
         "roofline": roofline, "layer": layer, "stages_ms": stages, "cpu_baseline": cpu,
+        "routing_vs_oracle": routing,
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
                     "max": round(step_ms[-1], 4)},
     }

@@ -101,8 +101,30 @@ class MoELayer:
             self.sh_ws, self.sh_ws_bytes = self.sw_ws, self.sw_ws_bytes
         self.y = torch.empty((T, d), dtype=self.tdt, device=device)
         self.stats = torch.zeros((4,), dtype=torch.int32, device=device)
-        # [a | u] of the routed and shared experts, kept by a training forward
+        # [a | u] of the routed and shared experts, kept by a training forward;
+        # au_valid is set by such a forward and cleared by prepare_backward
         self.au_perm = self.au_shared = None
+        self.au_valid = False
+
+    def _check(self, name, t, shape, dtype):
+        """Raise ValueError unless t is a contiguous tensor of this shape and
+        dtype on this layer's device (the C ABI gets bare pointers)."""
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if t.device != self.y.device:
+            raise ValueError(f"{name}: on {t.device}, the layer is on {self.y.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+
+    def _check_inputs(self, h, b=None):
+        s = self.shape
+        self._check("h", h, (s.T, s.d_model), self.tdt)
+        if b is not None:
+            self._check("b", b, (s.E_r,), torch.float32)
 
     # individual stages -------------------------------------------------
     def route(self, h, b, stream=None):
@@ -185,6 +207,7 @@ class MoELayer:
                 stream=None):
         """One layer forward; when gamma is given, b is updated in place after
         the loads are counted (the update affects the next call)."""
+        self._check_inputs(h, b)
         # the shared experts on the side stream once h is ready on this one
         # (a raw stream handle cannot carry events: then in sequence)
         overlap = self.side is not None and not isinstance(stream, int)
@@ -206,6 +229,8 @@ class MoELayer:
         self.combine(h, stream)
         if gamma is not None and b is not None:
             self.bias_update(b, gamma, stream)
+        # a training forward has now written a | u for the backward
+        self.au_valid = self.au_perm is not None
         return self.y
 
     # backward -----------------------------------------------------------
@@ -267,6 +292,9 @@ class MoELayer:
             self.au_shared = torch.empty((T, 2 * f), **bf) if s.E_s else None
         else:
             self.au_perm = self.au_shared = None
+        # the new a | u buffers hold nothing until a forward fills them
+        self.au_valid = False
+        self.bw_ready = True
         if self.capacity is not None:   # the router's gradient covers every pick
             self.all_offsets = torch.empty((E + 1,), **i32)
             self.all_row_token = torch.empty((T * K,), **i32)
@@ -279,6 +307,13 @@ class MoELayer:
         that forward."""
         s = self.shape
         T, K, E, d, f = s.T, s.K, s.E_r, s.d_model, s.d_ffn
+        if not getattr(self, "bw_ready", False):
+            raise RuntimeError("backward() needs prepare_backward() and then a forward()")
+        if self.au_perm is not None and not self.au_valid:
+            raise RuntimeError("backward() reads the a | u of the last forward: call forward() "
+                               "after prepare_backward() and before backward()")
+        self._check_inputs(h)
+        self._check("dy", dy, (T, d), self.tdt)
 
         def shared_backward(st):  # needs only dy, h and the forward's a | u
             L.moe_grouped_swiglu_backward(s.E_s, d, f, T, T, self.sh_offsets, self.sh_rows, h,

@@ -261,6 +261,24 @@ def test_dsv3_prefill_backward_sampled():
         e_dg = rel_err(run.dgates[t].cpu().numpy().astype(np.float64), dg_ref)
         say(f"token {t}: dh {e_dh:.2e} dgates {e_dg:.2e}")
         assert e_dh <= TOL and e_dg <= TOL
+    # the shared expert's weight gradients reduce over all T rows: a block of
+    # hidden units is an exact sub-problem (each unit's gradients depend only on
+    # its own gate, up and down weights), so the oracle runs on those units alone
+    units = np.sort(rng.choice(cfg.d_ffn, 128, replace=False))
+    wsg, wsu, wsd = ws
+    _, rg, ru, rd = O.swiglu_backward(h, wsg[units], wsu[units], wsd[:, units], dyh)
+    for name, got, ref in (("dws_gate", run.dws_gate[0][units], rg),
+                           ("dws_up", run.dws_up[0][units], ru),
+                           ("dws_down", run.dws_down[0][:, units], rd)):
+        e_w = rel_err(to_host_f64(got.contiguous()), ref)
+        say(f"shared {name} on {len(units)} hidden units x {T} rows: {e_w:.2e}")
+        assert e_w <= TOL
+    # the shared expert's input gradient on a token sample (rows are independent)
+    toks = np.sort(rng.choice(T, 64, replace=False))
+    rdx, _, _, _ = O.swiglu_backward(h[toks], *ws, dyh[toks])
+    e_dx = rel_err(to_host_f64(run.dx_shared)[toks], rdx)
+    say(f"shared dx on {len(toks)} tokens: {e_dx:.2e}")
+    assert e_dx <= TOL
     # router gradients of every token from the GPU's gate gradients
     r_dz, _, r_de = O.router_backward(h, host_array(lay.e), idx, cfg.score,
                                       run.dgates.cpu().numpy())
@@ -268,3 +286,32 @@ def test_dsv3_prefill_backward_sampled():
     assert rel_err(run.de.cpu().numpy().astype(np.float64), r_de) <= 1e-3
     del run, lay
     torch.cuda.empty_cache()
+
+
+def test_backward_call_order_is_enforced():
+    """backward() reads the a | u a training forward stores: it must come after
+    prepare_backward() and a forward, else it raises before launching anything."""
+    T, d, f, E, K = 128, 256, 128, 8, 2
+    h, e, w, ws, b = _small_bf16_layer(T, d, f, E, K, 1, "sigmoid", 50)
+    shape = LayerShape(T, d, E, K, 1, f, "bf16", "sigmoid")
+    run = MoELayer(shape, e, *w, *ws)
+    dy = _bf16((T, d), 1.0, 51)
+    with pytest.raises(RuntimeError):
+        run.backward(h, dy)                       # no prepare_backward
+    run.forward(h, b)
+    run.prepare_backward()
+    with pytest.raises(RuntimeError):
+        run.backward(h, dy)                       # a | u not written since prepare
+    run.forward(h, b)
+    run.backward(h, dy)                           # the documented order
+    torch.cuda.synchronize()
+    dh0 = run.dh.clone()
+    run.prepare_backward()                        # e.g. after a weight update
+    with pytest.raises(RuntimeError):
+        run.backward(h, dy)
+    run.forward(h, b)
+    run.backward(h, dy)
+    torch.cuda.synchronize()
+    assert torch.equal(run.dh, dh0)
+    with pytest.raises(ValueError):
+        run.backward(h, dy[:-1])                  # dy of the wrong shape

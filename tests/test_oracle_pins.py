@@ -132,6 +132,81 @@ def test_topk_bias_changes_pick():
     assert O.biased_topk(s, b, 1).tolist() == [[1]]
 
 
+# ------------------------------------------------------------------ top-K margin
+
+def test_topk_margin_hand_computed():
+    # dyadic scores, all differences exact: sorted v = 0.875, 0.5, 0.25, 0.125
+    s = np.array([[0.5, 0.125, 0.875, 0.25]], dtype=np.float32)
+    assert O.topk_margin(s, None, 1)[0] == 0.375     # v_(1) - v_(2)
+    assert O.topk_margin(s, None, 2)[0] == 0.25      # v_(2) - v_(3)
+    assert O.topk_margin(s, None, 3)[0] == 0.125     # v_(3) - v_(4)
+
+
+def test_topk_margin_is_taken_on_biased_values():
+    # s alone sorts 0.75, 0.5, 0.375, 0.25 (margins 0.25, 0.125, 0.125);
+    # v = s + b = 0.25, 0.75, 0.25, 0.375 sorts 0.75, 0.375, 0.25, 0.25
+    s = np.array([[0.75, 0.5, 0.25, 0.375]], dtype=np.float32)
+    b = np.array([-0.5, 0.25, 0.0, 0.0], dtype=np.float32)
+    assert O.topk_margin(s, b, 1)[0] == 0.375
+    assert O.topk_margin(s, b, 2)[0] == 0.125
+    assert O.topk_margin(s, b, 3)[0] == 0.0          # exact tie between experts 0 and 2
+
+
+def test_topk_margin_exact_ties_and_K_equals_E():
+    s = np.array([[0.5, 0.5, 0.5, 0.25],
+                  [0.25, 0.5, 0.25, 0.75]], dtype=np.float32)
+    assert O.topk_margin(s, None, 1).tolist() == [0.0, 0.25]
+    assert O.topk_margin(s, None, 2).tolist() == [0.0, 0.25]
+    assert O.topk_margin(s, None, 3).tolist() == [0.25, 0.0]
+    assert np.all(np.isinf(O.topk_margin(s, None, 4)))
+    assert np.all(O.topk_margin(s, None, 4) > 0)
+
+
+def test_topk_margin_separates_selected_from_unselected():
+    # the margin is min v over the picked set minus max v over the rest, with the
+    # picked set from biased_topk (itself pinned by brute force above)
+    rng = np.random.default_rng(7)
+    for E, K in [(8, 2), (16, 4), (32, 8), (10, 9)]:
+        s = (rng.integers(0, 64, size=(50, E)) / 64.0).astype(np.float32)
+        b = (rng.integers(-8, 9, size=E) / 128.0).astype(np.float32)
+        v = O.biased_values(s, b).astype(np.float64)
+        idx = O.biased_topk(s, b, K)
+        m = O.topk_margin(s, b, K)
+        for t in range(s.shape[0]):
+            sel = np.zeros(E, bool)
+            sel[idx[t]] = True
+            assert m[t] == v[t, sel].min() - v[t, ~sel].max()
+            assert m[t] >= 0
+
+
+def test_topk_margin_bounds_the_bias_moves_that_keep_the_pick():
+    # A token whose margin is m keeps its picked set under any bias change of
+    # max-norm below m/2, and some change of max-norm m/2 + eps can move it
+    # (unless m == 0, where the tie rule decides).
+    rng = np.random.default_rng(8)
+    E, K = 12, 3
+    s = (rng.integers(0, 1024, size=(200, E)) / 1024.0).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    idx = O.biased_topk(s, b, K)
+    m = O.topk_margin(s, b, K)
+    for t in range(s.shape[0]):
+        if m[t] == 0:
+            continue
+        for _ in range(5):
+            db = (rng.uniform(-1, 1, E) * (m[t] / 2) * 0.999).astype(np.float32)
+            assert np.array_equal(O.biased_topk(s[t:t + 1], db, K)[0], idx[t])
+        # push the K-th picked value down and the best unpicked one up by m/2 + eps
+        v = s[t].astype(np.float64)
+        sel = idx[t]
+        kth = sel[np.argmin(v[sel])]
+        rest = np.setdiff1d(np.arange(E), sel)
+        out = rest[np.argmax(v[rest])]
+        db = np.zeros(E, np.float32)
+        db[kth] = -np.float32(m[t] / 2 + 2 ** -12)
+        db[out] = np.float32(m[t] / 2 + 2 ** -12)
+        assert out in O.biased_topk(s[t:t + 1], db, K)[0]
+
+
 def test_router_permutation_equivariant():
     rng = np.random.default_rng(5)
     h = rng.standard_normal((32, 24)).astype(np.float32)
@@ -251,6 +326,44 @@ def test_bias_update_worked_example_from_routing():
     assert c.tolist() == ex["loads"]
     b1 = O.bias_update(np.zeros(4, np.float32), c, 4, 1, ex["gamma"])
     assert np.array_equal(b1, np.array(ex["b1"], dtype=np.float32))
+
+
+def test_load_stats_worked_example():
+    # designs page, section 1: loads (3, 0, 0, 1) over T = 4, K = 1 -> max 3, min 0, MaxVio 2.0
+    ex = _load("bias_update_example.json")
+    st = O.load_stats(np.array(ex["loads"], dtype=np.int32), ex["T"], ex["K"])
+    assert st["max_load"] == 3 and st["min_load"] == 0
+    assert st["max_vio"] == pytest.approx(ex["max_vio"], abs=1e-12)
+
+
+def test_load_stats_by_enumeration():
+    # max / min over experts of the count of (t, k) picks, counted one by one;
+    # E_r > T*K leaves experts with no load
+    rng = np.random.default_rng(9)
+    for T, K, E in [(5, 2, 16), (40, 3, 12), (7, 1, 9)]:
+        s = rng.random((T, E)).astype(np.float32)
+        idx = O.biased_topk(s, None, K)
+        counts = [sum(1 for t in range(T) for k in range(K) if idx[t, k] == i) for i in range(E)]
+        st = O.load_stats(O.load_count(idx, E), T, K)
+        assert st["max_load"] == max(counts)
+        assert st["min_load"] == min(counts)
+        if E > T * K:
+            assert st["min_load"] == 0
+        cbar = K * T / E
+        assert st["max_vio"] == pytest.approx((max(counts) - cbar) / cbar, rel=1e-15)
+
+
+def test_load_stats_uniform_and_collapse():
+    T, K, E = 64, 2, 8
+    # token t picks experts 2(t mod 4) and 2(t mod 4) + 1: every expert holds T*K/E
+    idx = np.array([[2 * (t % 4), 2 * (t % 4) + 1] for t in range(T)], dtype=np.int32)
+    st = O.load_stats(O.load_count(idx, E), T, K)
+    assert st == dict(max_load=16, min_load=16, max_vio=0.0)
+    # every token on experts 3 and 5: max T, min 0, MaxVio = E/K - 1
+    idx = np.tile(np.array([3, 5], np.int32), (T, 1))
+    st = O.load_stats(O.load_count(idx, E), T, K)
+    assert st["max_load"] == T and st["min_load"] == 0
+    assert st["max_vio"] == pytest.approx(E / K - 1, abs=1e-12)
 
 
 def test_bias_update_fixed_points():
