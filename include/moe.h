@@ -42,16 +42,25 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums are passed as 32-bit ints.  A C++ translation unit gives them that
+ * fixed underlying type, so any int a caller passes is a value of the type and
+ * the library's range checks on it are well defined. */
+#ifdef __cplusplus
+#define MOE_ENUM : int32_t
+#else
+#define MOE_ENUM
+#endif
+
+typedef enum MOE_ENUM {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, K > E_r, ...            */
   MOE_ERR_UNSUPPORTED = 2,  /* valid but not built: shape alignment, dtype mix  */
   MOE_ERR_HIP = 3           /* the HIP runtime reported an error on launch      */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum MOE_ENUM { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-typedef enum {
+typedef enum MOE_ENUM {
   MOE_SIGMOID = 0,  /* s = sigmoid(z): DeepSeek-V3 affinity                      */
   MOE_SOFTMAX = 1   /* p = softmax(z) over all E_r experts: Mixtral / GShard     */
 } moe_score_fn;

@@ -9,7 +9,8 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+# MOE_LIB may name another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1

@@ -1,9 +1,14 @@
 """Build the HIP library libmoe_mi355x.so in-tree with hipcc for gfx950.
 
-    python -m sparse_mixture_experts_biased_amd.build [-j N]
+    python -m sparse_mixture_experts_biased_amd.build [-j N] [--sanitize]
 
 Object files go to _build/ at the repository root; the shared library is
 written next to this file, where the Python binding loads it.
+
+--sanitize builds libmoe_mi355x_san.so instead (objects in _build_san/): the
+host code under AddressSanitizer and UndefinedBehaviorSanitizer, the device
+code unchanged.  The binding loads it when MOE_LIB names it; the process needs
+the ASan runtime preloaded (see sanitizer_env()).
 """
 from __future__ import annotations
 
@@ -41,35 +46,64 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS
+# host-only sanitizers: each flag applies to the host compilation alone
+SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=undefined -Xarch_host -fno-omit-frame-pointer "
+             "-shared-libsan").split()
+SAN_BUILD = os.path.join(ROOT, "_build_san")
+SAN_LIB_PATH = os.path.join(PKG, "libmoe_mi355x_san.so")
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + \
+        list(extra)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, sanitize: bool = False) -> str:
+    build_dir = SAN_BUILD if sanitize else BUILD
+    lib_path = SAN_LIB_PATH if sanitize else LIB_PATH
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, 16))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + extra
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib_path}")
+    return lib_path
+
+
+def sanitizer_env() -> dict:
+    """Environment for a Python process that loads the sanitized library: the
+    ASan runtime preloaded (Python itself is not instrumented), leak checks
+    off (the interpreter keeps its allocations), MOE_LIB set."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    rt = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(rt) or not os.path.exists(rt):
+        raise RuntimeError("the ASan runtime of the HIP toolchain was not found")
+    env = dict(os.environ)
+    env.update(LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1", MOE_LIB=SAN_LIB_PATH)
+    return env
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", "--jobs", type=int, default=8)
+    ap.add_argument("--sanitize", action="store_true",
+                    help="host code under ASan + UBSan, into libmoe_mi355x_san.so")
     args = ap.parse_args(argv)
-    build(args.jobs, verbose=True)
+    build(args.jobs, verbose=True, sanitize=args.sanitize)
 
 
 if __name__ == "__main__":
