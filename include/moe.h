@@ -85,6 +85,8 @@ typedef struct {
 
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
+/* Scratch of moe_grouped_swiglu_noalloc: one array of this size per GPU. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /*
  * moe_route -- router scores, biased top-K selection, unbiased gates, loads.
@@ -266,6 +268,37 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
                               const void* w_up, const void* w_down, const float* row_scale,
                               void* y, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * moe_grouped_swiglu_noalloc -- moe_grouped_swiglu that allocates nothing, for
+ * callers that cannot allocate device memory or take a workspace: code under
+ * HIP graph capture, tight serving loops (decode-sized batches), harnesses
+ * that forbid hipMalloc.
+ *
+ * The same computation, outputs and argument meanings as moe_grouped_swiglu,
+ * without the workspace arguments: its scratch (the activations and the tile
+ * list) is a device array of MOE_NOALLOC_SCRATCH_BYTES (32 MiB) inside the
+ * library, one per GPU, loaded with the library's code on that GPU and held
+ * until the process ends.  Its device address is looked up on the first call
+ * on each device (hipGetSymbolAddress, which may load the library's code on
+ * that device); later calls only launch.  Calls no hipMalloc or hipFree.
+ *
+ * The current device must be the stream's device.  Every call on one GPU
+ * uses that GPU's one array: calls that overlap on one GPU (on different
+ * streams, or from several threads) race and give wrong results; calls in
+ * order on one stream are safe.  Nothing in the array has to start at zero.
+ *
+ * Errors: the arguments are checked as for moe_grouped_swiglu, before any
+ * launch; a call whose scratch need (moe_grouped_swiglu_workspace_size)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_UNSUPPORTED with the
+ * sizes in moe_last_error() -- e.g. at d_ffn = 2048 (bf16) up to about 8000
+ * grouped rows fit.
+ */
+moe_status moe_grouped_swiglu_noalloc(int n_groups, int d_model, int d_ffn, int rows,
+                                      int x_rows, const int32_t* offsets,
+                                      const int32_t* row_index, const void* x, moe_dtype dtype,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      const float* row_scale, void* y, void* stream);
 
 /*
  * moe_grouped_swiglu_train -- moe_grouped_swiglu for a training forward pass:

@@ -22,7 +22,7 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size
             "moe_combine_backward", "moe_grouped_swiglu_backward_workspace_size",
             "moe_grouped_swiglu_backward", "moe_route_backward",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
-            "moe_grouped_swiglu_train", "moe_combine",
+            "moe_grouped_swiglu_train", "moe_grouped_swiglu_noalloc", "moe_combine",
             "moe_bias_update", "moe_calib_mfma_loop", "moe_calib_stream_read",
             "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
                                 _sz, _p], _i),
         "moe_grouped_swiglu_train": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p,
                                       _p, _p, _sz, _p], _i),
+        "moe_grouped_swiglu_noalloc": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p,
+                                        _p, _p], _i),
         "moe_combine": ([_i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _p], _i),
         "moe_bias_update": ([_i, _i, _i, _f, _p, _p, _p, _p], _i),
         "moe_calib_mfma_loop": ([_i, _i, _p, _p, ctypes.POINTER(ctypes.c_double), _p], _i),
@@ -213,6 +215,14 @@ def moe_grouped_swiglu_train(n_groups, d_model, d_ffn, rows, x_rows, offsets, ro
                                            _ptr(w_up), _ptr(w_down), _ptr(row_scale), _ptr(y),
                                            _ptr(au), _ptr(workspace), workspace_bytes,
                                            _stream(stream)))
+
+
+def moe_grouped_swiglu_noalloc(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x,
+                               dtype, w_gate, w_up, w_down, row_scale, y, stream=None):
+    _check(load().moe_grouped_swiglu_noalloc(n_groups, d_model, d_ffn, rows, x_rows,
+                                             _ptr(offsets), _ptr(row_index), _ptr(x), dtype,
+                                             _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                             _ptr(row_scale), _ptr(y), _stream(stream)))
 
 
 def moe_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates, dtype, y,

@@ -213,7 +213,8 @@ moe_status grouped_swiglu(const char* fn, int n_groups, int d_model, int d_ffn, 
                           int x_rows, const int32_t* offsets, const int32_t* row_index,
                           const void* x, moe_dtype dtype, const void* w_gate, const void* w_up,
                           const void* w_down, const float* row_scale, void* y, void* au,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          bool launch = true) {
   if (n_groups < 1 || d_model < 1 || d_ffn < 1 || rows < 0 || x_rows < 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: n_groups=%d d_model=%d d_ffn=%d rows=%d x_rows=%d", fn,
                 n_groups, d_model, d_ffn, rows, x_rows);
@@ -244,6 +245,7 @@ moe_status grouped_swiglu(const char* fn, int n_groups, int d_model, int d_ffn, 
   const size_t need = moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
   if (workspace_bytes < need)
     return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  if (!launch) return MOE_OK;
   if (rows == 0) return MOE_OK;
   hipError_t err;
   if (dtype == MOE_BF16)
@@ -273,6 +275,69 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
   return grouped_swiglu("moe_grouped_swiglu", n_groups, d_model, d_ffn, rows, x_rows, offsets,
                         row_index, x, dtype, w_gate, w_up, w_down, row_scale, y, nullptr,
                         workspace, workspace_bytes, stream);
+}
+
+// ---- the form that allocates nothing: its workspace is one file-scope device
+// array per GPU, found once per device with hipGetSymbolAddress.  In host code
+// `scratch` only names the symbol; kernels get the address from g_scratch.
+
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array (the current device's), looked up
+// on the first call on that device.
+moe_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond %d devices", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (p == nullptr) return fail(MOE_ERR_HIP, "%s: scratch array has no device address", fn);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_grouped_swiglu_noalloc(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                                      const int32_t* offsets, const int32_t* row_index,
+                                      const void* x, moe_dtype dtype, const void* w_gate,
+                                      const void* w_up, const void* w_down,
+                                      const float* row_scale, void* y, void* stream) {
+  const char* fn = "moe_grouped_swiglu_noalloc";
+  const size_t cap = MOE_NOALLOC_SCRATCH_BYTES;
+  if (n_groups >= 1 && d_model >= 1 && d_ffn >= 1 && rows >= 0 && valid_dtype(dtype)) {
+    const size_t need =
+        moe::swiglu_workspace_bytes(n_groups, d_model, d_ffn, rows, dtype == MOE_BF16);
+    if (need > cap)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "%s: rows=%d x d_ffn=%d needs %zu bytes of scratch, more than the %zu this "
+                  "form holds per GPU; call moe_grouped_swiglu with a workspace instead",
+                  fn, rows, d_ffn, need, cap);
+  }
+  // every argument is checked before the scratch address is looked up
+  void* const probe = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  moe_status st = grouped_swiglu(fn, n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index,
+                                 x, dtype, w_gate, w_up, w_down, row_scale, y, nullptr, probe, cap,
+                                 stream, /*launch=*/false);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(fn, &ws);
+  if (st != MOE_OK) return st;
+  return grouped_swiglu(fn, n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x, dtype,
+                        w_gate, w_up, w_down, row_scale, y, nullptr, ws, cap, stream);
 }
 
 moe_status moe_grouped_swiglu_train(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
