@@ -310,6 +310,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="dsv3_prefill",
                     choices=["dsv3_prefill", "dsv3_decode", "dsv3_skewed", "mixtral_8x7b"])
     ap.add_argument("--rotate", type=int, default=10, help="token batches cycled through")
+    ap.add_argument("--tokens", type=int, default=None, metavar="T",
+                    help="override the workload's token count T (same layer otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--capacity-factor", type=float, default=None, metavar="CF",
                     help="cap every expert at ceil(CF*T*K/E_r) rows (token dropping)")
@@ -348,6 +350,11 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     load()
     cfg = CONFIGS[args.workload]
+    if args.tokens is not None:
+        if args.tokens < 1:
+            log("--tokens must be >= 1")
+            return 2
+        cfg = cfg.with_tokens(args.tokens)
     log(f"workload {cfg.name}: T={cfg.T} d_model={cfg.d_model} E_r={cfg.E_r} K={cfg.K} "
         f"E_s={cfg.E_s} d_ffn={cfg.d_ffn} {cfg.dtype} {cfg.score}")
     t0 = time.perf_counter()

@@ -335,8 +335,8 @@ moe_status moe_grouped_swiglu_train(int n_groups, int d_model, int d_ffn, int ro
  *   gates    [T, K] fp32
  *   y        [T, d_model] out (dtype), fp32 accumulation in a fixed order,
  *            bf16 output rounded to nearest even.  Deterministic.
- * Limits: d_model % 8 == 0; bf16 y_perm under 2 GiB (it is read through one
- * buffer descriptor), else MOE_ERR_UNSUPPORTED.
+ * Limits: d_model % 8 == 0; T*K <= INT32_MAX.  y_perm may be any size (each
+ * gathered row is addressed from its own base).
  */
 moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h,
                        const void* y_shared, const void* y_perm, const int32_t* slot_row,

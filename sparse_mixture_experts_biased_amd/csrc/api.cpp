@@ -368,8 +368,6 @@ moe_status moe_combine(int T, int d_model, int K, int E_s, const void* h, const 
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
   if (static_cast<long long>(T) * K > INT32_MAX)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: T*K overflows int32");
-  if (dtype == MOE_BF16 && static_cast<long long>(T) * K * d_model * 2 >= (1ll << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_combine: bf16 y_perm exceeds 2 GiB");
   return hip_status(moe::launch_combine(T, d_model, K, E_s, h, y_shared, y_perm, slot_row, gates,
                                         dtype == MOE_BF16, y, as_stream(stream)),
                     "moe_combine");

@@ -30,13 +30,13 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4& v, floa
 // U 16-byte chunks of the row per lane per iteration.  The loads of an
 // iteration -- h, the first shared expert's row, the K gathered rows -- are
 // all issued before any of them is used, so a wave keeps U * (K + 2) loads in
-// flight.  The gathered rows go through buffer loads whose offset is out of
-// range (reads zeros, no memory access) for a dropped or invalid slot, so no
-// branch sits between them.  The sum is taken in the fixed order h, shared
+// flight.  Each gathered row has a buffer descriptor of its own (based at the
+// row, one row long), so y_perm may exceed the 4 GiB a 32-bit offset reaches;
+// a dropped or invalid slot gets an empty descriptor, whose loads read zeros
+// without a memory access, so no branch sits between the loads.  KM bounds K
+// (the registers hold KM rows).  The sum is taken in the fixed order h, shared
 // experts 0..E_s-1, k = 0..K-1.
-constexpr uint32_t kOffNone = 0x80000000u;  // beyond every buffer (sizes < 2 GiB)
-
-template <int U>
+template <int KM, int U>
 __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     int T, int d, int K, int E_s, const uint16_t* __restrict__ h,
     const uint16_t* __restrict__ ysh, const uint16_t* __restrict__ yp,
@@ -45,28 +45,28 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   if (t >= T) return;
-  const int TK = T * K;
+  const long long TK = static_cast<long long>(T) * K;
   const int vecs = d / 8;
-  const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(yp), 0, static_cast<int>(static_cast<uint32_t>(TK) * d * 2u),
-      0x00020000);
   // the token's slots and gates: lane k holds entry k, then each is broadcast
   const int sl = lane < K ? slot_row[static_cast<size_t>(t) * K + lane] : -1;
   const float gl = lane < K ? gates[static_cast<size_t>(t) * K + lane] : 0.0f;
-  uint32_t poff[MOE_MAX_TOPK_DEV];
-  float g[MOE_MAX_TOPK_DEV];
+  __amdgpu_buffer_rsrc_t rs[KM];
+  float g[KM];
 #pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+  for (int k = 0; k < KM; ++k) {
     const int s = __builtin_amdgcn_readlane(sl, k);
     g[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), k));
-    poff[k] = (k < K && s >= 0 && s < TK) ? static_cast<uint32_t>(s) * d * 2u : kOffNone;
+    const bool ok = k < K && s >= 0 && s < TK;
+    rs[k] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(yp + (ok ? static_cast<size_t>(s) * d : 0)), 0, ok ? d * 2 : 0,
+        0x00020000);
   }
   const uint4* hr = reinterpret_cast<const uint4*>(h + static_cast<size_t>(t) * d);
   const uint4* s0 = reinterpret_cast<const uint4*>(ysh + static_cast<size_t>(t) * d);
   uint4* yr = reinterpret_cast<uint4*>(y + static_cast<size_t>(t) * d);
   for (int c0 = lane; c0 < vecs; c0 += U * kWave) {
     // a chunk past the row end (only when U * kWave does not divide d / 8)
-    // reads whatever the buffer bounds allow and is never stored
+    // reads zeros (past the descriptor's row) and is never stored
     bool ok[U];
     uint32_t cb[U];
 #pragma unroll
@@ -74,19 +74,18 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
       ok[u] = c0 + u * kWave < vecs;
       cb[u] = static_cast<uint32_t>(c0 + u * kWave) * 16u;
     }
-    uint4 vh[U], vs[U], vp[MOE_MAX_TOPK_DEV][U];
+    uint4 vh[U], vs[U], vp[KM][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       vh[u] = ok[u] ? hr[c0 + u * kWave] : make_uint4(0, 0, 0, 0);
       vs[u] = (ok[u] && E_s > 0) ? s0[c0 + u * kWave] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
-      if (k < K)
+    for (int k = 0; k < KM; ++k)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-          vp[k][u] = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(rsP, poff[k] + cb[u], 0, 0));
+      for (int u = 0; u < U; ++u)
+        vp[k][u] = __builtin_bit_cast(uint4,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rs[k], cb[u], 0, 0));
     float acc[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -101,8 +100,9 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
       for (int u = 0; u < U; ++u)
         if (ok[u]) add_bf16x8(acc[u], sr[c0 + u * kWave], 1.0f);
     }
+    // k past K: an empty descriptor read zeros, and its gate is 0
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    for (int k = 0; k < KM; ++k)
       if (k < K)
 #pragma unroll
         for (int u = 0; u < U; ++u) add_bf16x8(acc[u], vp[k][u], g[k]);
@@ -154,12 +154,24 @@ hipError_t launch_combine(int T, int d, int K, int E_s, const void* h, const voi
                           int bf16, void* y, hipStream_t s) {
   dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(kThreads);
   ProfScope prof_(s, "combine");
-  if (bf16)
-    hipLaunchKernelGGL(combine_bf16_kernel<kChunksPerIter>, grid, block, 0, s, T, d, K, E_s,
-                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(y_shared),
-                       static_cast<const uint16_t*>(y_perm), slot_row, gates,
-                       static_cast<uint16_t*>(y));
-  else
+  if (bf16) {
+    const uint16_t* hb = static_cast<const uint16_t*>(h);
+    const uint16_t* sb = static_cast<const uint16_t*>(y_shared);
+    const uint16_t* pb = static_cast<const uint16_t*>(y_perm);
+    uint16_t* yb = static_cast<uint16_t*>(y);
+    if (K <= 2)
+      hipLaunchKernelGGL((combine_bf16_kernel<2, kChunksPerIter>), grid, block, 0, s, T, d, K,
+                         E_s, hb, sb, pb, slot_row, gates, yb);
+    else if (K <= 4)
+      hipLaunchKernelGGL((combine_bf16_kernel<4, kChunksPerIter>), grid, block, 0, s, T, d, K,
+                         E_s, hb, sb, pb, slot_row, gates, yb);
+    else if (K <= 8)
+      hipLaunchKernelGGL((combine_bf16_kernel<8, kChunksPerIter>), grid, block, 0, s, T, d, K,
+                         E_s, hb, sb, pb, slot_row, gates, yb);
+    else
+      hipLaunchKernelGGL((combine_bf16_kernel<MOE_MAX_TOPK_DEV, kChunksPerIter>), grid, block, 0,
+                         s, T, d, K, E_s, hb, sb, pb, slot_row, gates, yb);
+  } else
     hipLaunchKernelGGL(combine_f32_kernel, grid, block, 0, s, T, d, K, E_s,
                        static_cast<const float*>(h), static_cast<const float*>(y_shared),
                        static_cast<const float*>(y_perm), slot_row, gates,

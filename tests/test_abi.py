@@ -192,8 +192,9 @@ def test_combine_and_bias_update_reject_bad_arguments():
     assert lib.moe_combine(10, 64, 2, 1, P, None, P, P, P, 1, P, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(10, 60, 2, 0, P, None, P, P, P, 1, P, None) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(10, 64, 17, 0, P, None, P, P, P, 1, P, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_combine(1 << 17, 8192, 8, 0, P, None, P, P, P, 1, P, None) == \
-        L.MOE_ERR_UNSUPPORTED   # bf16 y_perm of 16 GiB
+    # T*K past int32 is refused; a large y_perm alone is not (rows have their own bases)
+    assert lib.moe_combine(1 << 28, 64, 16, 0, P, None, P, P, P, 1, P, None) == \
+        L.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(10, 8, 2, -0.1, P, P, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(10, 8, 2, float("nan"), P, P, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_bias_update(10, 8, 2, 0.1, None, P, None, None) == L.MOE_ERR_INVALID_ARG

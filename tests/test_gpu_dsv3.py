@@ -39,6 +39,24 @@ def test_dsv3_prefill_full_size(dsv3):
     say(str(res))
 
 
+def test_dsv3_prefill_32k_tokens(dsv3):
+    """T = 32768 at the DeepSeek-V3 shape: 262144 routed rows, so y_perm
+    (3.8 GB) is larger than a buffer descriptor with a signed 32-bit size
+    covers.  Every token's routing, two rows of every expert, and a sample of
+    layer rows."""
+    from dataclasses import replace
+    cfg = replace(dsv3.cfg, T=32768)
+    h = make_tokens(cfg, step=1, device="cuda")
+    run = runner_for(dsv3, T=cfg.T)
+    assert run.y_perm.numel() * 2 > (1 << 31)
+    res = check_layer(dsv3, h, dsv3.b, cfg.gamma, run, n_tok_sample=8, seed=6,
+                      rows_per_expert=2)
+    assert res["experts_checked"] == int((run.loads > 0).sum())
+    say(str(res))
+    del run
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cf", [1.0, 1.25])
 def test_dsv3_prefill_capacity_factor(dsv3, cf):
     """Capacity-bounded dispatch at full size: C = ceil(CF*T*K/E_r) = 128 / 160
@@ -107,8 +125,10 @@ def test_dsv3_skewed_20_steps(dsv3, golden_dir):
             # full layer check (sampled) on the first and the last step
             view = type(lay)(cfg, h, e, b_before, lay.w_gate, lay.w_up, lay.w_down,
                              lay.ws_gate, lay.ws_up, lay.ws_down)
+            # two rows of every expert on the first step, all rows of 4 experts on the last
             res = check_layer(view, h, b_before, cfg.gamma, run, n_tok_sample=8,
-                              seed=10 + step, rows_per_expert=2)
+                              seed=10 + step, n_exp_sample=4,
+                              rows_per_expert=2 if step == 0 else None)
             b = res["b_new"]
         else:
             run.forward(h, b, cfg.gamma)
