@@ -8,7 +8,10 @@
 // Token-major: one wave per token row, 16-byte vector loads, all of an
 // iteration's loads in flight before the first is used; every output element
 // is accumulated in fp32 in a fixed order (h, shared experts, then k =
-// 0..K-1), so the result is deterministic.
+// 0..K-1), so the result is deterministic.  Every input is read once and the
+// output written once, so the loads and the store are non-temporal: they do
+// not displace the expert weights and tiles from the caches (measured at the
+// prefill shape: 0.177 -> 0.145 ms with caches flushed between calls).
 #include "common.h"
 
 namespace moe {
@@ -16,7 +19,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = kThreads / kWave;
-constexpr int kChunksPerIter = 2;  // 16-byte chunks of a row per lane and iteration
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kNonTemporal = 2;    // buffer-load cache policy: non-temporal
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4& v, float w) {
   const uint32_t p[4] = {v.x, v.y, v.z, v.w};
@@ -61,12 +65,15 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
         const_cast<uint16_t*>(yp + (ok ? static_cast<size_t>(s) * d : 0)), 0, ok ? d * 2 : 0,
         0x00020000);
   }
-  const uint4* hr = reinterpret_cast<const uint4*>(h + static_cast<size_t>(t) * d);
-  const uint4* s0 = reinterpret_cast<const uint4*>(ysh + static_cast<size_t>(t) * d);
-  uint4* yr = reinterpret_cast<uint4*>(y + static_cast<size_t>(t) * d);
+  const __amdgpu_buffer_rsrc_t rsH = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(h + static_cast<size_t>(t) * d), 0, d * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(ysh + (E_s > 0 ? static_cast<size_t>(t) * d : 0)), 0,
+      E_s > 0 ? d * 2 : 0, 0x00020000);
+  u32x4* yr = reinterpret_cast<u32x4*>(y + static_cast<size_t>(t) * d);
   for (int c0 = lane; c0 < vecs; c0 += U * kWave) {
     // a chunk past the row end (only when U * kWave does not divide d / 8)
-    // reads zeros (past the descriptor's row) and is never stored
+    // reads zeros (past the descriptors' rows) and is never stored
     bool ok[U];
     uint32_t cb[U];
 #pragma unroll
@@ -77,15 +84,17 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     uint4 vh[U], vs[U], vp[KM][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      vh[u] = ok[u] ? hr[c0 + u * kWave] : make_uint4(0, 0, 0, 0);
-      vs[u] = (ok[u] && E_s > 0) ? s0[c0 + u * kWave] : make_uint4(0, 0, 0, 0);
+      vh[u] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rsH, cb[u], 0, kNonTemporal));
+      vs[u] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rsS, cb[u], 0, kNonTemporal));
     }
 #pragma unroll
     for (int k = 0; k < KM; ++k)
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        vp[k][u] = __builtin_bit_cast(uint4,
-                                      __builtin_amdgcn_raw_buffer_load_b128(rs[k], cb[u], 0, 0));
+        vp[k][u] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs[k], cb[u], 0, kNonTemporal));
     float acc[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -109,12 +118,12 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ok[u]) {
-        uint4 o;
+        u32x4 o;
         o.x = pack_bf16x2(acc[u][0], acc[u][1]);
         o.y = pack_bf16x2(acc[u][2], acc[u][3]);
         o.z = pack_bf16x2(acc[u][4], acc[u][5]);
         o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-        yr[c0 + u * kWave] = o;
+        __builtin_nontemporal_store(o, &yr[c0 + u * kWave]);
       }
     }
   }
@@ -159,18 +168,19 @@ hipError_t launch_combine(int T, int d, int K, int E_s, const void* h, const voi
     const uint16_t* sb = static_cast<const uint16_t*>(y_shared);
     const uint16_t* pb = static_cast<const uint16_t*>(y_perm);
     uint16_t* yb = static_cast<uint16_t*>(y);
+    // 16-byte chunks per lane and iteration: 4 when few rows are gathered
     if (K <= 2)
-      hipLaunchKernelGGL((combine_bf16_kernel<2, kChunksPerIter>), grid, block, 0, s, T, d, K,
-                         E_s, hb, sb, pb, slot_row, gates, yb);
+      hipLaunchKernelGGL((combine_bf16_kernel<2, 4>), grid, block, 0, s, T, d, K, E_s, hb, sb,
+                         pb, slot_row, gates, yb);
     else if (K <= 4)
-      hipLaunchKernelGGL((combine_bf16_kernel<4, kChunksPerIter>), grid, block, 0, s, T, d, K,
-                         E_s, hb, sb, pb, slot_row, gates, yb);
+      hipLaunchKernelGGL((combine_bf16_kernel<4, 4>), grid, block, 0, s, T, d, K, E_s, hb, sb,
+                         pb, slot_row, gates, yb);
     else if (K <= 8)
-      hipLaunchKernelGGL((combine_bf16_kernel<8, kChunksPerIter>), grid, block, 0, s, T, d, K,
-                         E_s, hb, sb, pb, slot_row, gates, yb);
+      hipLaunchKernelGGL((combine_bf16_kernel<8, 2>), grid, block, 0, s, T, d, K, E_s, hb, sb,
+                         pb, slot_row, gates, yb);
     else
-      hipLaunchKernelGGL((combine_bf16_kernel<MOE_MAX_TOPK_DEV, kChunksPerIter>), grid, block, 0,
-                         s, T, d, K, E_s, hb, sb, pb, slot_row, gates, yb);
+      hipLaunchKernelGGL((combine_bf16_kernel<MOE_MAX_TOPK_DEV, 2>), grid, block, 0, s, T, d, K,
+                         E_s, hb, sb, pb, slot_row, gates, yb);
   } else
     hipLaunchKernelGGL(combine_f32_kernel, grid, block, 0, s, T, d, K, E_s,
                        static_cast<const float*>(h), static_cast<const float*>(y_shared),

@@ -34,14 +34,22 @@ class LayerShape:
 class MoELayer:
     def __init__(self, shape: LayerShape, e, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
                  ws_down=None, device="cuda", capacity_factor: Optional[float] = None,
-                 diagnostics: bool = False, overlap_shared: bool = True):
+                 diagnostics: bool = False, overlap_shared: bool = True,
+                 shared_start: str = "layer"):
         """capacity_factor: None dispatches every copy; a factor CF caps each
         expert at C = ceil(CF*T*K/E_r) rows, admitted in token order.
         diagnostics: route with moe_route_stats and fill the router's balance
         diagnostics (moe_router_diag) after the dispatch of every forward.
         overlap_shared: run the shared experts (which need no routing) on a
         second stream, side by side with the routing and the routed experts,
-        joined before the combine; False runs them in sequence."""
+        joined before the combine; False runs them in sequence.
+        shared_start: with overlap_shared, when the side stream starts them:
+        "layer" (as soon as h is ready) or "routed" (once the router and the
+        dispatch are done, so those small kernels have every CU to themselves
+        and the shared experts overlap the routed experts instead)."""
+        if shared_start not in ("layer", "routed"):
+            raise ValueError(f"shared_start must be 'layer' or 'routed', not {shared_start!r}")
+        self.shared_start = shared_start
         s = self.shape = shape
         self.capacity = (None if capacity_factor is None else
                          L.moe_expert_capacity(s.T, s.K, s.E_r, capacity_factor))
@@ -211,16 +219,24 @@ class MoELayer:
         # the shared experts on the side stream once h is ready on this one
         # (a raw stream handle cannot carry events: then in sequence)
         overlap = self.side is not None and not isinstance(stream, int)
+        main = None
         if overlap:
             main = stream if stream is not None else torch.cuda.current_stream()
+
+        def start_shared():
             self.ev_in.record(main)
             self.side.wait_event(self.ev_in)
             self.shared_experts(h, self.side)
             self.ev_sh.record(self.side)
+
+        if overlap and self.shared_start == "layer":
+            start_shared()
         self.route(h, b, stream)
         self.permute(stream=stream)
         if self.diagnostics:
             self.router_diag(stream)
+        if overlap and self.shared_start == "routed":
+            start_shared()
         self.routed_experts(h, stream)
         if overlap:
             main.wait_event(self.ev_sh)

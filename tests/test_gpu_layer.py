@@ -61,8 +61,9 @@ def test_mixtral_layer_ragged_tokens():
 
 
 def test_shared_expert_overlap_matches_sequential():
-    """The shared experts on the side stream give the same bits as run in
-    sequence, forward and backward, and again on a second call."""
+    """The shared experts on the side stream (started with the layer, or once
+    the routing is done) give the same bits as run in sequence, forward and
+    backward, and again on a second call."""
     from dataclasses import replace
     from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
     cfg = replace(CONFIGS["dsv3_prefill"], T=300, d_model=1024, E_r=32, K=4, d_ffn=512)
@@ -73,9 +74,10 @@ def test_shared_expert_overlap_matches_sequential():
     dy = torch.randn(cfg.T, cfg.d_model, generator=torch.Generator("cuda").manual_seed(5),
                      device="cuda").to(torch.bfloat16)
     outs = {}
-    for name, overlap in (("overlap", True), ("sequential", False)):
+    for name, overlap, start in (("overlap", True, "layer"), ("overlap-routed", True, "routed"),
+                                 ("sequential", False, "layer")):
         run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
-                       lay.ws_down, overlap_shared=overlap)
+                       lay.ws_down, overlap_shared=overlap, shared_start=start)
         run.prepare_backward()
         ys = []
         for _ in range(2):
@@ -85,5 +87,6 @@ def test_shared_expert_overlap_matches_sequential():
         assert torch.equal(ys[0], ys[1]), name
         outs[name] = (ys[0], run.dh.clone(), run.dws_gate.clone(), run.dws_down.clone(),
                       run.de.clone())
-    for a, b in zip(outs["overlap"], outs["sequential"]):
-        assert torch.equal(a, b)
+    for name in ("overlap", "overlap-routed"):
+        for a, b in zip(outs[name], outs["sequential"]):
+            assert torch.equal(a, b), name
