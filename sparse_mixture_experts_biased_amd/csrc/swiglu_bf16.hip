@@ -452,14 +452,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Buffer load of BYTES per lane into LDS: lane l's data lands at lds + l * BYTES
 // (lds is wave-uniform).  Only voffset takes part in the range check, so an
 // out-of-range voffset reads zeros while the uniform soffset moves along k.
-template <int BYTES>
+// Cache policy of the weight loads: non-temporal.  Within a launch each
+// weight slice is needed only by the row tiles of its expert that run side by
+// side (at most a few, on one XCD), so the expert weights -- gigabytes per
+// launch -- are streamed past the caches instead of displacing the gathered
+// token rows and activations that every column tile re-reads.  Measured:
+// decode-shape gate/up 2.10 -> 1.90 ms, down 1.11 -> 1.03 ms; Mixtral down
+// 1.18 -> 1.11 ms; prefill unchanged.
+constexpr int kWeightPolicy = 2;
+
+template <int BYTES, int AUX = 0>
 __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
                                     uint32_t soff) {
   static_assert(BYTES == 4 || BYTES == 16, "dword or 16-byte loads");
   if constexpr (BYTES == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, voff, soff, 0, AUX);
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, AUX);
 }
 
 template <bool GATEUP, int BK, bool AU = false>
@@ -616,8 +625,8 @@ void bf16_stream_kernel(
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const int add = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;
-      dma<16>((GATEUP && i >= kNI / 2) ? rb1 : rb0,
-              st + G::kTileBytes + kRPI * (wave + 8 * i) * G::kRow, b_off,
+      dma<16, kWeightPolicy>((GATEUP && i >= kNI / 2) ? rb1 : rb0,
+                             st + G::kTileBytes + kRPI * (wave + 8 * i) * G::kRow, b_off,
               bcol + static_cast<uint32_t>(add) * rowbytes + kb);
     }
     kb += G::kRow;
@@ -969,7 +978,8 @@ void bf16_regs_stream_kernel(
         __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0)); \
     _Pragma("unroll") for (int i = 0; i < kBLoads; ++i) SB[i] = __builtin_bit_cast(          \
         uint4, __builtin_amdgcn_raw_buffer_load_b128((!GATEUP || i < kBLoads / 2) ? rb0 : rb1, \
-                                                     bb, bcol + kb + b_row_add(i), 0));     \
+                                                     bb, bcol + kb + b_row_add(i),         \
+                                                     kWeightPolicy));                      \
     kb += kBK * 2;                                                                          \
   } while (0)
 #define MOE_STORE_SLICE(SA, SB, STAGE)                                                      \
@@ -1383,7 +1393,8 @@ void bf16_wdma_kernel(
     __builtin_amdgcn_sched_barrier(0); /* rows before weights: see the step's waits */      \
     _Pragma("unroll") for (int i = 0; i < kNI; ++i) {                                       \
       const int add_ = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;                  \
-      dma<16>((GATEUP && i >= kNI / 2) ? rb1 : rb0, (ST) + kRPI * (wave + 8 * i) * G::kRow,   \
+      dma<16, kWeightPolicy>((GATEUP && i >= kNI / 2) ? rb1 : rb0,                          \
+                             (ST) + kRPI * (wave + 8 * i) * G::kRow,                          \
               b_off | zmask_, bcol + static_cast<uint32_t>(add_) * rowbytes + kb);          \
     }                                                                                       \
     kb += kBK * 2;                                                                          \
@@ -1595,10 +1606,18 @@ void bf16_wdma_kernel(
 #pragma unroll
       for (int it = 0; it < kRoundRows / kReadRows; ++it) {
         if (rl < c_nrows - r0 - it * kReadRows)
+        {
           // vector copies: a uint4 assignment is a memcpy, whose LDS load
-          // carries no alias scope
-          *reinterpret_cast<bf16x8_t*>(dst + static_cast<size_t>(it) * kReadRows * ldo) =
+          // carries no alias scope.  The down product's rows (y_perm, read
+          // once by the combine) leave through non-temporal stores.
+          const bf16x8_t v_ =
               *reinterpret_cast<const bf16x8_t*>(a_st + (soff + it * kReadRows * kOutRowBytes));
+          bf16x8_t* d_ = reinterpret_cast<bf16x8_t*>(dst + static_cast<size_t>(it) * kReadRows * ldo);
+          if (GATEUP)
+            *d_ = v_;
+          else
+            __builtin_nontemporal_store(v_, d_);
+        }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
