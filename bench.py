@@ -35,15 +35,16 @@ def algorithmic(cfg, n_touched, n_touched_shared, rows=None):
 
     Per touched routed or shared expert: W_gate + W_up = 2 * d * f bf16 words
     (gate/up launch) and W_down = d * f words (down launch).  Per token: h read
-    once (d words) and y written once (d words).  Per assignment row: the
-    activation (f words) written by gate/up.  Expert flops: 6 d f per row
-    (2 d f each for gate, up and down), rows = T*K routed (the kept copies
-    under a capacity) + T*E_s shared.
+    once (d words) and y written once (d words).  The activation the gate/up
+    launch writes for the down launch (f words per assignment row) is a staged
+    intermediate, overhead against these bytes, as are x rows re-read per
+    column tile.  Expert flops: 6 d f per row (2 d f each for gate, up and
+    down), rows = T*K routed (the kept copies under a capacity) + T*E_s shared.
     """
     d, f, T, K = cfg.d_model, cfg.d_ffn, cfg.T, cfg.K
     rows = T * K if rows is None else rows
     eb = 2 if cfg.dtype == "bf16" else 4
-    gateup_bytes = n_touched * 2 * d * f * eb + T * d * eb + rows * f * eb
+    gateup_bytes = n_touched * 2 * d * f * eb + T * d * eb
     gateup_flops = 4.0 * d * f * rows
     layer_bytes = (n_touched + n_touched_shared) * 3 * d * f * eb + 2 * T * d * eb
     layer_flops = 6.0 * d * f * (rows + T * cfg.E_s) + 2.0 * T * d * cfg.E_r

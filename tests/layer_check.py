@@ -46,7 +46,7 @@ def check_permutation_valid(idx, offsets, row_token, slot_row, E):
 
 
 def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=0,
-                check_all_tokens=False, rows_per_expert=None):
+                check_all_tokens=False, rows_per_expert=None, label=None):
     """Run one layer forward on the GPU and compare with the oracle.  With a
     capacity (run.capacity), the oracle's capacity dispatch of the whole batch
     decides which copies are kept.
@@ -191,7 +191,7 @@ def check_layer(lay, h, b_in, gamma, run, n_tok_sample=16, n_exp_sample=4, seed=
         for j in range(c.E_s):
             ref = O.swiglu(h_host[toks], *shared(j))
             assert rel_err(ysh[j][toks], ref) <= tol
-    record_parity(c.name, T, res)
+    record_parity(label or c.name, T, res)
     return res
 
 

@@ -50,7 +50,7 @@ def test_dsv3_prefill_32k_tokens(dsv3):
     run = runner_for(dsv3, T=cfg.T)
     assert run.y_perm.numel() * 2 > (1 << 31)
     res = check_layer(dsv3, h, dsv3.b, cfg.gamma, run, n_tok_sample=8, seed=6,
-                      rows_per_expert=2)
+                      rows_per_expert=2, label="dsv3_prefill T=32768")
     assert res["experts_checked"] == int((run.loads > 0).sum())
     say(str(res))
     del run
@@ -96,7 +96,7 @@ def test_dsv3_decode_full_size(dsv3):
     run = runner_for(dsv3, T=cfg.T)
     # all 64 tokens and every row of every touched expert
     res = check_layer(dsv3, h, dsv3.b, cfg.gamma, run, seed=4, check_all_tokens=True,
-                      rows_per_expert=cfg.T * cfg.K)
+                      rows_per_expert=cfg.T * cfg.K, label="dsv3_decode")
     assert res["expert_rows_checked"] == cfg.T * cfg.K
     n_exp = int((run.loads > 0).sum())
     say(f"decode: {n_exp} distinct experts touched; {res}")
@@ -128,7 +128,8 @@ def test_dsv3_skewed_20_steps(dsv3, golden_dir):
             # two rows of every expert on the first step, all rows of 4 experts on the last
             res = check_layer(view, h, b_before, cfg.gamma, run, n_tok_sample=8,
                               seed=10 + step, n_exp_sample=4,
-                              rows_per_expert=2 if step == 0 else None)
+                              rows_per_expert=2 if step == 0 else None,
+                              label=f"dsv3_skewed step {step}")
             b = res["b_new"]
         else:
             run.forward(h, b, cfg.gamma)
