@@ -316,77 +316,96 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(int n_groups, int row
 
 enum { kTrCopy = 0, kTrAct = 1 };
 
-// Transposes the rows of one row tile (<= 128 grouped rows of one expert) and
-// 64 source columns into the expert's [C, mpad] block: dst column = the row's
-// position inside its expert.  The expert's last tile also writes the zero
-// padding columns.  kTrAct: the source value is SiLU(a) * u from src = [a | u]
-// (ld 2C).  Grid (tiles, C / 64), 256 threads.  Global traffic is in 16-byte
-// pieces both ways (8 columns of a source row in, 8 consecutive block columns
-// of a destination row out; tile starts inside an expert and the padded widths
-// are multiples of 64), transposed through LDS.
+// Transposes the rows of one 256-row tile (rows m0 .. m0 + nr of one expert)
+// and 64 source columns into the expert's [C, mpad] block: block column = the
+// row's position inside its expert.  The expert's last tile also writes the
+// zero padding columns.  kTrAct: the source value is SiLU(a) * u from src =
+// [a | u] (ld 2C).  Grid (tiles, C / 64), 256 threads.
+//
+// Load: each thread takes one 8-column piece (16 bytes) of 8 rows -- rows 2p,
+// 2p + 1 of four 64-row bands -- with all eight loads issued before any is
+// used.  LDS: [64 columns][256 rows], element (c, r) at row position
+// r ^ (16 (c >> 3)); a thread writes each of its columns for its row pair as
+// one 32-bit word, and the XOR puts the 64 lanes' words of one write in 64
+// distinct banks.  The XOR leaves bits 0-2 of r alone, so any 8 consecutive
+// rows of a column stay one aligned 16-byte piece.  Store: 16-byte pieces of
+// the block rows, consecutive lanes along a row.
 template <int TR>
 __global__ __launch_bounds__(256) void pad_transpose_kernel(
     int C, int rows, int src_rows, const TileInfo* __restrict__ tiles,
-    const int32_t* __restrict__ meta, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ kpad, const int32_t* __restrict__ row_index,
-    const uint16_t* __restrict__ src, int ld_src, uint16_t* __restrict__ dst) {
-  constexpr int kTR = kBM + 8;  // LDS row: 128 tile rows + 16 bytes of skew
-  __shared__ __attribute__((aligned(16))) uint16_t t[64][kTR];
+    const int32_t* __restrict__ meta, const int32_t* __restrict__ kpad,
+    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ src, int ld_src,
+    uint16_t* __restrict__ dst) {
+  constexpr int kTM = 256;  // rows of a tile
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][kTM];
   if (static_cast<int>(blockIdx.x) >= meta[0]) return;
   const TileInfo ti = tiles[blockIdx.x];
   const int g = ti.group;
   const int m0 = ti.m0;
-  const int nr = min(ti.m1 - ti.m0, kBM);
+  const int nr = min(ti.m1 - ti.m0, kTM);
   const int c0 = blockIdx.y * 64;
-  const int gstart = offsets[g];
+  const int p0 = m0 - tiles[ti.gstart].m0;  // first block column of this tile (a multiple of 256)
   const int mpad = kpad[g + 1] - kpad[g];
   uint16_t* blk = dst + static_cast<size_t>(kpad[g]) * C;  // [C, mpad]
-  // load: rows m0..m0+nr, columns c0..c0+63, one 16-byte piece (8 columns) per step
-  for (int q = threadIdx.x; q < kBM * 8; q += 256) {
-    const int r = q / 8, c8 = (q % 8) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < nr && c0 + c8 < C) {
-      const int gr = m0 + r;
-      const int sr = row_index ? row_index[gr] : gr;
-      if (sr >= 0 && sr < src_rows) {
-        const uint16_t* sp = src + static_cast<size_t>(sr) * ld_src + c0 + c8;
-        if (TR == kTrAct) {
-          const uint4 av = *reinterpret_cast<const uint4*>(sp);
-          const uint4 uv = *reinterpret_cast<const uint4*>(sp + C);
-          const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-          uint32_t o[4];
+  const int tid = threadIdx.x;
+  const int c8 = tid & 7;     // 8-column piece
+  const int pr = tid >> 3;    // row pair 0..31
+  uint4 v[4][2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float lo = silu(__uint_as_float(aw[i] << 16)) * __uint_as_float(uw[i] << 16);
-            const float hi = silu(__uint_as_float(aw[i] & 0xffff0000u)) *
-                             __uint_as_float(uw[i] & 0xffff0000u);
-            o[i] = pack_bf16x2(lo, hi);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 64 * i + 2 * pr + h;
+      v[i][h] = make_uint4(0, 0, 0, 0);
+      if (r < nr && c0 + 8 * c8 < C) {
+        const int gr = m0 + r;
+        const int sr = row_index ? row_index[gr] : gr;
+        if (sr >= 0 && sr < src_rows) {
+          const uint16_t* sp = src + static_cast<size_t>(sr) * ld_src + c0 + 8 * c8;
+          if (TR == kTrAct) {
+            const uint4 av = *reinterpret_cast<const uint4*>(sp);
+            const uint4 uv = *reinterpret_cast<const uint4*>(sp + C);
+            const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float lo = silu(__uint_as_float(aw[q] << 16)) * __uint_as_float(uw[q] << 16);
+              const float hi = silu(__uint_as_float(aw[q] & 0xffff0000u)) *
+                               __uint_as_float(uw[q] & 0xffff0000u);
+              o[q] = pack_bf16x2(lo, hi);
+            }
+            v[i][h] = make_uint4(o[0], o[1], o[2], o[3]);
+          } else {
+            v[i][h] = *reinterpret_cast<const uint4*>(sp);
           }
-          v = make_uint4(o[0], o[1], o[2], o[3]);
-        } else {
-          v = *reinterpret_cast<const uint4*>(sp);
         }
       }
     }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int swz = 16 * c8;  // the XOR of every column this thread writes (c >> 3 == c8)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      t[c8 + 2 * i][r] = static_cast<uint16_t>(w[i] & 0xffffu);
-      t[c8 + 2 * i + 1][r] = static_cast<uint16_t>(w[i] >> 16);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo[4] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w};
+    const uint32_t hi[4] = {v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+    const int rpos = (64 * i + 2 * pr) ^ swz;  // even: the pair is one aligned word
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t a = (j & 1) ? (lo[j / 2] >> 16) : (lo[j / 2] & 0xffffu);
+      const uint32_t b = (j & 1) ? (hi[j / 2] >> 16) : (hi[j / 2] & 0xffffu);
+      *reinterpret_cast<uint32_t*>(&t[8 * c8 + j][rpos]) = a | (b << 16);
     }
   }
   __syncthreads();
-  const int p0 = m0 - gstart;  // first column of this tile inside the expert block
-  const bool last = ti.m1 - m0 <= kBM;
-  const int width = last ? mpad - p0 : nr;  // the last tile also writes the padding
-  // width <= 128 (the padding rounds the last tile's rows up to 64), and LDS
-  // rows past nr hold the zeros the load wrote for them
+  const bool last = ti.m1 - m0 <= kTM;
+  // the last tile also writes the padding: width = mpad - p0 <= 256, a multiple
+  // of 64; LDS rows past nr hold the zeros loaded for them
+  const int width = last ? mpad - p0 : nr;
   const int w8 = width / 8;
-  for (int q = threadIdx.x; q < 64 * w8; q += 256) {
-    const int c = q / w8, r8 = (q % w8) * 8;
+  for (int q = tid; q < 64 * w8; q += 256) {
+    const int c = q / w8, r8 = q - c * w8;
     if (c0 + c >= C) continue;
-    *reinterpret_cast<uint4*>(blk + static_cast<size_t>(c0 + c) * mpad + p0 + r8) =
-        *reinterpret_cast<const uint4*>(&t[c][r8]);
+    const int pos = (8 * r8) ^ (16 * (c >> 3));
+    *reinterpret_cast<uint4*>(blk + static_cast<size_t>(c0 + c) * mpad + p0 + 8 * r8) =
+        *reinterpret_cast<const uint4*>(&t[c][pos]);
   }
 }
 
@@ -977,27 +996,35 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
                                   uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, void* ws,
                                   hipStream_t s) {
   BwdWorkspace w = bwd_layout(ws, n_groups, d, f, rows);
-  SwigluWorkspace tl{};
-  tl.tiles = w.tiles.tiles;
-  tl.group_tile_start = w.tiles.group_tile_start;
-  tl.meta = w.tiles.meta;
-  hipError_t err = launch_build_tiles(n_groups, rows, kBM, offsets, tl, s);
+  // one 256-row tile list serves the activation-gradient products and the
+  // transposes; the 128-row list only the a | u recompute
+  SwigluWorkspace t256{};
+  t256.tiles = w.tiles256.tiles;
+  t256.group_tile_start = w.tiles256.group_tile_start;
+  t256.meta = w.tiles256.meta;
+  hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, t256, s);
   if (err != hipSuccess) return err;
-  const int max_tiles = max_tiles_for(rows, n_groups, kBM);
+  const int max_tiles256 = max_tiles_for(rows, n_groups, 256);
   ProfScope prof_(s, "swiglu_backward");
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, n_groups, rows, offsets,
                      w.kpad);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  GemmArgs a{};
-  a.tiles = tl.tiles;
-  a.meta = tl.meta;
-  a.n_groups = n_groups;
-  a.row_index = row_index;
-  a.a_rows = x_rows;
   // 1. a = x W_gate^T, u = x W_up^T  -> au [rows, 2f], unless the forward
   //    pass stored them
   if (au == nullptr) {
+    SwigluWorkspace tl{};
+    tl.tiles = w.tiles.tiles;
+    tl.group_tile_start = w.tiles.group_tile_start;
+    tl.meta = w.tiles.meta;
+    if ((err = launch_build_tiles(n_groups, rows, kBM, offsets, tl, s)) != hipSuccess) return err;
+    const int max_tiles = max_tiles_for(rows, n_groups, kBM);
+    GemmArgs a{};
+    a.tiles = tl.tiles;
+    a.meta = tl.meta;
+    a.n_groups = n_groups;
+    a.row_index = row_index;
+    a.a_rows = x_rows;
     a.N = f; a.K = d; a.NT = (f + kBN - 1) / kBN;
     a.A = x; a.lda = d;
     a.ldb = d; a.b_stride = static_cast<size_t>(f) * d;
@@ -1010,14 +1037,10 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   }
   // 2. d act = dy W_down (B = W_down^T [f, d]) -> [rows, f], held in the daT
   //    region (rpad >= rows; daT is written only in step 4), with the forward
-  //    pass's down-direction kernels over 256-row tiles; then da, du -> dadu
-  SwigluWorkspace t256{};
-  t256.tiles = w.tiles256.tiles;
-  t256.group_tile_start = w.tiles256.group_tile_start;
-  t256.meta = w.tiles256.meta;
+  //    pass's down-direction kernels over the 256-row tiles; then da, du -> dadu
   uint16_t* dact = w.daT;
   if ((err = launch_grouped_nt_bf16(n_groups, d, f, rows, offsets, t256, dy, wd_t, dact,
-                                    "bwd_dact_bf16", s)) != hipSuccess)
+                                    "bwd_dact_bf16", s, /*tiles_built=*/true)) != hipSuccess)
     return err;
   {
     const long n8 = static_cast<long>(rows) * (f / 8);
@@ -1029,21 +1052,22 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
   }
   // 3. dx = [da | du] [W_gate^T | W_up^T]^T  (K = 2f, B = [d, 2f]) -> dx [rows, d]
   if ((err = launch_grouped_nt_bf16(n_groups, 2 * f, d, rows, offsets, t256, w.dadu, wgu_t, dx,
-                                    "bwd_dx_bf16", s)) != hipSuccess)
+                                    "bwd_dx_bf16", s, /*tiles_built=*/true)) != hipSuccess)
     return err;
   // 4. per-expert transposed activations (rows padded to 64 per expert)
   {
-    dim3 gd(max_tiles, (d + 63) / 64), gf(max_tiles, (f + 63) / 64);
+    ProfScope pt_(s, "bwd_transpose");
+    dim3 gd(max_tiles256, (d + 63) / 64), gf(max_tiles256, (f + 63) / 64);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gd, dim3(256), 0, s, d, rows, x_rows,
-                       tl.tiles, tl.meta, offsets, w.kpad, row_index, x, d, w.xT);
+                       t256.tiles, t256.meta, w.kpad, row_index, x, d, w.xT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gd, dim3(256), 0, s, d, rows, rows,
-                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, dy, d, w.dyT);
+                       t256.tiles, t256.meta, w.kpad, nullptr, dy, d, w.dyT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrAct>, gf, dim3(256), 0, s, f, rows, rows,
-                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, au, 2 * f, w.actT);
+                       t256.tiles, t256.meta, w.kpad, nullptr, au, 2 * f, w.actT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gf, dim3(256), 0, s, f, rows, rows,
-                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.dadu, 2 * f, w.daT);
+                       t256.tiles, t256.meta, w.kpad, nullptr, w.dadu, 2 * f, w.daT);
     hipLaunchKernelGGL(pad_transpose_kernel<kTrCopy>, gf, dim3(256), 0, s, f, rows, rows,
-                       tl.tiles, tl.meta, offsets, w.kpad, nullptr, w.dadu + f, 2 * f, w.duT);
+                       t256.tiles, t256.meta, w.kpad, nullptr, w.dadu + f, 2 * f, w.duT);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // 5. weight gradients, K = the expert's (padded) rows

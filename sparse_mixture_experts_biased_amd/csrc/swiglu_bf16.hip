@@ -1796,9 +1796,12 @@ hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_ro
 
 hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
                                   const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
-                                  uint16_t* C, const char* name, hipStream_t s) {
-  hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, w, s);
-  if (err != hipSuccess) return err;
+                                  uint16_t* C, const char* name, hipStream_t s,
+                                  bool tiles_built) {
+  if (!tiles_built) {
+    hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, w, s);
+    if (err != hipSuccess) return err;
+  }
   const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
   return launch_down<256, 256, 512, 2>(n_groups, K, N, rows, mfma_bound, w, A, W, nullptr, C,
                                        name, s);

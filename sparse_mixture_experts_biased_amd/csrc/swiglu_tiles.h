@@ -89,10 +89,12 @@ hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* off
 // Grouped C = A W[g]^T over the rows of each group (bf16, fp32 accumulation):
 // A [rows, K], W [n_groups, N, K], C [rows, N]; K a multiple of 64.  Builds a
 // 256-row tile list into w's tile arrays (sized by swiglu_layout with min_bm
-// <= 256) and runs the grouped SwiGLU's down-direction kernels.  `name` tags
-// the launch in the profile records.
+// <= 256; tiles_built: w already holds that list for these offsets) and runs
+// the grouped SwiGLU's down-direction kernels.  `name` tags the launch in the
+// profile records.
 hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
                                   const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
-                                  uint16_t* C, const char* name, hipStream_t s);
+                                  uint16_t* C, const char* name, hipStream_t s,
+                                  bool tiles_built = false);
 
 }  // namespace moe
