@@ -112,7 +112,7 @@ typedef struct {
  * selection ranks v = fl32(s + b); equal v -> the lower expert id is picked.
  * With MOE_SOFTMAX and a non-NULL b, the bias is added to p.  Deterministic.
  * Limits: 1 <= K <= min(E_r, MOE_MAX_TOPK), E_r <= 512, d_model % 8 == 0
- * (bf16 tokens: d_model % 32 == 0).
+ * (bf16 tokens: d_model % 32 == 0 and d_model <= 2^20).
  */
 size_t moe_route_workspace_size(int T, int d_model, int E_r, moe_dtype h_dtype);
 moe_status moe_route(int T, int d_model, int E_r, int K, moe_score_fn fn,

@@ -74,6 +74,9 @@ moe_status route_checked(const char* name, int T, int d_model, int E_r, int K, m
   if (h_dtype == MOE_BF16 && d_model % 32 != 0)
     return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 tokens need d_model %% 32 == 0 (got %d)", name,
                 d_model);
+  if (h_dtype == MOE_BF16 && d_model > (1 << 20))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: bf16 tokens need d_model <= 1048576 (got %d)", name,
+                d_model);
   if (!h || !e || !topk_idx || !gates || !loads)
     return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
   const bool stats = p_mean != nullptr;

@@ -304,80 +304,137 @@ __device__ __forceinline__ void split3(const float4& p, const float4& q, bf16x8_
 }
 
 // zpart[s][t][i] = sum over k in split s of h[t][k] * e[i][k].
-// Workgroup: 128 tokens x 128 experts, four waves in 2 x 2, each 64 x 64 as
-// 2 x 2 blocks of 32 x 32; operands straight from global memory (h rows and
-// e rows are both k-contiguous: one 16-byte / two 16-byte loads per lane).
-__global__ __launch_bounds__(256) void route_logits_mfma_kernel(int T, int d, int E, int klen,
+// Workgroup: 128 tokens x 128 experts, eight waves in 2 x 4, each 64 x 32 as
+// two blocks of 32 x 32; two waves per SIMD, so one wave's centroid split
+// (vector ALU) runs while the other's products occupy the matrix core.  k in
+// 64-wide slices staged through LDS with coalesced 16-byte loads (h: eight
+// lanes per 128-byte row of a slice; e in fp32: sixteen lanes per 256-byte
+// row), double-buffered: the next slice's loads are in flight in registers
+// while the current one is multiplied.  (Fragment loads straight from global
+// memory touch one cache line per row for every 16 bytes they bring, and that
+// request rate bounded the kernel.)  The 16-byte chunks of a row are
+// XOR-swizzled so fragment reads (32 rows, one chunk) and staging writes are
+// bank-conflict free; each centroid fragment (8 fp32) is split exactly into
+// its three bf16 parts after the read.
+constexpr int kZK = 64;       // k per slice
+constexpr int kZThreads = 512;
+__device__ __forceinline__ int zswz_h(int r, int c) {  // 128-byte rows, 8 chunks
+  return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+}
+__device__ __forceinline__ int zswz_e(int r, int c) {  // 256-byte rows, 16 chunks
+  return r * 256 + ((c ^ (r & 15)) << 4);
+}
+
+__global__ __launch_bounds__(kZThreads) void route_logits_mfma_kernel(int T, int d, int E, int klen,
                                                                 const uint16_t* __restrict__ h,
                                                                 const float* __restrict__ e,
-                                                                float* __restrict__ zpart) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+                                                                float* __restrict__ zpart,
+                                                                int32_t* __restrict__ lpad) {
+  constexpr int kHB = kZT * kZK * 2, kEB = kZE * kZK * 4, kStage = kHB + kEB;
+  __shared__ __attribute__((aligned(16))) char lds[2 * kStage];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   const int fr = lane & 31, fh = lane >> 5;
-  const int t_base = blockIdx.x * kZT + (wave >> 1) * 64;
-  const int e_base = blockIdx.y * kZE + (wave & 1) * 64;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int t0 = blockIdx.x * kZT, x0 = blockIdx.y * kZE;
   const int split = blockIdx.z;
-  const int k_begin = split * klen;
+  const size_t k_begin = static_cast<size_t>(split) * klen;
+  // the first workgroup clears the padded load counters the selection counts into
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = tid; i < E; i += kZThreads) lpad[static_cast<size_t>(i) * kLoadStride] = 0;
 
-  const uint16_t* hp[2];
-  const float* ep[2];
+  // Buffer descriptors based at the tile's first row: a row past T (or E)
+  // is past the descriptor's range and reads zeros, without a branch.  k past
+  // klen (the upper half of a last 32-wide slice) reads the next split's
+  // values, or zeros, and is replaced by zeros on the way into LDS.
+  const int h_rows = min(kZT, T - t0), e_rows = min(kZE, E - x0);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(h + static_cast<size_t>(t0) * d + k_begin), 0,
+      h_rows * d * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(e + static_cast<size_t>(x0) * d + k_begin), 0, e_rows * d * 4,
+      0x00020000);
+  // staging slots: h rows hr + 64 p (chunk hc), e rows er + 32 p (chunk ec)
+  const int hr = tid >> 3, hc = tid & 7;
+  const int er = tid >> 4, ec = tid & 15;
+  uint4 hv[2], ev[4];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int t = t_base + b * 32 + fr;
-    const int ex = e_base + b * 32 + fr;
-    hp[b] = (t < T) ? h + static_cast<size_t>(t) * d + k_begin + fh * 8 : nullptr;
-    ep[b] = (ex < E) ? e + static_cast<size_t>(ex) * d + k_begin + fh * 8 : nullptr;
-  }
-  f32x16_t acc[2][2];
+    for (int p = 0; p < 2; ++p)
+      hv[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rh, ((hr + 64 * p) * d + k0 + hc * 8) * 2, 0, 0));
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      ev[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            re, ((er + 32 * p) * d + k0 + ec * 4) * 4, 0, 0));
+  };
+  auto masked = [](const uint4& v, uint32_t m) {
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+  };
+  auto store = [&](char* st, int k0) {
+    const uint32_t hm = k0 + hc * 8 < klen ? ~0u : 0u, em = k0 + ec * 4 < klen ? ~0u : 0u;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      *reinterpret_cast<uint4*>(st + zswz_h(hr + 64 * p, hc)) = masked(hv[p], hm);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<uint4*>(st + kHB + zswz_e(er + 32 * p, ec)) = masked(ev[p], em);
+  };
+
+  f32x16_t acc[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[a][b][q] = 0.0f;
+    for (int q = 0; q < 16; ++q) acc[a][q] = 0.0f;
 
-  uint4 ha[2];
-  float4 e0[2], e1[2];
-#define MOE_FETCH(K)                                                                         \
-  do {                                                                                       \
-    _Pragma("unroll") for (int b = 0; b < 2; ++b) {                                          \
-      ha[b] = hp[b] ? *reinterpret_cast<const uint4*>(hp[b] + (K)) : make_uint4(0, 0, 0, 0);  \
-      e0[b] = ep[b] ? *reinterpret_cast<const float4*>(ep[b] + (K)) : make_float4(0, 0, 0, 0); \
-      e1[b] = ep[b] ? *reinterpret_cast<const float4*>(ep[b] + (K) + 4) : make_float4(0, 0, 0, 0); \
-    }                                                                                        \
-  } while (0)
-  MOE_FETCH(0);
-  for (int k = 0; k < klen; k += 16) {
-    bf16x8_t af[2], bh[2], bm[2], bl[2];
+  // klen is a multiple of 32.  Slice j + 1 is
+  // written to the other stage while slice j is multiplied: that stage was
+  // last read in step j - 1, which every wave finished before the barrier
+  // that ended it.
+  const int n_slices = (klen + kZK - 1) / kZK;
+  load(0);
+  store(lds, 0);
+  __syncthreads();
+  for (int j = 0; j < n_slices; ++j) {
+    const char* hs = lds + (j & 1) * kStage;
+    const char* es = hs + kHB;
+    const bool more = j + 1 < n_slices;
+    if (more) load((j + 1) * kZK);
+    // 16-k step st: A = tokens wm*64 + a*32 + fr (chunk 2st + fh), B =
+    // experts wn*32 + fr (fp32 chunks 4st + 2fh, 4st + 2fh + 1)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      af[b] = __builtin_bit_cast(bf16x8_t, ha[b]);
-      split3(e0[b], e1[b], bh[b], bm[b], bl[b]);
+    for (int st = 0; st < kZK / 16; ++st) {
+      bf16x8_t af[2], bh, bm, bl;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const bf16x8_t*>(
+            hs + zswz_h(wm * 64 + a * 32 + fr, 2 * st + fh));
+      const int r = wn * 32 + fr;
+      const float4 p0 = *reinterpret_cast<const float4*>(es + zswz_e(r, 4 * st + 2 * fh));
+      const float4 p1 = *reinterpret_cast<const float4*>(es + zswz_e(r, 4 * st + 2 * fh + 1));
+      split3(p0, p1, bh, bm, bl);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bl, acc[a], 0, 0, 0);
+        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bm, acc[a], 0, 0, 0);
+        acc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bh, acc[a], 0, 0, 0);
+      }
     }
-    if (k + 16 < klen) MOE_FETCH(k + 16);
+    if (more) store(lds + ((j + 1) & 1) * kStage, (j + 1) * kZK);
+    __syncthreads();
+  }
+  // D[row = token][col = expert]: lane (col + 32*((row/4)%2)), register (row%4) + 4*(row/8)
+  float* zs = zpart + static_cast<size_t>(split) * T * E;
+  const int ex = x0 + wn * 32 + fr;
+  if (ex < E) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bl[b], acc[a][b], 0, 0, 0);
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bm[b], acc[a][b], 0, 0, 0);
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bh[b], acc[a][b], 0, 0, 0);
+      for (int q = 0; q < 16; ++q) {
+        const int t = t0 + wm * 64 + a * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
+        if (t < T) zs[static_cast<size_t>(t) * E + ex] = acc[a][q];
       }
   }
-#undef MOE_FETCH
-  // D[row = token][col = expert]: lane (col + 32*((row/4)%2)), register (row%4) + 4*(row/8)
-  float* zs = zpart + static_cast<size_t>(split) * T * E;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int ex = e_base + b * 32 + fr;
-      if (ex >= E) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int t = t_base + a * 32 + 8 * (q >> 2) + 4 * fh + (q & 3);
-        if (t < T) zs[static_cast<size_t>(t) * E + ex] = acc[a][b][q];
-      }
-    }
 }
 
 // One wave per token: z = sum_s zpart[s] (fixed order), then selection.
@@ -397,11 +454,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(int T, int E, int K, in
 #pragma unroll
   for (int j = 0; j < EJ; ++j) {
     const int ex = lane + kWave * j;
-    float acc = 0.0f;
-    if (ex < E)
-      for (int s = 0; s < S; ++s) acc += zpart[(static_cast<size_t>(s) * T + t) * E + ex];
-    z[j] = acc;
+    z[j] = 0.0f;
     bias[j] = (b != nullptr && ex < E) ? b[ex] : 0.0f;
+  }
+  // partials of four splits in flight at once, added in split order
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float v[4][EJ];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < EJ; ++j) {
+        const int ex = lane + kWave * j;
+        v[u][j] = (s0 + u < S && ex < E)
+                      ? zpart[(static_cast<size_t>(s0 + u) * T + t) * E + ex]
+                      : 0.0f;
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < EJ; ++j)
+        if (s0 + u < S) z[j] += v[u][j];
   }
   select_token<EJ>(t, E, K, fn, z, bias, idx_out, gate_out, loads, kLoadStride, prow, lsq);
 }
@@ -414,11 +486,6 @@ __global__ __launch_bounds__(256) void compact_loads_kernel(int E, const int32_t
 }
 
 // Zeroes the strided counters.
-__global__ __launch_bounds__(256) void zero_strided_kernel(int n, int32_t* __restrict__ p) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[static_cast<size_t>(i) * kLoadStride] = 0;
-}
-
 // ------------------------------------------------------------ diagnostics
 
 constexpr int kStatChunk = 64;  // tokens per partial sum
@@ -497,7 +564,7 @@ int route_splits(int T, int d, int E, int h_bf16) {
   if (!h_bf16 || d % 32 != 0) return 0;
   const int tiles = ((T + kZT - 1) / kZT) * ((E + kZE - 1) / kZE);
   int S = 1;
-  while (tiles * S < 256 && S < 8 && d % (32 * 2 * S) == 0) S *= 2;
+  while (tiles * S < 256 && S < 16 && d % (32 * 2 * S) == 0) S *= 2;
   return S;
 }
 
@@ -570,12 +637,11 @@ hipError_t launch_route(int T, int d, int E, int K, int fn, const void* h, int h
   float* zpart = static_cast<float*>(ws);
   int32_t* lpad = reinterpret_cast<int32_t*>(
       static_cast<char*>(ws) + align_up(static_cast<size_t>(S) * T * E * sizeof(float), 256));
-  hipLaunchKernelGGL(zero_strided_kernel, dim3((E + 255) / 256), dim3(256), 0, s, E, lpad);
   {
     ProfScope prof_(s, "route_logits");
     dim3 grid((T + kZT - 1) / kZT, (E + kZE - 1) / kZE, S);
-    hipLaunchKernelGGL(route_logits_mfma_kernel, grid, dim3(256), 0, s, T, d, E, d / S,
-                       static_cast<const uint16_t*>(h), e, zpart);
+    hipLaunchKernelGGL(route_logits_mfma_kernel, grid, dim3(kZThreads), 0, s, T, d, E, d / S,
+                       static_cast<const uint16_t*>(h), e, zpart, lpad);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -55,6 +55,8 @@ def test_route_rejects_bad_arguments():
     assert lib.moe_route(64, 128, 8, 2, 0, P, 5, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_INVALID_ARG
     # bf16 tokens run the matrix-core logits: d_model % 32 and a workspace are required
     assert lib.moe_route(64, 136, 8, 2, 0, P, 1, P, None, P, P, P, P, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    rc, msg = _st(lib.moe_route(64, (1 << 20) + 32, 8, 2, 0, P, 1, P, None, P, P, P, P, 1 << 40, None))
+    assert rc == L.MOE_ERR_UNSUPPORTED and "1048576" in msg
     need = L.moe_route_workspace_size(4096, 7168, 256, L.MOE_BF16)
     assert need >= 4096 * 256 * 4
     rc, msg = _st(lib.moe_route(4096, 7168, 256, 8, 0, P, 1, P, None, P, P, P, P, need - 1, None))

@@ -65,6 +65,8 @@ ROUTE_CASES = [
     (40, 128, 12, 12, "sigmoid", torch.float32, "uniform"),   # K = E_r
     (129, 256, 512, 16, "sigmoid", torch.bfloat16, "uniform"),
     (90, 128, 32, 4, "softmax", torch.float32, "uniform"),    # softmax + bias on p
+    (300, 1792, 256, 8, "sigmoid", torch.bfloat16, "uniform"),  # 3.5 k-slices per split
+    (32768, 320, 128, 8, "sigmoid", torch.bfloat16, "uniform"),  # one split, 5 k-slices
 ]
 
 
