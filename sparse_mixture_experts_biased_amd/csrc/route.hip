@@ -150,20 +150,9 @@ __device__ __forceinline__ void select_token(int t, int E, int K, int fn, const 
       sv[k] = sj;
     }
   }
-  // ascending expert id (sentinel ids sort last)
-#pragma unroll
-  for (int a = 0; a < MOE_MAX_TOPK_DEV - 1; ++a)
-#pragma unroll
-    for (int c = 0; c < MOE_MAX_TOPK_DEV - 1 - a; ++c)
-      if (sel[c] > sel[c + 1]) {
-        int ti = sel[c]; sel[c] = sel[c + 1]; sel[c + 1] = ti;
-        float tf = sv[c]; sv[c] = sv[c + 1]; sv[c + 1] = tf;
-      }
-  float den = 0.0f;
-#pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
-    if (k < K) den += sv[k];
-  den = fmaxf(den, 1e-12f);
+  // ascending expert id: lane k < K takes pick k and counts the picks that
+  // order before it (a tie, reachable only with non-finite scores, goes by
+  // pick order), then one lane permute puts pick k on the lane of its rank
   int my_id = 0;
   float my_s = 0.0f;
 #pragma unroll
@@ -172,6 +161,21 @@ __device__ __forceinline__ void select_token(int t, int E, int K, int fn, const 
       my_id = sel[k];
       my_s = sv[k];
     }
+  int rank = lane;  // lanes >= K keep their place
+  if (lane < K) {
+    rank = 0;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+      if (k < K) rank += (sel[k] < my_id || (sel[k] == my_id && k < lane)) ? 1 : 0;
+  }
+  my_id = __builtin_amdgcn_ds_permute(rank * 4, my_id);
+  my_s = __int_as_float(__builtin_amdgcn_ds_permute(rank * 4, __float_as_int(my_s)));
+  // the gate denominator in ascending id order
+  float den = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (k < K) den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+  den = fmaxf(den, 1e-12f);
   if (lane < K) {
     idx_out[static_cast<size_t>(t) * K + lane] = my_id;
     gate_out[static_cast<size_t>(t) * K + lane] = my_s / den;
