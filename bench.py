@@ -51,6 +51,50 @@ def algorithmic(cfg, n_touched, n_touched_shared, rows=None):
     return gateup_bytes, gateup_flops, layer_bytes, layer_flops
 
 
+def stage_rooflines(cfg, stages, n_touched, rows):
+    """Achieved rate of the non-GEMM stages and of the down launch against
+    their bound, from the library's per-stage event times (ms per call).
+
+    Algorithmic bytes (staged intermediates such as the split-K logit
+    partials are overhead):
+      route   (logits + top-K): h read, centroids read, bias read, ids and
+              gates written; fp32-exact logits are 2 T d E_r flops, run as
+              three bf16 products each on the matrix cores
+      permute (histogram, scan, assignment): ids read, offsets, row_token
+              and slot_row written
+      combine: h, the shared outputs, K gathered rows read and y written,
+              plus ids and gates
+      routed.down: W_down of the touched experts, the activation read and
+              y_perm written
+    """
+    d, f, T, K, E, Es = cfg.d_model, cfg.d_ffn, cfg.T, cfg.K, cfg.E_r, cfg.E_s
+    eb = 2 if cfg.dtype == "bf16" else 4
+    out = {}
+
+    def put(name, ms, nbytes, flops=None, mfma_mult=None):
+        if not ms:
+            return
+        rec = dict(ms=round(ms, 5), algorithmic_bytes=int(nbytes),
+                   hbm_gbs=round(nbytes / ms / 1e6, 1),
+                   hbm_frac=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4))
+        if flops is not None:
+            rec["flops"] = flops
+            if mfma_mult:
+                rec["mfma_tflops"] = round(flops * mfma_mult / ms / 1e9, 1)
+                rec["mfma_frac"] = round(flops * mfma_mult / ms / 1e9 / BF16_PEAK_TFLOPS, 4)
+        out[name] = rec
+
+    route_ms = stages.get("route_logits", 0.0) + stages.get("route_topk", 0.0)
+    route_bytes = T * d * eb + E * d * 4 + E * 4 + T * K * 8 + E * 4
+    put("route", route_ms, route_bytes, 2.0 * T * d * E, 3 if eb == 2 else None)
+    perm_ms = sum(stages.get(k, 0.0) for k in ("perm_hist", "perm_scan", "perm_assign"))
+    put("permute", perm_ms, T * K * 4 + (E + 1) * 4 + 2 * T * K * 4)
+    put("combine", stages.get("combine"), (K + Es + 2) * T * d * eb + T * K * 8)
+    put("routed.down", stages.get(f"routed.down_{cfg.dtype}"),
+        n_touched * d * f * eb + rows * (f + d) * eb, 2.0 * d * f * rows, 1)
+    return out
+
+
 def recorded_traffic(workload: str):
     """HBM bytes per routed gate/up launch from the FETCH_SIZE / WRITE_SIZE
     counter runs summarised in profiles/hbm_traffic_<workload>.md, already
@@ -493,7 +537,9 @@ def main(argv=None):
                                 f"rows per expert, {cfg.T * cfg.K - kept_rows} of "
                                 f"{cfg.T * cfg.K} copies dropped)"),
                    "tokens_per_step": cfg.T, "parallelism": "single GPU"},
-        "roofline": roofline, "layer": layer, "stages_ms": stages, "cpu_baseline": cpu,
+        "roofline": roofline, "layer": layer, "stages_ms": stages,
+        "stage_rooflines": stage_rooflines(cfg, stages, n_touched, kept_rows),
+        "cpu_baseline": cpu,
         "routing_vs_oracle": routing,
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
                     "max": round(step_ms[-1], 4)},

@@ -56,3 +56,22 @@ def test_cpu_baseline_large_budget_covers_every_expert(lay):
     assert f"{n} of {n} touched routed experts" in out["sample"]
     assert "time x1)" in out["sample"]
     assert routing["tokens"] == CFG.T and routing["flipped"] == 1
+
+
+def test_stage_rooflines_bytes_and_fractions():
+    cfg = CONFIGS["dsv3_prefill"]
+    T, d, K, E, f = cfg.T, cfg.d_model, cfg.K, cfg.E_r, cfg.d_ffn
+    stages = {"route_logits": 0.05, "route_topk": 0.02, "perm_hist": 0.01, "perm_scan": 0.01,
+              "perm_assign": 0.01, "combine": 0.1, "routed.down_bf16": 1.5}
+    r = bench.stage_rooflines(cfg, stages, n_touched=256, rows=T * K)
+    # combine: h, one shared output, K gathered rows read, y written (bf16), ids + gates
+    assert r["combine"]["algorithmic_bytes"] == (K + 3) * T * d * 2 + T * K * 8 == 646184960
+    assert r["combine"]["hbm_frac"] == pytest.approx(646184960 / 0.1e-3 / 8e12, abs=1e-4)
+    assert r["route"]["ms"] == pytest.approx(0.07)
+    assert r["route"]["algorithmic_bytes"] == T * d * 2 + E * d * 4 + 2 * E * 4 + T * K * 8
+    # fp32-exact logits, three bf16 products each on the matrix cores
+    assert r["route"]["mfma_tflops"] == pytest.approx(3 * 2 * T * d * E / 0.07e-3 / 1e12, rel=1e-3)
+    assert r["permute"]["ms"] == pytest.approx(0.03)
+    assert r["routed.down"]["algorithmic_bytes"] == 256 * d * f * 2 + T * K * (f + d) * 2
+    # a stage the run did not time is left out
+    assert "combine" not in bench.stage_rooflines(cfg, {"route_logits": 0.05}, 256, T * K)
