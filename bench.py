@@ -30,7 +30,7 @@ def log(msg):
     sys.stderr.flush()
 
 
-def algorithmic(cfg, n_touched, n_touched_shared, rows=None):
+def algorithmic(cfg, n_touched, n_touched_shared, rows=None, fused=False):
     """Algorithmic bytes / flops of the gate/up launch and of the whole layer.
 
     Per touched routed or shared expert: W_gate + W_up = 2 * d * f bf16 words
@@ -40,18 +40,20 @@ def algorithmic(cfg, n_touched, n_touched_shared, rows=None):
     intermediate, overhead against these bytes, as are x rows re-read per
     column tile.  Expert flops: 6 d f per row (2 d f each for gate, up and
     down), rows = T*K routed (the kept copies under a capacity) + T*E_s shared.
+    fused: the gate/up launch also runs the shared experts (moe_experts_swiglu).
     """
     d, f, T, K = cfg.d_model, cfg.d_ffn, cfg.T, cfg.K
     rows = T * K if rows is None else rows
     eb = 2 if cfg.dtype == "bf16" else 4
-    gateup_bytes = n_touched * 2 * d * f * eb + T * d * eb
-    gateup_flops = 4.0 * d * f * rows
+    gu_experts = n_touched + (n_touched_shared if fused else 0)
+    gateup_bytes = gu_experts * 2 * d * f * eb + T * d * eb
+    gateup_flops = 4.0 * d * f * (rows + (T * cfg.E_s if fused else 0))
     layer_bytes = (n_touched + n_touched_shared) * 3 * d * f * eb + 2 * T * d * eb
     layer_flops = 6.0 * d * f * (rows + T * cfg.E_s) + 2.0 * T * d * cfg.E_r
     return gateup_bytes, gateup_flops, layer_bytes, layer_flops
 
 
-def stage_rooflines(cfg, stages, n_touched, rows):
+def stage_rooflines(cfg, stages, n_touched, rows, fused=False):
     """Achieved rate of the non-GEMM stages and of the down launch against
     their bound, from the library's per-stage event times (ms per call).
 
@@ -65,7 +67,8 @@ def stage_rooflines(cfg, stages, n_touched, rows):
       combine: h, the shared outputs, K gathered rows read and y written,
               plus ids and gates
       routed.down: W_down of the touched experts, the activation read and
-              y_perm written
+              y_perm written (fused: experts.down, the shared experts' W_down
+              and rows included)
     """
     d, f, T, K, E, Es = cfg.d_model, cfg.d_ffn, cfg.T, cfg.K, cfg.E_r, cfg.E_s
     eb = 2 if cfg.dtype == "bf16" else 4
@@ -90,16 +93,20 @@ def stage_rooflines(cfg, stages, n_touched, rows):
     perm_ms = sum(stages.get(k, 0.0) for k in ("perm_hist", "perm_scan", "perm_assign"))
     put("permute", perm_ms, T * K * 4 + (E + 1) * 4 + 2 * T * K * 4)
     put("combine", stages.get("combine"), (K + Es + 2) * T * d * eb + T * K * 8)
-    put("routed.down", stages.get(f"routed.down_{cfg.dtype}"),
+    if fused:
+        n_touched, rows = n_touched + Es, rows + Es * T
+    name = "experts.down" if fused else "routed.down"
+    put(name, stages.get(f"{name}_{cfg.dtype}"),
         n_touched * d * f * eb + rows * (f + d) * eb, 2.0 * d * f * rows, 1)
     return out
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per routed gate/up launch from the FETCH_SIZE / WRITE_SIZE
-    counter runs summarised in profiles/hbm_traffic_<workload>.md, already
-    scaled by the copy calibration.  None when no such record exists or the
-    kernel sources changed since the counters were taken (their hash differs)."""
+def recorded_traffic(workload: str, launch: str = "routed.gateup_bf16"):
+    """HBM bytes per gate/up launch (`launch`: its stage name) from the
+    FETCH_SIZE / WRITE_SIZE counter runs summarised in
+    profiles/hbm_traffic_<workload>.md, already scaled by the copy calibration.
+    None when no such record exists or the kernel sources changed since the
+    counters were taken (their hash differs)."""
     import re
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
@@ -107,9 +114,10 @@ def recorded_traffic(workload: str):
     digest = kernel_source_hash()
     with open(path) as fh:
         for line in fh:
-            m = re.match(r"traffic routed\.gateup_bf16 (\S+) bytes=(\d+) .*sources=([0-9a-f]+)", line)
-            if m and m.group(1) == workload and digest.startswith(m.group(3)):
-                return int(m.group(2))
+            m = re.match(r"traffic (\S+) (\S+) bytes=(\d+) .*sources=([0-9a-f]+)", line)
+            if (m and m.group(1) == launch and m.group(2) == workload
+                    and digest.startswith(m.group(4))):
+                return int(m.group(3))
     return None
 
 
@@ -369,6 +377,9 @@ def main(argv=None):
     ap.add_argument("--serial-shared", action="store_true",
                     help="run the shared experts after the routed ones on one stream "
                          "(default: on a second stream beside the routing)")
+    ap.add_argument("--fused-shared", action="store_true",
+                    help="run the shared experts inside the routed experts' grouped launches "
+                         "(moe_experts_swiglu) instead of launches of their own")
     ap.add_argument("--diagnostics", action="store_true",
                     help="route with the router statistics and compute the balance diagnostics "
                          "(Switch f.P, z-loss, load entropy, MaxVio, dropped rate) every step")
@@ -422,7 +433,7 @@ def main(argv=None):
     run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
                    lay.ws_down, capacity_factor=args.capacity_factor,
                    overlap_shared=not args.serial_shared, shared_start=args.shared_start,
-                   diagnostics=args.diagnostics)
+                   diagnostics=args.diagnostics, fuse_shared=args.fused_shared)
     b = lay.b.clone() if lay.b is not None else None
     b_host0 = host_array(lay.b) if lay.b is not None else None
     gamma = cfg.gamma if b is not None else None
@@ -483,11 +494,16 @@ def main(argv=None):
     loads = run.loads.cpu().numpy()
     n_touched = int((loads > 0).sum())
     kept_rows = int(run.offsets[-1].item())
-    gu_bytes, gu_flops, layer_bytes, layer_flops = algorithmic(cfg, n_touched, cfg.E_s, kept_rows)
+    # the forward's expert launches: fused (routed + shared) unless a training
+    # forward or --unfused-shared kept them apart
+    fused = run.fuse_shared and dy is None
+    pfx = "experts." if fused else "routed."
+    gu_bytes, gu_flops, layer_bytes, layer_flops = algorithmic(cfg, n_touched, cfg.E_s, kept_rows,
+                                                               fused)
     stages = {k: round(v[1] / v[0], 5) for k, v in prof.items()}
     log("per-kernel average ms: " + json.dumps(stages))
     log(f"wall {wall * 1000:.2f} ms, events {ev_ms:.2f} ms over {args.steps} steps")
-    routed_ms = stages.get("routed.gateup_bf16")
+    routed_ms = stages.get(pfx + "gateup_bf16")
     sec = routed_ms / 1000.0
     gbs = gu_bytes / sec / 1e9
     tfs = gu_flops / sec / 1e12
@@ -500,9 +516,10 @@ def main(argv=None):
         roofline = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None)
     # the counter record covers the dispatch without a capacity limit
-    traffic = recorded_traffic(cfg.name) if run.capacity is None else None
+    traffic = recorded_traffic(cfg.name, pfx + "gateup_bf16") if run.capacity is None else None
     roofline["traffic"] = traffic
-    roofline.update(kernel="gateup_bf16 (routed experts)", avg_ms=round(routed_ms, 4),
+    roofline.update(kernel="gateup_bf16 (routed + shared experts)" if fused
+                    else "gateup_bf16 (routed experts)", avg_ms=round(routed_ms, 4),
                     algorithmic_bytes=gu_bytes, algorithmic_flops=gu_flops,
                     hbm_gbs=round(gbs, 1), mfma_tflops=round(tfs, 1),
                     mfma_frac=round(tfs / BF16_PEAK_TFLOPS, 4))
@@ -538,7 +555,7 @@ def main(argv=None):
                                 f"{cfg.T * cfg.K} copies dropped)"),
                    "tokens_per_step": cfg.T, "parallelism": "single GPU"},
         "roofline": roofline, "layer": layer, "stages_ms": stages,
-        "stage_rooflines": stage_rooflines(cfg, stages, n_touched, kept_rows),
+        "stage_rooflines": stage_rooflines(cfg, stages, n_touched, kept_rows, fused),
         "cpu_baseline": cpu,
         "routing_vs_oracle": routing,
         "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),

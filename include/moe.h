@@ -270,6 +270,49 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
                               void* stream);
 
 /*
+ * moe_experts_swiglu -- the routed and the shared experts of one layer in one
+ * grouped launch per product (gate/up, then down).
+ *
+ * Defined by: Sparse MoE routing-math page, section 0 (layer output: the
+ * always-active shared experts beside the gated routed experts; SwiGLU
+ * expert) and section 3 (all local experts in one grouped GEMM over
+ * variable-sized token buckets).  The same per-row results as
+ * moe_grouped_swiglu on the routed rows followed by moe_grouped_swiglu on the
+ * shared rows; one launch lets the shared experts' matrix-core work run on
+ * the CUs beside the routed experts' weight streaming.
+ *
+ *   E_r, E_s   routed and shared experts (E_s = 0 allowed)
+ *   T, K       tokens and picks per token
+ *   offsets    [E_r + 1] int32 device, from moe_permute / moe_permute_capacity
+ *   row_token  [T*K] int32 device, from the same call
+ *   h          [T, d_model] tokens, fp32 or bf16 (dtype)
+ *   w_gate, w_up [E_r, d_ffn, d_model]; w_down [E_r, d_model, d_ffn]
+ *   ws_gate, ws_up [E_s, d_ffn, d_model]; ws_down [E_s, d_model, d_ffn]
+ *              (may be NULL when E_s = 0)
+ *   y          [T*K + E_s*T, d_model] out: rows 0 .. T*K-1 are y_perm (routed
+ *              row r = expert output for row_token[r]; rows past offsets[E_r]
+ *              are not written), then shared expert j's output for token t at
+ *              row T*K + j*T + t -- so y + T*K*d_model is moe_combine's
+ *              y_shared and y its y_perm
+ *   workspace  device scratch of at least moe_experts_swiglu_workspace_size()
+ *              bytes (the combined row index, activations, tile list)
+ * bf16: fp32 accumulation on the matrix cores, activations and y rounded to
+ * bf16; fp32 runs the two sets of experts as two grouped launches.
+ * Limits: those of moe_grouped_swiglu with rows = T*K + E_s*T and x = h;
+ * E_r, E_s <= MOE_MAX_EXPERTS; bf16 also needs E_r + 8*E_s row groups or
+ * fewer, at most 2048 (MOE_ERR_UNSUPPORTED otherwise; separate
+ * moe_grouped_swiglu calls then serve).
+ */
+size_t moe_experts_swiglu_workspace_size(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                                         moe_dtype dtype);
+moe_status moe_experts_swiglu(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                              const int32_t* offsets, const int32_t* row_token, const void* h,
+                              moe_dtype dtype, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * moe_grouped_swiglu_noalloc -- moe_grouped_swiglu that allocates nothing, for
  * callers that cannot allocate device memory or take a workspace: code under
  * HIP graph capture, tight serving loops (decode-sized batches), harnesses

@@ -22,7 +22,8 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size
             "moe_combine_backward", "moe_grouped_swiglu_backward_workspace_size",
             "moe_grouped_swiglu_backward", "moe_route_backward",
             "moe_grouped_swiglu_workspace_size", "moe_grouped_swiglu",
-            "moe_grouped_swiglu_train", "moe_grouped_swiglu_noalloc", "moe_combine",
+            "moe_grouped_swiglu_train", "moe_grouped_swiglu_noalloc",
+            "moe_experts_swiglu_workspace_size", "moe_experts_swiglu", "moe_combine",
             "moe_bias_update", "moe_calib_mfma_loop", "moe_calib_stream_read",
             "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
             "moe_version"]
@@ -81,6 +82,9 @@ def load() -> ctypes.CDLL:
         "moe_grouped_swiglu_workspace_size": ([_i, _i, _i, _i, _i], _sz),
         "moe_grouped_swiglu": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
                                 _sz, _p], _i),
+        "moe_experts_swiglu_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+        "moe_experts_swiglu": ([_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p, _p,
+                                _p, _p, _sz, _p], _i),
         "moe_grouped_swiglu_train": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p,
                                       _p, _p, _sz, _p], _i),
         "moe_grouped_swiglu_noalloc": ([_i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p, _p,
@@ -205,6 +209,19 @@ def moe_grouped_swiglu(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_inde
                                      _ptr(row_index), _ptr(x), dtype, _ptr(w_gate), _ptr(w_up),
                                      _ptr(w_down), _ptr(row_scale), _ptr(y), _ptr(workspace),
                                      workspace_bytes, _stream(stream)))
+
+
+def moe_experts_swiglu_workspace_size(E_r, E_s, T, K, d_model, d_ffn, dtype) -> int:
+    return int(load().moe_experts_swiglu_workspace_size(E_r, E_s, T, K, d_model, d_ffn, dtype))
+
+
+def moe_experts_swiglu(E_r, E_s, T, K, d_model, d_ffn, offsets, row_token, h, dtype, w_gate,
+                       w_up, w_down, ws_gate, ws_up, ws_down, y, workspace, workspace_bytes,
+                       stream=None):
+    _check(load().moe_experts_swiglu(E_r, E_s, T, K, d_model, d_ffn, _ptr(offsets),
+                                     _ptr(row_token), _ptr(h), dtype, _ptr(w_gate), _ptr(w_up),
+                                     _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
+                                     _ptr(y), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def moe_grouped_swiglu_train(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x,

@@ -64,6 +64,16 @@ def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
+def is_stale(lib_path: str) -> bool:
+    """True when lib_path is missing or older than a source it is built from."""
+    if not os.path.exists(lib_path):
+        return True
+    t = os.path.getmtime(lib_path)
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + \
+        [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    return any(os.path.getmtime(f) > t for f in srcs)
+
+
 def build(jobs: int = 8, verbose: bool = False, sanitize: bool = False) -> str:
     build_dir = SAN_BUILD if sanitize else BUILD
     lib_path = SAN_LIB_PATH if sanitize else LIB_PATH

@@ -280,6 +280,121 @@ moe_status moe_grouped_swiglu(int n_groups, int d_model, int d_ffn, int rows, in
                         workspace, workspace_bytes, stream);
 }
 
+// ---- routed and shared experts in one call
+
+namespace {
+
+// fp32: the combined row index, the shared offsets, then one grouped
+// workspace that the routed and the shared launches use in turn.
+struct ExpertsF32Layout {
+  int32_t* row_index;
+  int32_t* sh_off;
+  void* ws;
+  size_t bytes;
+};
+ExpertsF32Layout experts_f32_layout(void* base, int E_r, int E_s, int T, int K, int d_model,
+                                    int d_ffn) {
+  const int TK = T * K, rows = TK + E_s * T;
+  const size_t ri = moe::align_up(static_cast<size_t>(rows) * 4, 256);
+  const size_t so = moe::align_up(static_cast<size_t>(E_s + 1) * 4, 256);
+  size_t w = moe::swiglu_workspace_bytes(E_r, d_model, d_ffn, TK, 0);
+  if (E_s > 0) w = std::max(w, moe::swiglu_workspace_bytes(E_s, d_model, d_ffn, E_s * T, 0));
+  char* b = static_cast<char*>(base);
+  return ExpertsF32Layout{b ? reinterpret_cast<int32_t*>(b) : nullptr,
+                          b ? reinterpret_cast<int32_t*>(b + ri) : nullptr,
+                          b ? b + ri + so : nullptr, ri + so + w};
+}
+
+size_t experts_workspace_bytes(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                               moe_dtype dtype) {
+  if (dtype == MOE_BF16) return moe::experts_layout(nullptr, E_r, E_s, T, K, d_ffn).bytes;
+  return experts_f32_layout(nullptr, E_r, E_s, T, K, d_model, d_ffn).bytes;
+}
+
+bool experts_shape_ok(int E_r, int E_s, int T, int K, int d_model, int d_ffn) {
+  return E_r >= 1 && E_s >= 0 && T >= 1 && K >= 1 && K <= E_r && d_model >= 1 && d_ffn >= 1 &&
+         E_r <= MOE_MAX_EXPERTS && E_s <= MOE_MAX_EXPERTS &&
+         static_cast<long long>(T) * (K + E_s) <= INT32_MAX;
+}
+
+}  // namespace
+
+size_t moe_experts_swiglu_workspace_size(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                                         moe_dtype dtype) {
+  if (!experts_shape_ok(E_r, E_s, T, K, d_model, d_ffn) || !valid_dtype(dtype)) return 0;
+  return experts_workspace_bytes(E_r, E_s, T, K, d_model, d_ffn, dtype);
+}
+
+moe_status moe_experts_swiglu(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                              const int32_t* offsets, const int32_t* row_token, const void* h,
+                              moe_dtype dtype, const void* w_gate, const void* w_up,
+                              const void* w_down, const void* ws_gate, const void* ws_up,
+                              const void* ws_down, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_experts_swiglu";
+  if (!experts_shape_ok(E_r, E_s, T, K, d_model, d_ffn))
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s: E_r=%d E_s=%d T=%d K=%d d_model=%d d_ffn=%d (need E_r, T, K, d_model, d_ffn "
+                ">= 1, E_s >= 0, K <= E_r, E_r and E_s <= %d, T*(K+E_s) <= INT32_MAX)",
+                fn, E_r, E_s, T, K, d_model, d_ffn, MOE_MAX_EXPERTS);
+  if (!valid_dtype(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: bad dtype", fn);
+  if (!offsets || !row_token || !h || !w_gate || !w_up || !w_down || !y || !workspace)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (E_s > 0 && (!ws_gate || !ws_up || !ws_down))
+    return fail(MOE_ERR_INVALID_ARG, "%s: null shared-expert weights with E_s=%d", fn, E_s);
+  const int TK = T * K, rows = TK + E_s * T;
+  const int align = dtype == MOE_BF16 ? 64 : 16;
+  if (d_model % align || d_ffn % align)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d_model=%d and d_ffn=%d must be multiples of %d", fn,
+                d_model, d_ffn, align);
+  if (static_cast<long long>(rows) * d_ffn > (1LL << 40) ||
+      static_cast<long long>(d_model) * d_ffn > INT32_MAX)
+    return fail(MOE_ERR_INVALID_ARG, "%s: sizes overflow", fn);
+  if (dtype == MOE_BF16) {
+    const long long lim = (1LL << 31) - 1;
+    if (2LL * T * d_model > lim || 2LL * rows * d_ffn > lim || 2LL * d_model * d_ffn > lim)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "%s: bf16 operands must each be under 2 GiB "
+                  "(h %lld, activations %lld, one weight matrix %lld bytes)",
+                  fn, 2LL * T * d_model, 2LL * rows * d_ffn, 2LL * d_model * d_ffn);
+    const int n_groups = moe::experts_layout(nullptr, E_r, E_s, T, K, d_ffn).n_groups;
+    if (n_groups > moe::kMaxExpertGroups)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: %d row groups > %d (E_r=%d, E_s=%d)", fn, n_groups,
+                  moe::kMaxExpertGroups, E_r, E_s);
+  }
+  const size_t need = experts_workspace_bytes(E_r, E_s, T, K, d_model, d_ffn, dtype);
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  hipStream_t s = as_stream(stream);
+  hipError_t err;
+  if (dtype == MOE_BF16) {
+    err = moe::launch_experts_bf16(
+        E_r, E_s, T, K, d_model, d_ffn, offsets, row_token, static_cast<const uint16_t*>(h),
+        static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+        static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(ws_gate),
+        static_cast<const uint16_t*>(ws_up), static_cast<const uint16_t*>(ws_down),
+        static_cast<uint16_t*>(y), workspace, s);
+    return hip_status(err, fn);
+  }
+  // fp32: the routed experts, then the shared ones, as two grouped launches
+  const ExpertsF32Layout L = experts_f32_layout(workspace, E_r, E_s, T, K, d_model, d_ffn);
+  err = moe::launch_experts_rows(T, K, E_s, row_token, L.row_index, L.sh_off, s);
+  if (err == hipSuccess)
+    err = moe::launch_swiglu_f32(E_r, d_model, d_ffn, TK, T, offsets, L.row_index,
+                                 static_cast<const float*>(h), static_cast<const float*>(w_gate),
+                                 static_cast<const float*>(w_up),
+                                 static_cast<const float*>(w_down), nullptr,
+                                 static_cast<float*>(y), L.ws, s);
+  if (err == hipSuccess && E_s > 0)
+    err = moe::launch_swiglu_f32(E_s, d_model, d_ffn, E_s * T, T, L.sh_off, L.row_index + TK,
+                                 static_cast<const float*>(h), static_cast<const float*>(ws_gate),
+                                 static_cast<const float*>(ws_up),
+                                 static_cast<const float*>(ws_down), nullptr,
+                                 static_cast<float*>(y) + static_cast<size_t>(TK) * d_model,
+                                 L.ws, s);
+  return hip_status(err, fn);
+}
+
 // ---- the form that allocates nothing: its workspace is one file-scope device
 // array per GPU, found once per device with hipGetSymbolAddress.  In host code
 // `scratch` only names the symbol; kernels get the address from g_scratch.

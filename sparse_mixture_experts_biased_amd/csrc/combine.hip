@@ -71,14 +71,17 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
       const_cast<uint16_t*>(ysh + (E_s > 0 ? static_cast<size_t>(t) * d : 0)), 0,
       E_s > 0 ? d * 2 : 0, 0x00020000);
   u32x4* yr = reinterpret_cast<u32x4*>(y + static_cast<size_t>(t) * d);
-  for (int c0 = lane; c0 < vecs; c0 += U * kWave) {
-    // a chunk past the row end (only when U * kWave does not divide d / 8)
-    // reads zeros (past the descriptors' rows) and is never stored
+  // blockIdx.y of gridDim.y: this wave's share of the row's 16-byte chunks
+  const int per = (vecs + gridDim.y - 1) / gridDim.y;
+  const int c_beg = blockIdx.y * per, c_end = min(vecs, c_beg + per);
+  for (int c0 = c_beg + lane; c0 < c_end; c0 += U * kWave) {
+    // a chunk past the share (only when U * kWave does not divide it) is
+    // never stored; past the row end it reads zeros (past the descriptors)
     bool ok[U];
     uint32_t cb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      ok[u] = c0 + u * kWave < vecs;
+      ok[u] = c0 + u * kWave < c_end;
       cb[u] = static_cast<uint32_t>(c0 + u * kWave) * 16u;
     }
     uint4 vh[U], vs[U], vp[KM][U];
@@ -161,7 +164,12 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
 hipError_t launch_combine(int T, int d, int K, int E_s, const void* h, const void* y_shared,
                           const void* y_perm, const int32_t* slot_row, const float* gates,
                           int bf16, void* y, hipStream_t s) {
-  dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(kThreads);
+  // small batches: up to 8 waves share a row, so about 2048 waves run
+  int split = 1;
+  if (bf16)
+    while (split < 8 && static_cast<long long>(T) * split < 2048 && d / 8 >= 128 * split)
+      split *= 2;
+  dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock, split), block(kThreads);
   ProfScope prof_(s, "combine");
   if (bf16) {
     const uint16_t* hb = static_cast<const uint16_t*>(h);

@@ -113,11 +113,10 @@ __global__ __launch_bounds__(NTHR)
 __attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
                                    Tile<BM, BNW, NTHR>::kWavesPerEU)))
 void bf16_tile_kernel(
-    int Kdim, int N, int x_rows, int n_groups, int NT, const TileInfo* __restrict__ tiles,
-    const int32_t* __restrict__ gts, const int32_t* __restrict__ meta,
-    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-    const float* __restrict__ row_scale, uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
+    int Kdim, int N, int x_rows, int NT, const TileInfo* __restrict__ tiles,
+    const int32_t* __restrict__ meta, const int32_t* __restrict__ row_index,
+    const uint16_t* __restrict__ A, const WeightSet W, const float* __restrict__ row_scale,
+    uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using TL = Tile<BM, BNW, NTHR>;
   constexpr int kALoads = TL::kALoads;
   constexpr int kBLoads = TL::kBLoads;
@@ -131,11 +130,13 @@ void bf16_tile_kernel(
   const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
   const int w = xcd * per_xcd + slot;
   if (slot >= per_xcd || w >= total) return;
-  // gts[g] * NT <= w < gts[g + 1] * NT implies gts[g] <= w / NT < gts[g + 1]:
-  // tile w / NT belongs to the group of work item w.
-  const int g = tiles[w / NT].group;
-  const int gstart = gts[g];
-  const int nmt = gts[g + 1] - gstart;
+  // a group's items are the NT column tiles of each of its tiles, so tile
+  // w / NT belongs to the group of work item w; its record holds the group's
+  // first tile and tile count, and the group's weight index
+  const TileInfo t0 = tiles[w / NT];
+  const int g = t0.group;
+  const int gstart = t0.gstart;
+  const int nmt = max(t0.ntiles, 1);
   int mtile, ntile;
   item_tile(w - gstart * NT, nmt, NT, mtile, ntile);
   const TileInfo ti = tiles[gstart + mtile];
@@ -173,11 +174,11 @@ void bf16_tile_kernel(
     a_off[i] = (sr >= 0) ? (static_cast<uint32_t>(sr) * Kdim + lc * 8) * 2u : kOff;
   }
   const int wbytes = static_cast<int>(static_cast<uint32_t>(N) * Kdim * 2u);
+  const size_t wmat = static_cast<size_t>(N) * Kdim;
   const __amdgpu_buffer_rsrc_t rsB0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(W0 + static_cast<size_t>(g) * N * Kdim), 0, wbytes, kBufferFlags);
+      const_cast<uint16_t*>(W.base(false, g, wmat)), 0, wbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsB1 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(GATEUP ? W1 + static_cast<size_t>(g) * N * Kdim : W0), 0, wbytes,
-      kBufferFlags);
+      const_cast<uint16_t*>(W.base(GATEUP, g, wmat)), 0, wbytes, kBufferFlags);
   uint32_t b_off[kBLoads];
 #pragma unroll
   for (int i = 0; i < kBLoads; ++i) {
@@ -476,8 +477,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bf16_stream_kernel(
     int Kdim, int N, int x_rows, int rows, int NT, const TileInfo* __restrict__ tiles,
     const int32_t* __restrict__ meta, const int32_t* __restrict__ row_index,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W0,
-    const uint16_t* __restrict__ W1, const float* __restrict__ row_scale,
+    const uint16_t* __restrict__ A, const WeightSet W, const float* __restrict__ row_scale,
     uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using G = StreamGeom<BK>;
   constexpr int BM = 256, BNW = 256, NTHR = 512;
@@ -557,8 +557,8 @@ void bf16_stream_kernel(
   const uint32_t b_off = static_cast<uint32_t>(kRPI * wave + drow) * rowbytes +
                          static_cast<uint32_t>(dchunk) * 16u;
   auto set_weights = [&]() {
-    rb0 = buffer_rsrc(W0 + static_cast<size_t>(l_g) * N * Kdim, wbytes);
-    rb1 = buffer_rsrc((GATEUP ? W1 : W0) + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    rb0 = buffer_rsrc(W.base(false, l_g, static_cast<size_t>(N) * Kdim), wbytes);
+    rb1 = buffer_rsrc(W.base(GATEUP, l_g, static_cast<size_t>(N) * Kdim), wbytes);
     bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
   };
   set_weights();
@@ -881,8 +881,7 @@ __attribute__((amdgpu_waves_per_eu(Tile<BM, BNW, NTHR>::kWavesPerEU,
 void bf16_regs_stream_kernel(
     int Kdim, int N, int x_rows, int rows, int max_tiles, int NT,
     const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
-    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A, const WeightSet W,
     const float* __restrict__ row_scale, uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using TL = Tile<BM, BNW, NTHR>;
   constexpr int kALoads = TL::kALoads;
@@ -964,8 +963,8 @@ void bf16_regs_stream_kernel(
   uint32_t bcol;
   const uint32_t bb = static_cast<uint32_t>(lr) * rowbytes + static_cast<uint32_t>(lc) * 16u;
   auto set_weights = [&]() {
-    rb0 = buffer_rsrc(W0 + static_cast<size_t>(l_g) * N * Kdim, wbytes);
-    rb1 = buffer_rsrc((GATEUP ? W1 : W0) + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    rb0 = buffer_rsrc(W.base(false, l_g, static_cast<size_t>(N) * Kdim), wbytes);
+    rb1 = buffer_rsrc(W.base(GATEUP, l_g, static_cast<size_t>(N) * Kdim), wbytes);
     bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
   };
   set_weights();
@@ -1290,9 +1289,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bf16_wdma_kernel(
     int Kdim, int N, int x_rows, int rows, int max_tiles, int NT,
     const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
-    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, uint16_t* __restrict__ out,
-    uint16_t* __restrict__ au) {
+    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A, const WeightSet W,
+    uint16_t* __restrict__ out, uint16_t* __restrict__ au) {
   using G = StreamGeom<64>;
   using TL = Tile<256, 256, 512>;
   constexpr int BM = 256, BNW = 256, NTHR = 512;
@@ -1375,8 +1373,8 @@ void bf16_wdma_kernel(
   __amdgpu_buffer_rsrc_t rb0, rb1;
   uint32_t bcol;
   auto set_weights = [&]() {
-    rb0 = buffer_rsrc(W0 + static_cast<size_t>(l_g) * N * Kdim, wbytes);
-    rb1 = buffer_rsrc((GATEUP ? W1 : W0) + static_cast<size_t>(l_g) * N * Kdim, wbytes);
+    rb0 = buffer_rsrc(W.base(false, l_g, static_cast<size_t>(N) * Kdim), wbytes);
+    rb1 = buffer_rsrc(W.base(GATEUP, l_g, static_cast<size_t>(N) * Kdim), wbytes);
     bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
   };
   set_weights();
@@ -1705,30 +1703,28 @@ int stream_grid() {
 // else the one-tile-per-workgroup kernel.
 template <int BM, int BNW, int NTHR, int NSETS>
 hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
-                       const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
+                       const SwigluWorkspace& w, const uint16_t* A, const WeightSet& W,
                        const float* row_scale, uint16_t* C, const char* name, hipStream_t s) {
   const int max_tiles = max_tiles_for(rows, n_groups, BM);
   const int nt = (N + BNW - 1) / BNW;
   ProfScope prof_(s, name);
   if (stream_shape(K, N, 256) && mfma_bound) {
     hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
-                       s, K, N, rows, rows, nt, w.tiles, w.meta, nullptr, A, W, nullptr,
-                       row_scale, C, nullptr);
+                       s, K, N, rows, rows, nt, w.tiles, w.meta, nullptr, A, W, row_scale, C,
+                       nullptr);
   } else if (BM == 256 && BNW == 256 && row_scale == nullptr && wdma_shape(K, N, 256)) {
     hipLaunchKernelGGL((bf16_wdma_kernel<false>), dim3(stream_grid()), dim3(512), 0, s, K, N,
-                       rows, rows, max_tiles, nt, w.tiles, w.meta, nullptr, A, W, nullptr, C,
-                       nullptr);
+                       rows, rows, max_tiles, nt, w.tiles, w.meta, nullptr, A, W, C, nullptr);
   } else if (stream_shape(K, N, BNW)) {
     hipLaunchKernelGGL((bf16_regs_stream_kernel<false, BM, BNW, NTHR>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, K, N, rows, rows, max_tiles, nt, w.tiles, w.meta,
-                       nullptr, A, W, nullptr, row_scale, C, nullptr);
+                       nullptr, A, W, row_scale, C, nullptr);
   } else {
     long blocks = static_cast<long>(max_tiles) * nt;
     blocks = (blocks + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL((bf16_tile_kernel<false, BM, BNW, NTHR, NSETS>),
-                       dim3(static_cast<unsigned>(blocks)), dim3(NTHR), 0, s, K, N, rows,
-                       n_groups, nt, w.tiles, w.group_tile_start, w.meta, nullptr, A, W, nullptr,
-                       row_scale, C, nullptr);
+                       dim3(static_cast<unsigned>(blocks)), dim3(NTHR), 0, s, K, N, rows, nt,
+                       w.tiles, w.meta, nullptr, A, W, row_scale, C, nullptr);
   }
   return hipGetLastError();
 }
@@ -1741,54 +1737,52 @@ hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
 template <int BM, int BNW, int NTHR, int NSETS, bool AU>
 hipError_t launch_gateup(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                          bool mfma_bound, const int32_t* row_index, const uint16_t* x,
-                         const uint16_t* wg, const uint16_t* wu, uint16_t* act, uint16_t* au,
+                         const WeightSet& W, uint16_t* act, uint16_t* au,
                          const SwigluWorkspace& w, hipStream_t s) {
   const int max_tiles = max_tiles_for(rows, n_groups, BM);
   const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
   ProfScope prof_(s, "gateup_bf16");
   if (stream_shape(d_model, d_ffn, 128) && mfma_bound) {
     hipLaunchKernelGGL((bf16_stream_kernel<true, kStreamBK, AU>), dim3(stream_grid()), dim3(512),
-                       0, s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, wg,
-                       wu, nullptr, act, au);
+                       0, s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, W,
+                       nullptr, act, au);
   } else if (!AU && BM == 256 && BNW == 256 && wdma_shape(d_model, d_ffn, 128)) {
     hipLaunchKernelGGL((bf16_wdma_kernel<true, false>), dim3(stream_grid()), dim3(512), 0, s,
                        d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles, w.meta, row_index,
-                       x, wg, wu, act, nullptr);
+                       x, W, act, nullptr);
   } else if (stream_shape(d_model, d_ffn, BNW / 2)) {
     hipLaunchKernelGGL((bf16_regs_stream_kernel<true, BM, BNW, NTHR, AU>), dim3(stream_grid()),
                        dim3(NTHR), 0, s, d_model, d_ffn, x_rows, rows, max_tiles, nt1, w.tiles,
-                       w.meta, row_index, x, wg, wu, nullptr, act, au);
+                       w.meta, row_index, x, W, nullptr, act, au);
   } else {
     long blocks1 = static_cast<long>(max_tiles) * nt1;
     blocks1 = (blocks1 + kNumXcd - 1) / kNumXcd * kNumXcd;
     hipLaunchKernelGGL((bf16_tile_kernel<true, BM, BNW, NTHR, NSETS, AU>),
                        dim3(static_cast<unsigned>(blocks1)), dim3(NTHR), 0, s, d_model, d_ffn,
-                       x_rows, n_groups, nt1, w.tiles, w.group_tile_start, w.meta, row_index, x,
-                       wg, wu, nullptr, act, au);
+                       x_rows, nt1, w.tiles, w.meta, row_index, x, W, nullptr, act, au);
   }
   return hipGetLastError();
 }
 
+// Both products over the tile list already in w (n_groups: the number of
+// groups the list was built for).
 template <int BM, int BNW, int NTHR, int NSETS>
-hipError_t launch_tiles(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
-                        const int32_t* offsets, const int32_t* row_index, const uint16_t* x,
-                        const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
-                        const float* row_scale, uint16_t* y, uint16_t* au,
-                        const SwigluWorkspace& w, hipStream_t s) {
-  hipError_t err = launch_build_tiles(n_groups, rows, BM, offsets, w, s);
-  if (err != hipSuccess) return err;
+hipError_t launch_products(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                           const int32_t* row_index, const uint16_t* x, const WeightSet& Wgu,
+                           const WeightSet& Wd, const float* row_scale, uint16_t* y,
+                           uint16_t* au, const SwigluWorkspace& w, hipStream_t s) {
   uint16_t* act = static_cast<uint16_t*>(w.act);
   const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
-  err = au != nullptr
-            ? launch_gateup<BM, BNW, NTHR, NSETS, true>(n_groups, d_model, d_ffn, rows, x_rows,
-                                                        mfma_bound, row_index, x, wg, wu, act, au,
-                                                        w, s)
-            : launch_gateup<BM, BNW, NTHR, NSETS, false>(n_groups, d_model, d_ffn, rows, x_rows,
-                                                         mfma_bound, row_index, x, wg, wu, act,
-                                                         nullptr, w, s);
+  hipError_t err =
+      au != nullptr
+          ? launch_gateup<BM, BNW, NTHR, NSETS, true>(n_groups, d_model, d_ffn, rows, x_rows,
+                                                      mfma_bound, row_index, x, Wgu, act, au, w,
+                                                      s)
+          : launch_gateup<BM, BNW, NTHR, NSETS, false>(n_groups, d_model, d_ffn, rows, x_rows,
+                                                       mfma_bound, row_index, x, Wgu, act,
+                                                       nullptr, w, s);
   if (err != hipSuccess) return err;
-
-  return launch_down<BM, BNW, NTHR, NSETS>(n_groups, d_ffn, d_model, rows, mfma_bound, w, act, wd,
+  return launch_down<BM, BNW, NTHR, NSETS>(n_groups, d_ffn, d_model, rows, mfma_bound, w, act, Wd,
                                            row_scale, y, "down_bf16", s);
 }
 
@@ -1803,8 +1797,8 @@ hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const in
     if (err != hipSuccess) return err;
   }
   const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
-  return launch_down<256, 256, 512, 2>(n_groups, K, N, rows, mfma_bound, w, A, W, nullptr, C,
-                                       name, s);
+  return launch_down<256, 256, 512, 2>(n_groups, K, N, rows, mfma_bound, w, A,
+                                       WeightSet::one(W, W), nullptr, C, name, s);
 }
 
 hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
@@ -1813,8 +1807,26 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
                               const uint16_t* wd, const float* row_scale, uint16_t* y,
                               uint16_t* au, void* ws, hipStream_t s) {
   SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
-  return launch_tiles<256, 256, 512, 2>(n_groups, d_model, d_ffn, rows, x_rows, offsets,
-                                        row_index, x, wg, wu, wd, row_scale, y, au, w, s);
+  hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, w, s);
+  if (err != hipSuccess) return err;
+  return launch_products<256, 256, 512, 2>(n_groups, d_model, d_ffn, rows, x_rows, row_index, x,
+                                           WeightSet::one(wg, wu), WeightSet::one(wd, wd),
+                                           row_scale, y, au, w, s);
+}
+
+hipError_t launch_experts_bf16(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                               const int32_t* offsets, const int32_t* row_token,
+                               const uint16_t* h, const uint16_t* wg, const uint16_t* wu,
+                               const uint16_t* wd, const uint16_t* wsg, const uint16_t* wsu,
+                               const uint16_t* wsd, uint16_t* y, void* ws, hipStream_t s) {
+  const ExpertsLayout L = experts_layout(ws, E_r, E_s, T, K, d_ffn);
+  hipError_t err = launch_build_tiles_experts(E_r, E_s, T, K, L.shared_rows_per_group, offsets,
+                                              row_token, L.row_index, L.sw, s);
+  if (err != hipSuccess) return err;
+  return launch_products<256, 256, 512, 2>(L.n_groups, d_model, d_ffn, L.rows, T, L.row_index, h,
+                                           WeightSet{wg, wu, wsg, wsu, E_r},
+                                           WeightSet{wd, wd, wsd, wsd, E_r}, nullptr, y, nullptr,
+                                           L.sw, s);
 }
 
 }  // namespace moe

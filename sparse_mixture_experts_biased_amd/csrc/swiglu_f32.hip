@@ -147,7 +147,103 @@ __global__ __launch_bounds__(kThreads) void f32_tile_kernel(
   }
 }
 
+// Grouped row r of the combined routed + shared launch reads token
+// row_token[r] (r < T*K) or token (r - T*K) % T (the shared experts' rows).
+// sh_off (or NULL): [E_s + 1] the shared rows' offsets j*T, for the fp32 path
+// that runs them as a launch of their own.
+__global__ __launch_bounds__(256) void experts_rows_kernel(int TK, int T, int E_s,
+                                                           const int32_t* __restrict__ row_token,
+                                                           int32_t* __restrict__ row_index,
+                                                           int32_t* __restrict__ sh_off) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < TK) row_index[r] = row_token[r];
+  else if (r < TK + E_s * T) row_index[r] = (r - TK) % T;
+  if (sh_off != nullptr && r <= E_s) sh_off[r] = r * T;
+}
+
+// Tile list of the combined launch, one workgroup.  Routed expert g and the
+// q-th shared row group (shared expert q / per, part q % per) take the
+// positions g + ceil(g Q / E_r) and floor(q E_r / Q) + 1 + q, Q = E_s * per
+// (together a permutation of 0 .. E_r + Q - 1: the shared groups spread
+// evenly among the routed experts); tiles are laid out in position order and
+// carry their weight index (g, or E_r + q / per) as the group.
+__global__ __launch_bounds__(1024) void build_tiles_experts_kernel(
+    int E_r, int E_s, int per, int srows, int T, int TK, int bm, int max_tiles,
+    const int32_t* __restrict__ offsets, TileInfo* __restrict__ tiles,
+    int32_t* __restrict__ meta) {
+  __shared__ int32_t lo_s[kMaxExpertGroups], hi_s[kMaxExpertGroups], wi_s[kMaxExpertGroups];
+  __shared__ int32_t cnt[kMaxExpertGroups];
+  __shared__ int32_t part[1024];
+  const int Q = E_s * per, G = E_r + Q;
+  for (int x = threadIdx.x; x < G; x += 1024) {
+    int p, lo, hi, wi;
+    if (x < E_r) {
+      p = x + static_cast<int>((static_cast<long long>(x) * Q + E_r - 1) / E_r);
+      lo = min(max(offsets[x], 0), TK);
+      hi = min(max(offsets[x + 1], lo), TK);
+      wi = x;
+    } else {
+      const int q = x - E_r, j = q / per, i = q % per;
+      p = static_cast<int>(static_cast<long long>(q) * E_r / Q) + 1 + q;
+      lo = TK + j * T + i * srows;
+      hi = min(lo + srows, TK + (j + 1) * T);
+      wi = E_r + j;
+    }
+    lo_s[p] = lo;
+    hi_s[p] = hi;
+    wi_s[p] = wi;
+    cnt[p] = (hi - lo + bm - 1) / bm;
+  }
+  __syncthreads();
+  // exclusive prefix of cnt over positions: thread i owns positions 2i, 2i+1
+  const int i0 = 2 * threadIdx.x;
+  const int c0 = i0 < G ? cnt[i0] : 0, c1 = i0 + 1 < G ? cnt[i0 + 1] : 0;
+  part[threadIdx.x] = c0 + c1;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = threadIdx.x >= static_cast<unsigned>(off) ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const int base = part[threadIdx.x] - c0 - c1;
+  const int starts[2] = {base, base + c0};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int p = i0 + u;
+    if (p >= G) continue;
+    const int start = starts[u], nt = u == 0 ? c0 : c1;
+    for (int t = 0; t < nt && start + t < max_tiles; ++t)
+      tiles[start + t] = TileInfo{wi_s[p], lo_s[p] + t * bm, hi_s[p], start,
+                                  min(nt, max_tiles - start), {0, 0, 0}};
+  }
+  if (threadIdx.x == 1023) meta[0] = min(part[1023], max_tiles);
+}
+
 }  // namespace
+
+hipError_t launch_build_tiles_experts(int E_r, int E_s, int T, int K, int shared_rows_per_group,
+                                      const int32_t* offsets, const int32_t* row_token,
+                                      int32_t* row_index, const SwigluWorkspace& w,
+                                      hipStream_t s) {
+  const int TK = T * K, rows = TK + E_s * T;
+  const int per = (T + shared_rows_per_group - 1) / shared_rows_per_group;
+  ProfScope prof_(s, "tiles");
+  hipLaunchKernelGGL(experts_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, s, TK, T, E_s,
+                     row_token, row_index, nullptr);
+  hipLaunchKernelGGL(build_tiles_experts_kernel, dim3(1), dim3(1024), 0, s, E_r, E_s, per,
+                     shared_rows_per_group, T, TK, 256, max_tiles_for(rows, E_r + E_s * per, 256),
+                     offsets, w.tiles, w.meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_experts_rows(int T, int K, int E_s, const int32_t* row_token,
+                               int32_t* row_index, int32_t* sh_off, hipStream_t s) {
+  const int rows = T * K + E_s * T;
+  hipLaunchKernelGGL(experts_rows_kernel, dim3((max(rows, E_s + 1) + 255) / 256), dim3(256), 0, s,
+                     T * K, T, E_s, row_token, row_index, sh_off);
+  return hipGetLastError();
+}
 
 hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* offsets,
                               const SwigluWorkspace& w, hipStream_t s) {

@@ -30,6 +30,25 @@ struct SwigluWorkspace {
 
 inline int max_tiles_for(int rows, int n_groups, int bm) { return (rows + bm - 1) / bm + n_groups; }
 
+// The expert weights of one bf16 launch ([n, N, K] stacks).  A tile's group
+// field is its weight index g: g < n_first takes expert g of w0 (w1: the W_up
+// stack of gate/up), a later g takes expert g - n_first of s0 / s1 (shared
+// experts appended to a routed launch).
+struct WeightSet {
+  const uint16_t* w0;
+  const uint16_t* w1;
+  const uint16_t* s0;
+  const uint16_t* s1;
+  int n_first;
+  static WeightSet one(const uint16_t* a, const uint16_t* b) {
+    return WeightSet{a, b, a, b, 0x7fffffff};
+  }
+  __device__ __forceinline__ const uint16_t* base(bool second, int g, size_t mat) const {
+    return g < n_first ? (second ? w1 : w0) + static_cast<size_t>(g) * mat
+                       : (second ? s1 : s0) + static_cast<size_t>(g - n_first) * mat;
+  }
+};
+
 // Carve the caller's workspace; `base` may be nullptr to only size it.
 inline SwigluWorkspace swiglu_layout(void* base, int n_groups, int d_ffn, int rows,
                                      int elem_bytes, int min_bm) {
@@ -85,6 +104,52 @@ hipError_t launch_transpose_experts(int n, int rows, int cols, const uint16_t* s
 
 hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* offsets,
                               const SwigluWorkspace& w, hipStream_t s);
+
+// Routed and shared experts in one grouped launch (moe_experts_swiglu).
+// Grouped rows: the T*K routed rows (expert g on offsets[g] .. offsets[g+1]-1,
+// gathered through row_token), then shared expert j on rows T*K + j*T + t
+// (token t).  Each shared expert's rows are cut into groups of
+// shared_rows_per_group rows, and the tile list places those groups evenly
+// among the routed experts, so that each XCD's contiguous run of work items
+// (the persistent kernels' order) holds about the same share of them.
+struct ExpertsLayout {
+  int n_groups;                // E_r + E_s * groups per shared expert
+  int rows;                    // T*K + E_s*T
+  int shared_rows_per_group;
+  int32_t* row_index;          // [rows]: row_token, then the token of each shared row
+  SwigluWorkspace sw;          // activations and the tile list
+  size_t bytes;
+};
+inline int experts_shared_rows_per_group(int T) {
+  // about one group per XCD: ceil(T / 8) rounded up to a 256-row tile
+  return ((T + 8 * 256 - 1) / (8 * 256)) * 256;
+}
+inline ExpertsLayout experts_layout(void* base, int E_r, int E_s, int T, int K, int d_ffn) {
+  ExpertsLayout L{};
+  L.shared_rows_per_group = experts_shared_rows_per_group(T);
+  const int per = (T + L.shared_rows_per_group - 1) / L.shared_rows_per_group;
+  L.n_groups = E_r + E_s * per;
+  L.rows = T * K + E_s * T;
+  const size_t ri = align_up(static_cast<size_t>(L.rows) * sizeof(int32_t), 256);
+  L.row_index = base ? static_cast<int32_t*>(base) : nullptr;
+  L.sw = swiglu_layout(base ? static_cast<char*>(base) + ri : nullptr, L.n_groups, d_ffn, L.rows,
+                       2, 256);
+  L.bytes = ri + L.sw.bytes;
+  return L;
+}
+constexpr int kMaxExpertGroups = 2048;
+// Fills L.row_index and builds the 256-row tile list of the combined groups.
+hipError_t launch_build_tiles_experts(int E_r, int E_s, int T, int K, int shared_rows_per_group,
+                                      const int32_t* offsets, const int32_t* row_token,
+                                      int32_t* row_index, const SwigluWorkspace& w,
+                                      hipStream_t s);
+hipError_t launch_experts_rows(int T, int K, int E_s, const int32_t* row_token,
+                               int32_t* row_index, int32_t* sh_off, hipStream_t s);
+hipError_t launch_experts_bf16(int E_r, int E_s, int T, int K, int d_model, int d_ffn,
+                               const int32_t* offsets, const int32_t* row_token,
+                               const uint16_t* h, const uint16_t* wg, const uint16_t* wu,
+                               const uint16_t* wd, const uint16_t* wsg, const uint16_t* wsu,
+                               const uint16_t* wsd, uint16_t* y, void* ws, hipStream_t s);
 
 // Grouped C = A W[g]^T over the rows of each group (bf16, fp32 accumulation):
 // A [rows, K], W [n_groups, N, K], C [rows, N]; K a multiple of 64.  Builds a

@@ -35,7 +35,7 @@ class MoELayer:
     def __init__(self, shape: LayerShape, e, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
                  ws_down=None, device="cuda", capacity_factor: Optional[float] = None,
                  diagnostics: bool = False, overlap_shared: bool = True,
-                 shared_start: str = "layer"):
+                 shared_start: str = "layer", fuse_shared: bool = False):
         """capacity_factor: None dispatches every copy; a factor CF caps each
         expert at C = ceil(CF*T*K/E_r) rows, admitted in token order.
         diagnostics: route with moe_route_stats and fill the router's balance
@@ -46,7 +46,13 @@ class MoELayer:
         shared_start: with overlap_shared, when the side stream starts them:
         "layer" (as soon as h is ready) or "routed" (once the router and the
         dispatch are done, so those small kernels have every CU to themselves
-        and the shared experts overlap the routed experts instead)."""
+        and the shared experts overlap the routed experts instead).
+        fuse_shared: an inference forward runs the routed and the shared
+        experts in one grouped launch per product (moe_experts_swiglu): one
+        stream, no events (e.g. for a caller that captures the layer on a
+        single stream).  Same bits; at the DeepSeek-V3 shapes 1-2 % slower
+        than the shared experts on a side stream.  overlap_shared and
+        shared_start then only apply to training forwards."""
         if shared_start not in ("layer", "routed"):
             raise ValueError(f"shared_start must be 'layer' or 'routed', not {shared_start!r}")
         self.shared_start = shared_start
@@ -84,8 +90,15 @@ class MoELayer:
         self.slot_row = torch.empty((TK,), **i32)
         self.perm_ws_bytes = L.moe_permute_workspace_size(T, E)
         self.perm_ws = torch.empty((self.perm_ws_bytes,), dtype=torch.uint8, device=device)
-        self.y_perm = torch.empty((TK, d), dtype=self.tdt, device=device)
+        # y_perm and the shared outputs are the two parts of one buffer, the
+        # layout moe_experts_swiglu writes
+        self.y_all = torch.empty((TK + s.E_s * T, d), dtype=self.tdt, device=device)
+        self.y_perm = self.y_all[:TK]
         ws_bytes = L.moe_grouped_swiglu_workspace_size(E, d, s.d_ffn, TK, self.dt)
+        self.fuse_shared = bool(fuse_shared and s.E_s)
+        if self.fuse_shared:
+            ws_bytes = max(ws_bytes, L.moe_experts_swiglu_workspace_size(
+                E, s.E_s, T, s.K, d, s.d_ffn, self.dt))
         self.side = None
         if s.E_s:
             sh_bytes = L.moe_grouped_swiglu_workspace_size(s.E_s, d, s.d_ffn, s.E_s * T, self.dt)
@@ -100,7 +113,7 @@ class MoELayer:
                 self.ev_sh = torch.cuda.Event()
             self.sh_offsets = (torch.arange(s.E_s + 1, **i32) * T).contiguous()
             self.sh_rows = torch.arange(T, **i32).repeat(s.E_s).contiguous()
-            self.y_shared = torch.empty((s.E_s * T, d), dtype=self.tdt, device=device)
+            self.y_shared = self.y_all[TK:]
         else:
             self.sh_offsets = self.sh_rows = self.y_shared = None
         self.sw_ws_bytes = ws_bytes
@@ -201,6 +214,18 @@ class MoELayer:
         if self.profile_tags:
             L.moe_profile_tag("")
 
+    def experts_fused(self, h, stream=None):
+        """Routed and shared experts in one grouped launch per product."""
+        s = self.shape
+        if self.profile_tags:
+            L.moe_profile_tag("experts.")
+        L.moe_experts_swiglu(s.E_r, s.E_s, s.T, s.K, s.d_model, s.d_ffn, self.offsets,
+                             self.row_token, h, self.dt, self.w_gate, self.w_up, self.w_down,
+                             self.ws_gate, self.ws_up, self.ws_down, self.y_all, self.sw_ws,
+                             self.sw_ws_bytes, stream)
+        if self.profile_tags:
+            L.moe_profile_tag("")
+
     def combine(self, h, stream=None):
         s = self.shape
         L.moe_combine(s.T, s.d_model, s.K, s.E_s, h, self.y_shared, self.y_perm, self.slot_row,
@@ -216,6 +241,17 @@ class MoELayer:
         """One layer forward; when gamma is given, b is updated in place after
         the loads are counted (the update affects the next call)."""
         self._check_inputs(h, b)
+        if self.fuse_shared and self.au_perm is None:
+            self.route(h, b, stream)
+            self.permute(stream=stream)
+            if self.diagnostics:
+                self.router_diag(stream)
+            self.experts_fused(h, stream)
+            self.combine(h, stream)
+            if gamma is not None and b is not None:
+                self.bias_update(b, gamma, stream)
+            self.au_valid = False
+            return self.y
         # the shared experts on the side stream once h is ready on this one
         # (a raw stream handle cannot carry events: then in sequence)
         overlap = self.side is not None and not isinstance(stream, int)

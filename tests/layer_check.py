@@ -18,11 +18,12 @@ from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
 from synthetic import host_array
 
 
-def runner_for(lay, T=None, capacity_factor=None, diagnostics=False):
+def runner_for(lay, T=None, capacity_factor=None, diagnostics=False, fuse_shared=False):
     c = lay.cfg
     shape = LayerShape(T or c.T, c.d_model, c.E_r, c.K, c.E_s, c.d_ffn, c.dtype, c.score)
     return MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
-                    lay.ws_down, capacity_factor=capacity_factor, diagnostics=diagnostics)
+                    lay.ws_down, capacity_factor=capacity_factor, diagnostics=diagnostics,
+                    fuse_shared=fuse_shared)
 
 
 def _expert_source(w_gate, w_up, w_down):

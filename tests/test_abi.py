@@ -188,6 +188,37 @@ def test_grouped_swiglu_rejects_bad_arguments():
                                         need, None) == L.MOE_OK
 
 
+def test_experts_swiglu_rejects_bad_arguments():
+    lib = L.load()
+    P = ctypes.c_void_p(16)
+    T, K, E, Es, d, f = 4096, 8, 256, 1, 7168, 2048
+    need = L.moe_experts_swiglu_workspace_size(E, Es, T, K, d, f, L.MOE_BF16)
+    # activations of every routed and shared row, their row index, the tile list
+    assert need >= (T * K + Es * T) * (2 * f + 4)
+    assert L.moe_experts_swiglu_workspace_size(E, Es, T, K, d, f, L.MOE_F32) >= T * K * f * 4
+    assert L.moe_experts_swiglu_workspace_size(E, Es, T, E + 1, d, f, L.MOE_BF16) == 0
+
+    def call(*a, ws=need, shared=P):
+        return _st(lib.moe_experts_swiglu(*a, P, P, P, L.MOE_BF16, P, P, P, shared, shared, shared,
+                                          P, P, ws, None))
+    rc, msg = call(E, Es, T, K, d, f, ws=need - 1)
+    assert rc == L.MOE_ERR_INVALID_ARG and "workspace" in msg
+    rc, msg = call(E, Es, T, K, d, f, shared=None)
+    assert rc == L.MOE_ERR_INVALID_ARG and "shared" in msg
+    rc, msg = call(E, Es, T, E + 1, d, f)
+    assert rc == L.MOE_ERR_INVALID_ARG and "K <= E_r" in msg
+    rc, msg = call(E, Es, T, K, 7000, f)
+    assert rc == L.MOE_ERR_UNSUPPORTED and "multiples of 64" in msg
+    # more row groups than the tile builder takes: E_r + 8 E_s > 2048
+    rc, msg = call(1024, 200, T, K, 256, 256, ws=1 << 40)
+    assert rc == L.MOE_ERR_UNSUPPORTED and "row groups" in msg
+    # every bf16 operand under 2 GiB: activations of (K + E_s) T rows
+    rc, msg = call(E, Es, 65536, K, d, f, ws=1 << 42)
+    assert rc == L.MOE_ERR_UNSUPPORTED and "2 GiB" in msg
+    assert lib.moe_experts_swiglu(E, Es, T, K, d, f, None, P, P, L.MOE_BF16, P, P, P, P, P, P,
+                                  P, P, need, None) == L.MOE_ERR_INVALID_ARG
+
+
 def test_combine_and_bias_update_reject_bad_arguments():
     lib = L.load()
     P = ctypes.c_void_p(16)

@@ -57,6 +57,23 @@ def test_dsv3_prefill_32k_tokens(dsv3):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("T", [4096, 64])
+def test_dsv3_fused_shared_matches_side_stream(dsv3, T):
+    """Routed and shared experts in one grouped launch per product
+    (moe_experts_swiglu) give the same bits as the side-stream launches at
+    full size (prefill and decode batches)."""
+    cfg = dsv3.cfg
+    h = dsv3.h if T == cfg.T else make_tokens(CONFIGS["dsv3_decode"], device="cuda")
+    runs = [runner_for(dsv3, T=T, fuse_shared=f) for f in (False, True)]
+    ys = [r.forward(h, dsv3.b.clone()).clone() for r in runs]
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0].y_shared, runs[1].y_shared)
+    assert torch.equal(runs[0].y_perm, runs[1].y_perm)
+    assert torch.equal(ys[0], ys[1])
+    del runs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cf", [1.0, 1.25])
 def test_dsv3_prefill_capacity_factor(dsv3, cf):
     """Capacity-bounded dispatch at full size: C = ceil(CF*T*K/E_r) = 128 / 160

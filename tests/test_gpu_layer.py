@@ -90,3 +90,38 @@ def test_shared_expert_overlap_matches_sequential():
     for name in ("overlap", "overlap-routed"):
         for a, b in zip(outs[name], outs["sequential"]):
             assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("T,d,E,K,E_s,f,cf", [
+    (300, 1024, 32, 4, 1, 512, None),     # one shared row group
+    (2500, 512, 16, 2, 2, 256, None),     # two shared experts, 4 row groups each
+    (700, 512, 24, 3, 1, 256, 1.0),       # capacity: dropped copies leave a gap of rows
+    (64, 1024, 64, 8, 1, 512, None),      # decode-sized batch
+])
+def test_fused_shared_matches_separate_launches(T, d, E, K, E_s, f, cf):
+    """moe_experts_swiglu (routed + shared experts in one grouped launch per
+    product) gives the same bits as the separate launches, in sequence or with
+    the shared experts on the side stream, and the layer matches the oracle."""
+    from dataclasses import replace
+    from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
+    cfg = replace(CONFIGS["dsv3_prefill"], T=T, d_model=d, E_r=E, K=K, E_s=E_s, d_ffn=f)
+    say(f"fused vs separate: T={T} d={d} E={E} K={K} E_s={E_s} f={f} cf={cf}")
+    lay = make_layer(cfg, device="cuda")
+    shape = LayerShape(T, d, E, K, E_s, f, cfg.dtype, cfg.score)
+    runs = {}
+    for name, fuse, overlap in (("fused", True, True), ("side", False, True),
+                                ("serial", False, False)):
+        runs[name] = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate,
+                              lay.ws_up, lay.ws_down, capacity_factor=cf, fuse_shared=fuse,
+                              overlap_shared=overlap)
+    ys = {n: r.forward(lay.h, lay.b).clone() for n, r in runs.items()}
+    y2 = runs["fused"].forward(lay.h, lay.b).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(ys["fused"], y2)
+    for n in ("side", "serial"):
+        assert torch.equal(runs["fused"].y_shared, runs[n].y_shared), n
+        kept = int(runs[n].offsets[-1].item())
+        assert torch.equal(runs["fused"].y_perm[:kept], runs[n].y_perm[:kept]), n
+        assert torch.equal(ys["fused"], ys[n]), n
+    check_layer(lay, lay.h, None, None, runs["fused"], n_tok_sample=12, n_exp_sample=3, seed=8,
+                label=f"fused T={T} E_s={E_s}")

@@ -520,6 +520,10 @@ def _combine_gpu(h, y_shared, y_perm, slot_row, gates, E_s):
     (150, 1000, 4, 1, torch.bfloat16, False),
     (77, 520, 3, 0, torch.bfloat16, True),
     (500, 7168, 8, 1, torch.bfloat16, True),
+    # small batches split each row over several waves: 129 chunks in two
+    # shares of 65 and 64; the decode shape in eight shares of 112
+    (40, 1032, 5, 1, torch.bfloat16, False),
+    (64, 7168, 8, 1, torch.bfloat16, False),
 ])
 def test_combine_parity(T, d, K, E_s, dtype, drop):
     say(f"moe_combine T={T} d={d} K={K} E_s={E_s} {dtype} dropped slots={drop}")

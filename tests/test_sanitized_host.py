@@ -18,7 +18,7 @@ def test_abi_tests_clean_under_asan_and_ubsan(tmp_path):
         B.hipcc()
     except RuntimeError:
         pytest.skip("no HIP toolchain to build the sanitized library")
-    if not os.path.exists(B.SAN_LIB_PATH):
+    if B.is_stale(B.SAN_LIB_PATH):
         B.build(sanitize=True)
     env = B.sanitizer_env()
     log = str(tmp_path / "san")
