@@ -581,3 +581,40 @@ def test_bias_update_parity(T, E, K, gamma):
     ls = O.load_stats(loads, T, K)
     assert st[0] == ls["max_load"] and st[1] == ls["min_load"]
     assert st[2] == pytest.approx(ls["max_vio"], rel=1e-6, abs=1e-7)
+
+
+@pytest.mark.parametrize("T,d,f,E,K,E_s,dtype", [
+    (333, 256, 192, 5, 2, 1, torch.bfloat16),    # tile kernel (N not a multiple of the column tile)
+    (300, 512, 256, 16, 4, 2, torch.bfloat16),   # streaming kernels, two shared experts
+    (100, 512, 256, 8, 2, 0, torch.bfloat16),    # no shared experts
+    (64, 128, 256, 8, 2, 1, torch.float32),      # fp32: two grouped launches inside
+    (90, 64, 32, 6, 3, 2, torch.float32),
+])
+def test_experts_swiglu_parity(T, d, f, E, K, E_s, dtype):
+    """moe_experts_swiglu: routed rows first (y_perm), then the shared experts'
+    rows (token order, expert by expert), each against the oracle's grouped
+    SwiGLU of the same rows."""
+    say(f"moe_experts_swiglu T={T} d={d} f={f} E={E} K={K} E_s={E_s} {dtype}")
+    rng = np.random.default_rng(T + E + E_s)
+    idx = O.biased_topk(rng.random((T, E)).astype(np.float32), None, K)
+    off, rt, _ = O.permute(idx, E)
+    x = _tokens(T, d, dtype, 60 + T)
+    wg, wu, wd = _weights(E, d, f, dtype, 61 + E)
+    sw = _weights(max(E_s, 1), d, f, dtype, 62 + E)
+    dt = L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32
+    wsb = L.moe_experts_swiglu_workspace_size(E, E_s, T, K, d, f, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    y = torch.zeros((T * K + E_s * T, d), dtype=dtype, device=DEV)
+    L.moe_experts_swiglu(E, E_s, T, K, d, f, torch.from_numpy(off).to(DEV),
+                         torch.from_numpy(rt).to(DEV), x, dt, wg, wu, wd,
+                         *(sw if E_s else (None, None, None)), y, ws, wsb)
+    torch.cuda.synchronize()
+    kind = "bf16" if dtype == torch.bfloat16 else "f32"
+    yh = to_host_f64(y)
+    ref = O.grouped_swiglu(host_array(x), off, rt, (host_array(wg), host_array(wu), host_array(wd)))
+    assert rel_err(yh[:T * K], ref) <= out_tol(kind)
+    if E_s:
+        sh_off = (np.arange(E_s + 1) * T).astype(np.int32)
+        sh_rows = np.tile(np.arange(T, dtype=np.int32), E_s)
+        ref_s = O.grouped_swiglu(host_array(x), sh_off, sh_rows, tuple(host_array(w) for w in sw))
+        assert rel_err(yh[T * K:], ref_s) <= out_tol(kind)
