@@ -53,9 +53,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(int E, int n_chunks, int TK,
   __shared__ int32_t part[1024];
   __shared__ int32_t total_s;
   const int e = threadIdx.x;
+  // chunk counts in batches of kB loads in flight (one at a time, every load
+  // waited for the one before)
+  constexpr int kB = 8;
   int tot = 0;
   if (e < E)
-    for (int c = 0; c < n_chunks; ++c) tot += counts[static_cast<size_t>(c) * E + e];
+    for (int c0 = 0; c0 < n_chunks; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        v[u] = c0 + u < n_chunks ? counts[static_cast<size_t>(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) tot += v[u];
+    }
   if (cap >= 0) tot = min(tot, cap);  // kept rows of expert e
   // inclusive Hillis-Steele scan over experts
   part[e] = (e < E) ? tot : 0;
@@ -74,11 +84,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(int E, int n_chunks, int TK,
   }
   if (e < E) {
     int run = excl;
-    for (int c = 0; c < n_chunks; ++c) {
-      size_t q = static_cast<size_t>(c) * E + e;
-      int v = counts[q];
-      counts[q] = run;
-      run += v;
+    for (int c0 = 0; c0 < n_chunks; c0 += kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        v[u] = c0 + u < n_chunks ? counts[static_cast<size_t>(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (c0 + u < n_chunks) {
+          counts[static_cast<size_t>(c0 + u) * E + e] = run;
+          run += v[u];
+        }
     }
   }
   __syncthreads();
@@ -106,18 +122,37 @@ __global__ __launch_bounds__(kChunk) void assign_kernel(int T, int E, int K, int
   }
   __syncthreads();
   if (t >= T) return;
-  for (int k = 0; k < K; ++k) {
-    size_t q = static_cast<size_t>(t) * K + k;
-    int ex = idx[q];
-    if (ex < 0 || ex >= E) {
+  // the token's ids and segment bases (and offsets) loaded before any store,
+  // so their loads are in flight together
+  int exs[MOE_MAX_TOPK_DEV], bs[MOE_MAX_TOPK_DEV], os[MOE_MAX_TOPK_DEV];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    exs[k] = -1;
+    if (k < K) {
+      const int ex = idx[static_cast<size_t>(t) * K + k];
+      exs[k] = (ex >= 0 && ex < E) ? ex : -1;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    const bool ok = k < K && exs[k] >= 0;
+    bs[k] = ok ? base[static_cast<size_t>(blockIdx.x) * E + exs[k]] : 0;
+    os[k] = (ok && cap >= 0) ? offsets[exs[k]] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
+    if (k >= K) break;
+    const size_t q = static_cast<size_t>(t) * K + k;
+    const int ex = exs[k];
+    if (ex < 0) {
       slot_row[q] = -1;
       continue;
     }
     const uint32_t* row = bits + ex * kWords;
     int rank = __popc(row[w] & (bit - 1u));
     for (int ww = 0; ww < w; ++ww) rank += __popc(row[ww]);
-    int slot = base[static_cast<size_t>(blockIdx.x) * E + ex] + rank;
-    if (cap >= 0 && slot - offsets[ex] >= cap) {  // expert full: dropped
+    const int slot = bs[k] + rank;
+    if (cap >= 0 && slot - os[k] >= cap) {  // expert full: dropped
       slot_row[q] = -1;
       continue;
     }
