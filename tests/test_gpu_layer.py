@@ -125,3 +125,19 @@ def test_fused_shared_matches_separate_launches(T, d, E, K, E_s, f, cf):
         assert torch.equal(ys["fused"], ys[n]), n
     check_layer(lay, lay.h, None, None, runs["fused"], n_tok_sample=12, n_exp_sample=3, seed=8,
                 label=f"fused T={T} E_s={E_s}")
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+def test_single_token_layer(fuse):
+    """One token through the whole bf16 layer (router tile of one row, one
+    split-K partial per split, one row per touched expert, one shared row)."""
+    from dataclasses import replace
+    from sparse_mixture_experts_biased_amd import LayerShape, MoELayer
+    cfg = replace(CONFIGS["dsv3_prefill"], T=1, d_model=512, E_r=16, K=4, d_ffn=256)
+    lay = make_layer(cfg, device="cuda")
+    shape = LayerShape(1, cfg.d_model, cfg.E_r, cfg.K, cfg.E_s, cfg.d_ffn, cfg.dtype, cfg.score)
+    run = MoELayer(shape, lay.e, lay.w_gate, lay.w_up, lay.w_down, lay.ws_gate, lay.ws_up,
+                   lay.ws_down, fuse_shared=fuse)
+    res = check_layer(lay, lay.h, lay.b, cfg.gamma, run, check_all_tokens=True, seed=1,
+                      label=f"single token fuse={fuse}")
+    assert res["experts_checked"] == cfg.K
