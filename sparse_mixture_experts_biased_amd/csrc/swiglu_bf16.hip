@@ -472,6 +472,18 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, void* lds, uint32
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 4, voff, soff, 0, AUX);
 }
 
+// The same load with the LDS destination passed through an empty asm: the
+// compiler then cannot tie the load to an LDS object and inserts no wait for
+// it before LDS reads.  For kernels whose own explicit waits and barriers
+// order every such load before the reads of its data.
+template <int AUX = 0>
+__device__ __forceinline__ void dma16_unscoped(__amdgpu_buffer_rsrc_t rs, void* lds, uint32_t voff,
+                                               uint32_t soff) {
+  lds_ptr_t l = (lds_ptr_t)lds;
+  asm volatile("" : "+s"(l));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, l, 16, voff, soff, 0, AUX);
+}
+
 template <bool GATEUP, int BK, bool AU = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bf16_stream_kernel(
@@ -1272,17 +1284,24 @@ void bf16_regs_stream_kernel(
 // weights of the next slice and meets the barrier.  Loads complete in order
 // and each step issues its row loads before its weight loads, so neither
 // wait covers the newest weight slice: every weight slice has about two steps
-// to arrive (the register-staged kernel gives it one).  The slice count is
-// padded to a multiple of the three weight stages with slices that read
-// zeros (out-of-range offsets move no data), so every item starts on the
-// first stage and the stage of each step is known when compiling; the row
-// stages alternate at run time.  The MFMAs take the weight fragment first,
+// to arrive (the register-staged kernel gives it one).  The weight stages
+// rotate through the slices of all items back to back (the step loop is
+// unrolled over the three stages, so the stage of each step is known when
+// compiling), and an item may end on any of the three: each unrolled step
+// closes the item when its last slice has been multiplied.  The row stages
+// alternate at run time.  The MFMAs take the weight fragment first,
 // so the epilogue packs four consecutive output columns per 8-byte LDS write.
 // Every LDS access keeps its alias scope: an LDS access the compiler cannot
 // tell apart from the weight stages would wait for every weight slice in
 // flight.  Used for groups of fewer rows than a tile on average (weight
-// streaming) when K has at least kMinStreamSlices slices.
+// streaming) when K has at least kWdmaMinSlices slices.
 constexpr int kWdmaStages = 3;
+// The next item's records are fetched on every third step and reach the load
+// side through three dependent fetches (group record, row-tile record, row
+// indices), the first of them up to two steps after the item changed: the
+// load side may move on again 11 steps after it last did, so an item needs at
+// least that many slices.
+constexpr int kWdmaMinSlices = 12;
 
 template <bool GATEUP, bool AU = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1317,8 +1336,7 @@ void bf16_wdma_kernel(
   const int end = min(total, (xcd + 1) * per_xcd);
   if (first >= end) return;
   const int n_items = (end - first + nslot - 1) / nslot;
-  const int nk = Kdim / kBK;
-  const int nkp = (nk + kWdmaStages - 1) / kWdmaStages * kWdmaStages;  // with zero slices
+  const int nk = Kdim / kBK;  // at least kWdmaMinSlices
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar
@@ -1328,8 +1346,7 @@ void bf16_wdma_kernel(
   const int lr = tid >> 3;  // 0 .. kRP-1
   const uint32_t rowbytes = static_cast<uint32_t>(Kdim) * 2u;
   const uint32_t wbytes = static_cast<uint32_t>(N) * rowbytes;
-  const uint32_t kb_end = static_cast<uint32_t>(nk) * kBK * 2u;    // past the last real slice
-  const uint32_t kbp_end = static_cast<uint32_t>(nkp) * kBK * 2u;  // past the last padded one
+  const uint32_t kb_end = static_cast<uint32_t>(nk) * kBK * 2u;  // past the last slice
   const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(A, static_cast<uint32_t>(x_rows) * rowbytes);
   const __amdgpu_buffer_rsrc_t rsT =
       buffer_rsrc(tiles, static_cast<uint32_t>(max_tiles) * sizeof(TileInfo));
@@ -1381,19 +1398,18 @@ void bf16_wdma_kernel(
   uint32_t kb = 0;  // byte offset of the load side's next k-slice
 
   // Loads the x rows of the load side's slice into sa, then sends its weight
-  // slice into stage ST; zero slices (past K) read nothing.
+  // slice into stage ST.
   uint4 sa[kALoads];
 #define MOE_WLOAD(ST)                                                                        \
   do {                                                                                      \
-    const uint32_t zmask_ = kb < kb_end ? 0u : kOff;                                        \
     _Pragma("unroll") for (int i = 0; i < kALoads; ++i) sa[i] = __builtin_bit_cast(           \
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i] | zmask_, kb, 0));        \
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0));                 \
     __builtin_amdgcn_sched_barrier(0); /* rows before weights: see the step's waits */      \
     _Pragma("unroll") for (int i = 0; i < kNI; ++i) {                                       \
       const int add_ = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;                  \
-      dma<16, kWeightPolicy>((GATEUP && i >= kNI / 2) ? rb1 : rb0,                          \
-                             (ST) + kRPI * (wave + 8 * i) * G::kRow,                          \
-              b_off | zmask_, bcol + static_cast<uint32_t>(add_) * rowbytes + kb);          \
+      dma16_unscoped<kWeightPolicy>((GATEUP && i >= kNI / 2) ? rb1 : rb0,                   \
+                             (ST) + kRPI * (wave + 8 * i) * G::kRow, b_off,                   \
+                             bcol + static_cast<uint32_t>(add_) * rowbytes + kb);           \
     }                                                                                       \
     kb += kBK * 2;                                                                          \
   } while (0)
@@ -1408,16 +1424,20 @@ void bf16_wdma_kernel(
   // in lane l, dword (l & 7) of the tile record of the next item's group
   // start (l & 8 == 0) or of its row tile (l & 8 != 0); ri holds, in lane
   // j + 8 i, the source row of tile row 8 * wave + j + kRP * i.  Refetched on
-  // every third step, after that step's loads, and read three steps later.
+  // every third step, after that step's loads, and read three steps later
+  // (ri into ri_l, which the load side takes when it changes item, on any
+  // step).  After the next item changes, the group record is read one fetch
+  // later, the row-tile record two and the row indices three.
   static_assert(kALoads * 8 <= kWave, "one lane per gathered row of the wave");
-  int p = 0, ri = -1;
+  int p = 0, ri = -1, ri_l = -1;
   int n_g = 0, n_ntile = 0, n_m0 = 0, n_nrows = 0;
   int nw = first + min(1, n_items - 1) * nslot;  // next item
   int t0rec = nw / NT;                           // a tile of its group
   int rec = 0;                                   // its row tile
   int fa = 0;                                    // fetches since nw changed
 
-#define MOE_WADVANCE()                                                                       \
+  // Read the records and row indices fetched three steps ago.
+#define MOE_WDECODE()                                                                        \
   do {                                                                                      \
     if (fa == 1) { /* the group record just arrived: locate the row tile */                 \
       const int gstart_ = __builtin_amdgcn_readlane(p, 3);                                  \
@@ -1429,14 +1449,21 @@ void bf16_wdma_kernel(
     }                                                                                       \
     n_m0 = __builtin_amdgcn_readlane(p, 9);                                                 \
     n_nrows = min(__builtin_amdgcn_readlane(p, 10) - n_m0, BM);                             \
-    if (kb == kbp_end) {                                                                    \
+    if (GATEUP) /* a register of its own: ri's is then free for the next fetch */            \
+      asm volatile("v_mov_b32 %0, %1" : "=&v"(ri_l) : "v"(ri));                             \
+  } while (0)
+  // Move the load side to the next item once all slices of the current one
+  // are issued.
+#define MOE_WSWITCH()                                                                        \
+  do {                                                                                      \
+    if (kb == kb_end) {                                                                     \
       if (l_item + 1 < n_items) {                                                           \
         ++l_item;                                                                           \
         kb = 0;                                                                             \
         l_g = n_g; l_ntile = n_ntile; l_m0 = n_m0; l_nrows = n_nrows;                       \
         set_weights();                                                                      \
         _Pragma("unroll") for (int i = 0; i < kALoads; ++i) {                               \
-          const int sr_ = gather ? __builtin_amdgcn_ds_bpermute(((lane >> 3) + 8 * i) * 4, ri) \
+          const int sr_ = gather ? __builtin_amdgcn_ds_bpermute(((lane >> 3) + 8 * i) * 4, ri_l) \
                                  : l_m0 + kRP * i + lr;                                     \
           a_off[i] = a_offset(i, l_nrows, sr_);                                             \
         }                                                                                   \
@@ -1444,7 +1471,7 @@ void bf16_wdma_kernel(
         t0rec = nw / NT;                                                                    \
         fa = 0;                                                                             \
       } else {                                                                              \
-        kb = kbp_end - kBK * 2; /* past the last item: its last slice again */              \
+        kb = kb_end - kBK * 2; /* past the last item: its last slice again */               \
       }                                                                                     \
     }                                                                                       \
   } while (0)
@@ -1628,7 +1655,8 @@ void bf16_wdma_kernel(
   // weights, multiply slice k, wait for slice k + 1's weights, barrier.  The
   // wait leaves in flight what was issued after those weights: this step's
   // row and weight loads (kALoads + kNI) and the fetch loads of the steps
-  // between (position 1 of each three issues them).
+  // between (position 1 of each three issues them).  A step that multiplied
+  // an item's last slice writes its output tile before the next step.
   constexpr int kNF = GATEUP ? 2 : 1;  // fetch loads
   // (slice 1's loads go last, as in a step, so that the loop sees the same
   // loads in flight from the prologue as from its own last step)
@@ -1639,8 +1667,11 @@ void bf16_wdma_kernel(
   // the compiler may sink slice 1's row loads below its weight loads (they
   // read memory nothing here writes); using them here keeps them first
   asm volatile("" ::"v"(sa[0].x), "v"(sa[1].x), "v"(sa[2].x), "v"(sa[3].x) : "memory");
+  int kc = 0;  // slices of the compute-side item multiplied
+  int jc = 0;  // items finished
 #define MOE_WSTEP(U, BCUR, BNEXT, WAITN)                                                     \
-  if ((U) == 1) MOE_WADVANCE();                                                             \
+  if ((U) == 1) MOE_WDECODE();                                                              \
+  MOE_WSWITCH();                                                                            \
   MOE_WSTORE((gk + 1) & 1);                                                                 \
   __builtin_amdgcn_sched_barrier(0); /* the stores' waits must not cover the new loads */   \
   MOE_WLOAD(BNEXT);                                                                         \
@@ -1648,26 +1679,26 @@ void bf16_wdma_kernel(
   compute(a_st + (gk & 1) * kTile, BCUR);                                                   \
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(WAITN)      \
                : "memory");                                                                 \
-  ++gk;
-  for (int j = 0; j < n_items; ++j) {
-    for (int kt = 0; kt < nkp; kt += kWdmaStages) {
-      MOE_WSTEP(0, b0, b2, kALoads + kNI)
-      MOE_WSTEP(1, b1, b0, kALoads + kNI + kNF)
-      MOE_WSTEP(2, b2, b1, kALoads + kNI + kNF)
-    }
-    epilogue(((gk + 1) & 1) * kTile);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;
-    c_m0 = l_m0;
-    c_nrows = l_nrows;
-    c_n0 = l_ntile * kCols;
+  ++gk;                                                                                     \
+  if (++kc == nk) {                                                                         \
+    epilogue(((gk + 1) & 1) * kTile);                                                       \
+    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                        \
+        _Pragma("unroll") for (int nb = 0; nb < kNB; ++nb)                                  \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;           \
+    c_m0 = l_m0;                                                                            \
+    c_nrows = l_nrows;                                                                      \
+    c_n0 = l_ntile * kCols;                                                                 \
+    kc = 0;                                                                                 \
+    if (++jc == n_items) break;                                                             \
+  }
+  for (;;) {
+    MOE_WSTEP(0, b0, b2, kALoads + kNI)
+    MOE_WSTEP(1, b1, b0, kALoads + kNI + kNF)
+    MOE_WSTEP(2, b2, b1, kALoads + kNI + kNF)
   }
 #undef MOE_WSTEP
-#undef MOE_WADVANCE
+#undef MOE_WDECODE
+#undef MOE_WSWITCH
 #undef MOE_WFETCH
 #undef MOE_WLOAD
 #undef MOE_WSTORE
@@ -1676,9 +1707,9 @@ void bf16_wdma_kernel(
 }
 
 // Shapes the weight-DMA streaming kernel takes (K of whole slices, at least
-// kMinStreamSlices of them; N of whole column tiles).
+// kWdmaMinSlices of them; N of whole column tiles).
 bool wdma_shape(int K, int N, int cols) {
-  return K % kBK == 0 && K / kBK >= kMinStreamSlices && N % cols == 0;
+  return K % kBK == 0 && K / kBK >= kWdmaMinSlices && N % cols == 0;
 }
 
 // Workgroups of the streaming kernels: one per CU, a multiple of the XCD count.

@@ -348,6 +348,15 @@ SWIGLU_CASES = [
     (2000, 1024, 2048, 96, 4, torch.bfloat16),  # ~83-row groups, several items per workgroup
     (40, 1024, 1024, 64, 2, torch.bfloat16),    # decode-like: 0-4 rows per group
     (600, 768, 1536, 16, 2, torch.bfloat16),    # 12 and 24 slices: no zero slices padded in
+    # weight-DMA kernel, several items per workgroup, items of 12, 13, 16, 20
+    # and 24 slices: the three weight stages rotate through the items, so an
+    # item ends (and the load side changes item) on every one of them
+    (1200, 832, 1024, 96, 4, torch.bfloat16),   # gate/up 13 slices, 3 items per workgroup
+    (1200, 768, 1280, 96, 4, torch.bfloat16),   # gate/up 12 slices (the fewest), down 20
+    (1000, 1536, 1024, 96, 2, torch.bfloat16),  # down 16 slices, 2-3 items per workgroup
+    # K = 512 with four items per workgroup: too few slices for the weight-DMA
+    # kernel, the register-staged one takes the gate/up product
+    (1000, 512, 2048, 64, 4, torch.bfloat16),
 ]
 
 
