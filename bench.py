@@ -383,6 +383,10 @@ def main(argv=None):
     ap.add_argument("--diagnostics", action="store_true",
                     help="route with the router statistics and compute the balance diagnostics "
                          "(Switch f.P, z-loss, load entropy, MaxVio, dropped rate) every step")
+    ap.add_argument("--stage-events", default="dominant", choices=["dominant", "all"],
+                    help="which launches carry hipEvents in the timed steps: only the gate/up "
+                         "launch the roofline reports (default; the other stages are timed in "
+                         "a few extra steps after the timed region) or every launch")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy a BYTES-sized buffer 3 times (calibrates HBM byte counters)")
     ap.add_argument("--calibrate", action="store_true",
@@ -403,7 +407,8 @@ def main(argv=None):
     import torch
 
     from sparse_mixture_experts_biased_amd import (LayerShape, MoELayer, load,
-                                                   moe_profile_enable, moe_profile_report)
+                                                   moe_profile_enable, moe_profile_only,
+                                                   moe_profile_report)
     from synthetic import CONFIGS, host_array, make_layer, make_tokens
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
@@ -467,6 +472,13 @@ def main(argv=None):
         step(i)
     torch.cuda.synchronize()
     moe_profile_report()  # drop warm-up records
+    # the forward's expert launches: fused (routed + shared) unless a training
+    # forward or --unfused-shared kept them apart
+    fused = run.fuse_shared and dy is None
+    pfx = "experts." if fused else "routed."
+    # in the timed steps only the launch the roofline reports carries events
+    # (each event pair is a queue packet of its own between two launches)
+    moe_profile_only(pfx + "gateup" if args.stage_events == "dominant" else "")
     moe_profile_enable(True)
     if cfg.steps > 1 and gamma is not None:
         stats_hist = torch.zeros((args.steps, 4), dtype=torch.int32, device="cuda")
@@ -488,16 +500,25 @@ def main(argv=None):
     prof = moe_profile_report()
     ev_ms = evs[0].elapsed_time(evs[-1])
     step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-
-    ms_per_step = wall * 1000.0 / args.steps
-    tokens_per_s = cfg.T / (ms_per_step / 1000.0)
     loads = run.loads.cpu().numpy()
     n_touched = int((loads > 0).sum())
     kept_rows = int(run.offsets[-1].item())
-    # the forward's expert launches: fused (routed + shared) unless a training
-    # forward or --unfused-shared kept them apart
-    fused = run.fuse_shared and dy is None
-    pfx = "experts." if fused else "routed."
+    layer_stats = run.stats_host()  # the last timed step's load statistics
+    if args.stage_events == "dominant":
+        # every stage's launch time from a few more steps with all events on
+        # (outside the timed region; the timed gate/up figure is kept)
+        moe_profile_only("")
+        moe_profile_enable(True)
+        for i in range(min(5, args.steps)):
+            run.forward(hs[i % len(hs)], b, gamma, stream)
+            if dy is not None:
+                run.backward(hs[i % len(hs)], dy, stream)
+        torch.cuda.synchronize()
+        moe_profile_enable(False)
+        prof = {**moe_profile_report(), **prof}
+
+    ms_per_step = wall * 1000.0 / args.steps
+    tokens_per_s = cfg.T / (ms_per_step / 1000.0)
     gu_bytes, gu_flops, layer_bytes, layer_flops = algorithmic(cfg, n_touched, cfg.E_s, kept_rows,
                                                                fused)
     stages = {k: round(v[1] / v[0], 5) for k, v in prof.items()}
@@ -528,7 +549,7 @@ def main(argv=None):
                  hbm_frac=round(layer_bytes / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
                  mfma_tflops=round(layer_flops / (ms_per_step / 1000.0) / 1e12, 1),
                  mfma_frac=round(layer_flops / (ms_per_step / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                 experts_touched=n_touched, stats=run.stats_host())
+                 experts_touched=n_touched, stats=layer_stats)
     # the roofline fraction the layer attains: the larger of its MFMA and HBM fractions
     layer["attainable_frac"] = max(layer["hbm_frac"], layer["mfma_frac"])
 

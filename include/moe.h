@@ -417,6 +417,11 @@ moe_status moe_profile_enable(int on);
  * NULL or "" clears it), e.g. to tell the routed and the shared grouped
  * SwiGLU calls apart. */
 moe_status moe_profile_tag(const char* tag);
+/* Restricts the records to kernels whose name (with its tag prefix) contains
+ * one of the comma-separated substrings in `names` (host string, copied), so
+ * that a timed run brackets only the launches it reports; NULL or "" records
+ * every kernel again.  The other launches then carry no events at all. */
+moe_status moe_profile_only(const char* names);
 moe_status moe_profile_report(char* buf, size_t buf_bytes);
 
 /*

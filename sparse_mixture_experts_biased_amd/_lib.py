@@ -25,7 +25,8 @@ EXPORTED = ["moe_route_workspace_size", "moe_route", "moe_permute_workspace_size
             "moe_grouped_swiglu_train", "moe_grouped_swiglu_noalloc",
             "moe_experts_swiglu_workspace_size", "moe_experts_swiglu", "moe_combine",
             "moe_bias_update", "moe_calib_mfma_loop", "moe_calib_stream_read",
-            "moe_profile_enable", "moe_profile_tag", "moe_profile_report", "moe_last_error",
+            "moe_profile_enable", "moe_profile_tag", "moe_profile_only", "moe_profile_report",
+            "moe_last_error",
             "moe_version"]
 
 
@@ -95,6 +96,7 @@ def load() -> ctypes.CDLL:
         "moe_calib_stream_read": ([_i, _p, _sz, _p, _p], _i),
         "moe_profile_enable": ([_i], _i),
         "moe_profile_tag": ([ctypes.c_char_p], _i),
+        "moe_profile_only": ([ctypes.c_char_p], _i),
         "moe_profile_report": ([ctypes.c_char_p, _sz], _i),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_version": ([], ctypes.c_char_p),
@@ -274,6 +276,12 @@ def moe_profile_enable(on: bool = True):
 
 def moe_profile_tag(tag: str = ""):
     _check(load().moe_profile_tag(tag.encode()))
+
+
+def moe_profile_only(names: str = ""):
+    """Record only kernels whose tagged name contains one of the
+    comma-separated substrings ("" records all)."""
+    _check(load().moe_profile_only(names.encode()))
 
 
 def moe_profile_report() -> dict:

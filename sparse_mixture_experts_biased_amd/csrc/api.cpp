@@ -550,6 +550,7 @@ struct ProfRec {
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::string g_prof_tag;
+std::vector<std::string> g_prof_only;  // record only names containing one of these (empty: all)
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -571,10 +572,16 @@ namespace moe {
 int prof_begin(hipStream_t s, const char* name) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return -1;
+  const std::string full = g_prof_tag + name;
+  if (!g_prof_only.empty()) {
+    bool hit = false;
+    for (const std::string& f : g_prof_only) hit = hit || full.find(f) != std::string::npos;
+    if (!hit) return -1;
+  }
   hipEvent_t a = prof_event(), b = prof_event();
   if (!a || !b) return -1;
   if (hipEventRecord(a, s) != hipSuccess) return -1;
-  g_prof_recs.push_back(ProfRec{g_prof_tag + name, a, b, false});
+  g_prof_recs.push_back(ProfRec{full, a, b, false});
   return static_cast<int>(g_prof_recs.size()) - 1;
 }
 
@@ -593,6 +600,24 @@ extern "C" {
 moe_status moe_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_only(const char* names) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only.clear();
+  if (names) {
+    std::string cur;
+    for (const char* c = names;; ++c) {
+      if (*c == ',' || *c == '\0') {
+        if (!cur.empty()) g_prof_only.push_back(cur);
+        cur.clear();
+        if (*c == '\0') break;
+      } else {
+        cur += *c;
+      }
+    }
+  }
   return MOE_OK;
 }
 
