@@ -1372,6 +1372,14 @@ void bf16_wdma_kernel(
     l_m0 = ti.m0;
     l_nrows = min(ti.m1 - ti.m0, BM);
   }
+  // x-row loads a step issues for the load-side item: only those of row
+  // passes that hold rows of the item (a load whose every lane is out of range
+  // still costs an issue slot and address-unit time).  The rows of the passes
+  // left out keep stale values in LDS; only waves with no row of the item
+  // would read them, and those skip their multiply.
+  static_assert(kALoads == 4, "the step's waits below are written for four row passes");
+  auto x_loads = [](int nrows) { return min(max((nrows + kRP - 1) / kRP, 1), kALoads); };
+  int l_na = x_loads(l_nrows);
   uint32_t a_off[kALoads];
 #pragma unroll
   for (int i = 0; i < kALoads; ++i) {
@@ -1399,11 +1407,11 @@ void bf16_wdma_kernel(
 
   // Loads the x rows of the load side's slice into sa, then sends its weight
   // slice into stage ST.
-  uint4 sa[kALoads];
+  uint4 sa[kALoads] = {};
 #define MOE_WLOAD(ST)                                                                        \
   do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) sa[i] = __builtin_bit_cast(           \
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0));                 \
+    _Pragma("unroll") for (int i = 0; i < kALoads; ++i) if (i < l_na) sa[i] =               \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, a_off[i], kb, 0)); \
     __builtin_amdgcn_sched_barrier(0); /* rows before weights: see the step's waits */      \
     _Pragma("unroll") for (int i = 0; i < kNI; ++i) {                                       \
       const int add_ = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;                  \
@@ -1461,6 +1469,7 @@ void bf16_wdma_kernel(
         ++l_item;                                                                           \
         kb = 0;                                                                             \
         l_g = n_g; l_ntile = n_ntile; l_m0 = n_m0; l_nrows = n_nrows;                       \
+        l_na = x_loads(l_nrows);                                                            \
         set_weights();                                                                      \
         _Pragma("unroll") for (int i = 0; i < kALoads; ++i) {                               \
           const int sr_ = gather ? __builtin_amdgcn_ds_bpermute(((lane >> 3) + 8 * i) * 4, ri_l) \
@@ -1654,7 +1663,7 @@ void bf16_wdma_kernel(
   // the rows of slice k + 1, load the rows of slice k + 2 and send its
   // weights, multiply slice k, wait for slice k + 1's weights, barrier.  The
   // wait leaves in flight what was issued after those weights: this step's
-  // row and weight loads (kALoads + kNI) and the fetch loads of the steps
+  // row and weight loads (l_na + kNI) and the fetch loads of the steps
   // between (position 1 of each three issues them).  A step that multiplied
   // an item's last slice writes its output tile before the next step.
   constexpr int kNF = GATEUP ? 2 : 1;  // fetch loads
@@ -1669,7 +1678,9 @@ void bf16_wdma_kernel(
   asm volatile("" ::"v"(sa[0].x), "v"(sa[1].x), "v"(sa[2].x), "v"(sa[3].x) : "memory");
   int kc = 0;  // slices of the compute-side item multiplied
   int jc = 0;  // items finished
-#define MOE_WSTEP(U, BCUR, BNEXT, WAITN)                                                     \
+#define MOE_WWAIT(N)                                                                         \
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory")
+#define MOE_WSTEP(U, BCUR, BNEXT, WAITB)                                                     \
   if ((U) == 1) MOE_WDECODE();                                                              \
   MOE_WSWITCH();                                                                            \
   MOE_WSTORE((gk + 1) & 1);                                                                 \
@@ -1677,8 +1688,14 @@ void bf16_wdma_kernel(
   MOE_WLOAD(BNEXT);                                                                         \
   if ((U) == 1) MOE_WFETCH();                                                               \
   compute(a_st + (gk & 1) * kTile, BCUR);                                                   \
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(WAITN)      \
-               : "memory");                                                                 \
+  if (l_na == 4)                                                                            \
+    MOE_WWAIT((WAITB) + 4);                                                                 \
+  else if (l_na == 3)                                                                       \
+    MOE_WWAIT((WAITB) + 3);                                                                 \
+  else if (l_na == 2)                                                                       \
+    MOE_WWAIT((WAITB) + 2);                                                                 \
+  else                                                                                      \
+    MOE_WWAIT((WAITB) + 1);                                                                 \
   ++gk;                                                                                     \
   if (++kc == nk) {                                                                         \
     epilogue(((gk + 1) & 1) * kTile);                                                       \
@@ -1692,11 +1709,12 @@ void bf16_wdma_kernel(
     if (++jc == n_items) break;                                                             \
   }
   for (;;) {
-    MOE_WSTEP(0, b0, b2, kALoads + kNI)
-    MOE_WSTEP(1, b1, b0, kALoads + kNI + kNF)
-    MOE_WSTEP(2, b2, b1, kALoads + kNI + kNF)
+    MOE_WSTEP(0, b0, b2, kNI)
+    MOE_WSTEP(1, b1, b0, kNI + kNF)
+    MOE_WSTEP(2, b2, b1, kNI + kNF)
   }
 #undef MOE_WSTEP
+#undef MOE_WWAIT
 #undef MOE_WDECODE
 #undef MOE_WSWITCH
 #undef MOE_WFETCH
