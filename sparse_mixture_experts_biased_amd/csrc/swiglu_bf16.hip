@@ -1724,6 +1724,408 @@ void bf16_wdma_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ---------------------------------------------------------------- streaming, both operands by LDS DMA
+//
+// The weight-DMA kernel with the x rows sent into LDS by buffer loads with an
+// LDS destination too, into three stages of their own, so both operands of a
+// slice are issued two slices ahead of its multiply and the rows need no
+// staging registers or LDS stores.  The LDS holds three weight stages (256
+// rows x 64 k, 32 KB each) and three x-row stages of kXdmaRows rows (20 KB
+// each): the tile list for this kernel is built with row tiles of at most
+// kXdmaRows rows (a group with more rows gets further row tiles, which read
+// its weights again).  A step sends the x rows of the slice two ahead (only
+// the 8-row loads that hold rows of the item, so each wave issues 0 to 3 of
+// them), then its weights, multiplies its own slice, waits for the next
+// slice and meets the barrier; the stage of every step is a compile-time LDS
+// object.  Rows 160..191 of the third wave row do not exist: that wave reads
+// rows 128..159 again for its second row block, whose results belong to rows
+// past the item and are never written out.  The output tile is staged
+// through the weight stage just multiplied (free until the next step sends
+// a slice into it).  Used for groups of fewer rows than a tile on average
+// when K has at least kWdmaMinSlices slices.
+constexpr int kXdmaRows = 160;
+
+template <bool GATEUP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bf16_xdma_kernel(
+    int Kdim, int N, int x_rows, int rows, int max_tiles, int NT,
+    const TileInfo* __restrict__ tiles, const int32_t* __restrict__ meta,
+    const int32_t* __restrict__ row_index, const uint16_t* __restrict__ A, const WeightSet W,
+    uint16_t* __restrict__ out) {
+  using G = StreamGeom<64>;
+  constexpr int BNW = 256, NTHR = 512;
+  constexpr int kWavesN = 2;                   // waves: 4 along rows x 2 along weight rows
+  constexpr int kNB = BNW / kWavesN / 32;      // 32-wide weight blocks per wave
+  constexpr int kCols = GATEUP ? BNW / 2 : BNW;
+  constexpr int kNI = G::kNI, kRPI = G::kRPI;  // weight loads per wave and slice, rows per load
+  constexpr int kXI = 3;                       // x-row load slots per wave
+  constexpr int kXLoads = kXdmaRows / kRPI;    // 8-row x loads per slice (20)
+  constexpr uint32_t kOff = 0x80000000u;       // beyond every buffer (sizes < 2 GiB)
+  constexpr int kTile = G::kTileBytes;         // one weight slice stage
+  constexpr int kXTile = kXdmaRows * G::kRow;  // one x-row slice stage
+  static_assert(kWdmaStages == 3, "the step loop is unrolled over three stages");
+  static_assert(kXLoads <= 8 * kXI && kXLoads > 8 * (kXI - 1), "three load slots per wave");
+  static_assert(kXdmaRows % 32 == 0 && kXdmaRows > 128 && kXdmaRows <= 192,
+                "the third wave row holds the rows past 128");
+  __shared__ __attribute__((aligned(16))) char a0[kXTile];  // x-row stages
+  __shared__ __attribute__((aligned(16))) char a1[kXTile];
+  __shared__ __attribute__((aligned(16))) char a2[kXTile];
+  __shared__ __attribute__((aligned(16))) char b0[kTile];   // weight stages
+  __shared__ __attribute__((aligned(16))) char b1[kTile];
+  __shared__ __attribute__((aligned(16))) char b2[kTile];
+
+  // ---- this workgroup's items: first, first + nslot, ... below end
+  const int total = meta[0] * NT;
+  const int nslot = gridDim.x / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+  const int first = xcd * per_xcd + static_cast<int>(blockIdx.x) / kNumXcd;
+  const int end = min(total, (xcd + 1) * per_xcd);
+  if (first >= end) return;
+  const int n_items = (end - first + nslot - 1) / nslot;
+  const int nk = Kdim / kBK;  // at least kWdmaMinSlices
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: scalar
+  const int lane = tid % kWave;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const uint32_t rowbytes = static_cast<uint32_t>(Kdim) * 2u;
+  const uint32_t wbytes = static_cast<uint32_t>(N) * rowbytes;
+  const uint32_t kb_end = static_cast<uint32_t>(nk) * kBK * 2u;  // past the last slice
+  const __amdgpu_buffer_rsrc_t rsA = buffer_rsrc(A, static_cast<uint32_t>(x_rows) * rowbytes);
+  const __amdgpu_buffer_rsrc_t rsT =
+      buffer_rsrc(tiles, static_cast<uint32_t>(max_tiles) * sizeof(TileInfo));
+  const bool gather = GATEUP && row_index != nullptr;
+  const __amdgpu_buffer_rsrc_t rsR =
+      buffer_rsrc(row_index, gather ? static_cast<uint32_t>(rows) * 4u : 0u);
+
+  // Load slot i of a wave sends tile rows kRPI (wave + 8 i) + drow (x rows)
+  // or weight rows kRPI (wave + 8 i) + drow; lane l lands at LDS chunk l % 8
+  // of its row, so it loads the k chunk that the swizzle stores there.
+  const int drow = lane / G::kChunks;
+  const int dchunk = (lane % G::kChunks) ^ drow ^ (wave & 1);
+  auto a_offset = [&](int i, int nrows, int sr) -> uint32_t {
+    return (kRPI * (wave + 8 * i) + drow < nrows && sr >= 0 && sr < x_rows)
+               ? static_cast<uint32_t>(sr) * rowbytes + static_cast<uint32_t>(dchunk) * 16u
+               : kOff;
+  };
+  // x-row loads this wave issues per slice for an item of nrows rows: the
+  // slots whose 8 rows start below nrows
+  auto x_loads = [&](int nrows) {
+    const int m = min((nrows + kRPI - 1) / kRPI, kXLoads);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kXI; ++i) n += (wave + 8 * i < m) ? 1 : 0;
+    return n;
+  };
+
+  // ---- load-side item
+  int l_item = 0, l_g, l_ntile, l_m0, l_nrows;
+  {
+    const TileInfo t0 = tiles[first / NT];
+    int mt;
+    item_tile(first - t0.gstart * NT, max(t0.ntiles, 1), NT, mt, l_ntile);
+    const TileInfo ti = tiles[t0.gstart + mt];
+    l_g = t0.group;
+    l_m0 = ti.m0;
+    l_nrows = min(ti.m1 - ti.m0, kXdmaRows);
+  }
+  int l_nx = x_loads(l_nrows);
+  uint32_t a_off[kXI];
+#pragma unroll
+  for (int i = 0; i < kXI; ++i) {
+    const int r = kRPI * (wave + 8 * i) + drow;
+    int sr = l_m0 + r;
+    if (gather) sr = (r < l_nrows) ? row_index[l_m0 + r] : -1;
+    a_off[i] = a_offset(i, l_nrows, sr);
+  }
+  const uint32_t b_off = static_cast<uint32_t>(kRPI * wave + drow) * rowbytes +
+                         static_cast<uint32_t>(dchunk) * 16u;
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  uint32_t bcol;
+  auto set_weights = [&]() {
+    rb0 = buffer_rsrc(W.base(false, l_g, static_cast<size_t>(N) * Kdim), wbytes);
+    rb1 = buffer_rsrc(W.base(GATEUP, l_g, static_cast<size_t>(N) * Kdim), wbytes);
+    bcol = static_cast<uint32_t>(l_ntile * kCols) * rowbytes;
+  };
+  set_weights();
+  uint32_t kb = 0;  // byte offset of the load side's next k-slice
+
+  // Sends the x rows of the load side's slice into x stage AST, then its
+  // weights into weight stage BST.
+#define MOE_XLOAD(AST, BST)                                                                  \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < kXI; ++i) if (i < l_nx)                           \
+        dma16_unscoped<0>(rsA, (AST) + kRPI * (wave + 8 * i) * G::kRow, a_off[i], kb);      \
+    __builtin_amdgcn_sched_barrier(0); /* rows before weights: see the step's waits */      \
+    _Pragma("unroll") for (int i = 0; i < kNI; ++i) {                                       \
+      const int add_ = GATEUP ? kRPI * 8 * (i % (kNI / 2)) : kRPI * 8 * i;                  \
+      dma16_unscoped<kWeightPolicy>((GATEUP && i >= kNI / 2) ? rb1 : rb0,                   \
+                                    (BST) + kRPI * (wave + 8 * i) * G::kRow, b_off,          \
+                                    bcol + static_cast<uint32_t>(add_) * rowbytes + kb);    \
+    }                                                                                       \
+    kb += kBK * 2;                                                                          \
+  } while (0)
+
+  // ---- next item, fetched ahead as in the weight-DMA kernel (p: tile
+  // records, ri: in lane j + 8 i the source row of tile row 8 wave + j + 64 i)
+  int p = 0, ri = -1, ri_l = -1;
+  int n_g = 0, n_ntile = 0, n_m0 = 0, n_nrows = 0;
+  int nw = first + min(1, n_items - 1) * nslot;  // next item
+  int t0rec = nw / NT;                           // a tile of its group
+  int rec = 0;                                   // its row tile
+  int fa = 0;                                    // fetches since nw changed
+
+#define MOE_XDECODE()                                                                        \
+  do {                                                                                      \
+    if (fa == 1) { /* the group record just arrived: locate the row tile */                 \
+      const int gstart_ = __builtin_amdgcn_readlane(p, 3);                                  \
+      const int gnt_ = max(__builtin_amdgcn_readlane(p, 4), 1);                             \
+      int mt_;                                                                              \
+      item_tile(nw - gstart_ * NT, gnt_, NT, mt_, n_ntile);                                 \
+      n_g = __builtin_amdgcn_readlane(p, 0);                                                \
+      rec = gstart_ + mt_;                                                                  \
+    }                                                                                       \
+    n_m0 = __builtin_amdgcn_readlane(p, 9);                                                 \
+    n_nrows = min(__builtin_amdgcn_readlane(p, 10) - n_m0, kXdmaRows);                      \
+    if (GATEUP) /* a register of its own: ri's is then free for the next fetch */            \
+      asm volatile("v_mov_b32 %0, %1" : "=&v"(ri_l) : "v"(ri));                             \
+  } while (0)
+#define MOE_XSWITCH()                                                                        \
+  do {                                                                                      \
+    if (kb == kb_end) {                                                                     \
+      if (l_item + 1 < n_items) {                                                           \
+        ++l_item;                                                                           \
+        kb = 0;                                                                             \
+        l_g = n_g; l_ntile = n_ntile; l_m0 = n_m0; l_nrows = n_nrows;                       \
+        l_nx = x_loads(l_nrows);                                                            \
+        set_weights();                                                                      \
+        _Pragma("unroll") for (int i = 0; i < kXI; ++i) {                                   \
+          const int sr_ = gather ? __builtin_amdgcn_ds_bpermute(((lane >> 3) + 8 * i) * 4, ri_l) \
+                                 : l_m0 + kRPI * (wave + 8 * i) + drow;                     \
+          a_off[i] = a_offset(i, l_nrows, sr_);                                             \
+        }                                                                                   \
+        nw = first + min(l_item + 1, n_items - 1) * nslot;                                  \
+        t0rec = nw / NT;                                                                    \
+        fa = 0;                                                                             \
+      } else {                                                                              \
+        kb = kb_end - kBK * 2; /* past the last item: its last slice again */               \
+      }                                                                                     \
+    }                                                                                       \
+  } while (0)
+#define MOE_XFETCH()                                                                         \
+  do {                                                                                      \
+    int z_ = 0;                                                                             \
+    asm volatile("" : "+v"(z_));                                                            \
+    const int ln_ = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z_));     \
+    if (GATEUP) { /* without row_index every load is out of range: no branch */             \
+      const int r_ = wave * 8 + (ln_ & 7) + 64 * ((ln_ >> 3) & 3);                          \
+      ri = __builtin_amdgcn_raw_buffer_load_b32(                                            \
+          rsR, r_ < n_nrows ? static_cast<uint32_t>(n_m0 + r_) * 4u : kOff, 0, 0);          \
+    }                                                                                       \
+    p = __builtin_amdgcn_raw_buffer_load_b32(                                               \
+        rsT, static_cast<uint32_t>((ln_ & 8) ? rec : t0rec) * 32u + (ln_ & 7) * 4u, 0, 0);  \
+    fa = min(fa + 1, 3);                                                                    \
+  } while (0)
+
+  // ---- compute side (trails the load side by two slices)
+  int c_m0 = l_m0, c_nrows = l_nrows, c_n0 = l_ntile * kCols;
+
+  int brow[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    if (GATEUP) {
+      const int half = kNB / 2;
+      const int base = wn * (BNW / 2 / kWavesN);
+      brow[nb] = (nb < half) ? base + nb * 32 : BNW / 2 + base + (nb - half) * 32;
+    } else {
+      brow[nb] = wn * (BNW / kWavesN) + nb * 32;
+    }
+  }
+  // tile rows of the wave's two 32-row blocks (rows past kXdmaRows are not
+  // in the stage: the third wave row reads its first block again instead)
+  const int arow0 = wm * 64;
+  const int arow1 = min(wm * 64 + 32, kXdmaRows - 32);
+
+  f32x16_t acc[2][kNB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mb][nb][q] = 0.0f;
+
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  constexpr int kSteps = kBK / 16;
+
+  // As in the weight-DMA kernel: both row blocks of a busy wave, weight block
+  // by weight block, the weight fragment first; the fragments of 16-k step
+  // kk + 1 are read between the MFMAs of step kk.
+  auto compute = [&](const char* as, const char* bs) {
+    if (wm * 64 >= c_nrows) return;
+    bf16x8_t bq[kSteps][kNB], aq[kSteps][2];
+#pragma unroll
+    for (int kk = 0; kk < kSteps; ++kk) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        bq[kk][nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(brow[nb] + fr, kk * 2 + fh));
+      aq[kk][0] = *reinterpret_cast<const bf16x8_t*>(as + swz(arow0 + fr, kk * 2 + fh));
+      aq[kk][1] = *reinterpret_cast<const bf16x8_t*>(as + swz(arow1 + fr, kk * 2 + fh));
+    }
+#pragma unroll
+    for (int kk = 0; kk < kSteps; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq[kk][nb], aq[kk][mb],
+                                                                acc[mb][nb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kNB + 2, 0);
+#pragma unroll
+    for (int st = 0; st + 1 < kSteps; ++st) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 2; i < kNB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kNB, 0);
+  };
+
+  // Output tile of the compute-side item, staged through the weight stage
+  // stg (just multiplied) in rounds of kRoundRows rows.  Block (mb, nb) of a
+  // lane holds tile row wm*64 + mb*32 + (lane & 31) at the four consecutive
+  // weight columns 8*(q/4) + 4*(lane/32) + 0..3 of registers q: one 8-byte
+  // LDS write each, at 16-byte chunk (col / 8) XOR (row & 15) of a bf16 row
+  // of kCols, read back as whole 16-byte chunks.
+  constexpr int kOutRowBytes = kCols * 2;
+  constexpr int kRoundRows = kTile / kOutRowBytes;
+  constexpr int kOutChunks = kCols / 8;
+  constexpr int kReadRows = NTHR / kOutChunks;
+  static_assert(kRoundRows % 64 == 0, "rounds hold whole waves' rows");
+  static_assert(NTHR % kOutChunks == 0 && kReadRows % 16 == 0, "read-out rows keep row & 15");
+  auto epilogue = [&](char* stg) {
+    int ez = 0;  // opaque zero: keeps the lane-id computation inside the loop
+    asm volatile("" : "+v"(ez));
+    const int e_lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, ez));
+    const int etid = wave * kWave + e_lane;
+    const int e_fr = e_lane & 31, e_fh = e_lane >> 5;
+#pragma unroll
+    for (int r0 = 0; r0 < kXdmaRows; r0 += kRoundRows) {
+      if (r0 >= c_nrows) break;
+      if (wm * 64 >= r0 && wm * 64 < r0 + kRoundRows) {  // a wave's 64 rows lie in one round
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          // rows past the item are staged too (never written out)
+          const int R = wm * 64 + mb * 32 + e_fr - r0;
+          int roff = R * kOutRowBytes;
+          asm("" : "+v"(roff));  // one opaque offset: keeps each store's pointer chain short
+#pragma unroll
+          for (int nb = 0; nb < (GATEUP ? kNB / 2 : kNB); ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int col = (GATEUP ? wn * (BNW / 2 / kWavesN) : wn * (BNW / kWavesN)) + nb * 32 +
+                              8 * g + 4 * e_fh;
+              float v[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float gv = acc[mb][nb][4 * g + j];
+                v[j] = GATEUP ? silu(gv) * acc[mb][nb + kNB / 2][4 * g + j] : gv;
+              }
+              // one 64-bit store (two 32-bit ones get merged without their alias
+              // scope), a few pointer steps from the stage
+              *reinterpret_cast<uint64_t*>(
+                  stg + (roff + ((((col >> 3) ^ (R & 15)) << 4) + (col & 4) * 2))) =
+                  static_cast<uint64_t>(pack_bf16x2(v[0], v[1])) |
+                  (static_cast<uint64_t>(pack_bf16x2(v[2], v[3])) << 32);
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const int rl = etid / kOutChunks, cl = etid % kOutChunks;
+      int soff = rl * kOutRowBytes + ((cl ^ (rl & 15)) << 4);
+      asm("" : "+v"(soff));
+      uint16_t* dst = out + static_cast<size_t>(c_m0 + r0 + rl) * N + c_n0 + cl * 8;
+#pragma unroll
+      for (int it = 0; it < kRoundRows / kReadRows; ++it) {
+        if (rl < c_nrows - r0 - it * kReadRows) {
+          // vector copies (a uint4 assignment is a memcpy, whose LDS load
+          // carries no alias scope); the down product's rows leave through
+          // non-temporal stores
+          const bf16x8_t v_ =
+              *reinterpret_cast<const bf16x8_t*>(stg + (soff + it * kReadRows * kOutRowBytes));
+          bf16x8_t* d_ = reinterpret_cast<bf16x8_t*>(dst + static_cast<size_t>(it) * kReadRows * N);
+          if (GATEUP)
+            *d_ = v_;
+          else
+            __builtin_nontemporal_store(v_, d_);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+
+  // ---- stream.  Prologue: slice 0 in LDS, slice 1 in flight.  Step k
+  // (stages k % 3): send slice k + 2, multiply slice k, wait for slice k + 1,
+  // barrier.  The wait leaves in flight what was issued after slice k + 1's
+  // weights: this step's x-row and weight loads (l_nx + kNI), after the fetch
+  // loads that position 1 of each three issues first (so that the records
+  // they bring have three steps of loads behind them when read).
+  constexpr int kNF = GATEUP ? 2 : 1;  // fetch loads
+  MOE_XLOAD(a0, b0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  MOE_XLOAD(a1, b1);
+  int kc = 0;  // slices of the compute-side item multiplied
+  int jc = 0;  // items finished
+#define MOE_XWAIT(N)                                                                         \
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory")
+#define MOE_XSTEP(U, ACUR, BCUR, ANEXT, BNEXT, WAITB)                                        \
+  if ((U) == 1) MOE_XDECODE();                                                              \
+  MOE_XSWITCH();                                                                            \
+  if ((U) == 1) MOE_XFETCH();                                                               \
+  MOE_XLOAD(ANEXT, BNEXT);                                                                  \
+  compute(ACUR, BCUR);                                                                      \
+  if (l_nx == 3)                                                                            \
+    MOE_XWAIT((WAITB) + 3);                                                                 \
+  else if (l_nx == 2)                                                                       \
+    MOE_XWAIT((WAITB) + 2);                                                                 \
+  else if (l_nx == 1)                                                                       \
+    MOE_XWAIT((WAITB) + 1);                                                                 \
+  else                                                                                      \
+    MOE_XWAIT(WAITB);                                                                       \
+  if (++kc == nk) {                                                                         \
+    epilogue(BCUR);                                                                         \
+    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                        \
+        _Pragma("unroll") for (int nb = 0; nb < kNB; ++nb)                                  \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.0f;           \
+    c_m0 = l_m0;                                                                            \
+    c_nrows = l_nrows;                                                                      \
+    c_n0 = l_ntile * kCols;                                                                 \
+    kc = 0;                                                                                 \
+    if (++jc == n_items) break;                                                             \
+  }
+  for (;;) {
+    MOE_XSTEP(0, a0, b0, a2, b2, kNI)
+    MOE_XSTEP(1, a1, b1, a0, b0, kNI + kNF)
+    MOE_XSTEP(2, a2, b2, a1, b1, kNI)
+  }
+#undef MOE_XSTEP
+#undef MOE_XWAIT
+#undef MOE_XDECODE
+#undef MOE_XSWITCH
+#undef MOE_XFETCH
+#undef MOE_XLOAD
+  // the trailing slices still write LDS: drain them before exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Shapes the weight-DMA streaming kernel takes (K of whole slices, at least
 // kWdmaMinSlices of them; N of whole column tiles).
 bool wdma_shape(int K, int N, int cols) {
@@ -1753,11 +2155,15 @@ int stream_grid() {
 template <int BM, int BNW, int NTHR, int NSETS>
 hipError_t launch_down(int n_groups, int K, int N, int rows, bool mfma_bound,
                        const SwigluWorkspace& w, const uint16_t* A, const WeightSet& W,
-                       const float* row_scale, uint16_t* C, const char* name, hipStream_t s) {
-  const int max_tiles = max_tiles_for(rows, n_groups, BM);
+                       const float* row_scale, uint16_t* C, const char* name, hipStream_t s,
+                       int tile_rows = BM) {
+  const int max_tiles = max_tiles_for(rows, n_groups, tile_rows);
   const int nt = (N + BNW - 1) / BNW;
   ProfScope prof_(s, name);
-  if (stream_shape(K, N, 256) && mfma_bound) {
+  if (tile_rows == kXdmaRows && BNW == 256 && row_scale == nullptr && wdma_shape(K, N, 256)) {
+    hipLaunchKernelGGL((bf16_xdma_kernel<false>), dim3(stream_grid()), dim3(512), 0, s, K, N,
+                       rows, rows, max_tiles, nt, w.tiles, w.meta, nullptr, A, W, C);
+  } else if (stream_shape(K, N, 256) && mfma_bound) {
     hipLaunchKernelGGL((bf16_stream_kernel<false, kStreamBK>), dim3(stream_grid()), dim3(512), 0,
                        s, K, N, rows, rows, nt, w.tiles, w.meta, nullptr, A, W, row_scale, C,
                        nullptr);
@@ -1787,11 +2193,15 @@ template <int BM, int BNW, int NTHR, int NSETS, bool AU>
 hipError_t launch_gateup(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                          bool mfma_bound, const int32_t* row_index, const uint16_t* x,
                          const WeightSet& W, uint16_t* act, uint16_t* au,
-                         const SwigluWorkspace& w, hipStream_t s) {
-  const int max_tiles = max_tiles_for(rows, n_groups, BM);
+                         const SwigluWorkspace& w, hipStream_t s, int tile_rows = BM) {
+  const int max_tiles = max_tiles_for(rows, n_groups, tile_rows);
   const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
   ProfScope prof_(s, "gateup_bf16");
-  if (stream_shape(d_model, d_ffn, 128) && mfma_bound) {
+  if (!AU && tile_rows == kXdmaRows && BNW == 256 && wdma_shape(d_model, d_ffn, 128)) {
+    hipLaunchKernelGGL((bf16_xdma_kernel<true>), dim3(stream_grid()), dim3(512), 0, s, d_model,
+                       d_ffn, x_rows, rows, max_tiles, nt1, w.tiles, w.meta, row_index, x, W,
+                       act);
+  } else if (stream_shape(d_model, d_ffn, 128) && mfma_bound) {
     hipLaunchKernelGGL((bf16_stream_kernel<true, kStreamBK, AU>), dim3(stream_grid()), dim3(512),
                        0, s, d_model, d_ffn, x_rows, rows, nt1, w.tiles, w.meta, row_index, x, W,
                        nullptr, act, au);
@@ -1819,20 +2229,34 @@ template <int BM, int BNW, int NTHR, int NSETS>
 hipError_t launch_products(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                            const int32_t* row_index, const uint16_t* x, const WeightSet& Wgu,
                            const WeightSet& Wd, const float* row_scale, uint16_t* y,
-                           uint16_t* au, const SwigluWorkspace& w, hipStream_t s) {
+                           uint16_t* au, const SwigluWorkspace& w, hipStream_t s,
+                           int tile_rows = BM) {
   uint16_t* act = static_cast<uint16_t*>(w.act);
   const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
   hipError_t err =
       au != nullptr
           ? launch_gateup<BM, BNW, NTHR, NSETS, true>(n_groups, d_model, d_ffn, rows, x_rows,
                                                       mfma_bound, row_index, x, Wgu, act, au, w,
-                                                      s)
+                                                      s, tile_rows)
           : launch_gateup<BM, BNW, NTHR, NSETS, false>(n_groups, d_model, d_ffn, rows, x_rows,
                                                        mfma_bound, row_index, x, Wgu, act,
-                                                       nullptr, w, s);
+                                                       nullptr, w, s, tile_rows);
   if (err != hipSuccess) return err;
   return launch_down<BM, BNW, NTHR, NSETS>(n_groups, d_ffn, d_model, rows, mfma_bound, w, act, Wd,
-                                           row_scale, y, "down_bf16", s);
+                                           row_scale, y, "down_bf16", s, tile_rows);
+}
+
+// Row-tile size of the tile list for both products: kXdmaRows when the groups
+// average at most kXdmaMaxAvgRows rows (so that few of them need a second row
+// tile, which reads their weights again) and both products take the kernel
+// that sends both operands by LDS DMA (inference forms), else 256.
+constexpr int kXdmaMaxAvgRows = 128;
+int products_tile_rows(int n_groups, int d_model, int d_ffn, int rows, bool au,
+                       bool row_scale) {
+  return (rows <= kXdmaMaxAvgRows * static_cast<long>(n_groups) && !au && !row_scale &&
+          wdma_shape(d_model, d_ffn, 128) && wdma_shape(d_ffn, d_model, 256))
+             ? kXdmaRows
+             : 256;
 }
 
 }  // namespace
@@ -1856,11 +2280,13 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
                               const uint16_t* wd, const float* row_scale, uint16_t* y,
                               uint16_t* au, void* ws, hipStream_t s) {
   SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
-  hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, w, s);
+  const int bm = products_tile_rows(n_groups, d_model, d_ffn, rows, au != nullptr,
+                                    row_scale != nullptr);
+  hipError_t err = launch_build_tiles(n_groups, rows, bm, offsets, w, s);
   if (err != hipSuccess) return err;
   return launch_products<256, 256, 512, 2>(n_groups, d_model, d_ffn, rows, x_rows, row_index, x,
                                            WeightSet::one(wg, wu), WeightSet::one(wd, wd),
-                                           row_scale, y, au, w, s);
+                                           row_scale, y, au, w, s, bm);
 }
 
 hipError_t launch_experts_bf16(int E_r, int E_s, int T, int K, int d_model, int d_ffn,

@@ -359,6 +359,37 @@ SWIGLU_CASES = [
     (1000, 512, 2048, 64, 4, torch.bfloat16),
 ]
 
+# (T, d, f, E, K, hot): the first `hot` experts' scores raised by 0.5, so
+# they take most tokens and need several row tiles while the average stays
+# below 128 rows (160-row tiles, both operands sent by LDS DMA)
+SWIGLU_SKEW_CASES = [
+    (1500, 1024, 1024, 64, 4, 4),
+    (700, 768, 1280, 80, 2, 2),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,K,hot", SWIGLU_SKEW_CASES)
+def test_grouped_swiglu_skewed_groups(T, d, f, E, K, hot):
+    say(f"moe_grouped_swiglu skewed T={T} d={d} f={f} E={E} K={K} hot={hot}")
+    rng = np.random.default_rng(T + d + f + hot)
+    scores = rng.random((T, E)).astype(np.float32)
+    scores[:, :hot] += 0.5
+    idx = O.biased_topk(scores, None, K)
+    off, rt, _ = O.permute(idx, E)
+    loads = np.diff(off)
+    assert loads[:hot].min() > 160 and T * K <= 128 * E  # several row tiles, 160-row tiles
+    x = _tokens(T, d, torch.bfloat16, 60 + T)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, 70 + E)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(rt).to(DEV), wg, wu, wd,
+                    T * K)
+    ref = O.grouped_swiglu(host_array(x), off, rt, (host_array(wg), host_array(wu), host_array(wd)))
+    yh = to_host_f64(y)
+    assert rel_err(yh, ref) <= out_tol("bf16")
+    for i in range(E):
+        lo, hi = off[i], off[i + 1]
+        if hi > lo:
+            assert rel_err(yh[lo:hi], ref[lo:hi]) <= 4 * out_tol("bf16")
+
 
 @pytest.mark.parametrize("T,d,f,E,K,dtype", SWIGLU_CASES)
 def test_grouped_swiglu_parity(T, d, f, E, K, dtype):
