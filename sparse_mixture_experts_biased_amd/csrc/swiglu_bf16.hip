@@ -1730,20 +1730,20 @@ void bf16_wdma_kernel(
 // LDS destination too, into three stages of their own, so both operands of a
 // slice are issued two slices ahead of its multiply and the rows need no
 // staging registers or LDS stores.  The LDS holds three weight stages (256
-// rows x 64 k, 32 KB each) and three x-row stages of kXdmaRows rows (20 KB
+// rows x 64 k, 32 KB each) and three x-row stages of kXdmaRows rows (21 KB
 // each): the tile list for this kernel is built with row tiles of at most
 // kXdmaRows rows (a group with more rows gets further row tiles, which read
 // its weights again).  A step sends the x rows of the slice two ahead (only
 // the 8-row loads that hold rows of the item, so each wave issues 0 to 3 of
 // them), then its weights, multiplies its own slice, waits for the next
 // slice and meets the barrier; the stage of every step is a compile-time LDS
-// object.  Rows 160..191 of the third wave row do not exist: that wave reads
-// rows 128..159 again for its second row block, whose results belong to rows
-// past the item and are never written out.  The output tile is staged
+// object.  Rows kXdmaRows..191 of the third wave row do not exist: lanes of
+// its second row block read the stage's last row for them, and their results
+// belong to rows past the item, never written out.  The output tile is staged
 // through the weight stage just multiplied (free until the next step sends
 // a slice into it).  Used for groups of fewer rows than a tile on average
 // when K has at least kWdmaMinSlices slices.
-constexpr int kXdmaRows = 160;
+constexpr int kXdmaRows = 168;
 
 template <bool GATEUP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1765,8 +1765,8 @@ void bf16_xdma_kernel(
   constexpr int kXTile = kXdmaRows * G::kRow;  // one x-row slice stage
   static_assert(kWdmaStages == 3, "the step loop is unrolled over three stages");
   static_assert(kXLoads <= 8 * kXI && kXLoads > 8 * (kXI - 1), "three load slots per wave");
-  static_assert(kXdmaRows % 32 == 0 && kXdmaRows > 128 && kXdmaRows <= 192,
-                "the third wave row holds the rows past 128");
+  static_assert(kXdmaRows % kRPI == 0 && kXdmaRows > 160 && kXdmaRows <= 192,
+                "the third wave row holds the rows past 128, its second block some of them");
   __shared__ __attribute__((aligned(16))) char a0[kXTile];  // x-row stages
   __shared__ __attribute__((aligned(16))) char a1[kXTile];
   __shared__ __attribute__((aligned(16))) char a2[kXTile];
@@ -1942,10 +1942,11 @@ void bf16_xdma_kernel(
       brow[nb] = wn * (BNW / kWavesN) + nb * 32;
     }
   }
-  // tile rows of the wave's two 32-row blocks (rows past kXdmaRows are not
-  // in the stage: the third wave row reads its first block again instead)
-  const int arow0 = wm * 64;
-  const int arow1 = min(wm * 64 + 32, kXdmaRows - 32);
+  // tile rows of this lane's fragment in the wave's two 32-row blocks (rows
+  // past kXdmaRows are not in the stage: the third wave row's second block
+  // reads its last row instead, for results that are never written out)
+  const int arow0 = wm * 64 + (lane & 31);
+  const int arow1 = min(wm * 64 + 32 + (lane & 31), kXdmaRows - 1);
 
   f32x16_t acc[2][kNB];
 #pragma unroll
@@ -1970,8 +1971,8 @@ void bf16_xdma_kernel(
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         bq[kk][nb] = *reinterpret_cast<const bf16x8_t*>(bs + swz(brow[nb] + fr, kk * 2 + fh));
-      aq[kk][0] = *reinterpret_cast<const bf16x8_t*>(as + swz(arow0 + fr, kk * 2 + fh));
-      aq[kk][1] = *reinterpret_cast<const bf16x8_t*>(as + swz(arow1 + fr, kk * 2 + fh));
+      aq[kk][0] = *reinterpret_cast<const bf16x8_t*>(as + swz(arow0, kk * 2 + fh));
+      aq[kk][1] = *reinterpret_cast<const bf16x8_t*>(as + swz(arow1, kk * 2 + fh));
     }
 #pragma unroll
     for (int kk = 0; kk < kSteps; ++kk)
