@@ -1035,12 +1035,26 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
     if ((err = rows_gemm(a, max_tiles * a.NT, s)) != hipSuccess) return err;
     au = w.au;
   }
+  // The activation-gradient products of steps 2 and 3 run over the 256-row
+  // tiles, or, for groups of at most 128 rows on average, over tiles for the
+  // kernel that sends both operands by LDS DMA, built into the 128-row list's
+  // arrays (sized for more tiles; step 1 is done with them by then).
+  const int nt_rows = grouped_nt_tile_rows(n_groups, rows, d, f, 2 * f, d);
+  SwigluWorkspace tnt = t256;
+  if (nt_rows != 256) {
+    tnt.tiles = w.tiles.tiles;
+    tnt.group_tile_start = w.tiles.group_tile_start;
+    tnt.meta = w.tiles.meta;
+    if ((err = launch_build_tiles(n_groups, rows, nt_rows, offsets, tnt, s)) != hipSuccess)
+      return err;
+  }
   // 2. d act = dy W_down (B = W_down^T [f, d]) -> [rows, f], held in the daT
   //    region (rpad >= rows; daT is written only in step 4), with the forward
-  //    pass's down-direction kernels over the 256-row tiles; then da, du -> dadu
+  //    pass's down-direction kernels; then da, du -> dadu
   uint16_t* dact = w.daT;
-  if ((err = launch_grouped_nt_bf16(n_groups, d, f, rows, offsets, t256, dy, wd_t, dact,
-                                    "bwd_dact_bf16", s, /*tiles_built=*/true)) != hipSuccess)
+  if ((err = launch_grouped_nt_bf16(n_groups, d, f, rows, offsets, tnt, dy, wd_t, dact,
+                                    "bwd_dact_bf16", s, /*tiles_built=*/true, nt_rows)) !=
+      hipSuccess)
     return err;
   {
     const long n8 = static_cast<long>(rows) * (f / 8);
@@ -1051,8 +1065,9 @@ hipError_t launch_swiglu_backward(int n_groups, int d, int f, int rows, int x_ro
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // 3. dx = [da | du] [W_gate^T | W_up^T]^T  (K = 2f, B = [d, 2f]) -> dx [rows, d]
-  if ((err = launch_grouped_nt_bf16(n_groups, 2 * f, d, rows, offsets, t256, w.dadu, wgu_t, dx,
-                                    "bwd_dx_bf16", s, /*tiles_built=*/true)) != hipSuccess)
+  if ((err = launch_grouped_nt_bf16(n_groups, 2 * f, d, rows, offsets, tnt, w.dadu, wgu_t, dx,
+                                    "bwd_dx_bf16", s, /*tiles_built=*/true, nt_rows)) !=
+      hipSuccess)
     return err;
   // 4. per-expert transposed activations (rows padded to 64 per expert)
   {

@@ -2264,14 +2264,25 @@ int products_tile_rows(int n_groups, int d_model, int d_ffn, int rows, bool au,
 hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
                                   const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
                                   uint16_t* C, const char* name, hipStream_t s,
-                                  bool tiles_built) {
+                                  bool tiles_built, int tile_rows) {
+  if (tile_rows != 256 && tile_rows != kXdmaRows) return hipErrorInvalidValue;
   if (!tiles_built) {
-    hipError_t err = launch_build_tiles(n_groups, rows, 256, offsets, w, s);
+    hipError_t err = launch_build_tiles(n_groups, rows, tile_rows, offsets, w, s);
     if (err != hipSuccess) return err;
   }
   const bool mfma_bound = rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups);
   return launch_down<256, 256, 512, 2>(n_groups, K, N, rows, mfma_bound, w, A,
-                                       WeightSet::one(W, W), nullptr, C, name, s);
+                                       WeightSet::one(W, W), nullptr, C, name, s, tile_rows);
+}
+
+int grouped_nt_tile_rows(int n_groups, int rows, int K1, int N1, int K2, int N2) {
+  const auto fits = [&](int K, int N) {
+    return wdma_shape(K, N, 256) &&
+           static_cast<long long>(rows) * N * 2 < (1ll << 31);  // 32-bit buffer offsets
+  };
+  return (rows <= kXdmaMaxAvgRows * static_cast<long>(n_groups) && fits(K1, N1) && fits(K2, N2))
+             ? kXdmaRows
+             : 256;
 }
 
 hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, int x_rows,

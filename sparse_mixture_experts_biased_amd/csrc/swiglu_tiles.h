@@ -153,13 +153,19 @@ hipError_t launch_experts_bf16(int E_r, int E_s, int T, int K, int d_model, int 
 
 // Grouped C = A W[g]^T over the rows of each group (bf16, fp32 accumulation):
 // A [rows, K], W [n_groups, N, K], C [rows, N]; K a multiple of 64.  Builds a
-// 256-row tile list into w's tile arrays (sized by swiglu_layout with min_bm
-// <= 256; tiles_built: w already holds that list for these offsets) and runs
-// the grouped SwiGLU's down-direction kernels.  `name` tags the launch in the
-// profile records.
+// tile list of tile_rows-row tiles into w's tile arrays (sized by
+// swiglu_layout with min_bm <= tile_rows; tiles_built: w already holds that
+// list for these offsets) and runs the grouped SwiGLU's down-direction
+// kernels.  tile_rows is 256 or what grouped_nt_tile_rows returns.  `name`
+// tags the launch in the profile records.
 hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
                                   const SwigluWorkspace& w, const uint16_t* A, const uint16_t* W,
                                   uint16_t* C, const char* name, hipStream_t s,
-                                  bool tiles_built = false);
+                                  bool tiles_built = false, int tile_rows = 256);
+
+// Row-tile size for a pair of such products over the same groups, (K1, N1)
+// and (K2, N2): the rows of the kernel that sends both operands by LDS DMA
+// when the groups average at most 128 rows and both shapes fit it, else 256.
+int grouped_nt_tile_rows(int n_groups, int rows, int K1, int N1, int K2, int N2);
 
 }  // namespace moe

@@ -58,8 +58,24 @@ def test_transpose_experts():
     (300, 128, 128, 1, 1, True),      # one group, identity rows (shared-expert form)
     (1300, 512, 512, 4, 1, False)])   # streaming-kernel shapes in the a|u forward
 def test_grouped_swiglu_backward_parity(T, d, f, E, K, identity, stored):
+    _check_grouped_backward(T, d, f, E, K, identity, stored)
+
+
+# Groups of at most 128 rows on average with K and N of whole slices and column
+# tiles: the activation-gradient products run over the row tiles of the kernel
+# that sends both operands by LDS DMA; hot: expert 0 takes most tokens (a group
+# of several such row tiles beside small ones).
+@pytest.mark.parametrize("stored", [False, True], ids=["recompute", "stored_au"])
+@pytest.mark.parametrize("T,d,f,E,K,hot", [
+    (1000, 1024, 768, 16, 2, False),
+    (900, 768, 1024, 16, 2, True)])
+def test_grouped_swiglu_backward_dma_tiles(T, d, f, E, K, hot, stored):
+    _check_grouped_backward(T, d, f, E, K, False, stored, hot=hot)
+
+
+def _check_grouped_backward(T, d, f, E, K, identity, stored, hot=False):
     say(f"moe_grouped_swiglu_backward T={T} d={d} f={f} E={E} K={K} identity={identity} "
-        f"stored={stored}")
+        f"stored={stored} hot={hot}")
     rng = np.random.default_rng(T + E)
     x = _bf16((T, d), 1.0, 3 + T)
     wg = _bf16((E, f, d), 1 / math.sqrt(d), 4)
@@ -69,8 +85,13 @@ def test_grouped_swiglu_backward_parity(T, d, f, E, K, identity, stored):
         off = np.array([0, T], np.int32)
         rt = None
     else:
-        idx = O.biased_topk(rng.random((T, E)).astype(np.float32), None, K)
+        scores = rng.random((T, E)).astype(np.float32)
+        if hot:
+            scores[:, 0] += 0.6
+        idx = O.biased_topk(scores, None, K)
         off, rt, _ = O.permute(idx, E)
+        if hot:
+            assert np.diff(off)[0] > 2 * 168 and off[-1] <= 128 * E
     rows = int(off[-1])
     dy = _bf16((rows, d), 1.0, 7)
     gu_t, d_t = _prep_t(wg, wu, wd)
