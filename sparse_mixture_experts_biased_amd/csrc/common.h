@@ -23,7 +23,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU(x) = x * sigma(x), with the hardware reciprocal (about 1 ulp) in place
+// of an IEEE division: the products are rounded to bf16 or summed in fp32 far
+// above that error, and x -> -inf still gives -0 (rcp(inf) = 0).
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 // ---------------------------------------------------------------- sizes
 
