@@ -1741,8 +1741,9 @@ void bf16_wdma_kernel(
 // its second row block read the stage's last row for them, and their results
 // belong to rows past the item, never written out.  The output tile is staged
 // through the weight stage just multiplied (free until the next step sends
-// a slice into it).  Used for groups of fewer rows than a tile on average
-// when K has at least kWdmaMinSlices slices.
+// a slice into it).  Used for groups of at most 128 rows on average when K
+// has at least kWdmaMinSlices slices: the inference forms of both products,
+// and the backward's activation-gradient products.
 constexpr int kXdmaRows = 168;
 
 template <bool GATEUP>
