@@ -350,36 +350,54 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(
   const int tid = threadIdx.x;
   const int c8 = tid & 7;     // 8-column piece
   const int pr = tid >> 3;    // row pair 0..31
-  uint4 v[4][2];
+  // Branch-free loads, so that a thread's eight index loads, then its eight
+  // data loads, are in flight together: a row past the tile, a piece past C
+  // or an invalid source row loads from a valid address (the tile's first row,
+  // source row 0) and is zeroed afterwards.
+  const bool col_ok = c0 + 8 * c8 < C && src_rows > 0;
+  const int col = col_ok ? c0 + 8 * c8 : 0;
+  int sr[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = 64 * i + 2 * pr + h;
-      v[i][h] = make_uint4(0, 0, 0, 0);
-      if (r < nr && c0 + 8 * c8 < C) {
-        const int gr = m0 + r;
-        const int sr = row_index ? row_index[gr] : gr;
-        if (sr >= 0 && sr < src_rows) {
-          const uint16_t* sp = src + static_cast<size_t>(sr) * ld_src + c0 + 8 * c8;
-          if (TR == kTrAct) {
-            const uint4 av = *reinterpret_cast<const uint4*>(sp);
-            const uint4 uv = *reinterpret_cast<const uint4*>(sp + C);
-            const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-            uint32_t o[4];
+      const int gr = m0 + (r < nr ? r : 0);  // nr >= 1: m0 is a row of the tile
+      sr[i][h] = row_index ? row_index[gr] : gr;
+    }
+  bool ok[4][2];
+  uint4 av[4][2], uv[4][2];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float lo = silu(__uint_as_float(aw[q] << 16)) * __uint_as_float(uw[q] << 16);
-              const float hi = silu(__uint_as_float(aw[q] & 0xffff0000u)) *
-                               __uint_as_float(uw[q] & 0xffff0000u);
-              o[q] = pack_bf16x2(lo, hi);
-            }
-            v[i][h] = make_uint4(o[0], o[1], o[2], o[3]);
-          } else {
-            v[i][h] = *reinterpret_cast<const uint4*>(sp);
-          }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 64 * i + 2 * pr + h;
+      ok[i][h] = r < nr && col_ok && sr[i][h] >= 0 && sr[i][h] < src_rows;
+      const uint16_t* sp =
+          src + (ok[i][h] ? static_cast<size_t>(sr[i][h]) * ld_src + col : static_cast<size_t>(0));
+      av[i][h] = *reinterpret_cast<const uint4*>(sp);
+      if (TR == kTrAct) uv[i][h] = *reinterpret_cast<const uint4*>(sp + C);
+    }
+  uint4 v[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 x = av[i][h];
+      if (TR == kTrAct) {
+        const uint4 u4 = uv[i][h];
+        const uint32_t aw[4] = {x.x, x.y, x.z, x.w}, uw[4] = {u4.x, u4.y, u4.z, u4.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = silu(__uint_as_float(aw[q] << 16)) * __uint_as_float(uw[q] << 16);
+          const float hi =
+              silu(__uint_as_float(aw[q] & 0xffff0000u)) * __uint_as_float(uw[q] & 0xffff0000u);
+          o[q] = pack_bf16x2(lo, hi);
         }
+        x = make_uint4(o[0], o[1], o[2], o[3]);
       }
+      v[i][h] = ok[i][h] ? x : make_uint4(0, 0, 0, 0);
     }
   const int swz = 16 * c8;  // the XOR of every column this thread writes (c >> 3 == c8)
 #pragma unroll
