@@ -30,15 +30,17 @@ __global__ __launch_bounds__(kChunk) void hist_kernel(int T, int E, int K,
                                                       const int32_t* __restrict__ idx,
                                                       int32_t* __restrict__ counts) {
   extern __shared__ int32_t cnt[];
+  // the token's K ids loaded together (before any is used), then counted
+  const int t = blockIdx.x * kChunk + threadIdx.x;
+  int ex[MOE_MAX_TOPK_DEV];
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    ex[k] = (t < T && k < K) ? idx[static_cast<size_t>(t) * K + k] : -1;
   for (int i = threadIdx.x; i < E; i += kChunk) cnt[i] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kChunk + threadIdx.x;
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      int ex = idx[static_cast<size_t>(t) * K + k];
-      if (ex >= 0 && ex < E) atomicAdd(&cnt[ex], 1);
-    }
-  }
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (ex[k] >= 0 && ex[k] < E) atomicAdd(&cnt[ex[k]], 1);
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += kChunk)
     counts[static_cast<size_t>(blockIdx.x) * E + i] = cnt[i];
@@ -108,31 +110,27 @@ __global__ __launch_bounds__(kChunk) void assign_kernel(int T, int E, int K, int
                                                         int32_t* __restrict__ row_token,
                                                         int32_t* __restrict__ slot_row) {
   extern __shared__ uint32_t bits[];  // [E][kWords]
-  for (int i = threadIdx.x; i < E * kWords; i += kChunk) bits[i] = 0u;
-  __syncthreads();
   const int tl = threadIdx.x;
   const int t = blockIdx.x * kChunk + tl;
   const int w = tl / 32;
   const uint32_t bit = 1u << (tl % 32);
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      int ex = idx[static_cast<size_t>(t) * K + k];
-      if (ex >= 0 && ex < E) atomicOr(&bits[ex * kWords + w], bit);
-    }
-  }
-  __syncthreads();
-  if (t >= T) return;
-  // the token's ids and segment bases (and offsets) loaded before any store,
-  // so their loads are in flight together
+  // the token's K ids loaded together (before any is used)
   int exs[MOE_MAX_TOPK_DEV], bs[MOE_MAX_TOPK_DEV], os[MOE_MAX_TOPK_DEV];
 #pragma unroll
-  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
-    exs[k] = -1;
-    if (k < K) {
-      const int ex = idx[static_cast<size_t>(t) * K + k];
-      exs[k] = (ex >= 0 && ex < E) ? ex : -1;
-    }
-  }
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    exs[k] = (t < T && k < K) ? idx[static_cast<size_t>(t) * K + k] : -1;
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (exs[k] >= E) exs[k] = -1;
+  for (int i = threadIdx.x; i < E * kWords; i += kChunk) bits[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k)
+    if (exs[k] >= 0) atomicOr(&bits[exs[k] * kWords + w], bit);
+  __syncthreads();
+  if (t >= T) return;
+  // the segment bases (and offsets) loaded before any store, so their loads
+  // are in flight together
 #pragma unroll
   for (int k = 0; k < MOE_MAX_TOPK_DEV; ++k) {
     const bool ok = k < K && exs[k] >= 0;
