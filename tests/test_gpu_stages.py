@@ -391,6 +391,50 @@ def test_grouped_swiglu_skewed_groups(T, d, f, E, K, hot):
             assert rel_err(yh[lo:hi], ref[lo:hi]) <= 4 * out_tol("bf16")
 
 
+def _random_swiglu_shapes(n):
+    """n seeded shapes over the kernels' selection rules: K of 8 to 28 slices,
+    N a multiple of the column tile or not, 2 to 600 rows per expert on
+    average, 4 to 128 experts (the oracle's work kept to a few seconds); every
+    other one with both products of whole slices and column tiles."""
+    out = []
+    i = 0
+    while len(out) < n:
+        rng = np.random.default_rng(1000 + i)
+        i += 1
+        if i % 2:  # both products of whole slices and column tiles: the streaming kernels
+            d = int(rng.choice([768, 1024, 1280, 1536, 1792]))
+            f = int(rng.choice([768, 1024, 1280, 1536]))
+        else:
+            d = int(rng.choice([512, 640, 768, 896, 1024, 1280, 1536]))
+            f = int(rng.choice([256, 384, 512, 768, 1024, 1280, 1536, 2048]))
+        E = int(rng.choice([4, 8, 16, 32, 64, 128]))
+        K = int(rng.integers(1, min(8, E) + 1))
+        avg = int(rng.choice([2, 20, 80, 130, 200, 300, 600]))
+        T = max(1, avg * E // K)
+        if T * K * d * f * 6 <= 6e9:
+            out.append((T, d, f, E, K, 1000 + i - 1))
+    return out
+
+
+@pytest.mark.parametrize("T,d,f,E,K,seed", _random_swiglu_shapes(16))
+def test_grouped_swiglu_random_shapes(T, d, f, E, K, seed):
+    say(f"moe_grouped_swiglu random T={T} d={d} f={f} E={E} K={K} seed={seed}")
+    rng = np.random.default_rng(seed)
+    idx = O.biased_topk(rng.random((T, E)).astype(np.float32), None, K)
+    off, rt, _ = O.permute(idx, E)
+    x = _tokens(T, d, torch.bfloat16, seed)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, seed + 1)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(rt).to(DEV), wg, wu, wd,
+                    T * K)
+    ref = O.grouped_swiglu(host_array(x), off, rt, (host_array(wg), host_array(wu), host_array(wd)))
+    yh = to_host_f64(y)
+    assert rel_err(yh, ref) <= out_tol("bf16")
+    for i in range(E):
+        lo, hi = off[i], off[i + 1]
+        if hi > lo:
+            assert rel_err(yh[lo:hi], ref[lo:hi]) <= 4 * out_tol("bf16"), i
+
+
 @pytest.mark.parametrize("T,d,f,E,K,dtype", SWIGLU_CASES)
 def test_grouped_swiglu_parity(T, d, f, E, K, dtype):
     say(f"moe_grouped_swiglu T={T} d={d} f={f} E={E} K={K} {dtype}")
