@@ -115,7 +115,8 @@ void prof_end(int token, hipStream_t s);
 struct ProfScope {
   int tok;
   hipStream_t s;
-  ProfScope(hipStream_t st, const char* name) : tok(prof_begin(st, name)), s(st) {}
+  // name nullptr: no record (a caller's own scope covers the launch)
+  ProfScope(hipStream_t st, const char* name) : tok(name ? prof_begin(st, name) : -1), s(st) {}
   ~ProfScope() { prof_end(tok, s); }
 };
 

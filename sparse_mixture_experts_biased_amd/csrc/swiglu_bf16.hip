@@ -2194,10 +2194,11 @@ template <int BM, int BNW, int NTHR, int NSETS, bool AU>
 hipError_t launch_gateup(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
                          bool mfma_bound, const int32_t* row_index, const uint16_t* x,
                          const WeightSet& W, uint16_t* act, uint16_t* au,
-                         const SwigluWorkspace& w, hipStream_t s, int tile_rows = BM) {
+                         const SwigluWorkspace& w, hipStream_t s, int tile_rows = BM,
+                         const char* prof_name = "gateup_bf16") {
   const int max_tiles = max_tiles_for(rows, n_groups, tile_rows);
   const int nt1 = (d_ffn + BNW / 2 - 1) / (BNW / 2);
-  ProfScope prof_(s, "gateup_bf16");
+  ProfScope prof_(s, prof_name);
   if (!AU && tile_rows == kXdmaRows && BNW == 256 && wdma_shape(d_model, d_ffn, 128)) {
     hipLaunchKernelGGL((bf16_xdma_kernel<true>), dim3(stream_grid()), dim3(512), 0, s, d_model,
                        d_ffn, x_rows, rows, max_tiles, nt1, w.tiles, w.meta, row_index, x, W,
@@ -2260,6 +2261,57 @@ int products_tile_rows(int n_groups, int d_model, int d_ffn, int rows, bool au,
              : 256;
 }
 
+// Matrix-core-bound inference forms (groups of at least 256 rows on average):
+// a row tile of the LDS-fed kernel costs about as much with a few rows as
+// with 256 (its steps wait on the slice loads, not on the multiply), so each
+// group's last rows, when fewer than kSplitRows, go to a second launch of the
+// kernel that sends both operands by LDS DMA, which streams such tiles about
+// twice as fast.  Both products need whole slices and column tiles for it.
+constexpr int kSplitRows = 128;
+bool split_remainders(int n_groups, int d_model, int d_ffn, int rows, bool au, bool row_scale) {
+  // one group (a shared expert): its remainder is known here
+  if (n_groups == 1 && (rows % 256 == 0 || rows % 256 >= kSplitRows)) return false;
+  return !au && !row_scale && rows >= kDmaMinRowsPerGroup * static_cast<long>(n_groups) &&
+         stream_shape(d_model, d_ffn, 128) && stream_shape(d_ffn, d_model, 256) &&
+         wdma_shape(d_model, d_ffn, 128) && wdma_shape(d_ffn, d_model, 256) &&
+         static_cast<long long>(rows) * d_model * 2 < (1ll << 31) &&
+         static_cast<long long>(rows) * d_ffn * 2 < (1ll << 31) &&
+         max_tiles_for(rows, n_groups, 256) + n_groups <= max_tiles_for(rows, n_groups, 32);
+}
+
+// The products over the two tile lists of launch_build_split_tiles: the full
+// tiles on the LDS-fed kernel, then the remainders on the both-operands-by-DMA
+// kernel, each product's two launches timed as one.
+hipError_t launch_products_split(int n_groups, int d_model, int d_ffn, int rows, int x_rows,
+                                 const int32_t* offsets, const int32_t* row_index,
+                                 const uint16_t* x, const WeightSet& Wgu, const WeightSet& Wd,
+                                 uint16_t* y, const SwigluWorkspace& w, hipStream_t s) {
+  const int off2 = max_tiles_for(rows, n_groups, 256);
+  hipError_t err = launch_build_split_tiles(n_groups, rows, kSplitRows, off2, offsets, w, s);
+  if (err != hipSuccess) return err;
+  SwigluWorkspace w2 = w;
+  w2.tiles = w.tiles + off2;
+  w2.meta = w.meta + 2;
+  uint16_t* act = static_cast<uint16_t*>(w.act);
+  {
+    ProfScope prof_(s, "gateup_bf16");
+    err = launch_gateup<256, 256, 512, 2, false>(n_groups, d_model, d_ffn, rows, x_rows, true,
+                                                 row_index, x, Wgu, act, nullptr, w, s, 256,
+                                                 nullptr);
+    if (err != hipSuccess) return err;
+    err = launch_gateup<256, 256, 512, 2, false>(n_groups, d_model, d_ffn, rows, x_rows, true,
+                                                 row_index, x, Wgu, act, nullptr, w2, s,
+                                                 kXdmaRows, nullptr);
+    if (err != hipSuccess) return err;
+  }
+  ProfScope prof_(s, "down_bf16");
+  err = launch_down<256, 256, 512, 2>(n_groups, d_ffn, d_model, rows, true, w, act, Wd, nullptr,
+                                      y, nullptr, s, 256);
+  if (err != hipSuccess) return err;
+  return launch_down<256, 256, 512, 2>(n_groups, d_ffn, d_model, rows, true, w2, act, Wd,
+                                       nullptr, y, nullptr, s, kXdmaRows);
+}
+
 }  // namespace
 
 hipError_t launch_grouped_nt_bf16(int n_groups, int K, int N, int rows, const int32_t* offsets,
@@ -2292,6 +2344,9 @@ hipError_t launch_swiglu_bf16(int n_groups, int d_model, int d_ffn, int rows, in
                               const uint16_t* wd, const float* row_scale, uint16_t* y,
                               uint16_t* au, void* ws, hipStream_t s) {
   SwigluWorkspace w = swiglu_layout(ws, n_groups, d_ffn, rows, 2, 32);
+  if (split_remainders(n_groups, d_model, d_ffn, rows, au != nullptr, row_scale != nullptr))
+    return launch_products_split(n_groups, d_model, d_ffn, rows, x_rows, offsets, row_index, x,
+                                 WeightSet::one(wg, wu), WeightSet::one(wd, wd), y, w, s);
   const int bm = products_tile_rows(n_groups, d_model, d_ffn, rows, au != nullptr,
                                     row_scale != nullptr);
   hipError_t err = launch_build_tiles(n_groups, rows, bm, offsets, w, s);

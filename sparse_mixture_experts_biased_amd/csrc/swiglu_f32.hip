@@ -60,6 +60,66 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(int n_groups, int row
   }
 }
 
+// The split lists of launch_build_split_tiles, one workgroup: group g of m
+// rows has r = m % 256 rows past its last full 256-row tile; with 0 < r <
+// small_rows those rows form one tile of the second list, else they end the
+// first list's tiles of g as a partial tile.  Each list is in group order with
+// its own group starts.
+__global__ __launch_bounds__(1024) void build_split_tiles_kernel(
+    int n_groups, int rows, int small_rows, int off2, const int32_t* __restrict__ offsets,
+    TileInfo* __restrict__ tiles, int32_t* __restrict__ meta) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t carry1_s, carry2_s;
+  if (threadIdx.x == 0) carry1_s = carry2_s = 0;
+  __syncthreads();
+  for (int g0 = 0; g0 < n_groups; g0 += 1024) {
+    const int g = g0 + threadIdx.x;
+    int lo = 0, hi = 0, n1 = 0, n2 = 0;
+    if (g < n_groups) {
+      lo = min(max(offsets[g], 0), rows);
+      hi = min(max(offsets[g + 1], lo), rows);
+      const int m = hi - lo, full = m / 256, r = m - full * 256;
+      n2 = (r > 0 && r < small_rows) ? 1 : 0;
+      n1 = full + ((r > 0 && n2 == 0) ? 1 : 0);
+    }
+    // inclusive scans of n1, then n2
+    part[threadIdx.x] = n1;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = threadIdx.x >= static_cast<unsigned>(off) ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const int c1 = carry1_s, s1 = c1 + part[threadIdx.x] - n1, t1 = c1 + part[1023];
+    __syncthreads();
+    part[threadIdx.x] = n2;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int v = threadIdx.x >= static_cast<unsigned>(off) ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const int c2 = carry2_s, s2 = c2 + part[threadIdx.x] - n2, t2 = c2 + part[1023];
+    if (g < n_groups) {
+      for (int i = 0; i < n1; ++i)
+        tiles[s1 + i] = TileInfo{g, lo + i * 256, hi, s1, n1, {0, 0, 0}};
+      if (n2) tiles[off2 + s2] = TileInfo{g, lo + (hi - lo) / 256 * 256, hi, s2, 1, {0, 0, 0}};
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      carry1_s = t1;
+      carry2_s = t2;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    meta[0] = carry1_s;
+    meta[2] = carry2_s;
+  }
+}
+
 // ---------------------------------------------------------------- fp32 GEMM tiles
 
 constexpr int kBM = 64, kBN = 64, kBK = 16, kThreads = 256;
@@ -252,6 +312,17 @@ hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* off
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, n_groups, rows, bm,
                        max_tiles_for(rows, n_groups, bm), offsets, w.group_tile_start, w.tiles,
                        w.meta);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_build_split_tiles(int n_groups, int rows, int small_rows, int off2,
+                                    const int32_t* offsets, const SwigluWorkspace& w,
+                                    hipStream_t s) {
+  {
+    ProfScope prof_(s, "tiles");
+    hipLaunchKernelGGL(build_split_tiles_kernel, dim3(1), dim3(1024), 0, s, n_groups, rows,
+                       small_rows, off2, offsets, w.tiles, w.meta);
   }
   return hipGetLastError();
 }

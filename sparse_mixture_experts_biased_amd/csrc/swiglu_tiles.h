@@ -105,6 +105,16 @@ hipError_t launch_transpose_experts(int n, int rows, int cols, const uint16_t* s
 hipError_t launch_build_tiles(int n_groups, int rows, int bm, const int32_t* offsets,
                               const SwigluWorkspace& w, hipStream_t s);
 
+// Two tile lists for matrix-core-bound launches: 256-row tiles in w.tiles
+// (count in w.meta[0]) except each group's last rows when they are fewer than
+// small_rows, which get one tile of their own in a second list at
+// w.tiles + off2 (count in w.meta[2]), for a kernel that streams such tiles
+// faster.  off2 >= max_tiles_for(rows, n_groups, 256); w's tile array must
+// hold off2 + n_groups tiles.
+hipError_t launch_build_split_tiles(int n_groups, int rows, int small_rows, int off2,
+                                    const int32_t* offsets, const SwigluWorkspace& w,
+                                    hipStream_t s);
+
 // Routed and shared experts in one grouped launch (moe_experts_swiglu).
 // Grouped rows: the T*K routed rows (expert g on offsets[g] .. offsets[g+1]-1,
 // gathered through row_token), then shared expert j on rows T*K + j*T + t

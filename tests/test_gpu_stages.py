@@ -391,6 +391,45 @@ def test_grouped_swiglu_skewed_groups(T, d, f, E, K, hot):
             assert rel_err(yh[lo:hi], ref[lo:hi]) <= 4 * out_tol("bf16")
 
 
+# (T, d, f, E, K, hot, bump): groups of at least 256 rows on average with K and
+# N of whole slices and column tiles in both products, so each group's last
+# rows, when fewer than 128, run on the second launch over their own tile list
+# (both-operands-by-DMA kernel) and the full tiles on the LDS-fed kernel; the
+# first `hot` experts' scores raised by `bump` to mix groups of several full
+# tiles with small and empty ones
+SWIGLU_SPLIT_CASES = [
+    (1100, 1024, 768, 4, 1, 0, 0.0),      # every group: full tiles + a small remainder
+    (2100, 768, 1024, 16, 2, 4, 0.8),     # small and empty groups beside four large ones
+    (2100, 1024, 1024, 16, 2, 4, 0.6),    # small remainders, partial tiles, small groups
+    (1300, 768, 1280, 12, 3, 3, 0.45),    # mostly remainders of 128 rows or more (partial)
+    (1100, 1024, 768, 1, 1, 0, 0.0),      # one group (a shared expert's form): 4 full tiles + 76 rows
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,K,hot,bump", SWIGLU_SPLIT_CASES)
+def test_grouped_swiglu_split_remainders(T, d, f, E, K, hot, bump):
+    say(f"moe_grouped_swiglu split T={T} d={d} f={f} E={E} K={K} hot={hot}")
+    rng = np.random.default_rng(T + E + hot)
+    scores = rng.random((T, E)).astype(np.float32)
+    if hot:
+        scores[:, :hot] += bump
+    idx = O.biased_topk(scores, None, K)
+    off, rt, _ = O.permute(idx, E)
+    m = np.diff(off)
+    assert T * K >= 256 * E and np.any((m % 256 > 0) & (m % 256 < 128))
+    x = _tokens(T, d, torch.bfloat16, 80 + T)
+    wg, wu, wd = _weights(E, d, f, torch.bfloat16, 90 + E)
+    y = _swiglu_gpu(x, torch.from_numpy(off).to(DEV), torch.from_numpy(rt).to(DEV), wg, wu, wd,
+                    T * K)
+    ref = O.grouped_swiglu(host_array(x), off, rt, (host_array(wg), host_array(wu), host_array(wd)))
+    yh = to_host_f64(y)
+    assert rel_err(yh, ref) <= out_tol("bf16")
+    for i in range(E):
+        lo, hi = off[i], off[i + 1]
+        if hi > lo:
+            assert rel_err(yh[lo:hi], ref[lo:hi]) <= 4 * out_tol("bf16"), i
+
+
 def _random_swiglu_shapes(n):
     """n seeded shapes over the kernels' selection rules: K of 8 to 28 slices,
     N a multiple of the column tile or not, 2 to 600 rows per expert on
